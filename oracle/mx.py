@@ -1,0 +1,159 @@
+"""fp64 oracle of the MXFP8 backward: E4M3 elements with one e8m0 scale per 32.
+
+The pages name the formats only: MXFP8 block scaling for the expert GEMMs and a
+group-aware MXFP8 quantisation (NVIDIA article, "Optimization 1" and its list of
+Transformer Engine building blocks), and an fp8_bwd mode with a bf16 forward and an
+fp8 backward (Prime Mega MoE pages).  The element and scale encodings are the OCP
+Microscaling (MX) v1.0 ones: E4M3 "FN" (bias 7, max 448, no infinities, 0x7F/0xFF
+NaN) and E8M0 (2^(code-127)).
+
+Readings:
+* Scale rule: X = the smallest integer with amax <= 448 * 2^X (so x / 2^X never
+  saturates), clamped to [-127, 127]; an all-zero block takes X = 0 (code 127).
+* Element rounding: x / 2^X rounded to the nearest E4M3 value, ties to even; the
+  code's sign bit is the sign bit of x.
+* Blocks lie along each backward GEMM's contraction axis.  Row-wise: 32 consecutive
+  columns of a row (dY' and W_down along H; dG, dU, W_gate and W_up along I).
+  Column-wise and group-aware: 32 consecutive rows of one expert's group, the first
+  block starting at the expert's first row, a short last block padded with zeros
+  (A and w*dY' for dW_down; X and dG, dU for dW_gate, dW_up).
+* B1 quantises the unweighted dY' and applies w after the GEMM; B2 quantises w*dY'.
+  dG and dU are quantised from their unrounded values.  Outputs stay unquantised.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .moe import build_index, sigmoid, silu, _f64
+
+E4M3_MAX = 448.0
+BLOCK = 32
+
+__all__ = ["e4m3_decode", "e4m3_round", "e4m3_encode", "e8m0_exponent", "quantize_blocks",
+           "qdq_rows", "qdq_cols_grouped", "layer_backward_mx"]
+
+
+def e4m3_decode(code):
+    """Value of an E4M3 (FN) code; 0x7F and 0xFF (NaN) are returned as nan."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return s * val
+
+
+def e4m3_round(v):
+    """Nearest E4M3 value to v (|v| <= 448), ties to even, as fp64."""
+    v = _f64(v)
+    a = np.abs(v)
+    _, ex = np.frexp(a)                  # a = m * 2^ex, m in [0.5, 1)
+    e = ex - 1                           # floor(log2 a) for a > 0
+    quantum = np.where(a >= 2.0 ** -6, np.exp2(np.maximum(e, -6) - 3.0), 2.0 ** -9)
+    return np.rint(v / quantum) * quantum
+
+
+def e4m3_encode(v):
+    """E4M3 code of a value already on the E4M3 grid (|v| <= 448); sign from signbit."""
+    v = _f64(v)
+    sign = np.signbit(v).astype(np.int64) << 7
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    e = ex - 1
+    normal = a >= 2.0 ** -6
+    mant_n = np.where(normal, a / np.exp2(np.where(normal, e, 0)) * 8.0 - 8.0, 0.0)
+    code_n = ((e + 7) << 3) + mant_n.astype(np.int64)
+    code_s = (a / 2.0 ** -9).astype(np.int64)
+    return (sign | np.where(normal, code_n, code_s)).astype(np.uint8)
+
+
+def e8m0_exponent(amax):
+    """Smallest X with amax <= 448 * 2^X, clamped to [-127, 127]; 0 for amax == 0."""
+    a = _f64(amax)
+    _, ex = np.frexp(np.where(a > 0, a / E4M3_MAX, 1.0))
+    X = ex - 1                                          # 2^X <= a/448 < 2^(X+1)
+    X = np.where(a > np.ldexp(E4M3_MAX, X), X + 1, X)   # exact comparison
+    X = np.where(a > np.ldexp(E4M3_MAX, X), X + 1, X)
+    X = np.where(a == 0, 0, X)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def quantize_blocks(blocks):
+    """Quantise an array [..., 32] block by block along the last axis.
+
+    Returns (codes uint8 [..., 32], scale codes uint8 [...], dequantised fp64)."""
+    b = _f64(blocks)
+    X = e8m0_exponent(np.max(np.abs(b), axis=-1))
+    scaled = b / np.exp2(X)[..., None]
+    q = e4m3_round(scaled)
+    codes = e4m3_encode(np.where(q == 0, np.copysign(0.0, scaled), q))
+    deq = q * np.exp2(X)[..., None]
+    return codes, (X + 127).astype(np.uint8), deq
+
+
+def qdq_rows(m):
+    """Row-wise MX quantize-dequantize of a matrix [M, K] (K % 32 == 0)."""
+    m = _f64(m)
+    M, K = m.shape
+    _, _, deq = quantize_blocks(m.reshape(M, K // BLOCK, BLOCK))
+    return deq.reshape(M, K)
+
+
+def qdq_cols_grouped(m, offsets):
+    """Column-wise MX quantize-dequantize of a ragged [R, N] matrix: 32-row blocks
+    that start at each group's first row; a short last block is padded with zeros."""
+    m = _f64(m)
+    out = np.zeros_like(m)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for r0 in range(lo, hi, BLOCK):
+            r1 = min(r0 + BLOCK, hi)
+            blk = np.zeros((BLOCK, m.shape[1]))
+            blk[: r1 - r0] = m[r0:r1]
+            _, _, deq = quantize_blocks(blk.T)          # [N, 32]
+            out[r0:r1] = deq.T[: r1 - r0]
+    return out
+
+
+def layer_backward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, topk_w, saved):
+    """The backward with the eight backward-GEMM operands quantize-dequantized to
+    MXFP8 at the points listed in the module docstring; fp64 everywhere else."""
+    index = saved["index"]
+    x = _f64(inp["x"]); dy = _f64(inp["dy"])
+    T, H = x.shape
+    I = inp["w_gate"].shape[2]
+    wflat = _f64(topk_w).reshape(-1)
+    dX = np.zeros((T, H))
+    dWg = np.zeros((e_local, H, I)); dWu = np.zeros((e_local, H, I)); dWd = np.zeros((e_local, I, H))
+    d_topk_w = np.zeros(T * k)
+    for e in range(e_local):
+        lo, hi = int(index["offsets"][e]), int(index["offsets"][e + 1])
+        if hi == lo:
+            continue
+        rows = index["row_src"][lo:hi]
+        tok = rows // k
+        we = wflat[rows]
+        g, u, a = saved["G"][lo:hi], saved["U"][lo:hi], saved["A"][lo:hi]
+        wg = _f64(inp["w_gate"][e]); wu = _f64(inp["w_up"][e]); wd = _f64(inp["w_down"][e])
+        xe, dye = x[tok], dy[tok]
+        seg = np.array([0, hi - lo])
+        # B1: dA' = Q(dY') Q(Wd)^T, both row-wise along H
+        dap = qdq_rows(dye) @ qdq_rows(wd).T
+        d_w = np.sum(dap * a, axis=1)
+        da = we[:, None] * dap
+        s = sigmoid(g)
+        du = da * g * s
+        dg = da * u * s * (1.0 + g * (1.0 - s))
+        # B2: dWd = Q_col(A)^T Q_col(w dY')
+        dWd[e] = qdq_cols_grouped(a, seg).T @ qdq_cols_grouped(we[:, None] * dye, seg)
+        # B3: dXp = Q(dG) Q(Wg)^T + Q(dU) Q(Wu)^T, row-wise along I
+        dxe = qdq_rows(dg) @ qdq_rows(wg).T + qdq_rows(du) @ qdq_rows(wu).T
+        # B4: dWg = Q_col(X)^T Q_col(dG), dWu = Q_col(X)^T Q_col(dU)
+        qx = qdq_cols_grouped(xe, seg)
+        dWg[e] = qx.T @ qdq_cols_grouped(dg, seg)
+        dWu[e] = qx.T @ qdq_cols_grouped(du, seg)
+        dX[tok] += dxe
+        d_topk_w[rows] = d_w
+    return {"dx": dX, "dw_gate": dWg, "dw_up": dWu, "dw_down": dWd,
+            "d_topk_w": d_topk_w.reshape(T, k)}
