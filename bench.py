@@ -1,0 +1,195 @@
+"""Benchmark: dropless MoE layer forward + backward on one MI355X.
+
+One step = one pass of the whole hot path over one batch: top-k routing, dispatch
+(index build), gate/up GEMM + SwiGLU, down GEMM, combine, and the backward (dA GEMM +
+SwiGLU backward, dW_down, dX GEMM, dW_gate/dW_up, unpermute-sum, router backward).
+Inputs are seeded synthetic tensors of the Qwen3-30B-A3B MoE layer shape (T=4096
+tokens, H=2048, I=768, 128 experts, top-8, Gaussian router logits) already resident
+in HBM.  value = algorithmic TFLOP/s of the step (6RHI forward + 12RHI backward over
+the R routed rows; tile padding is not counted).
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+WORKLOAD = "qwen3_30b"
+
+
+def kernel_work(name, T, H, I, k, R, El):
+    """Algorithmic bytes and flops of one launch of a hot-path kernel (bf16 data).
+
+    Per routed row and per expert weights, as in the design notes: each kernel's
+    bytes are the operands it must read and the results it must write once."""
+    b = 2
+    W_gu = 2 * El * H * I * b
+    W_d = El * I * H * b
+    row_h, row_i, row_2i = R * H * b, R * I * b, R * 2 * I * b
+    table = {
+        "fwd_gateup": (row_h + W_gu + row_2i + row_i, 4.0 * R * H * I),
+        "fwd_down": (row_i + W_d + row_h, 2.0 * R * H * I),
+        "bwd_dA": (row_h + W_d + row_2i + row_i + row_2i, 2.0 * R * H * I),
+        "bwd_dWd": (row_i + row_h + W_d, 2.0 * R * H * I),
+        "bwd_dX": (row_2i + W_gu + row_h, 4.0 * R * H * I),
+        "bwd_dWgu": (row_h + row_2i + W_gu, 4.0 * R * H * I),
+        "gather": (T * H * b + row_h, 0.0),
+        "combine": (row_h + T * H * b, 0.0),
+        "unpermute_dx": (row_h + T * H * b, 0.0),
+    }
+    return table.get(name, (0.0, 0.0))
+
+
+def cpu_baseline(cfg, inp, budget_s=15.0):
+    """The oracle as it stands, on the host cores, over a bounded sample: routing and
+    index for all tokens, then forward + backward of whole experts (all their rows) in
+    order until the time budget is spent."""
+    from oracle import moe as om
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = min(16, os.cpu_count() or 1)
+        ctx = threadpool_limits(limits=limit)
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        ctx = None
+    try:
+        t0 = time.perf_counter()
+        idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
+        ix = om.build_index(idx, cfg.e_begin, cfg.e_local)
+        rows_done = 0
+        n_exp = 0
+        for e in range(cfg.e_local):
+            om.expert_sample(inp, cfg.k, ix, w, [e])        # forward + backward of expert e
+            rows_done += int(ix["counts"][e])
+            n_exp += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    flops = 18.0 * rows_done * cfg.H * cfg.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or 1, "kind": "oracle",
+            "sample": f"fp64 numpy oracle: routing + index of all {cfg.T} tokens, then forward+backward of "
+                      f"{n_exp} of {cfg.e_local} experts ({rows_done} of {int(ix['counts'].sum())} rows) "
+                      f"in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              f"(the path is single-GPU: no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import combine_top_router_amd.lib as L
+    from combine_top_router_amd.layer import MoeLayer
+
+    cfg = wl.CONFIGS[WORKLOAD]
+    inp = wl.make_inputs(cfg)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    x, wg, wu, wd, dy = t(inp["x"]), t(inp["w_gate"]), t(inp["w_up"]), t(inp["w_down"]), t(inp["dy"])
+    layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.forward(logits, x, wg, wu, wd, stream)
+        layer.backward(dy, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    R = int(layer.offsets[-1].item())
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+
+    # per-kernel durations from HIP events recorded inside the library on the launch stream
+    L.moe_timing_enable(True)
+    per = {}
+    for _ in range(max(3, min(args.steps, 10))):
+        step()
+        for name, kms in L.moe_timing_read():
+            per.setdefault(name, []).append(kms)
+    L.moe_timing_enable(False)
+    kernels = {}
+    for name, v in per.items():
+        avg = float(np.mean(v))
+        byts, flops = kernel_work(name, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)
+        kernels[name] = {"ms": round(avg, 4), "launches_per_step": len(v) // max(1, len(per["route_topk"])),
+                         "GB/s": round(byts / avg / 1e6, 1) if byts else None,
+                         "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None}
+    gemm = {n: kernels[n] for n in ("fwd_gateup", "fwd_down", "bwd_dA", "bwd_dWd", "bwd_dX", "bwd_dWgu")
+            if n in kernels}
+    dom = max(gemm, key=lambda n: gemm[n]["ms"])
+    byts, flops = kernel_work(dom, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)
+    avg_ms = gemm[dom]["ms"]
+    achieved = byts / avg_ms / 1e6
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": int(byts), "avg_ms": avg_ms,
+                "mfma_frac": round(flops / avg_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+
+    flops_step = 18.0 * R * cfg.H * cfg.I
+    fwd_names = ("route_topk", "index_hist", "index_scan", "index_rank", "tile_table", "fwd_gateup", "fwd_down",
+                 "combine")
+    fwd_ms = sum(v["ms"] * v["launches_per_step"] for n, v in kernels.items() if n in fwd_names)
+    gemm_ms = sum(v["ms"] * v["launches_per_step"] for n, v in gemm.items())
+    out = {
+        "metric": "MoE layer fwd+bwd ms & TFLOPS at Qwen3-30B-A3B shape, 1 MI355X; % MFMA peak",
+        "value": round(flops_step / ms / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B MoE layer, one GPU: T=4096 H=2048 I=768 E=128 top-8, "
+                               "Gaussian router logits, bf16", "T": cfg.T, "H": cfg.H, "I": cfg.I,
+                   "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
+        "mfma_frac_step": round(flops_step / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "mfma_frac_gemms": round(flops_step / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "fwd_ms_kernels": round(fwd_ms, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del layer, x, wg, wu, wd, dy, logits
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

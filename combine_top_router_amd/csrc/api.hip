@@ -1,0 +1,355 @@
+// Host entry points of libmoe: argument checks, workspace layout and launch order.
+// The declarations and their contracts are in include/moe.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+int bwd_bf16_nparts(int I);
+}
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  int64_t R_cap;
+  size_t es;         // element size of the data dtype
+  int max_tiles;     // row-group tile bound
+  int nparts;        // rowdot partials per row
+  int nchunks;
+  // saved
+  size_t off_gu, off_a, saved_bytes;
+  // scratch
+  size_t off_tiles, off_dgu, off_dxp, off_part, scratch_bytes;
+};
+
+int check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_EINVAL, "shape is NULL");
+  if (s->T < 0) return fail(MOE_EINVAL, "T = %d < 0", s->T);
+  if (s->H <= 0 || s->I <= 0) return fail(MOE_EINVAL, "H = %d and I = %d must be > 0", s->H, s->I);
+  if (s->E < 1 || s->E > 1024) return fail(MOE_EINVAL, "E = %d outside 1..1024", s->E);
+  if (s->k < 1 || s->k > s->E || s->k > 16) return fail(MOE_EINVAL, "k = %d outside 1..min(E, 16)", s->k);
+  if (s->e_local < 1 || s->e_begin < 0 || (int64_t)s->e_begin + s->e_local > s->E)
+    return fail(MOE_EINVAL, "local experts [%d, %d + %d) outside [0, E = %d)", s->e_begin, s->e_begin,
+                s->e_local, s->E);
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_EINVAL, "dtype = %d", s->dtype);
+  if (s->bwd != MOE_BWD_SAME && s->bwd != MOE_BWD_MXFP8) return fail(MOE_EINVAL, "bwd = %d", s->bwd);
+  if (s->renorm != 0 && s->renorm != 1) return fail(MOE_EINVAL, "renorm = %d", s->renorm);
+  if ((int64_t)s->T * s->k > 0x7fffffffLL) return fail(MOE_EINVAL, "T * k exceeds 2^31 - 1");
+  if (s->dtype == MOE_BF16 && (s->H % 64 != 0 || s->I % 64 != 0))
+    return fail(MOE_EINVAL, "bf16 needs H and I multiples of 64 (H = %d, I = %d)", s->H, s->I);
+  if (s->dtype == MOE_F32 && s->H % 4 != 0) return fail(MOE_EINVAL, "fp32 needs H a multiple of 4 (H = %d)", s->H);
+  if (s->bwd == MOE_BWD_MXFP8 && s->dtype != MOE_BF16)
+    return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs bf16 data");
+  return MOE_OK;
+}
+
+void layout(const moe_shape& s, Layout& L) {
+  const int El = s.e_local;
+  L.R_cap = (int64_t)s.T * (s.k < El ? s.k : El);
+  L.es = s.dtype == MOE_BF16 ? 2 : 4;
+  L.max_tiles = (int)ceil_div(L.R_cap, kGemmBM) + El;
+  L.nparts = s.dtype == MOE_BF16 ? bwd_bf16_nparts(s.I) : s.I;
+  L.nchunks = (int)ceil_div((int64_t)s.T * s.k, kSlotChunk);
+  const size_t R = (size_t)L.R_cap;
+  L.off_gu = 0;
+  L.off_a = align_up(R * 2 * s.I * L.es);
+  L.saved_bytes = L.off_a + align_up(R * s.I * L.es);
+  const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
+  L.off_tiles = 0;
+  L.off_dgu = align_up((size_t)(1 + 2 * L.max_tiles) * 4);
+  L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
+  L.off_part = L.off_dxp + align_up(R * s.H * L.es);
+  const size_t bwd_bytes = L.off_part + align_up(R * L.nparts * 4);
+  L.scratch_bytes = bwd_bytes > dispatch_bytes ? bwd_bytes : dispatch_bytes;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off); }
+template <typename T>
+const T* at(const void* base, size_t off) { return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off); }
+
+// ---- opt-in per-kernel timing of this host thread ----
+struct TimingRec {
+  const char* name;
+  int e0, e1;
+};
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  int used = 0;
+  std::vector<TimingRec> recs;
+  hipEvent_t next() {
+    if (used == (int)pool.size()) {
+      hipEvent_t ev = nullptr;
+      if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+      pool.push_back(ev);
+    }
+    return pool[used++];
+  }
+};
+thread_local Timing g_timing;
+
+#define REQUIRE(p) do { if (!(p)) return fail(MOE_EINVAL, "%s: %s is NULL", __func__, #p); } while (0)
+#define REQUIRE_WS(p) do { if (!(p)) return fail(MOE_EWORKSPACE, "%s: workspace %s is NULL", __func__, #p); } while (0)
+
+}  // namespace
+
+namespace moe {
+void ktimer_begin(const char* name, hipStream_t st) {
+  Timing& T = g_timing;
+  if (!T.on) return;
+  hipEvent_t ev = T.next();
+  if (!ev) return;
+  hipEventRecord(ev, st);
+  T.recs.push_back({name, T.used - 1, -1});
+}
+void ktimer_end(hipStream_t st) {
+  Timing& T = g_timing;
+  if (!T.on || T.recs.empty() || T.recs.back().e1 >= 0) return;
+  hipEvent_t ev = T.next();
+  if (!ev) return;
+  hipEventRecord(ev, st);
+  T.recs.back().e1 = T.used - 1;
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_timing_enable(int on) {
+  g_timing.on = on != 0;
+  g_timing.used = 0;
+  g_timing.recs.clear();
+  return MOE_OK;
+}
+
+int moe_timing_read(int capacity, const char** names, float* ms, int* count) {
+  REQUIRE(count);
+  Timing& T = g_timing;
+  *count = (int)T.recs.size();
+  if (capacity > 0) {
+    REQUIRE(names);
+    REQUIRE(ms);
+  }
+  int rc = MOE_OK;
+  if (!T.recs.empty()) {
+    hipError_t e = hipEventSynchronize(T.pool[T.used - 1]);
+    if (e != hipSuccess) rc = hip_status(e, __func__);
+    for (int i = 0; i < (int)T.recs.size() && i < capacity && rc == MOE_OK; ++i) {
+      names[i] = T.recs[i].name;
+      ms[i] = 0.f;
+      if (T.recs[i].e1 >= 0) hipEventElapsedTime(&ms[i], T.pool[T.recs[i].e0], T.pool[T.recs[i].e1]);
+    }
+  }
+  T.used = 0;
+  T.recs.clear();
+  return rc;
+}
+
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_workspace_bytes(const moe_shape* shape, size_t* saved_bytes, size_t* scratch_bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE(saved_bytes);
+  REQUIRE(scratch_bytes);
+  Layout L;
+  layout(*shape, L);
+  *saved_bytes = L.saved_bytes;
+  *scratch_bytes = L.scratch_bytes;
+  return MOE_OK;
+}
+
+int moe_route_topk(const moe_shape* shape, const float* logits, int32_t* topk_idx, float* topk_w,
+                   void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (shape->T == 0) return MOE_OK;
+  REQUIRE(logits);
+  REQUIRE(topk_idx);
+  REQUIRE(topk_w);
+  return hip_status(launch_route_topk(*shape, logits, topk_idx, topk_w, (hipStream_t)stream), __func__);
+}
+
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                 int32_t* offsets, int32_t* row_src, int32_t* row_of, void* xp, void* scratch,
+                 void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE(counts);
+  REQUIRE(offsets);
+  REQUIRE_WS(scratch);
+  if (shape->T > 0) {
+    REQUIRE(topk_idx);
+    REQUIRE(row_src);
+    REQUIRE(row_of);
+    if (xp) REQUIRE(x);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_index(*shape, topk_idx, counts, offsets, row_src, row_of, (int32_t*)scratch, st);
+  if (e == hipSuccess && xp && shape->T > 0) e = launch_gather(*shape, x, offsets, row_src, xp, st);
+  return hip_status(e, __func__);
+}
+
+int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t* offsets,
+            const int32_t* row_src, const float* topk_w, const void* w_gate, const void* w_up,
+            const void* w_down, void* yp, void* saved, void* scratch, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const moe_shape& s = *shape;
+  REQUIRE(offsets);
+  REQUIRE(w_gate);
+  REQUIRE(w_up);
+  REQUIRE(w_down);
+  REQUIRE_WS(saved);
+  REQUIRE_WS(scratch);
+  if (s.T == 0) return MOE_OK;
+  REQUIRE(row_src);
+  REQUIRE(topk_w);
+  REQUIRE(yp);
+  if (!xp) REQUIRE(x);
+  Layout L;
+  layout(s, L);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (s.dtype == MOE_BF16) {
+    int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
+    e = launch_tile_table(s, offsets, kGemmBM, tiles, st);
+    if (e != hipSuccess) return hip_status(e, __func__);
+    FwdArgs a{};
+    a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
+    a.x = (const bf16_t*)x; a.xp = (const bf16_t*)xp; a.offsets = offsets; a.row_src = row_src;
+    a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up; a.wd = (const bf16_t*)w_down;
+    a.tiles = tiles; a.max_tiles = L.max_tiles;
+    a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a); a.yp = (bf16_t*)yp;
+    e = launch_fwd_bf16(a, st);
+  } else {
+    FwdArgsF32 a{};
+    a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
+    a.x = (const float*)x; a.xp = (const float*)xp; a.offsets = offsets; a.row_src = row_src;
+    a.topk_w = topk_w; a.wg = (const float*)w_gate; a.wu = (const float*)w_up; a.wd = (const float*)w_down;
+    a.tiles = nullptr; a.max_tiles = L.max_tiles;
+    a.gu = at<float>(saved, L.off_gu); a.a = at<float>(saved, L.off_a); a.yp = (float*)yp;
+    e = launch_fwd_f32(a, st);
+  }
+  return hip_status(e, __func__);
+}
+
+int moe_combine(const moe_shape* shape, const void* yp, const int32_t* row_of, void* y, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (shape->T == 0) return MOE_OK;
+  REQUIRE(yp);
+  REQUIRE(row_of);
+  REQUIRE(y);
+  return hip_status(launch_combine(*shape, yp, row_of, y, (hipStream_t)stream), __func__);
+}
+
+int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* xp, const int32_t* offsets,
+            const int32_t* row_src, const int32_t* row_of, const float* topk_w, const void* w_gate,
+            const void* w_up, const void* w_down, const void* saved, void* dx, void* dw_gate, void* dw_up,
+            void* dw_down, float* d_topk_w, void* scratch, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const moe_shape& s = *shape;
+  if (s.bwd == MOE_BWD_MXFP8) return fail(MOE_EUNSUPPORTED, "the MXFP8 backward is not available in this build");
+  REQUIRE(offsets);
+  REQUIRE(w_gate);
+  REQUIRE(w_up);
+  REQUIRE(w_down);
+  REQUIRE(dw_gate);
+  REQUIRE(dw_up);
+  REQUIRE(dw_down);
+  REQUIRE_WS(saved);
+  REQUIRE_WS(scratch);
+  if (s.T > 0) {
+    REQUIRE(dy);
+    REQUIRE(row_src);
+    REQUIRE(row_of);
+    REQUIRE(topk_w);
+    REQUIRE(dx);
+    REQUIRE(d_topk_w);
+    if (!xp) REQUIRE(x);
+  }
+  Layout L;
+  layout(s, L);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (s.dtype == MOE_BF16) {
+    int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
+    e = launch_tile_table(s, offsets, kGemmBM, tiles, st);
+    if (e != hipSuccess) return hip_status(e, __func__);
+    BwdArgs a{};
+    a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
+    a.dy = (const bf16_t*)dy; a.x = (const bf16_t*)x; a.xp = (const bf16_t*)xp; a.offsets = offsets;
+    a.row_src = row_src; a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up;
+    a.wd = (const bf16_t*)w_down; a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a);
+    a.tiles = tiles; a.max_tiles = L.max_tiles;
+    a.dgu = at<bf16_t>(scratch, L.off_dgu); a.dxp = at<bf16_t>(scratch, L.off_dxp);
+    a.dw_part = at<float>(scratch, L.off_part);
+    a.dwg = (bf16_t*)dw_gate; a.dwu = (bf16_t*)dw_up; a.dwd = (bf16_t*)dw_down;
+    e = launch_bwd_bf16(a, st);
+    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st);
+    if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
+  } else {
+    BwdArgsF32 a{};
+    a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
+    a.dy = (const float*)dy; a.x = (const float*)x; a.xp = (const float*)xp; a.offsets = offsets;
+    a.row_src = row_src; a.topk_w = topk_w; a.wg = (const float*)w_gate; a.wu = (const float*)w_up;
+    a.wd = (const float*)w_down; a.gu = at<float>(saved, L.off_gu); a.a = at<float>(saved, L.off_a);
+    a.tiles = nullptr; a.max_tiles = L.max_tiles;
+    a.dgu = at<float>(scratch, L.off_dgu); a.dxp = at<float>(scratch, L.off_dxp);
+    a.dw_part = at<float>(scratch, L.off_part);
+    a.dwg = (float*)dw_gate; a.dwu = (float*)dw_up; a.dwd = (float*)dw_down;
+    e = launch_bwd_f32(a, st);
+    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st);
+    if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
+  }
+  return hip_status(e, __func__);
+}
+
+int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
+                       const float* topk_w, const float* d_topk_w, float* d_logits, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (shape->T == 0) return MOE_OK;
+  REQUIRE(topk_idx);
+  REQUIRE(topk_w);
+  REQUIRE(d_topk_w);
+  REQUIRE(d_logits);
+  if (!shape->renorm) REQUIRE(logits);
+  return hip_status(
+      launch_route_bwd(*shape, logits, topk_idx, topk_w, d_topk_w, d_logits, (hipStream_t)stream), __func__);
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// Internal helpers shared by the HIP kernels and the host entry points of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct elem;
+template <> struct elem<float> {
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct elem<bf16_t> {
+  __device__ static float load(const bf16_t* p) { return bf2f(*p); }
+  __device__ static void store(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// Host-side: the launch configuration constants shared by the host code and kernels.
+constexpr int kGemmBM = 128;     // rows of one row-group GEMM tile (bf16 path)
+constexpr int kGemmBN = 128;     // columns of one GEMM tile (bf16 path)
+constexpr int kSimtBM = 32;      // rows of one fp32 row-group tile
+constexpr int kSlotChunk = 4096; // (token, slot) pairs per histogram chunk
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Opt-in per-kernel timing of the calling host thread (moe_timing_enable): a pair of
+// HIP events recorded on the launch stream around each kernel.
+void ktimer_begin(const char* name, hipStream_t st);
+void ktimer_end(hipStream_t st);
+struct KTimer {
+  hipStream_t st;
+  KTimer(const char* name, hipStream_t s) : st(s) { ktimer_begin(name, s); }
+  ~KTimer() { ktimer_end(st); }
+};
+#define MOE_LAUNCH(name, kernel, grid, block, shmem, st, ...)              \
+  do {                                                                     \
+    ::moe::KTimer moe_kt_(name, st);                                       \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);       \
+  } while (0)
+
+// ---- launch wrappers (defined in the .hip files) ----
+hipError_t launch_route_topk(const moe_shape& s, const float* logits, int32_t* idx, float* w,
+                             hipStream_t st);
+hipError_t launch_route_bwd(const moe_shape& s, const float* logits, const int32_t* idx,
+                            const float* w, const float* dw, float* dlogits, hipStream_t st);
+hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                        int32_t* row_src, int32_t* row_of, int32_t* chunk_hist, hipStream_t st);
+hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
+                             hipStream_t st);
+hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offsets,
+                         const int32_t* row_src, void* xp, hipStream_t st);
+hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
+                          hipStream_t st, const char* name = "combine");
+hipError_t launch_dtopk(const moe_shape& s, const float* dw_part, int nparts, const int32_t* row_of,
+                        float* d_topk_w, hipStream_t st);
+
+// bf16 MFMA grouped GEMMs
+struct FwdArgs {
+  int T, H, I, k, El;
+  const bf16_t* x;        // [T, H]
+  const bf16_t* xp;       // [R_cap, H] or null (gather through row_src)
+  const int32_t* offsets; // [El + 1]
+  const int32_t* row_src; // [R_cap]
+  const float* topk_w;    // [T, k]
+  const bf16_t* wg;       // [El, H, I]
+  const bf16_t* wu;
+  const bf16_t* wd;       // [El, I, H]
+  const int32_t* tiles;   // row-group tile table
+  int max_tiles;
+  bf16_t* gu;             // [R_cap, 2I]  (g | u)
+  bf16_t* a;              // [R_cap, I]
+  bf16_t* yp;             // [R_cap, H]
+};
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+
+struct BwdArgs {
+  int T, H, I, k, El;
+  const bf16_t* dy;       // [T, H]
+  const bf16_t* x;
+  const bf16_t* xp;       // or null
+  const int32_t* offsets;
+  const int32_t* row_src;
+  const float* topk_w;
+  const bf16_t* wg;
+  const bf16_t* wu;
+  const bf16_t* wd;
+  const bf16_t* gu;       // saved
+  const bf16_t* a;        // saved
+  const int32_t* tiles;
+  int max_tiles;
+  bf16_t* dgu;            // scratch [R_cap, 2I]
+  bf16_t* dxp;            // scratch [R_cap, H]
+  float* dw_part;         // scratch [R_cap, I / 64]
+  bf16_t* dwg;            // [El, H, I]
+  bf16_t* dwu;
+  bf16_t* dwd;            // [El, I, H]
+};
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
+
+// fp32 (SIMT) grouped GEMMs: the same chain in fp32 arithmetic
+struct FwdArgsF32 {
+  int T, H, I, k, El;
+  const float* x; const float* xp; const int32_t* offsets; const int32_t* row_src;
+  const float* topk_w; const float* wg; const float* wu; const float* wd;
+  const int32_t* tiles; int max_tiles;
+  float* gu; float* a; float* yp;
+};
+hipError_t launch_fwd_f32(const FwdArgsF32& a, hipStream_t st);
+struct BwdArgsF32 {
+  int T, H, I, k, El;
+  const float* dy; const float* x; const float* xp; const int32_t* offsets; const int32_t* row_src;
+  const float* topk_w; const float* wg; const float* wu; const float* wd;
+  const float* gu; const float* a; const int32_t* tiles; int max_tiles;
+  float* dgu; float* dxp; float* dw_part;
+  float* dwg; float* dwu; float* dwd;
+};
+hipError_t launch_bwd_f32(const BwdArgsF32& a, hipStream_t st);
+
+}  // namespace moe

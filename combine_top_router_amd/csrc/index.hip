@@ -1,0 +1,293 @@
+// Dispatch index build, row gather, combine / unpermute-sum and the d_topk_w gather.
+//
+// Dispatch permutes tokens by expert and combine returns the per-expert results to
+// token order, accumulating them (NVIDIA DeepSeek-V3 MoE article, "Optimization 2",
+// and its Figure 3).  Expert counts stay on the device, so that no device-to-host
+// copy sits on the critical path (same article, "Optimization 1").
+//
+// The permutation is a stable counting sort of the (token, slot) ids by local expert:
+// 1) per-chunk expert histograms, 2) a column scan over chunks giving each chunk's
+// base position inside every expert group plus counts and offsets, 3) in-chunk ranks
+// from wavefront ballots (no atomic ordering), so the row order is deterministic:
+// expert-major, then token-ascending.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ idx, int TK, int e_begin,
+                                              int El, int32_t* __restrict__ chunk_hist) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < El; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * kSlotChunk;
+  const int s1 = min(TK, s0 + kSlotChunk);
+  for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
+    int e = idx[s] - e_begin;
+    if (e >= 0 && e < El) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += blockDim.x) chunk_hist[(size_t)blockIdx.x * El + e] = hist[e];
+}
+
+// One block of 1024 threads: column scan over chunks, counts and offsets.
+__global__ __launch_bounds__(1024) void k_scan(int nchunks, int El, int32_t* __restrict__ chunk_hist,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets) {
+  __shared__ int32_t buf[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < El) {
+    for (int c = 0; c < nchunks; ++c) {
+      int v = chunk_hist[(size_t)c * El + e];
+      chunk_hist[(size_t)c * El + e] = total;
+      total += v;
+    }
+    counts[e] = total;
+  }
+  buf[e] = e < El ? total : 0;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    int v = e >= off ? buf[e - off] : 0;
+    __syncthreads();
+    buf[e] += v;
+    __syncthreads();
+  }
+  if (e < El) offsets[e + 1] = buf[e];
+  if (e == 0) offsets[0] = 0;
+}
+
+// Ranks within each chunk, 256 slots per step; wave w of the block takes slots
+// [64w, 64w + 64) of the step, and the waves' per-expert counts are combined in order.
+__global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, int TK, int e_begin,
+                                              int El, int ebits, const int32_t* __restrict__ chunk_hist,
+                                              const int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ row_src,
+                                              int32_t* __restrict__ row_of) {
+  extern __shared__ int32_t sm[];
+  int32_t* base = sm;            // [El]: next free row of expert e for this chunk
+  int32_t* cnt = sm + El;        // [4][El]: per-wave counts of the current step
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < El; e += 256) {
+    base[e] = offsets[e] + chunk_hist[(size_t)blockIdx.x * El + e];
+    cnt[e] = cnt[El + e] = cnt[2 * El + e] = cnt[3 * El + e] = 0;
+  }
+  __syncthreads();
+  const int s0 = blockIdx.x * kSlotChunk;
+  const int s1 = min(TK, s0 + kSlotChunk);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int step = s0; step < s1; step += 256) {
+    const int s = step + tid;
+    int e = -1;
+    if (s < s1) {
+      e = idx[s] - e_begin;
+      if (e < 0 || e >= El) {
+        row_of[s] = -1;
+        e = -1;
+      }
+    }
+    const bool valid = e >= 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    const int tot = __popcll(peers);
+    if (valid && rank == 0) cnt[wv * El + e] = tot;
+    __syncthreads();
+    if (valid) {
+      int pos = base[e] + rank;
+      for (int w2 = 0; w2 < wv; ++w2) pos += cnt[w2 * El + e];
+      row_src[pos] = s;
+      row_of[s] = pos;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&base[e], tot);
+      cnt[wv * El + e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// Tile table of the row-group GEMMs: tiles[0] = number of tiles; entry i at
+// tiles[1 + 2i] = expert, tiles[2 + 2i] = first row of the tile inside the expert.
+__global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
+                                                     int32_t* __restrict__ tiles) {
+  __shared__ int32_t buf[1024];
+  const int e = threadIdx.x;
+  int n = 0;
+  if (e < El) n = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  buf[e] = n;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int v = e >= off ? buf[e - off] : 0;
+    __syncthreads();
+    buf[e] += v;
+    __syncthreads();
+  }
+  const int start = buf[e] - n;
+  for (int j = 0; j < n; ++j) {
+    tiles[1 + 2 * (start + j)] = e;
+    tiles[2 + 2 * (start + j)] = j * bm;
+  }
+  if (e == 1023) tiles[0] = buf[1023];
+}
+
+// xp[r] = x[row_src[r] / k]: one wave per row, 16-byte vectors.
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather(const T* __restrict__ x, int H, int k,
+                                                const int32_t* __restrict__ offsets, int El,
+                                                const int32_t* __restrict__ row_src, int R_cap,
+                                                T* __restrict__ xp) {
+  const int R = offsets[El];
+  const int lane = threadIdx.x & 63;
+  const int nvec = H * (int)sizeof(T) / 16;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4) {
+    const int t = row_src[r] / k;
+    const i32x4* src = reinterpret_cast<const i32x4*>(x + (size_t)t * H);
+    i32x4* dst = reinterpret_cast<i32x4*>(xp + (size_t)r * H);
+    for (int c = lane; c < nvec; c += 64) dst[c] = src[c];
+  }
+}
+
+// out[t] = sum_j rows[row_of[t*k + j]] in fp32, one rounding; 0 with no local slot.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ rows, int T_, int H, int k,
+                                                 const int32_t* __restrict__ row_of,
+                                                 T* __restrict__ out);
+
+template <>
+__global__ __launch_bounds__(256) void k_combine<bf16_t>(const bf16_t* __restrict__ rows, int T_, int H,
+                                                         int k, const int32_t* __restrict__ row_of,
+                                                         bf16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int my_r = lane < k ? row_of[(size_t)t * k + lane] : -1;
+  int rr[16];  // the token's rows, broadcast while every lane is active (k <= 16)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rr[j] = __shfl(my_r, j, 64);
+  const int nvec = H / 8;
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = rr[j];
+      if (j >= k || r < 0) continue;
+      const i32x4 v = reinterpret_cast<const i32x4*>(rows + (size_t)r * H)[c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(((uint32_t)v[q]) << 16);
+        acc[2 * q + 1] += __uint_as_float(((uint32_t)v[q]) & 0xffff0000u);
+      }
+    }
+    i32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (int)((uint32_t)f2bf(acc[2 * q]) | ((uint32_t)f2bf(acc[2 * q + 1]) << 16));
+    reinterpret_cast<i32x4*>(out + (size_t)t * H)[c] = o;
+  }
+}
+
+template <>
+__global__ __launch_bounds__(256) void k_combine<float>(const float* __restrict__ rows, int T_, int H, int k,
+                                                        const int32_t* __restrict__ row_of,
+                                                        float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int my_r = lane < k ? row_of[(size_t)t * k + lane] : -1;
+  int rr[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rr[j] = __shfl(my_r, j, 64);
+  const int nvec = H / 4;
+  for (int c = lane; c < nvec; c += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = rr[j];
+      if (j >= k || r < 0) continue;
+      acc += reinterpret_cast<const f32x4*>(rows + (size_t)r * H)[c];
+    }
+    reinterpret_cast<f32x4*>(out + (size_t)t * H)[c] = acc;
+  }
+}
+
+// d_topk_w[s] = sum of the row's partial rowdots, or 0 for a non-local slot.
+__global__ __launch_bounds__(256) void k_dtopk(const float* __restrict__ part, int nparts,
+                                               const int32_t* __restrict__ row_of, int TK,
+                                               float* __restrict__ d_topk_w) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= TK) return;
+  const int r = row_of[s];
+  float acc = 0.f;
+  if (r >= 0)
+    for (int p = 0; p < nparts; ++p) acc += part[(size_t)r * nparts + p];
+  d_topk_w[s] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                        int32_t* row_src, int32_t* row_of, int32_t* chunk_hist, hipStream_t st) {
+  const int TK = s.T * s.k;
+  const int El = s.e_local;
+  const int nchunks = (int)ceil_div(TK, kSlotChunk);
+  if (nchunks > 0)
+    MOE_LAUNCH("index_hist", k_hist, dim3(nchunks), dim3(256), El * sizeof(int32_t), st, idx, TK, s.e_begin, El,
+                       chunk_hist);
+  MOE_LAUNCH("index_scan", k_scan, dim3(1), dim3(1024), 0, st, nchunks, El, chunk_hist, counts, offsets);
+  int ebits = 0;
+  while ((1 << ebits) < El) ++ebits;
+  if (nchunks > 0)
+    MOE_LAUNCH("index_rank", k_rank, dim3(nchunks), dim3(256), 5 * El * sizeof(int32_t), st, idx, TK, s.e_begin,
+                       El, ebits, chunk_hist, offsets, row_src, row_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
+                             hipStream_t st) {
+  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offsets,
+                         const int32_t* row_src, void* xp, hipStream_t st) {
+  const int64_t R_cap = (int64_t)s.T * (s.k < s.e_local ? s.k : s.e_local);
+  if (R_cap == 0) return hipSuccess;
+  const int grid = (int)(ceil_div(R_cap, 4) < 8192 ? ceil_div(R_cap, 4) : 8192);
+  if (s.dtype == MOE_BF16)
+    MOE_LAUNCH("gather", k_gather<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)x, s.H, s.k, offsets,
+                       s.e_local, row_src, (int)R_cap, (bf16_t*)xp);
+  else
+    MOE_LAUNCH("gather", k_gather<float>, dim3(grid), dim3(256), 0, st, (const float*)x, s.H, s.k, offsets,
+                       s.e_local, row_src, (int)R_cap, (float*)xp);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
+                          hipStream_t st, const char* name) {
+  if (s.T == 0) return hipSuccess;
+  dim3 grid((unsigned)ceil_div(s.T, 4));
+  if (s.dtype == MOE_BF16)
+    MOE_LAUNCH(name, k_combine<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)rows, s.T, s.H, s.k, row_of,
+                       (bf16_t*)out);
+  else
+    MOE_LAUNCH(name, k_combine<float>, grid, dim3(256), 0, st, (const float*)rows, s.T, s.H, s.k, row_of,
+                       (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dtopk(const moe_shape& s, const float* dw_part, int nparts, const int32_t* row_of,
+                        float* d_topk_w, hipStream_t st) {
+  const int TK = s.T * s.k;
+  if (TK == 0) return hipSuccess;
+  MOE_LAUNCH("dtopk", k_dtopk, dim3((unsigned)ceil_div(TK, 256)), dim3(256), 0, st, dw_part, nparts, row_of, TK,
+                     d_topk_w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,164 @@
+/*
+ * moe.h -- C ABI of the dropless MoE layer hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The layer: top-k softmax routing over E experts, a stable permutation of the
+ * (token, slot) pairs into ragged per-expert row groups, a grouped gate/up GEMM with
+ * SwiGLU, a grouped down GEMM scaled by the routing weight, and the weighted combine
+ * back to token order; plus the whole backward.  Sources: the Prime Mega MoE pages
+ * (DeepSeek's fused Mega MoE chain "EP dispatch, two expert linear layers, SwiGLU,
+ * combine" and Prime Intellect's added backward, precision modes bf16 and fp8_bwd)
+ * and NVIDIA's DeepSeek-V3 MoE article (dropless MoE; "Optimization 1": grouped GEMM
+ * over each expert's real token count with device-resident shapes; "Optimization 2":
+ * dispatch permutes tokens by expert, combine restores token order and accumulates
+ * the per-expert outputs; group-aware MXFP8 quantisation).
+ *
+ * One GPU holds the local experts [e_begin, e_begin + e_local) of E.  Slots routed to
+ * other experts are not local: they get no row and contribute nothing here.
+ *
+ * Conventions shared by every call
+ *  - Pointers are device pointers unless stated.  Every call is asynchronous on
+ *    `stream` (a hipStream_t; NULL = the null stream).  No call allocates memory,
+ *    synchronises, copies device->host or prints.  Expert token counts never leave
+ *    the device: kernels read them from `offsets`.
+ *  - Arguments are checked on the host before any launch.  A call returns MOE_OK or a
+ *    negative moe_status and then nothing was launched; moe_last_error() returns a
+ *    thread-local message for the last failing call on this thread.
+ *  - Layouts are row-major.  x, dy, y, dx: [T, H].  w_gate, w_up: [e_local, H, I];
+ *    w_down: [e_local, I, H] (the local slice).  logits, d_logits: [T, E] fp32.
+ *    topk_idx [T, k] int32, topk_w and d_topk_w [T, k] fp32.
+ *  - Element type of x, weights, dy, y, dx, dW, xp, yp: fp32 when shape.dtype is
+ *    MOE_F32, bf16 (raw 16-bit) when MOE_BF16.
+ *  - Rows: R = sum of local counts <= R_cap = T * min(k, e_local).  Row order is
+ *    expert-major, token-ascending.  Row buffers are sized for R_cap; rows >= R are
+ *    left unspecified.
+ *  - The caller owns every buffer, including `saved` and `scratch` whose sizes come
+ *    from moe_workspace_bytes().  The library keeps no state between calls (apart
+ *    from the opt-in timing records of moe_timing_enable); calls with distinct
+ *    buffers may run concurrently on different streams.
+ *  - Outputs are overwritten, never accumulated.  dW slices of experts with no rows
+ *    are written as zeros; tokens with no local slot get y = 0 and dx = 0.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* a size, range or enum value is invalid, or a required pointer is NULL */
+  MOE_EUNSUPPORTED = -2, /* a valid but unsupported combination (e.g. MXFP8 with fp32 data) */
+  MOE_EWORKSPACE = -3,   /* a required workspace pointer (saved / scratch) is NULL */
+  MOE_EHIP = -4          /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_BWD_SAME = 0, MOE_BWD_MXFP8 = 1 } moe_bwd_prec;
+
+typedef struct {
+  int32_t T;        /* tokens, >= 0 */
+  int32_t H;        /* hidden size, > 0, multiple of 64 for MOE_BF16 */
+  int32_t I;        /* expert intermediate size, > 0, multiple of 64 for MOE_BF16 */
+  int32_t E;        /* routed experts, 1..1024 */
+  int32_t k;        /* experts per token, 1..min(E, 16) */
+  int32_t e_begin;  /* first local expert */
+  int32_t e_local;  /* local experts, >= 1, e_begin + e_local <= E */
+  int32_t dtype;    /* moe_dtype */
+  int32_t bwd;      /* moe_bwd_prec: MOE_BWD_MXFP8 needs MOE_BF16 */
+  int32_t renorm;   /* 1: weights = softmax over the k selected logits; 0: softmax over all E */
+} moe_shape;
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Message of the last failing call on this thread (host memory, owned by the library). */
+const char* moe_last_error(void);
+
+/* Byte sizes of the two caller-owned workspaces for `shape`:
+ *  saved   -- written by moe_fwd, read by moe_bwd (the saved G, U and A rows);
+ *  scratch -- temporary space of moe_dispatch, moe_fwd and moe_bwd; its contents do
+ *             not need to survive between calls.
+ * Both pointers must be non-NULL.  Returns MOE_EINVAL for an invalid shape. */
+int moe_workspace_bytes(const moe_shape* shape, size_t* saved_bytes, size_t* scratch_bytes);
+
+/* Top-k routing (NVIDIA article: a learned router activates the top-K experts;
+ * Prime Mega MoE pages: 128 experts, top-8).  For each token the k largest fp32
+ * logits are selected (ties to the lower expert id), ordered by logit descending, and
+ * weighted by a softmax over the selected logits (renorm = 1) or by the full softmax
+ * over all E logits (renorm = 0).  Writes topk_idx [T, k] and topk_w [T, k]. */
+int moe_route_topk(const moe_shape* shape, const float* logits, int32_t* topk_idx,
+                   float* topk_w, void* stream);
+
+/* Dispatch (NVIDIA article, "Optimization 2": tokens are permuted by expert).
+ * Builds counts [e_local], offsets [e_local + 1] (exclusive prefix of counts), the
+ * stable expert-major / token-ascending row order row_src [R_cap] (row -> t*k + j) and
+ * its inverse row_of [T*k] (slot -> row, or -1 if the slot's expert is not local,
+ * including ids outside [0, E)).  If xp is non-NULL, also gathers xp[r] = x[row_src[r]/k]
+ * ([R_cap, H]); with xp == NULL the gather is left to moe_fwd / moe_bwd, which then
+ * read x through row_src.  x may be NULL when xp is NULL.  Needs scratch. */
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
+                 int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* row_of,
+                 void* xp, void* scratch, void* stream);
+
+/* Expert MLP forward (Prime Mega MoE pages: two expert linear layers with SwiGLU
+ * between them; NVIDIA article Figure 3: two grouped GEMMs over the variable-length
+ * expert groups).  For each local row r of expert e and token t = row_src[r] / k:
+ *   g = x[t] W_gate[e], u = x[t] W_up[e], a = silu(g) * u,
+ *   yp[r] = topk_w[t, j] * (a W_down[e])          ([R_cap, H])
+ * g, u and a are kept in `saved` for moe_bwd.  xp may be NULL (rows read from x
+ * through row_src) or the buffer filled by moe_dispatch.  Needs saved and scratch. */
+int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t* offsets,
+            const int32_t* row_src, const float* topk_w, const void* w_gate, const void* w_up,
+            const void* w_down, void* yp, void* saved, void* scratch, void* stream);
+
+/* Combine (NVIDIA article, "Optimization 2": results return to token order and the
+ * per-expert outputs are accumulated): y[t] = sum over the token's local slots j of
+ * yp[row_of[t*k + j]], summed in fp32 and rounded once; 0 for a token with none. */
+int moe_combine(const moe_shape* shape, const void* yp, const int32_t* row_of, void* y,
+                void* stream);
+
+/* Backward of moe_fwd + moe_combine for upstream gradient dy [T, H] (Prime Mega MoE
+ * pages: the backward of the fused chain; fp8_bwd runs it in FP8).  Writes
+ *   dx [T, H], dw_gate / dw_up [e_local, H, I], dw_down [e_local, I, H],
+ *   d_topk_w [T, k] (0 for non-local slots).
+ * shape.bwd == MOE_BWD_MXFP8 runs the four backward GEMMs on MXFP8 operands (E4M3
+ * values with one e8m0 scale per 32 along each GEMM's contraction axis, column-wise
+ * blocks of 32 rows never crossing an expert group).  `saved` must hold what moe_fwd
+ * wrote for the same inputs.  Needs scratch. */
+int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* xp,
+            const int32_t* offsets, const int32_t* row_src, const int32_t* row_of,
+            const float* topk_w, const void* w_gate, const void* w_up, const void* w_down,
+            const void* saved, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+            float* d_topk_w, void* scratch, void* stream);
+
+/* Router backward through the routing weights: d_logits [T, E] fp32.  renorm = 1:
+ * d_logits[t, S_j] = w_j (d_w_j - sum_i w_i d_w_i) and 0 for unselected experts;
+ * renorm = 0 (needs logits): d_logits[t, e] = p_e (g_e - sum_j p_{S_j} d_w_j) with
+ * p = softmax(logits[t]) and g_e = d_w of the slot selecting e, else 0.  The top-k
+ * selection itself is piecewise constant and contributes no gradient. */
+int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
+                       const float* topk_w, const float* d_topk_w, float* d_logits,
+                       void* stream);
+
+/* Opt-in kernel timing for profilers and benchmarks (no effect on results).
+ * moe_timing_enable(1) makes every kernel that this host thread launches through the
+ * calls above be bracketed by two HIP events recorded on the call's stream; (0) stops
+ * it.  Either call discards pending records.  moe_timing_read() waits for the last
+ * recorded event, writes up to `capacity` kernel names (static strings owned by the
+ * library) and elapsed milliseconds in launch order, sets *count to the number of
+ * kernels recorded since the last read or enable, and discards the records.  The
+ * events are library-owned, reused, and live until the process ends. */
+int moe_timing_enable(int on);
+int moe_timing_read(int capacity, const char** names, float* ms, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

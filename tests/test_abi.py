@@ -1,0 +1,90 @@
+"""The C ABI library loads, exports every function include/moe.h declares, and rejects
+invalid arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from combine_top_router_amd import lib as L
+    if not os.path.exists(L.lib_path()):
+        pytest.skip("libmoe.so not built")
+    return L
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("moe_route_topk", "moe_dispatch", "moe_fwd", "moe_bwd", "moe_combine"):
+        assert n in names
+    assert set(names) == set(_lib().EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    raw = ctypes.CDLL(L.lib_path())
+    for n in _declared():
+        assert hasattr(raw, n), n
+    assert L.moe_abi_version() == 1
+
+
+def _shape(L, **kw):
+    base = dict(T=64, H=128, I=64, E=8, k=2, e_begin=0, e_local=8, dtype=L.MOE_BF16, bwd=0, renorm=1)
+    base.update(kw)
+    return L.MoeShape(**base)
+
+
+BAD = [
+    (dict(T=-1), -1), (dict(H=0), -1), (dict(E=0), -1), (dict(E=2000), -1), (dict(k=0), -1),
+    (dict(k=9), -1), (dict(k=17, E=32), -1), (dict(e_local=0), -1), (dict(e_begin=5, e_local=4), -1),
+    (dict(e_begin=-1), -1), (dict(dtype=7), -1), (dict(bwd=3), -1), (dict(renorm=2), -1),
+    (dict(H=100), -1), (dict(I=96), -1), (dict(dtype=0, H=130), -1),
+    (dict(dtype=0, bwd=1), -2),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_invalid_shapes_are_rejected(kw, code):
+    L = _lib()
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_workspace_bytes(_shape(L, **kw))
+    assert ei.value.code == code
+    assert L.moe_last_error()
+
+
+def test_null_pointers_are_rejected_before_launch():
+    L = _lib()
+    s = _shape(L)
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_route_topk(s, 0, 0, 0)
+    assert ei.value.code == L.MOE_EINVAL
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_dispatch(s, 8, 0, 8, 8, 8, 8, 0, 0)      # scratch is NULL
+    assert ei.value.code == L.MOE_EWORKSPACE
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_fwd(s, 8, 0, 8, 8, 8, 8, 8, 8, 8, 0, 8)  # saved is NULL
+    assert ei.value.code == L.MOE_EWORKSPACE
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_bwd(s, 8, 8, 0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 0, 8, 8, 8, 8)  # dw_gate is NULL
+    assert ei.value.code == L.MOE_EINVAL
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_route_topk_bwd(_shape(L, renorm=0), 0, 8, 8, 8, 8)  # renorm 0 needs logits
+    assert ei.value.code == L.MOE_EINVAL
+
+
+def test_workspace_sizes_grow_with_the_layer():
+    L = _lib()
+    small = L.moe_workspace_bytes(_shape(L))
+    big = L.moe_workspace_bytes(_shape(L, T=4096, H=2048, I=768, E=128, k=8, e_local=128))
+    assert all(b > a > 0 for a, b in zip(small, big))
+    # saved holds G|U and A for every possible row
+    R = 4096 * 8
+    assert big[0] >= R * 3 * 768 * 2

@@ -1,0 +1,155 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Integer outputs (top-k ids, counts, offsets, row order) must match bit for bit; float
+outputs within a relative Frobenius error of 1e-2 (bf16 runs) or 1e-5 (fp32 runs).
+Small layers are compared element by element in full; the full-size workloads on
+sampled tokens and experts, which the oracle evaluates one by one."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import moe as om
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_util import BF16_TOL, W_TOL, inputs, oracle_full, rel, run_layer, tol  # noqa: E402
+
+SMALL = {
+    "tiny_f32": wl.CONFIGS["tiny_f32"],
+    "tiny_bf16": wl.CONFIGS["tiny_bf16"],
+    "tiny_bf16_share": wl.CONFIGS["tiny_bf16"].replace(e_begin=3, e_local=4),
+    "tiny_f32_renorm0": wl.CONFIGS["tiny_f32"].replace(renorm=0, e_begin=1, e_local=6),
+    # several 128-row tiles per expert with ragged tails, and N tails of 64 columns
+    "ragged_bf16": wl.MoeConfig("ragged_bf16", 700, 192, 192, 6, 2, 0, 6, 5),
+    "ragged_bf16_share": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
+    "ragged_f32": wl.MoeConfig("ragged_f32", 300, 96, 80, 6, 2, 0, 6, 7, dtype="f32"),
+}
+
+
+def _check_ints(cfg, out, ref):
+    assert np.array_equal(out["topk_idx"], ref["topk_idx"])
+    ix = ref["index"]
+    assert np.array_equal(out["counts"], ix["counts"])
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    assert np.array_equal(out["row_of"], ix["row_of"])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused_gather", "xp"])
+def test_small_layer_parity(name, fuse):
+    cfg = SMALL[name]
+    print(f"[parity] {name} fuse={fuse}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp, fuse_gather=fuse)
+    ref = oracle_full(cfg, inp)
+    _check_ints(cfg, out, ref)
+    assert rel(out["topk_w"], ref["topk_w"]) < W_TOL
+    t = tol(cfg)
+    for key in ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits"):
+        err = rel(out[key], ref[key])
+        assert err < t, (key, err)
+    if not fuse:
+        assert np.array_equal(out["xp"], inp["x"][ix_tok(ref, cfg)])
+
+
+def ix_tok(ref, cfg):
+    return ref["index"]["row_src"] // cfg.k
+
+
+FULL = ["qwen3_30b", "skew_zipf", "qwen3_235b_ep8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_parity_sampled(name):
+    cfg = wl.CONFIGS[name]
+    print(f"[parity-full] {name}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp)
+    idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
+    assert np.array_equal(out["topk_idx"], idx)
+    assert rel(out["topk_w"], w) < W_TOL
+    ix = om.build_index(idx, cfg.e_begin, cfg.e_local)
+    ref = {"topk_idx": idx, "index": ix}
+    _check_ints(cfg, out, ref)
+    assert int(ix["counts"].sum()) == int(out["offsets"][-1])
+    rng = np.random.default_rng(123)
+    toks = np.sort(rng.choice(cfg.T, size=96, replace=False))
+    s = om.token_sample(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w, toks)
+    for key in ("y", "dx", "d_topk_w"):
+        err = rel(out[key][toks], s[key])
+        assert err < BF16_TOL, (key, err)
+    dl = om.router_backward(inp["logits"][toks], idx[toks], w[toks], out["d_topk_w"][toks], cfg.renorm)
+    assert rel(out["d_logits"][toks], dl) < 1e-5
+    counts = ix["counts"]
+    experts = sorted({int(np.argmax(counts)), int(np.argmin(counts)), int(rng.integers(cfg.e_local))})
+    es = om.expert_sample(inp, cfg.k, ix, w, experts)
+    for e, (dwg, dwu, dwd) in es.items():
+        for key, refv in (("dw_gate", dwg), ("dw_up", dwu), ("dw_down", dwd)):
+            if counts[e] == 0:
+                assert not out[key][e].any(), (key, e)
+            else:
+                err = rel(out[key][e], refv)
+                assert err < BF16_TOL, (key, e, int(counts[e]), err)
+
+
+def test_round_trip_gather_combine_is_exact():
+    """Dispatch-gather then an unweighted combine of the gathered rows gives
+    bf16(n_t * x[t]) bit for bit (n_t = local slots of token t)."""
+    from combine_top_router_amd.layer import MoeLayer
+    import combine_top_router_amd.lib as L
+    cfg = wl.CONFIGS["qwen3_30b"].replace(e_begin=40, e_local=50)
+    inp = wl.make_inputs(cfg, with_weights=False, with_dy=False)
+    layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16, fuse_gather=False)
+    x = torch.from_numpy(inp["x"]).cuda().to(torch.bfloat16)
+    layer.route(torch.from_numpy(inp["logits"]).cuda())
+    layer.dispatch(x)
+    L.moe_combine(layer.shape, layer.xp.data_ptr(), layer.row_of.data_ptr(), layer.y.data_ptr(),
+                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    R = int(layer.offsets[-1].item())
+    row_of = layer.row_of.cpu().numpy().reshape(cfg.T, cfg.k)
+    n = (row_of >= 0).sum(axis=1).astype(np.float32)
+    expect = wl.bf16_round(n[:, None] * inp["x"])
+    assert np.array_equal(layer.y.float().cpu().numpy(), expect)
+    xp = layer.xp[:R].float().cpu().numpy()
+    src = layer.row_src[:R].cpu().numpy()
+    assert np.array_equal(xp, inp["x"][src // cfg.k])
+
+
+def test_power_of_two_weight_scaling_is_exact():
+    cfg = SMALL["ragged_bf16"]
+    inp = inputs(cfg)
+    a = run_layer(cfg, inp)
+    b = run_layer(cfg, inp, scale_up=2.0)
+    assert np.array_equal(b["y"], 2 * a["y"])
+    assert np.array_equal(b["dw_gate"], 2 * a["dw_gate"])
+
+
+def test_deterministic_across_runs():
+    cfg = SMALL["ragged_bf16_share"]
+    inp = inputs(cfg)
+    a = run_layer(cfg, inp)
+    b = run_layer(cfg, inp)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_empty_expert_and_no_tokens():
+    cfg = wl.CONFIGS["tiny_bf16"]
+    inp = dict(inputs(cfg))
+    inp["logits"] = inp["logits"].copy()
+    inp["logits"][:, 5] = -1e4
+    out = run_layer(cfg, inp)
+    assert out["counts"][5] == 0
+    assert not out["dw_gate"][5].any() and not out["dw_up"][5].any() and not out["dw_down"][5].any()
+    ref = oracle_full(cfg, inp)
+    for key in ("y", "dx", "dw_gate", "dw_down", "d_logits"):
+        assert rel(out[key], ref[key]) < BF16_TOL, key
+    cfg0 = cfg.replace(T=0)
+    inp0 = {k_: (v[:0] if k_ in ("logits", "x", "dy") else v) for k_, v in inp.items()}
+    out0 = run_layer(cfg0, inp0)
+    assert out0["y"].shape == (0, cfg.H)
+    assert not out0["dw_gate"].any() and not out0["dw_down"].any()
+    assert not out0["counts"].any() and not out0["offsets"].any()
