@@ -84,7 +84,7 @@ void layout(const moe_shape& s, Layout& L) {
   L.saved_bytes = L.off_a + align_up(R * s.I * L.es);
   const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
   L.off_tiles = 0;
-  L.off_dgu = align_up((size_t)(1 + 2 * L.max_tiles) * 4);
+  L.off_dgu = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
   L.off_part = L.off_dxp + align_up(R * s.H * L.es);
   const size_t bwd_bytes = L.off_part + align_up(R * L.nparts * 4);

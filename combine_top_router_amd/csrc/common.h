@@ -47,7 +47,7 @@ constexpr int kGemmBN = 128;     // columns of one GEMM tile (bf16 path)
 constexpr int kSimtBM = 32;      // rows of one fp32 row-group tile
 constexpr int kSlotChunk = 4096; // (token, slot) pairs per histogram chunk
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Opt-in per-kernel timing of the calling host thread (moe_timing_enable): a pair of
 // HIP events recorded on the launch stream around each kernel.

@@ -103,6 +103,35 @@ __device__ __forceinline__ void store_mnmaj(bf16_t* s, const i32x4* v, int tid) 
 
 // The main loop: acc[mi][ni] (32x32 blocks) of this wave's 64x64 sub-tile.
 // P supplies load(kt, Stage&), the operand layouts and the wave's N-block columns.
+// Global loads run two K steps ahead of the MFMAs (two register stages), the LDS ring
+// has two stages, and there is one barrier per K step.
+template <class P>
+__device__ __forceinline__ void store_stage(bf16_t* buf, const Stage& st, int tid) {
+  if (P::A_KMAJ) store_kmaj(buf, st.a, tid); else store_mnmaj(buf, st.a, tid);
+  if (P::B_KMAJ) store_kmaj(buf + TILE_ELEMS, st.b, tid); else store_mnmaj(buf + TILE_ELEMS, st.b, tid);
+}
+
+template <class P>
+__device__ __forceinline__ void mma_stage(const bf16_t* buf, f32x16 (&acc)[2][2], int lane, int wm, int wn) {
+  const bf16_t* As = buf;
+  const bf16_t* Bs = buf + TILE_ELEMS;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 af[2], bf[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+      af[mi] = P::A_KMAJ ? frag_kmaj(As, wm * 64 + mi * 32, kk, lane) : frag_mnmaj(As, wm * 64 + mi * 32, kk, lane);
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      bf[ni] = P::B_KMAJ ? frag_kmaj(Bs, P::ncol(wn, ni), kk, lane) : frag_mnmaj(Bs, P::ncol(wn, ni), kk, lane);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
 template <class P>
 __device__ __forceinline__ void mainloop(P& p, int nk, bf16_t* lds, f32x16 (&acc)[2][2]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -114,42 +143,83 @@ __device__ __forceinline__ void mainloop(P& p, int nk, bf16_t* lds, f32x16 (&acc
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
   if (nk <= 0) return;
-  Stage st;
-  p.load(0, st);
-  {
-    bf16_t* As = lds;
-    bf16_t* Bs = lds + TILE_ELEMS;
-    if (P::A_KMAJ) store_kmaj(As, st.a, tid); else store_mnmaj(As, st.a, tid);
-    if (P::B_KMAJ) store_kmaj(Bs, st.b, tid); else store_mnmaj(Bs, st.b, tid);
-  }
+  Stage s0, s1;
+  p.load(0, s0);
+  store_stage<P>(lds, s0, tid);
+  if (nk > 1) p.load(1, s0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) p.load(kt + 1, st);
-    const bf16_t* As = lds + (kt & 1) * 2 * TILE_ELEMS;
-    const bf16_t* Bs = As + TILE_ELEMS;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[2], bf[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = P::A_KMAJ ? frag_kmaj(As, wm * 64 + mi * 32, kk, lane) : frag_mnmaj(As, wm * 64 + mi * 32, kk, lane);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bf[ni] = P::B_KMAJ ? frag_kmaj(Bs, P::ncol(wn, ni), kk, lane) : frag_mnmaj(Bs, P::ncol(wn, ni), kk, lane);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (more) {
-      bf16_t* As2 = lds + ((kt + 1) & 1) * 2 * TILE_ELEMS;
-      bf16_t* Bs2 = As2 + TILE_ELEMS;
-      if (P::A_KMAJ) store_kmaj(As2, st.a, tid); else store_mnmaj(As2, st.a, tid);
-      if (P::B_KMAJ) store_kmaj(Bs2, st.b, tid); else store_mnmaj(Bs2, st.b, tid);
-    }
+  // K steps in pairs so that the two register stages keep fixed registers
+  for (int kt = 0; kt < nk; kt += 2) {
+    // step kt: s0 holds step kt + 1, s1 receives step kt + 2
+    if (kt + 2 < nk) p.load(kt + 2, s1);
+    mma_stage<P>(lds, acc, lane, wm, wn);
+    if (kt + 1 < nk) store_stage<P>(lds + 2 * TILE_ELEMS, s0, tid);
     __syncthreads();
+    if (kt + 1 >= nk) break;
+    // step kt + 1: s1 holds step kt + 2, s0 receives step kt + 3
+    if (kt + 3 < nk) p.load(kt + 3, s0);
+    mma_stage<P>(lds + 2 * TILE_ELEMS, acc, lane, wm, wn);
+    if (kt + 2 < nk) store_stage<P>(lds, s1, tid);
+    __syncthreads();
+  }
+}
+
+// ---- epilogue staging ----
+// After the main loop the LDS ring is free.  Each wave writes one 32-row half (mi) of
+// its 64x64 fp32 accumulator to its own [32][EP_LD] region, so that lanes can then read
+// 8 consecutive columns of one row and issue 16-byte global loads and stores.
+constexpr int EP_LD = 72;  // row stride in floats: rows r and r + 4 fall on disjoint banks
+
+__device__ __forceinline__ void stage_acc(float* wsm, const f32x16 (&acc)[2][2], int mi, int lane) {
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      wsm[r * EP_LD + ni * 32 + (lane & 31)] = acc[mi][ni][i];
+    }
+}
+
+__device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+
+__device__ __forceinline__ i32x4 pack8(const float (&v)[8]) {
+  i32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = (int)((uint32_t)f2bf(v[2 * q]) | ((uint32_t)f2bf(v[2 * q + 1]) << 16));
+  return o;
+}
+
+__device__ __forceinline__ void unpack8(i32x4 u, float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(((uint32_t)u[q]) << 16);
+    v[2 * q + 1] = __uint_as_float(((uint32_t)u[q]) & 0xffff0000u);
+  }
+}
+
+// Generic epilogue walk for the "wn * 64 + ni * 32" column mapping: calls
+// f(row_in_tile, col_in_tile, v[8]) for every 8-column chunk of this wave's sub-tile.
+template <class F>
+__device__ __forceinline__ void epilogue_rows(bf16_t* lds, const f32x16 (&acc)[2][2], F&& f) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+  float* wsm = reinterpret_cast<float*>(lds) + wv * 32 * EP_LD;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    __syncthreads();
+    stage_acc(wsm, acc, mi, lane);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = (lane >> 3) + 8 * j, cc = (lane & 7) * 8;
+      float v[8];
+      read8(wsm + rr * EP_LD + cc, v);
+      f(wm * 64 + mi * 32 + rr, wn * 64 + cc, v);
+    }
   }
 }
 
@@ -159,15 +229,20 @@ __device__ __forceinline__ int acc_row(int wm, int mi, int i, int lane) {
   return wm * 64 + mi * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
 }
 
-// Common setup of the row-group GEMMs: tile -> expert, first row, valid rows.
+// Common setup of the row-group GEMMs: virtual tile v -> expert, first row, valid rows
+// and column tile, in the expert-major order of the tile table (see k_tile_table).
 struct RowTile {
-  int e, rs, cnt;
+  int e, rs, cnt, nt;
 };
-__device__ __forceinline__ bool row_tile(const int32_t* tiles, const int32_t* offsets, int mt, RowTile& t) {
-  if (mt >= tiles[0]) return false;
-  t.e = tiles[1 + 2 * mt];
-  const int m0 = tiles[2 + 2 * mt];
-  t.rs = offsets[t.e] + m0;
+__device__ __forceinline__ bool row_tile(const int32_t* tiles, const int32_t* offsets, int v, int NT, RowTile& t) {
+  const int q = v / NT;
+  if (q >= tiles[0]) return false;
+  const i32x4 ent = *reinterpret_cast<const i32x4*>(tiles + 4 + 4 * q);
+  t.e = ent[0];
+  const int local = v - ent[1] * NT;
+  const int mt = local % ent[2];
+  t.nt = local / ent[2];
+  t.rs = offsets[t.e] + mt * BM;
   t.cnt = min(BM, offsets[t.e + 1] - t.rs);
   return true;
 }
@@ -198,14 +273,13 @@ struct PGateUp {
   }
 };
 
-__global__ __launch_bounds__(NT) void k_fwd_gateup(FwdArgs a, int nvirt, int nwg) {
+__global__ __launch_bounds__(NT, 2) void k_fwd_gateup(FwdArgs a, int nvirt, int nwg) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * TILE_ELEMS];
   const int v = xcd_remap(blockIdx.x, nwg);
   if (v >= nvirt) return;
-  const int mt = v % a.max_tiles, nt = v / a.max_tiles;
   RowTile t;
-  if (!row_tile(a.tiles, a.offsets, mt, t)) return;
-  const int tid = threadIdx.x;
+  if (!row_tile(a.tiles, a.offsets, v, a.I / 64, t)) return;
+  const int tid = threadIdx.x, nt = t.nt;
   PGateUp p;
   for (int i = 0; i < 4; ++i) {
     const int r = t.rs + min((tid >> 3) + 32 * i, t.cnt - 1);
@@ -217,22 +291,34 @@ __global__ __launch_bounds__(NT) void k_fwd_gateup(FwdArgs a, int nvirt, int nwg
   p.n0 = nt * 64;
   f32x16 acc[2][2];
   mainloop(p, a.H / BK, lds, acc);
+  // epilogue: lane takes 8 intermediate columns of one row, G from block ni = 0 and U
+  // from ni = 1 (same columns), and writes 16-byte chunks of G, U and A
   const int lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-  const int col = p.n0 + wn * 32 + (lane & 31);
-  const int I2 = 2 * a.I;
+  float* wsm = reinterpret_cast<float*>(lds) + wv * 32 * EP_LD;
+  const size_t I2 = 2 * (size_t)a.I;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 2; ++mi) {
+    __syncthreads();
+    stage_acc(wsm, acc, mi, lane);
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rt = acc_row(wm, mi, i, lane);
+    for (int j = 0; j < 2; ++j) {
+      const int rr = (lane >> 2) + 16 * j, cc = (lane & 3) * 8;
+      const int rt = wm * 64 + mi * 32 + rr;
+      float g[8], u[8], av[8];
+      read8(wsm + rr * EP_LD + cc, g);
+      read8(wsm + rr * EP_LD + 32 + cc, u);
       if (rt < t.cnt) {
         const size_t r = (size_t)(t.rs + rt);
-        const float g = acc[mi][0][i], u = acc[mi][1][i];
-        a.gu[r * I2 + col] = f2bf(g);
-        a.gu[r * I2 + a.I + col] = f2bf(u);
-        a.a[r * a.I + col] = f2bf(silu_f(g) * u);
+        const int col = p.n0 + wn * 32 + cc;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
+        *reinterpret_cast<i32x4*>(a.gu + r * I2 + col) = pack8(g);
+        *reinterpret_cast<i32x4*>(a.gu + r * I2 + a.I + col) = pack8(u);
+        *reinterpret_cast<i32x4*>(a.a + r * a.I + col) = pack8(av);
       }
     }
+  }
 }
 
 // ---------------- K2: down projection * routing weight ----------------
@@ -257,14 +343,13 @@ struct PDown {
   }
 };
 
-__global__ __launch_bounds__(NT) void k_fwd_down(FwdArgs a, int nvirt, int nwg) {
+__global__ __launch_bounds__(NT, 2) void k_fwd_down(FwdArgs a, int nvirt, int nwg) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * TILE_ELEMS];
   const int v = xcd_remap(blockIdx.x, nwg);
   if (v >= nvirt) return;
-  const int mt = v % a.max_tiles, nt = v / a.max_tiles;
   RowTile t;
-  if (!row_tile(a.tiles, a.offsets, mt, t)) return;
-  const int tid = threadIdx.x;
+  if (!row_tile(a.tiles, a.offsets, v, (int)ceil_div(a.H, BN), t)) return;
+  const int tid = threadIdx.x, nt = t.nt;
   PDown p;
   for (int i = 0; i < 4; ++i) {
     const int r = t.rs + min((tid >> 3) + 32 * i, t.cnt - 1);
@@ -275,22 +360,17 @@ __global__ __launch_bounds__(NT) void k_fwd_down(FwdArgs a, int nvirt, int nwg) 
   p.n0 = nt * BN;
   f32x16 acc[2][2];
   mainloop(p, a.I / BK, lds, acc);
-  const int lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+  epilogue_rows(lds, acc, [&](int rt, int ct, const float (&v)[8]) {
+    const int col = p.n0 + ct;
+    if (rt < t.cnt && col < a.H) {
+      const size_t r = (size_t)(t.rs + rt);
+      const float w = a.topk_w[a.row_src[r]];
+      float o[8];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rt = acc_row(wm, mi, i, lane);
-      if (rt < t.cnt) {
-        const size_t r = (size_t)(t.rs + rt);
-        const float w = a.topk_w[a.row_src[r]];
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = p.n0 + PDown::ncol(wn, ni) + (lane & 31);
-          if (col < a.H) a.yp[r * a.H + col] = f2bf(w * acc[mi][ni][i]);
-        }
-      }
+      for (int q = 0; q < 8; ++q) o[q] = w * v[q];
+      *reinterpret_cast<i32x4*>(a.yp + r * a.H + col) = pack8(o);
     }
+  });
 }
 
 // ---------------- B1: dA' = dY' Wd^T, SwiGLU backward ----------------
@@ -309,14 +389,13 @@ struct PBwdDA {
   }
 };
 
-__global__ __launch_bounds__(NT) void k_bwd_da(BwdArgs a, int nvirt, int nwg, int nparts) {
+__global__ __launch_bounds__(NT, 2) void k_bwd_da(BwdArgs a, int nvirt, int nwg, int nparts) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * TILE_ELEMS];
   const int v = xcd_remap(blockIdx.x, nwg);
   if (v >= nvirt) return;
-  const int mt = v % a.max_tiles, nt = v / a.max_tiles;
   RowTile t;
-  if (!row_tile(a.tiles, a.offsets, mt, t)) return;
-  const int tid = threadIdx.x;
+  if (!row_tile(a.tiles, a.offsets, v, (int)ceil_div(a.I, BN), t)) return;
+  const int tid = threadIdx.x, nt = t.nt;
   const int n0 = nt * BN;
   PBwdDA p;
   const bf16_t* wd = a.wd + (size_t)t.e * a.I * a.H;
@@ -328,37 +407,38 @@ __global__ __launch_bounds__(NT) void k_bwd_da(BwdArgs a, int nvirt, int nwg, in
   }
   f32x16 acc[2][2];
   mainloop(p, a.H / BK, lds, acc);
-  const int lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-  const int I2 = 2 * a.I;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rt = acc_row(wm, mi, i, lane);
-      const bool rok = rt < t.cnt;
-      const size_t r = (size_t)(t.rs + (rok ? rt : 0));
+  // epilogue: SwiGLU backward on 8 columns per lane; the rowdot of dA' and A over this
+  // wave's 64 columns is reduced across the 8 lanes that share the row
+  const int lane = tid & 63, wn = (tid >> 6) >> 1;
+  const size_t I2 = 2 * (size_t)a.I;
+  epilogue_rows(lds, acc, [&](int rt, int ct, const float (&dap)[8]) {
+    const int col = n0 + ct;
+    const bool ok = rt < t.cnt && col < a.I;
+    float part = 0.f;
+    size_t r = 0;
+    if (ok) {
+      r = (size_t)(t.rs + rt);
       const float w = a.topk_w[a.row_src[r]];
-      float part = 0.f;
+      float g[8], u[8], av[8], dg[8], du[8];
+      unpack8(*reinterpret_cast<const i32x4*>(a.gu + r * I2 + col), g);
+      unpack8(*reinterpret_cast<const i32x4*>(a.gu + r * I2 + a.I + col), u);
+      unpack8(*reinterpret_cast<const i32x4*>(a.a + r * a.I + col), av);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int col = n0 + PBwdDA::ncol(wn, ni) + (lane & 31);
-        if (rok && col < a.I) {
-          const float dap = acc[mi][ni][i];
-          const float g = bf2f(a.gu[r * I2 + col]);
-          const float u = bf2f(a.gu[r * I2 + a.I + col]);
-          const float av = bf2f(a.a[r * a.I + col]);
-          part += dap * av;
-          const float da = w * dap;
-          const float sg = sigmoid_f(g);
-          a.dgu[r * I2 + a.I + col] = f2bf(da * g * sg);
-          a.dgu[r * I2 + col] = f2bf(da * u * sg * (1.f + g * (1.f - sg)));
-        }
+      for (int q = 0; q < 8; ++q) {
+        part += dap[q] * av[q];
+        const float da = w * dap[q];
+        const float sg = sigmoid_f(g[q]);
+        du[q] = da * g[q] * sg;
+        dg[q] = da * u[q] * sg * (1.f + g[q] * (1.f - sg));
       }
-      // rowdot over this wave's 64 columns: reduce across the 32 lanes of the row
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-      if (rok && (lane & 31) == 0) a.dw_part[r * nparts + nt * 2 + wn] = part;
+      *reinterpret_cast<i32x4*>(a.dgu + r * I2 + col) = pack8(dg);
+      *reinterpret_cast<i32x4*>(a.dgu + r * I2 + a.I + col) = pack8(du);
     }
+    part += __shfl_xor(part, 1, 64);
+    part += __shfl_xor(part, 2, 64);
+    part += __shfl_xor(part, 4, 64);
+    if (rt < t.cnt && (lane & 7) == 0) a.dw_part[(size_t)(t.rs + rt) * nparts + nt * 2 + wn] = part;
+  });
 }
 
 // ---------------- B3: dXp = dG Wg^T + dU Wu^T ----------------
@@ -385,14 +465,13 @@ struct PBwdDX {
   }
 };
 
-__global__ __launch_bounds__(NT) void k_bwd_dx(BwdArgs a, int nvirt, int nwg) {
+__global__ __launch_bounds__(NT, 2) void k_bwd_dx(BwdArgs a, int nvirt, int nwg) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * TILE_ELEMS];
   const int v = xcd_remap(blockIdx.x, nwg);
   if (v >= nvirt) return;
-  const int mt = v % a.max_tiles, nt = v / a.max_tiles;
   RowTile t;
-  if (!row_tile(a.tiles, a.offsets, mt, t)) return;
-  const int tid = threadIdx.x;
+  if (!row_tile(a.tiles, a.offsets, v, (int)ceil_div(a.H, BN), t)) return;
+  const int tid = threadIdx.x, nt = t.nt;
   const int n0 = nt * BN;
   PBwdDX p;
   p.I = a.I;
@@ -406,21 +485,11 @@ __global__ __launch_bounds__(NT) void k_bwd_dx(BwdArgs a, int nvirt, int nwg) {
   }
   f32x16 acc[2][2];
   mainloop(p, 2 * a.I / BK, lds, acc);
-  const int lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rt = acc_row(wm, mi, i, lane);
-      if (rt < t.cnt) {
-        const size_t r = (size_t)(t.rs + rt);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int col = n0 + PBwdDX::ncol(wn, ni) + (lane & 31);
-          if (col < a.H) a.dxp[r * a.H + col] = f2bf(acc[mi][ni][i]);
-        }
-      }
-    }
+  epilogue_rows(lds, acc, [&](int rt, int ct, const float (&v)[8]) {
+    const int col = n0 + ct;
+    if (rt < t.cnt && col < a.H)
+      *reinterpret_cast<i32x4*>(a.dxp + (size_t)(t.rs + rt) * a.H + col) = pack8(v);
+  });
 }
 
 // ---------------- weight gradients: contraction over an expert's rows ----------------
@@ -459,8 +528,9 @@ struct PWgrad {
   }
 };
 
-// B2 (which = 0): dWd[e] [I, H] = A_e^T (w dY')_e.   B4 (which = 1): [dWg | dWu][e] [H, 2I] = Xp_e^T [dG | dU]_e.
-__global__ __launch_bounds__(NT) void k_bwd_wgrad(BwdArgs a, int which, int tm, int tn, int nvirt, int nwg) {
+// B2 (WHICH = 0): dWd[e] [I, H] = A_e^T (w dY')_e.   B4 (WHICH = 1): [dWg | dWu][e] [H, 2I] = Xp_e^T [dG | dU]_e.
+template <int WHICH>
+__global__ __launch_bounds__(NT, 2) void k_bwd_wgrad(BwdArgs a, int tm, int tn, int nvirt, int nwg) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * TILE_ELEMS];
   const int v = xcd_remap(blockIdx.x, nwg);
   if (v >= nvirt) return;
@@ -473,7 +543,7 @@ __global__ __launch_bounds__(NT) void k_bwd_wgrad(BwdArgs a, int which, int tm, 
   p.m0 = mt * BM;
   p.n0 = nt * BN;
   p.row_src = a.row_src; p.topk_w = a.topk_w; p.k = a.k;
-  if (which == 0) {
+  if (WHICH == 0) {
     p.abase = a.a; p.lda = a.I; p.agather = false;
     p.bbase = a.dy; p.ldb = a.H; p.bgather = true; p.bscale = true;
     p.M = a.I; p.N = a.H;
@@ -485,27 +555,18 @@ __global__ __launch_bounds__(NT) void k_bwd_wgrad(BwdArgs a, int which, int tm, 
   }
   f32x16 acc[2][2];
   mainloop(p, (p.cnt + BK - 1) / BK, lds, acc);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = p.m0 + acc_row(wm, mi, i, lane);
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int n = p.n0 + PWgrad::ncol(wn, ni) + (lane & 31);
-        if (n >= p.N) continue;
-        const bf16_t val = f2bf(acc[mi][ni][i]);
-        if (which == 0) {
-          a.dwd[((size_t)e * a.I + m) * a.H + n] = val;
-        } else if (n < a.I) {
-          a.dwg[((size_t)e * a.H + m) * a.I + n] = val;
-        } else {
-          a.dwu[((size_t)e * a.H + m) * a.I + (n - a.I)] = val;
-        }
-      }
+  epilogue_rows(lds, acc, [&](int rt, int ct, const float (&vv)[8]) {
+    const int m = p.m0 + rt, n = p.n0 + ct;
+    if (m >= p.M || n >= p.N) return;
+    const i32x4 o = pack8(vv);
+    if (WHICH == 0) {
+      *reinterpret_cast<i32x4*>(a.dwd + ((size_t)e * a.I + m) * a.H + n) = o;
+    } else if (n < a.I) {
+      *reinterpret_cast<i32x4*>(a.dwg + ((size_t)e * a.H + m) * a.I + n) = o;
+    } else {
+      *reinterpret_cast<i32x4*>(a.dwu + ((size_t)e * a.H + m) * a.I + (n - a.I)) = o;
     }
+  });
 }
 
 inline int round8(int n) { return (n + 7) & ~7; }
@@ -534,7 +595,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   {
     const int tm = (int)ceil_div(a.I, BM), tn = (int)ceil_div(a.H, BN);
     const int nvirt = a.El * tm * tn, nwg = round8(nvirt);
-    MOE_LAUNCH("bwd_dWd", k_bwd_wgrad, dim3(nwg), dim3(NT), 0, st, a, 0, tm, tn, nvirt, nwg);
+    MOE_LAUNCH("bwd_dWd", k_bwd_wgrad<0>, dim3(nwg), dim3(NT), 0, st, a, tm, tn, nvirt, nwg);
   }
   if (a.max_tiles > 0) {
     const int nvirt = a.max_tiles * (int)ceil_div(a.H, BN), nwg = round8(nvirt);
@@ -543,7 +604,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   {
     const int tm = (int)ceil_div(a.H, BM), tn = (int)ceil_div(2 * a.I, BN);
     const int nvirt = a.El * tm * tn, nwg = round8(nvirt);
-    MOE_LAUNCH("bwd_dWgu", k_bwd_wgrad, dim3(nwg), dim3(NT), 0, st, a, 1, tm, tn, nvirt, nwg);
+    MOE_LAUNCH("bwd_dWgu", k_bwd_wgrad<1>, dim3(nwg), dim3(NT), 0, st, a, tm, tn, nvirt, nwg);
   }
   return hipGetLastError();
 }

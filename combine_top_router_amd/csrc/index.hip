@@ -113,8 +113,11 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, i
   }
 }
 
-// Tile table of the row-group GEMMs: tiles[0] = number of tiles; entry i at
-// tiles[1 + 2i] = expert, tiles[2 + 2i] = first row of the tile inside the expert.
+// Tile table of the row-group GEMMs.  tiles[0] = number of m-tiles; m-tile i (expert
+// major, then row-ascending) is entry tiles[4 + 4i .. 4i + 7] = {expert e, index of the
+// expert's first m-tile, number of m-tiles of the expert, 0}.  A GEMM with NT column
+// tiles enumerates its work as v = first * NT + (n-tile * tiles_of_e + m-tile in e), so
+// the m-tiles sharing one weight tile are adjacent and one expert's work is contiguous.
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
                                                      int32_t* __restrict__ tiles) {
   __shared__ int32_t buf[1024];
@@ -131,8 +134,8 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
   }
   const int start = buf[e] - n;
   for (int j = 0; j < n; ++j) {
-    tiles[1 + 2 * (start + j)] = e;
-    tiles[2 + 2 * (start + j)] = j * bm;
+    i32x4 ent = {e, start, n, 0};
+    *reinterpret_cast<i32x4*>(tiles + 4 + 4 * (start + j)) = ent;
   }
   if (e == 1023) tiles[0] = buf[1023];
 }
