@@ -43,8 +43,7 @@ __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __ex
 
 // Host-side: the launch configuration constants shared by the host code and kernels.
 constexpr int kGemmBM = 128;     // rows of one row-group GEMM tile (bf16 path)
-constexpr int kGemmBN = 128;     // columns of one GEMM tile (bf16 path)
-constexpr int kSimtBM = 32;      // rows of one fp32 row-group tile
+constexpr int kZeroBytes = 512;  // zeroed scratch area read in place of rows past a group's end
 constexpr int kSlotChunk = 4096; // (token, slot) pairs per histogram chunk
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -72,7 +71,7 @@ hipError_t launch_route_bwd(const moe_shape& s, const float* logits, const int32
 hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                         int32_t* row_src, int32_t* row_of, int32_t* chunk_hist, hipStream_t st);
 hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
-                             hipStream_t st);
+                             int32_t* zeros, hipStream_t st);
 hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offsets,
                          const int32_t* row_src, void* xp, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
@@ -116,7 +115,9 @@ struct BwdArgs {
   int max_tiles;
   bf16_t* dgu;            // scratch [R_cap, 2I]
   bf16_t* dxp;            // scratch [R_cap, H]
-  float* dw_part;         // scratch [R_cap, I / 64]
+  float* dw_part;         // scratch [R_cap, nparts]
+  bf16_t* aw;             // scratch [R_cap, I]: w * A
+  const bf16_t* zeros;    // scratch: kZeroBytes of zeros
   bf16_t* dwg;            // [El, H, I]
   bf16_t* dwu;
   bf16_t* dwd;            // [El, I, H]

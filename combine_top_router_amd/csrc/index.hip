@@ -119,9 +119,10 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, i
 // tiles enumerates its work as v = first * NT + (n-tile * tiles_of_e + m-tile in e), so
 // the m-tiles sharing one weight tile are adjacent and one expert's work is contiguous.
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
-                                                     int32_t* __restrict__ tiles) {
+                                                     int32_t* __restrict__ tiles, int32_t* __restrict__ zeros) {
   __shared__ int32_t buf[1024];
   const int e = threadIdx.x;
+  if (zeros && e < kZeroBytes / 4) zeros[e] = 0;
   int n = 0;
   if (e < El) n = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
   buf[e] = n;
@@ -252,8 +253,8 @@ hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts,
 }
 
 hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
-                             hipStream_t st) {
-  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles);
+                             int32_t* zeros, hipStream_t st) {
+  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles, zeros);
   return hipGetLastError();
 }
 
