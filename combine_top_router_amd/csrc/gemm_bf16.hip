@@ -33,7 +33,20 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64, NTHR = 512, NSTAGE = 3;
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+constexpr int BM = 128, BN = 256, BK = MOE_GEMM_BK;
+constexpr int NSTAGE = BK == 64 ? 3 : 6;  // LDS ring stages (48 KB or 24 KB each)
+constexpr int DEPTH = NSTAGE - 1;         // K steps in flight ahead of the MFMAs
+constexpr int NW = MOE_GEMM_WAVES;   // waves per workgroup: 2 along M x NW/2 along N
+constexpr int NTHR = 64 * NW;
+constexpr int WN = NW / 2;           // waves along N
+constexpr int NI = 8 / WN;           // 32-column accumulator blocks per wave
+constexpr int WCOLS = 32 * NI;       // columns per wave
 constexpr int A_ELEMS = BM * BK;                  // 8192 bf16
 constexpr int B_ELEMS = BN * BK;                  // 16384 bf16
 constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;    // 48 KB per stage
@@ -41,19 +54,22 @@ constexpr int A_LOADS = A_ELEMS * 2 / 16 / NTHR;  // 16-byte loads per thread pe
 constexpr int B_LOADS = B_ELEMS * 2 / 16 / NTHR;
 constexpr int LOADS = A_LOADS + B_LOADS;
 constexpr int LDS_ELEMS = NSTAGE * STAGE_ELEMS;   // 144 KB
-constexpr int IDS_INTS = 8 * 2 * BK;              // per wave, two K steps of gathered row indices
-static_assert(LOADS == 6, "the operand policies issue six loads per thread per stage");
+constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
+constexpr int IDS_INTS = NW * 2 * IDS_SLOT;       // per wave, two K steps of gathered row indices
 
 // ---- LDS layouts (16-byte chunk granularity) ----
-// K-major [rows][64]: chunk c of row r lives at c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int kmaj_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
-// MN-major [64][W]: chunk c of k-row r lives at c ^ ((r & 3) << 2).
+// K-major [rows][BK]: CPR_K chunks per row, RPW rows per 256-byte bank window; chunk c
+// of row r lives at c ^ ((r / RPW) % CPR_K), so the 16 rows a 16-byte LDS read touches
+// at once fall on distinct banks.
+constexpr int CPR_K = BK / 8, RPW = 128 / BK;
+__device__ __forceinline__ int kmaj_chunk(int r, int c) { return c ^ ((r / RPW) & (CPR_K - 1)); }
+// MN-major [BK][W]: chunk c of k-row r lives at c ^ ((r & 3) << 2).
 __device__ __forceinline__ int mnmaj_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
 
 // Slot s of a tile (16 bytes at element offset 8 s) -> (row, logical chunk).
 __device__ __forceinline__ void kmaj_slot(int s, int& r, int& c) {
-  r = s >> 3;
-  c = kmaj_chunk(r, s & 7);
+  r = s / CPR_K;
+  c = kmaj_chunk(r, s % CPR_K);
 }
 template <int W>
 __device__ __forceinline__ void mnmaj_slot(int s, int& r, int& c) {
@@ -64,7 +80,7 @@ __device__ __forceinline__ void mnmaj_slot(int s, int& r, int& c) {
 
 // Slot written by load q of this thread: each wave instruction fills 64 consecutive
 // slots (1 KB), lane l the l-th.
-__device__ __forceinline__ int load_slot(int q, int wv, int lane) { return (q * 8 + wv) * 64 + lane; }
+__device__ __forceinline__ int load_slot(int q, int wv, int lane) { return (q * NW + wv) * 64 + lane; }
 
 // Direct-to-LDS loads, written as inline assembly: the wave's 64 lanes each fetch 16
 // (or 4) bytes from their own global address into consecutive LDS slots starting at
@@ -89,7 +105,7 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
 __device__ __forceinline__ bf16x8 frag_kmaj(const bf16_t* s, int base, int kk, int lane) {
   const int r = base + (lane & 31);
   const int c = kk * 2 + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(s + r * 64 + (kmaj_chunk(r, c) << 3));
+  return *reinterpret_cast<const bf16x8*>(s + r * BK + (kmaj_chunk(r, c) << 3));
 }
 
 // Same fragment from an MN-major tile of width W with two transposing reads: in each
@@ -113,22 +129,22 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const bf16_t* s, int base, int kk, 
 }
 
 template <class P>
-__device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][2], int lane, int wm, int wn) {
+__device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][NI], int lane, int wm, int wn) {
   const bf16_t* As = st;
   const bf16_t* Bs = st + A_ELEMS;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 af[2], bf[2];
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8 af[2], bf[NI];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
       af[mi] = P::A_KMAJ ? frag_kmaj(As, wm * 64 + mi * 32, kk, lane) : frag_mnmaj<BM>(As, wm * 64 + mi * 32, kk, lane);
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
       bf[ni] = P::B_KMAJ ? frag_kmaj(Bs, P::ncol(wn, ni), kk, lane) : frag_mnmaj<BN>(Bs, P::ncol(wn, ni), kk, lane);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
   }
 }
@@ -141,42 +157,42 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][2],
 // overwrite.  `active` is false for waves whose 64 rows all lie past the tile's valid
 // rows: they skip the MFMAs.
 template <class P>
-__device__ __forceinline__ void mainloop(P& p, int nk, bf16_t* lds, f32x16 (&acc)[2][2], bool active) {
+__device__ __forceinline__ void mainloop(P& p, int nk, bf16_t* lds, f32x16 (&acc)[2][NI], bool active) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv & 1, wn = wv >> 1;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
   if (nk <= 0) return;
-  p.issue(0, lds);
-  p.issue(min(1, nk - 1), lds + STAGE_ELEMS);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) p.issue(min(d, nk - 1), lds + d * STAGE_ELEMS);
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    // wait for this thread's loads of step kt (step kt + 1's may still fly) and its
-    // LDS reads of step kt - 1, then a plain barrier (__syncthreads() would also wait
-    // for every load in flight)
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(P::NVMEM) : "memory");
-    const int nxt = cur == 0 ? 2 : cur - 1;  // (kt + 2) % 3
-    p.issue(min(kt + 2, nk - 1), lds + nxt * STAGE_ELEMS);
+    // wait for this thread's loads of step kt (the DEPTH - 1 later steps may still
+    // fly) and its LDS reads of step kt - 1, then a plain barrier (__syncthreads()
+    // would also wait for every load in flight)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((DEPTH - 1) * P::NVMEM) : "memory");
+    const int nxt = cur == 0 ? NSTAGE - 1 : cur - 1;  // (kt + DEPTH) % NSTAGE: the stage read in step kt - 1
+    p.issue(min(kt + DEPTH, nk - 1), lds + nxt * STAGE_ELEMS);
     if (active) mma_stage<P>(lds + cur * STAGE_ELEMS, acc, lane, wm, wn);
-    cur = cur == 2 ? 0 : cur + 1;
+    cur = cur == NSTAGE - 1 ? 0 : cur + 1;
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // the trailing duplicate loads
 }
 
 // ---- epilogue staging ----
 // After the main loop the LDS ring is free.  Each wave writes one 32-row half (mi) of
-// its 64x64 fp32 accumulator to its own [32][EP_LD] region, so that lanes can then read
-// 8 consecutive columns of one row and issue 16-byte global loads and stores.
-constexpr int EP_LD = 72;  // row stride in floats: rows r and r + 4 fall on disjoint banks
-static_assert(8 * 32 * EP_LD * 4 <= LDS_ELEMS * 2, "epilogue staging must fit in the LDS ring");
+// its 64 x WCOLS fp32 accumulator to its own [32][EP_LD] region, so that lanes can then
+// read 8 consecutive columns of one row and issue 16-byte global loads and stores.
+constexpr int EP_LD = WCOLS + 8;  // row stride in floats: rows r and r + 4 fall on disjoint banks
+static_assert(NW * 32 * EP_LD * 4 <= LDS_ELEMS * 2, "epilogue staging must fit in the LDS ring");
 
-__device__ __forceinline__ void stage_acc(float* wsm, const f32x16 (&acc)[2][2], int mi, int lane) {
+__device__ __forceinline__ void stage_acc(float* wsm, const f32x16 (&acc)[2][NI], int mi, int lane) {
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni)
+  for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
@@ -206,10 +222,13 @@ __device__ __forceinline__ void unpack8(i32x4 u, float (&v)[8]) {
   }
 }
 
-// Epilogue walk for the "wn * 64 + ni * 32" column mapping: calls
-// f(row_in_tile, col_in_tile, v[8]) for every 8-column chunk of this wave's sub-tile.
+// Epilogue walk for the "wn * WCOLS + ni * 32" column mapping: calls
+// f(row_in_tile, col_in_tile, v[8]) for every 8-column chunk of this wave's sub-tile;
+// the EP_LPR lanes sharing a row are consecutive.
+constexpr int EP_LPR = WCOLS / 8;      // lanes per row
+constexpr int EP_RPP = 64 / EP_LPR;    // rows per pass
 template <class F>
-__device__ __forceinline__ void epilogue_rows(bf16_t* lds, const f32x16 (&acc)[2][2], F&& f) {
+__device__ __forceinline__ void epilogue_rows(bf16_t* lds, const f32x16 (&acc)[2][NI], F&& f) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
   float* wsm = reinterpret_cast<float*>(lds) + wv * 32 * EP_LD;
 #pragma unroll
@@ -217,11 +236,11 @@ __device__ __forceinline__ void epilogue_rows(bf16_t* lds, const f32x16 (&acc)[2
     stage_acc(wsm, acc, mi, lane);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = (lane >> 3) + 8 * j, cc = (lane & 7) * 8;
+    for (int j = 0; j < 32 / EP_RPP; ++j) {
+      const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
       float v[8];
       read8(wsm + rr * EP_LD + cc, v);
-      f(wm * 64 + mi * 32 + rr, wn * 64 + cc, v);
+      f(wm * 64 + mi * 32 + rr, wn * WCOLS + cc, v);
     }
     __syncthreads();
   }
@@ -267,7 +286,7 @@ struct KRows {
   const bf16_t* p[NL];
   __device__ void issue(int kt, bf16_t* tile, int wv) const {
 #pragma unroll
-    for (int q = 0; q < NL; ++q) dma16(p[q] + kt * BK, tile + (q * 8 + wv) * 64 * 8);
+    for (int q = 0; q < NL; ++q) dma16(p[q] + kt * BK, tile + (q * NW + wv) * 64 * 8);
   }
 };
 
@@ -276,8 +295,11 @@ struct PGateUp {
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
   static constexpr int NVMEM = LOADS;
   // gate columns 0..127 and up columns 128..255 of the B tile; wave wn takes the same
-  // 32 intermediate columns of both, so G and U of one element share a lane
-  __device__ static int ncol(int wn, int ni) { return ni * 128 + wn * 32; }
+  // WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so
+  // G and U of one element share a lane
+  __device__ static int ncol(int wn, int ni) {
+    return (ni < NI / 2 ? 0 : 128) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
+  }
   KRows<A_LOADS> a;
   const bf16_t* b[B_LOADS];  // weight row k = 0 of the slot's column
   size_t bstep;              // elements per K step of the weights (64 rows)
@@ -285,7 +307,7 @@ struct PGateUp {
   __device__ void issue(int kt, bf16_t* st) const {
     a.issue(kt, st, wv);
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * bstep, st + A_ELEMS + (q * 8 + wv) * 64 * 8);
+    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * bstep, st + A_ELEMS + (q * NW + wv) * 64 * 8);
   }
 };
 
@@ -322,10 +344,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
       p.b[q] = (c < 16 ? wg : wu) + col + (size_t)r * a.I;
     }
     p.bstep = (size_t)BK * a.I;
-    f32x16 acc[2][2];
+    f32x16 acc[2][NI];
     mainloop(p, a.H / BK, lds, acc, wm * 64 < t.cnt);
-    // epilogue: lane takes 8 intermediate columns of one row, G from block ni = 0 and
-    // U from ni = 1 (same columns), and writes 16-byte chunks of G, U and A
+    // epilogue: lane takes 8 intermediate columns of one row, G from the gate blocks and
+    // U from the up blocks (same columns), and writes 16-byte chunks of G, U and A
+    constexpr int LPR = WCOLS / 16, RPP = 64 / LPR;
     float* wsm = reinterpret_cast<float*>(lds) + wv * 32 * EP_LD;
     const size_t I2 = 2 * (size_t)a.I;
 #pragma unroll
@@ -333,13 +356,13 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
       stage_acc(wsm, acc, mi, lane);
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int rr = (lane >> 2) + 16 * j, cc = (lane & 3) * 8;
+      for (int j = 0; j < 32 / RPP; ++j) {
+        const int rr = lane / LPR + RPP * j, cc = (lane % LPR) * 8;
         const int rt = wm * 64 + mi * 32 + rr;
         float g[8], u[8], av[8];
         read8(wsm + rr * EP_LD + cc, g);
-        read8(wsm + rr * EP_LD + 32 + cc, u);
-        const int col = n0 + wn * 32 + cc;
+        read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
+        const int col = n0 + wn * (WCOLS / 2) + cc;
         if (rt < t.cnt && col < a.I) {
           const size_t r = (size_t)(t.rs + rt);
 #pragma unroll
@@ -359,7 +382,7 @@ struct PMnB {
   // K-major A rows, MN-major B (row-major weights [K, N])
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
   static constexpr int NVMEM = LOADS;
-  __device__ static int ncol(int wn, int ni) { return wn * 64 + ni * 32; }
+  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   KRows<A_LOADS> a;
   const bf16_t* b[B_LOADS];
   size_t bstep;
@@ -367,7 +390,7 @@ struct PMnB {
   __device__ void issue(int kt, bf16_t* st) const {
     a.issue(kt, st, wv);
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * bstep, st + A_ELEMS + (q * 8 + wv) * 64 * 8);
+    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * bstep, st + A_ELEMS + (q * NW + wv) * 64 * 8);
   }
 };
 
@@ -398,7 +421,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
       p.b[q] = wd + (size_t)r * a.H + col;
     }
     p.bstep = (size_t)BK * a.H;
-    f32x16 acc[2][2];
+    f32x16 acc[2][NI];
     mainloop(p, a.I / BK, lds, acc, wm * 64 < t.cnt);
     epilogue_rows(lds, acc, [&](int rt, int ct, const float (&v)[8]) {
       const int col = n0 + ct;
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
 struct PKK {
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr int NVMEM = LOADS;
-  __device__ static int ncol(int wn, int ni) { return wn * 64 + ni * 32; }
+  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   KRows<A_LOADS> a;
   const bf16_t* b[B_LOADS];   // B rows for K steps [0, ksplit)
   const bf16_t* b2[B_LOADS];  // B3: W_up rows for K steps [ksplit, nk)
@@ -430,7 +453,7 @@ struct PKK {
     const int k0 = (second ? kt - ksplit : kt) * BK;
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q)
-      dma16((second ? b2[q] : b[q]) + k0, st + A_ELEMS + (q * 8 + wv) * 64 * 8);
+      dma16((second ? b2[q] : b[q]) + k0, st + A_ELEMS + (q * NW + wv) * 64 * 8);
   }
 };
 
@@ -462,7 +485,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, int nparts) {
       p.b[q] = wd + (size_t)min(n0 + r, a.I - 1) * a.H + c * 8;
       p.b2[q] = p.b[q];
     }
-    f32x16 acc[2][2];
+    f32x16 acc[2][NI];
     mainloop(p, a.H / BK, lds, acc, wm * 64 < t.cnt);
     const size_t I2 = 2 * (size_t)a.I;
     epilogue_rows(lds, acc, [&](int rt, int ct, const float (&dap)[8]) {
@@ -489,10 +512,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, int nparts) {
         *reinterpret_cast<i32x4*>(a.dgu + r * I2 + a.I + col) = pack8(du);
         *reinterpret_cast<i32x4*>(a.aw + r * a.I + col) = pack8(aw);
       }
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
-      part += __shfl_xor(part, 4, 64);
-      if (rt < t.cnt && (lane & 7) == 0) a.dw_part[(size_t)(t.rs + rt) * nparts + t.nt * 4 + wn] = part;
+#pragma unroll
+      for (int off = 1; off < EP_LPR; off <<= 1) part += __shfl_xor(part, off, 64);
+      if (rt < t.cnt && lane % EP_LPR == 0) a.dw_part[(size_t)(t.rs + rt) * nparts + t.nt * WN + wn] = part;
     });
   }
 }
@@ -525,7 +547,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dx(BwdArgs a) {
       p.b[q] = a.wg + woff + n * a.I + c * 8;
       p.b2[q] = a.wu + woff + n * a.I + c * 8;
     }
-    f32x16 acc[2][2];
+    f32x16 acc[2][NI];
     mainloop(p, 2 * a.I / BK, lds, acc, wm * 64 < t.cnt);
     epilogue_rows(lds, acc, [&](int rt, int ct, const float (&v)[8]) {
       const int col = n0 + ct;
@@ -549,7 +571,7 @@ struct PWgrad {
   static constexpr bool GATHER = AG || BG;
   static constexpr int NVMEM = LOADS + (GATHER ? 1 : 0);
   static constexpr int AR = 4, BR = 2;  // token rows per wave instruction of A and B
-  __device__ static int ncol(int wn, int ni) { return wn * 64 + ni * 32; }
+  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   const bf16_t* abase; int lda;
   const bf16_t* bbase; int ldb;
   const int32_t* row_src; const bf16_t* zeros; int k;
@@ -557,10 +579,10 @@ struct PWgrad {
   int32_t* ids;                    // this wave's two LDS slots of BK row indices
   int acol[A_LOADS], bcol[B_LOADS];  // element column of the lane's chunk
   __device__ void fetch_ids(int kt) const {  // row_src of step kt -> slot kt & 1
-    dma4(row_src + rs + min(kt * BK + lane, cnt - 1), ids + (kt & 1) * BK);
+    dma4(row_src + rs + min(kt * BK + lane, cnt - 1), ids + (kt & 1) * IDS_SLOT);
   }
   __device__ void issue(int kt, bf16_t* st) const {
-    const int32_t* my = ids + (kt & 1) * BK;
+    const int32_t* my = ids + (kt & 1) * IDS_SLOT;
     if (GATHER) {
       if (kt == 0) {
         fetch_ids(0);
@@ -573,23 +595,23 @@ struct PWgrad {
     const bf16_t* bp[B_LOADS];
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
-      const int kr = (q * 8 + wv) * AR + (lane >> 4);
+      const int kr = (q * NW + wv) * AR + (lane >> 4);
       int row = rs + kt * BK + kr;
       if (AG) row = my[kr] / k;
       ap[q] = kt * BK + kr < cnt ? abase + (size_t)row * lda + acol[q] : zeros;
     }
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
-      const int kr = (q * 8 + wv) * BR + (lane >> 5);
+      const int kr = (q * NW + wv) * BR + (lane >> 5);
       int row = rs + kt * BK + kr;
       if (BG) row = my[kr] / k;
       bp[q] = kt * BK + kr < cnt ? bbase + (size_t)row * ldb + bcol[q] : zeros;
     }
     if (GATHER) fetch_ids(kt + 1);
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) dma16(ap[q], st + (q * 8 + wv) * 64 * 8);
+    for (int q = 0; q < A_LOADS; ++q) dma16(ap[q], st + (q * NW + wv) * 64 * 8);
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(bp[q], st + A_ELEMS + (q * 8 + wv) * 64 * 8);
+    for (int q = 0; q < B_LOADS; ++q) dma16(bp[q], st + A_ELEMS + (q * NW + wv) * 64 * 8);
   }
 };
 
@@ -603,7 +625,7 @@ __device__ __forceinline__ void wgrad_tile(const BwdArgs& a, bf16_t* lds, int32_
   p.row_src = a.row_src; p.zeros = a.zeros; p.k = a.k;
   p.wv = wv;
   p.lane = lane;
-  p.ids = ids + wv * 2 * BK;
+  p.ids = ids + wv * 2 * IDS_SLOT;
   if (WHICH == 0) {
     p.abase = a.aw; p.lda = a.I;
     p.bbase = a.dy; p.ldb = a.H;
@@ -625,7 +647,7 @@ __device__ __forceinline__ void wgrad_tile(const BwdArgs& a, bf16_t* lds, int32_
     const int col = n0 + c * 8;
     p.bcol[q] = col < N ? col : n0;
   }
-  f32x16 acc[2][2];
+  f32x16 acc[2][NI];
   mainloop(p, (p.cnt + BK - 1) / BK, lds, acc, true);
   epilogue_rows(lds, acc, [&](int rt, int ct, const float (&vv)[8]) {
     const int m = m0 + rt, n = n0 + ct;
@@ -688,7 +710,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-int bwd_bf16_nparts(int I) { return 4 * (int)ceil_div(I, BN); }
+int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   const int nparts = bwd_bf16_nparts(a.I);
