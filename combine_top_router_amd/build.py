@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "index.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+SOURCES = ["api.hip", "route.hip", "index.hip", "gemm.hip", "gemm_f32.hip", "mx_quant.hip"]
 ARCH = "gfx950"
 
 

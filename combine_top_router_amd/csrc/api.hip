@@ -48,6 +48,9 @@ struct Layout {
   size_t off_gu, off_a, saved_bytes;
   // scratch
   size_t off_tiles, off_zeros, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
+  // MXFP8 backward buffers (scratch), 0 when unused
+  int64_t Rp;
+  size_t off_mx[17];
 };
 
 int check_shape(const moe_shape* s) {
@@ -68,6 +71,8 @@ int check_shape(const moe_shape* s) {
   if (s->dtype == MOE_F32 && s->H % 4 != 0) return fail(MOE_EINVAL, "fp32 needs H a multiple of 4 (H = %d)", s->H);
   if (s->bwd == MOE_BWD_MXFP8 && s->dtype != MOE_BF16)
     return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs bf16 data");
+  if (s->bwd == MOE_BWD_MXFP8 && s->H % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs H a multiple of 128 (H = %d)", s->H);
   return MOE_OK;
 }
 
@@ -89,7 +94,25 @@ void layout(const moe_shape& s, Layout& L) {
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
   L.off_part = L.off_dxp + align_up(R * s.H * L.es);
   L.off_aw = L.off_part + align_up(R * L.nparts * 4);
-  const size_t bwd_bytes = L.off_aw + (s.dtype == MOE_BF16 ? align_up(R * s.I * L.es) : 0);
+  size_t bwd_bytes = L.off_aw + (s.dtype == MOE_BF16 ? align_up(R * s.I * L.es) : 0);
+  L.Rp = 0;
+  for (int i = 0; i < 17; ++i) L.off_mx[i] = 0;
+  if (s.bwd == MOE_BWD_MXFP8) {
+    const size_t H = (size_t)s.H, I = (size_t)s.I, Eh = (size_t)El * s.H, Ei = (size_t)El * s.I;
+    L.Rp = mx_rp_cap(L.R_cap, El);
+    const size_t Rp = (size_t)L.Rp;
+    // codes then scales of: dY' rows, W_down rows, dG|dU rows, [W_gate|W_up] rows,
+    // A^T, (w dY')^T, Xp^T, (dG|dU)^T; then the padded offsets
+    const size_t sizes[17] = {R * H, R * H / 32, Ei * H, Ei * H / 32, R * 2 * I, R * 2 * I / 32, Eh * 2 * I,
+                              Eh * 2 * I / 32, I * Rp, I * Rp / 32, H * Rp, H * Rp / 32, H * Rp, H * Rp / 32,
+                              2 * I * Rp, 2 * I * Rp / 32, (size_t)(El + 1) * 4};
+    size_t off = bwd_bytes;
+    for (int i = 0; i < 17; ++i) {
+      L.off_mx[i] = off;
+      off += align_up(sizes[i]);
+    }
+    bwd_bytes = off;
+  }
   L.scratch_bytes = bwd_bytes > dispatch_bytes ? bwd_bytes : dispatch_bytes;
 }
 
@@ -284,7 +307,6 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   int rc = check_shape(shape);
   if (rc) return rc;
   const moe_shape& s = *shape;
-  if (s.bwd == MOE_BWD_MXFP8) return fail(MOE_EUNSUPPORTED, "the MXFP8 backward is not available in this build");
   REQUIRE(offsets);
   REQUIRE(w_gate);
   REQUIRE(w_up);
@@ -321,7 +343,18 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.dw_part = at<float>(scratch, L.off_part);
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
     a.dwg = (bf16_t*)dw_gate; a.dwu = (bf16_t*)dw_up; a.dwd = (bf16_t*)dw_down;
-    e = launch_bwd_bf16(a, st);
+    if (s.bwd == MOE_BWD_MXFP8) {
+      MxArgs m{};
+      uint8_t** bufs[16] = {&m.q_dy, &m.s_dy, &m.q_wd, &m.s_wd, &m.q_dgu, &m.s_dgu, &m.q_wg, &m.s_wg,
+                            &m.qt_a, &m.st_a, &m.qt_dy, &m.st_dy, &m.qt_x, &m.st_x, &m.qt_dgu, &m.st_dgu};
+      for (int i = 0; i < 16; ++i) *bufs[i] = at<uint8_t>(scratch, L.off_mx[i]);
+      m.poff = at<int32_t>(scratch, L.off_mx[16]);
+      m.Rp = (int)L.Rp;
+      m.R_cap = L.R_cap;
+      e = launch_bwd_mx(a, m, st);
+    } else {
+      e = launch_bwd_bf16(a, st);
+    }
     if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st);
     if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
   } else {
@@ -339,6 +372,18 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
   }
   return hip_status(e, __func__);
+}
+
+int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0) return fail(MOE_EINVAL, "rows = %lld < 0", (long long)rows);
+  if (K <= 0 || K % 32 != 0) return fail(MOE_EINVAL, "K = %d must be a positive multiple of 32", K);
+  if (rows == 0) return MOE_OK;
+  REQUIRE(x);
+  REQUIRE(codes);
+  REQUIRE(scales);
+  return hip_status(launch_mx_rows((const bf16_t*)x, nullptr, K, nullptr, 1, nullptr, 0, rows, rows, K, codes, scales,
+                                   "mx_quantize", (hipStream_t)stream),
+                    __func__);
 }
 
 int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_t* topk_idx,

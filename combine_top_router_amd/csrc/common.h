@@ -124,6 +124,41 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 
+// MXFP8 backward: E4M3 values with one e8m0 scale per 32 along each GEMM's contraction
+// axis.  Row-wise buffers are [rows, K] codes + [rows, K/32] scales; column-wise ones
+// are stored transposed, [N, Rp] codes + [N, Rp/32] scales, over a padded row space in
+// which every expert's rows start at poff[e], a multiple of kMxRowPad.
+constexpr int kMxRowPad = 128;
+struct MxArgs {
+  uint8_t* q_dy; uint8_t* s_dy;      // row-wise dY' (gathered dY rows)   [R_cap, H]
+  uint8_t* q_wd; uint8_t* s_wd;      // row-wise W_down along H           [El*I, H]
+  uint8_t* q_dgu; uint8_t* s_dgu;    // row-wise dG|dU along I            [R_cap, 2I]
+  uint8_t* q_wg; uint8_t* s_wg;      // row-wise [W_gate | W_up] along I  [El*H, 2I]
+  uint8_t* qt_a; uint8_t* st_a;      // column-wise A, transposed         [I, Rp]
+  uint8_t* qt_dy; uint8_t* st_dy;    // column-wise w * dY', transposed   [H, Rp]
+  uint8_t* qt_x; uint8_t* st_x;      // column-wise Xp, transposed        [H, Rp]
+  uint8_t* qt_dgu; uint8_t* st_dgu;  // column-wise dG|dU, transposed     [2I, Rp]
+  int32_t* poff;                     // [El + 1] padded row offsets
+  int Rp;                            // padded row capacity (multiple of kMxRowPad)
+  int64_t R_cap;                     // row capacity of the row-wise activation buffers
+};
+inline int64_t mx_rp_cap(int64_t R_cap, int El) { return ceil_div(R_cap + (int64_t)(kMxRowPad - 1) * El, kMxRowPad) * kMxRowPad; }
+
+// row-wise quantization of rows of K codes (K % 32 == 0).  rows >= 0 and no gather: a
+// fixed count; otherwise the count is offsets[El] (device-resident) and rows_bound an
+// upper bound.  With row_src, row r reads source row row_src[r] / k; with src2, the
+// last K / 2 columns of row r come from src2 (two matrices side by side).
+hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const int32_t* row_src, int k,
+                          const int32_t* offsets, int El, int64_t rows, int64_t rows_bound, int K, uint8_t* q,
+                          uint8_t* s, const char* name, hipStream_t st);
+// column-wise, group-aware quantization into the padded transposed layout; optional row
+// gather (row_src / k) and per-row scaling by topk_w[row_src[r]]
+hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int k, const float* topk_w,
+                          const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
+                          uint8_t* stt, const char* name, hipStream_t st);
+hipError_t launch_poff(const int32_t* offsets, int El, int32_t* poff, hipStream_t st);
+hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
+
 // fp32 (SIMT) grouped GEMMs: the same chain in fp32 arithmetic
 struct FwdArgsF32 {
   int T, H, I, k, El;

@@ -1,0 +1,200 @@
+// MXFP8 quantizers: E4M3 (OCP "FN": bias 7, max 448, no infinities) elements with one
+// e8m0 scale (2^(code - 127)) per block of 32 along a GEMM's contraction axis.
+//
+// The fp8 backward mode of the Prime Mega MoE pages (bf16 forward, FP8 backward) with
+// the group-aware MXFP8 quantisation of NVIDIA's DeepSeek-V3 MoE article: column-wise
+// blocks of 32 token rows start at each expert's first row and never cross experts.
+//
+// Scale rule: X = the smallest integer with amax <= 448 * 2^X (so x / 2^X never
+// saturates), clamped to [-127, 127], X = 0 for an all-zero block.  Elements: x / 2^X
+// rounded to the nearest E4M3 value, ties to even, sign bit from x.  All of it is
+// exact integer/exponent arithmetic on the fp32 value, so identical inputs give
+// identical codes on any correct implementation.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  const float m = frexpf(amax, &e);    // amax = m * 2^e, m in [0.5, 1)
+  // amax in [2^(e-1), 2^e): X = e - 9, plus one if amax > 1.75 * 2^(e-1) = 448 * 2^(e-9)
+  int X = e - 9 + (m > 0.875f ? 1 : 0);
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// E4M3 code of x * 2^-X (|x * 2^-X| <= 448 by the scale rule)
+__device__ __forceinline__ uint32_t e4m3_code(float x, int X) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = ldexpf(fabsf(x), -X);
+  uint32_t mag;
+  if (a >= 0.015625f) {                         // normal range: 3 mantissa bits
+    int e;
+    frexpf(a, &e);                              // a in [2^(e-1), 2^e)
+    const float q = rintf(ldexpf(a, 4 - e)) ;   // a / 2^(e-1-3), in [8, 16]
+    int ee = e - 1, mm = (int)q - 8;
+    if (mm == 8) { ee += 1; mm = 0; }           // rounded up into the next binade
+    mag = (uint32_t)(((ee + 7) << 3) | mm);
+  } else {                                      // subnormal: multiples of 2^-9
+    const float q = rintf(a * 512.f);           // 0..8
+    mag = (uint32_t)q;                          // 8 = 2^-6 = code 0x08, the smallest normal
+  }
+  return sign | mag;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Row-wise: 4 lanes per 32-element block, 8 elements per lane.
+// rows_fixed < 0 (or a gather) means the row count is offsets[El]; with src2, columns
+// >= K / 2 of row r come from src2 (two [rows, K / 2] matrices side by side).
+__global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src, const bf16_t* __restrict__ src2,
+                                                 int ld, const int32_t* __restrict__ row_src, int k,
+                                                 const int32_t* __restrict__ offsets, int El, int64_t rows_fixed,
+                                                 int K, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t rows = (row_src || rows_fixed < 0) ? (int64_t)offsets[El] : rows_fixed;
+  const int gpr = K / 8;                                    // 8-element groups per row
+  const int64_t total = rows * gpr;
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t g0 = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); g0 < total; g0 += stride) {
+    const int64_t g = g0 + lane;
+    const bool ok = g < total;
+    float v[8];
+    int64_t r = 0;
+    int c = 0;
+    if (ok) {
+      r = g / gpr;
+      c = (int)(g - r * gpr) * 8;
+      const int64_t sr = row_src ? (int64_t)(row_src[r] / k) : r;
+      const bf16_t* p = src2 && c >= K / 2 ? src2 + sr * ld + (c - K / 2) : src + sr * ld + c;
+      const i32x4 u = *reinterpret_cast<const i32x4*>(p);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { v[2 * j] = bf_lo((uint32_t)u[j]); v[2 * j + 1] = bf_hi((uint32_t)u[j]); }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    if (ok) {
+      const int X = mx_scale_exp(am);
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w0 |= e4m3_code(v[j], X) << (8 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w1 |= e4m3_code(v[4 + j], X) << (8 * j);
+      *reinterpret_cast<uint2*>(q + r * K + c) = make_uint2(w0, w1);
+      if ((c & 31) == 0) s[r * (K / 32) + (c >> 5)] = (uint8_t)(X + 127);
+    }
+  }
+}
+
+// Column-wise, transposed: one workgroup per (padded 32-row block, 256 columns).  The
+// block's rows are staged in LDS as fp32 (after the optional gather and row scaling),
+// then thread t quantizes column n0 + t: 32 codes to qt[n][pb*32 ..] and one scale.
+__global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
+                                                 const int32_t* __restrict__ row_src, int k,
+                                                 const float* __restrict__ topk_w,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ poff, int El, int N, int Rp,
+                                                 uint8_t* __restrict__ qt, uint8_t* __restrict__ stt) {
+  __shared__ float tile[32][257];
+  const int pb = blockIdx.x;                 // padded block of 32 rows
+  const int pr0 = pb * 32;
+  if (pr0 >= poff[El]) return;
+  int lo = 0, hi = El - 1;                   // expert: last e with poff[e] <= pr0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= pr0) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = offsets[e] + (pr0 - poff[e]);
+  const int nrow = min(32, offsets[e + 1] - r0);   // may be <= 0 in an expert's padding
+  const int n0 = blockIdx.y * 256;
+  const int tid = threadIdx.x;
+  // stage: 32 rows x 256 columns, 16-byte loads (4 per thread)
+  for (int i = tid; i < 32 * 32; i += 256) {
+    const int rr = i >> 5, cc = (i & 31) * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (rr < nrow && n0 + cc < N) {
+      const int r = r0 + rr;
+      const int sr = row_src ? row_src[r] / k : r;
+      const i32x4 u = *reinterpret_cast<const i32x4*>(src + (size_t)sr * ld + n0 + cc);
+      const float w = topk_w ? topk_w[row_src[r]] : 1.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { v[2 * j] = bf_lo((uint32_t)u[j]) * w; v[2 * j + 1] = bf_hi((uint32_t)u[j]) * w; }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[rr][cc + j] = v[j];
+  }
+  __syncthreads();
+  const int n = n0 + tid;
+  if (n >= N) return;
+  float am = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 32; ++rr) am = fmaxf(am, fabsf(tile[rr][tid]));
+  const int X = mx_scale_exp(am);
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc |= e4m3_code(tile[4 * j + b][tid], X) << (8 * b);
+    w[j] = acc;
+  }
+  uint8_t* dst = qt + (size_t)n * Rp + pr0;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  stt[(size_t)n * (Rp / 32) + pb] = (uint8_t)(X + 127);
+}
+
+// padded offsets: every expert's rows rounded up to kMxRowPad
+__global__ __launch_bounds__(1024) void k_poff(const int32_t* __restrict__ offsets, int El, int32_t* __restrict__ poff) {
+  __shared__ int32_t buf[1024];
+  const int e = threadIdx.x;
+  const int n = e < El ? (offsets[e + 1] - offsets[e] + kMxRowPad - 1) / kMxRowPad * kMxRowPad : 0;
+  buf[e] = n;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? buf[e - off] : 0;
+    __syncthreads();
+    buf[e] += v;
+    __syncthreads();
+  }
+  if (e < El) poff[e + 1] = buf[e];
+  if (e == 0) poff[0] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const int32_t* row_src, int k,
+                          const int32_t* offsets, int El, int64_t rows, int64_t rows_bound, int K, uint8_t* q,
+                          uint8_t* s, const char* name, hipStream_t st) {
+  if (rows_bound <= 0) return hipSuccess;
+  const int64_t blocks = ceil_div(rows_bound * (K / 8), 256);
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  MOE_LAUNCH(name, k_mx_rows, dim3(grid), dim3(256), 0, st, src, src2, ld, row_src, k, offsets, El, rows, K, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int k, const float* topk_w,
+                          const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
+                          uint8_t* stt, const char* name, hipStream_t st) {
+  if (Rp <= 0) return hipSuccess;
+  MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / 32), (unsigned)ceil_div(N, 256)), dim3(256), 0, st, src, ld,
+             row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt);
+  return hipGetLastError();
+}
+
+hipError_t launch_poff(const int32_t* offsets, int El, int32_t* poff, hipStream_t st) {
+  MOE_LAUNCH("mx_poff", k_poff, dim3(1), dim3(1024), 0, st, offsets, El, poff);
+  return hipGetLastError();
+}
+
+}  // namespace moe

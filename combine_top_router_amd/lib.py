@@ -12,7 +12,7 @@ __all__ = [
     "MoeShape", "MoeError", "load", "lib_path", "EXPORTS",
     "moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_topk",
     "moe_dispatch", "moe_fwd", "moe_combine", "moe_bwd", "moe_route_topk_bwd",
-    "moe_timing_enable", "moe_timing_read",
+    "moe_mx_quantize", "moe_timing_enable", "moe_timing_read",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
@@ -52,6 +52,7 @@ _SIG = {
     "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P]),
     "moe_bwd": (ctypes.c_int, [_S] + [_P] * 18),
     "moe_route_topk_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_mx_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
@@ -125,6 +126,10 @@ def moe_bwd(shape, dy, x, xp, offsets, row_src, row_of, topk_w, w_gate, w_up, w_
 def moe_route_topk_bwd(shape, logits, topk_idx, topk_w, d_topk_w, d_logits, stream=0):
     _check(load().moe_route_topk_bwd(ctypes.byref(shape), logits, topk_idx, topk_w, d_topk_w, d_logits, stream),
            "moe_route_topk_bwd")
+
+
+def moe_mx_quantize(x, rows, K, codes, scales, stream=0):
+    _check(load().moe_mx_quantize(x, rows, K, codes, scales, stream), "moe_mx_quantize")
 
 
 def moe_timing_enable(on: bool = True):

@@ -146,6 +146,17 @@ int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_
                        const float* topk_w, const float* d_topk_w, float* d_logits,
                        void* stream);
 
+/* MXFP8 quantisation of the backward (NVIDIA article: group-aware MXFP8 quantisation
+ * for the MXFP8 grouped GEMMs; Prime Mega MoE pages: fp8_bwd mode), exposed for tests
+ * and for callers that keep quantised weights: quantises `rows` rows of K bf16 values
+ * (K a multiple of 32, row-major [rows, K]) in blocks of 32 along each row into E4M3
+ * (OCP "FN") codes [rows, K] and e8m0 scale codes [rows, K / 32].  Scale: the smallest
+ * X with amax <= 448 * 2^X, clamped to [-127, 127], X = 0 for an all-zero block, stored
+ * as X + 127; codes: x / 2^X rounded to the nearest E4M3 value, ties to even, sign bit
+ * from x.  moe_bwd with MOE_BWD_MXFP8 applies the same rule to every operand it
+ * quantises. */
+int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales, void* stream);
+
 /* Opt-in kernel timing for profilers and benchmarks (no effect on results).
  * moe_timing_enable(1) makes every kernel that this host thread launches through the
  * calls above be bracketed by two HIP events recorded on the call's stream; (0) stops

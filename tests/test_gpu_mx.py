@@ -1,0 +1,170 @@
+"""Parity of the MXFP8 backward (fp8_bwd mode) with the oracle.
+
+The quantiser is compared code for code with the oracle's MX rule (integer work:
+bit-exact).  The layer: routing, index and the bf16 forward as in the bf16 runs
+(bit-exact integers, 1e-2 on y); the backward's outputs within a relative Frobenius
+error of 4e-2 of the oracle's MXFP8 backward, which quantises the same operands by
+the same rule in fp64.  Against the unquantised fp64 backward the error is the
+quantisation's own (E4M3 keeps 3 mantissa bits; dx passes two quantised GEMMs, about
+5%): checked only against the looser bound PLAIN_TOL, to catch gross mistakes."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import moe as om
+from oracle import mx as omx
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_util import BF16_TOL, W_TOL, inputs, rel, run_layer  # noqa: E402
+
+MX_TOL = 4e-2
+PLAIN_TOL = 1e-1
+GRADS = ("dx", "dw_gate", "dw_up", "dw_down", "d_topk_w")
+
+
+def _quantize_gpu(xb):
+    """bf16 tensor [rows, K] on the GPU -> (codes, scale codes) on the host."""
+    import combine_top_router_amd.lib as L
+    rows, K = xb.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=xb.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=xb.device)
+    L.moe_mx_quantize(xb.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(),
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def _quant_cases():
+    rng = np.random.default_rng(11)
+    rows, K = 96, 256
+    m = np.clip(rng.standard_normal((rows, K)), -7.0, 7.0)
+    # per-block magnitudes over the whole finite bf16 range, including the clamped scale ends
+    mag = np.exp2(rng.integers(-140, 125, size=(rows, K // 32)).astype(np.float64))
+    m = m * np.repeat(mag, 32, axis=1)
+    m[0, :32] = 0.0                                   # all-zero block: scale code 127
+    m[0, 32:64] = -0.0                                # negative zeros keep their sign bit
+    m[1, :32] = 448.0 * np.linspace(-1, 1, 32)        # amax exactly 448: X = 0
+    m[1, 32:64] = 449.0                               # just above: X = 1
+    m[2, :32] = np.arange(32) * 2.0 ** -9             # E4M3 subnormal grid, X = -12 ...
+    m[3, :32] = (np.arange(32) + 0.5) * 2.0 ** -3     # ties between neighbours of the grid
+    m[3, 0] = 448.0
+    m[4, :32] = 2.0 ** -133                           # bf16 subnormals, X clamped to -127
+    m[5, :] = 3.0e38                                  # near the bf16 maximum
+    return m
+
+
+def test_mx_quantize_is_bit_exact():
+    m = _quant_cases()
+    xb = torch.from_numpy(m.astype(np.float32)).to("cuda").to(torch.bfloat16)
+    mb = xb.float().cpu().numpy().astype(np.float64)      # the exact bf16 values
+    assert np.all(np.isfinite(mb))
+    mb[0, 32:64] = -0.0 * np.ones(32)
+    codes, scales = _quantize_gpu(xb)
+    rows, K = mb.shape
+    rc, rs, _ = omx.quantize_blocks(mb.reshape(rows, K // 32, 32))
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc.reshape(rows, K))
+
+
+def test_mx_quantize_empty_and_invalid():
+    import combine_top_router_amd.lib as L
+    xb = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    buf = torch.empty(256, dtype=torch.uint8, device="cuda")
+    L.moe_mx_quantize(xb.data_ptr(), 0, 64, buf.data_ptr(), buf.data_ptr(), 0)     # rows = 0: no-op
+    with pytest.raises(L.MoeError):
+        L.moe_mx_quantize(xb.data_ptr(), 4, 48, buf.data_ptr(), buf.data_ptr(), 0)  # K % 32 != 0
+    torch.cuda.synchronize()
+
+
+def _oracle_mx(cfg, inp):
+    idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
+    Y, saved = om.layer_forward(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w)
+    gmx = omx.layer_backward_mx(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w, saved)
+    g = om.layer_backward(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w, saved)
+    return idx, w, Y, saved["index"], gmx, g
+
+
+SMALL_MX = {
+    "tiny_bf16_mx": wl.CONFIGS["tiny_bf16"].replace(bwd="mxfp8"),
+    "tiny_bf16_mx_share": wl.CONFIGS["tiny_bf16"].replace(bwd="mxfp8", e_begin=3, e_local=4),
+    # several 128-row tiles and a ragged tail per expert, I not a multiple of 128
+    "ragged_mx": wl.MoeConfig("ragged_mx", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
+    "ragged_mx_share": wl.MoeConfig("ragged_mx_share", 500, 384, 320, 10, 3, 4, 5, 9, bwd="mxfp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_MX))
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused_gather", "xp"])
+def test_mx_layer_parity(name, fuse):
+    cfg = SMALL_MX[name]
+    print(f"[mx-parity] {name} fuse={fuse}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp, fuse_gather=fuse)
+    idx, w, Y, ix, gmx, g = _oracle_mx(cfg, inp)
+    assert np.array_equal(out["topk_idx"], idx)
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    assert rel(out["topk_w"], w) < W_TOL
+    assert rel(out["y"], Y) < BF16_TOL
+    for key in GRADS:
+        e_mx, e_plain = rel(out[key], gmx[key]), rel(out[key], g[key])
+        print(f"  {key}: vs mx oracle {e_mx:.3e}, vs unquantised {e_plain:.3e}", flush=True)
+        assert e_mx < MX_TOL, (key, e_mx)
+        assert e_plain < PLAIN_TOL, (key, e_plain)
+
+
+def test_mx_full_size_parity_sampled():
+    """235B-A22B EP=8 share (16 of 128 experts, H=4096, I=1536, T=16384, top-8) in fp8_bwd
+    mode: sampled tokens for dx and d_topk_w, sampled experts for the weight gradients,
+    each against the oracle's MXFP8 backward restricted to them."""
+    cfg = wl.CONFIGS["qwen3_235b_ep8_fp8bwd"]
+    print(f"[mx-parity-full] {cfg.name}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp)
+    idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
+    assert np.array_equal(out["topk_idx"], idx)
+    ix = om.build_index(idx, cfg.e_begin, cfg.e_local)
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    rng = np.random.default_rng(321)
+    # a sample of experts: the oracle's MXFP8 backward over the rows of those experts only
+    # (column-wise blocks never cross a group, so each expert's weight gradient depends on
+    # its own rows alone); dx and d_topk_w of the tokens whose every local slot lies in
+    # the sample are exact too
+    experts = np.sort(rng.choice(cfg.e_local, size=3, replace=False))
+    sub, tok, whole = _expert_subset(cfg, idx, w, inp, experts)
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        for j, e in enumerate(experts):
+            err = rel(out[key][e], sub[key][j])
+            print(f"  {key}[{e}]: {err:.3e}", flush=True)
+            assert err < MX_TOL, (key, e, err)
+    assert whole.sum() > 100
+    for key in ("dx", "d_topk_w"):
+        err = rel(out[key][tok[whole]], sub[key][whole])
+        print(f"  {key} ({int(whole.sum())} tokens): {err:.3e}", flush=True)
+        assert err < MX_TOL, (key, err)
+
+
+def _expert_subset(cfg, idx, w, inp, experts):
+    """The oracle's MXFP8 backward of the layer restricted to the given local experts
+    (renumbered 0..n-1; slots routed elsewhere dropped).  Their row groups, and so their
+    column-wise blocks, are unchanged, and the row-wise blocks are per row, so their
+    weight gradients are those of the whole layer; so are dx and d_topk_w of a token
+    whose local slots all go to these experts (`whole`)."""
+    lut = np.full(cfg.E, -1, dtype=np.int64)
+    lut[np.asarray(experts) + cfg.e_begin] = np.arange(len(experts))
+    mapped = lut[idx]
+    keep = mapped >= 0
+    tok = np.nonzero(keep.any(axis=1))[0]
+    local = (idx[tok] >= cfg.e_begin) & (idx[tok] < cfg.e_begin + cfg.e_local)
+    whole = np.all(keep[tok] == local, axis=1)
+    loc = {k_: inp[k_][tok] for k_ in ("x", "dy")}
+    for k_ in ("w_gate", "w_up", "w_down"):
+        loc[k_] = inp[k_][np.asarray(experts)]
+    idx_s, w_s = mapped[tok], np.where(keep[tok], w[tok], 0.0)
+    n = len(experts)
+    Y, saved = om.layer_forward(loc, cfg.k, 0, n, idx_s, w_s)
+    gmx = omx.layer_backward_mx(loc, cfg.k, 0, n, idx_s, w_s, saved)
+    return gmx, tok, whole
