@@ -9,12 +9,17 @@ in HBM.  value = algorithmic TFLOP/s of the step (6RHI forward + 12RHI backward 
 the R routed rows; tile padding is not counted).
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+[--workload NAME]: the default is the Qwen3-30B-A3B layer; the other names time the
+235B-A22B EP=8 share, the Zipf-skewed routing and the fp8_bwd mode for the design notes.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,7 +30,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-WORKLOAD = "qwen3_30b"
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 / MXFP8 MFMA
+WORKLOADS = {
+    "qwen3_30b": "Qwen3-30B-A3B MoE layer, one GPU: T=4096 H=2048 I=768 E=128 top-8, Gaussian router logits, bf16",
+    "qwen3_235b_ep8": "Qwen3-235B-A22B MoE layer, one GPU's EP=8 share: 16 of 128 experts, T=16384 H=4096 I=1536 "
+                      "top-8, Gaussian router logits, bf16",
+    "skew_zipf": "Zipf(1.2)-skewed routing at the 30B shape: T=16384 H=2048 I=768 E=128 top-8, 8 experts empty, bf16",
+    "qwen3_235b_ep8_fp8bwd": "fp8_bwd mode at the 235B-A22B EP=8 share: bf16 forward, MXFP8 backward GEMMs",
+}
+GEMMS = ("fwd_gateup", "fwd_down", "bwd_dA", "bwd_dWd", "bwd_dX", "bwd_dWgu",
+         "bwd_dA_mx", "bwd_dWd_mx", "bwd_dX_mx", "bwd_dWgu_mx")
 
 
 def kernel_work(name, T, H, I, k, R, El):
@@ -37,6 +51,7 @@ def kernel_work(name, T, H, I, k, R, El):
     W_gu = 2 * El * H * I * b
     W_d = El * I * H * b
     row_h, row_i, row_2i = R * H * b, R * I * b, R * 2 * I * b
+    q = 1 + 1 / 32                       # an MXFP8 element: one byte plus its share of a scale
     table = {
         "fwd_gateup": (row_h + W_gu + row_2i + row_i, 4.0 * R * H * I),
         "fwd_down": (row_i + W_d + row_h, 2.0 * R * H * I),
@@ -47,8 +62,38 @@ def kernel_work(name, T, H, I, k, R, El):
         "gather": (T * H * b + row_h, 0.0),
         "combine": (row_h + T * H * b, 0.0),
         "unpermute_dx": (row_h + T * H * b, 0.0),
+        # MXFP8 backward: fp8 operands, bf16 side inputs and outputs
+        "bwd_dA_mx": ((row_h + W_d) / b * q + row_2i + row_i + row_2i, 2.0 * R * H * I),
+        "bwd_dWd_mx": ((row_i + row_h) / b * q + W_d, 2.0 * R * H * I),
+        "bwd_dX_mx": ((row_2i + W_gu) / b * q + row_h, 4.0 * R * H * I),
+        "bwd_dWgu_mx": ((row_h + row_2i) / b * q + W_gu, 4.0 * R * H * I),
     }
     return table.get(name, (0.0, 0.0))
+
+
+def sources_sha256():
+    """Hash of the library's kernel sources (names and contents of csrc/*)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "combine_top_router_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` measured with the FETCH_SIZE / WRITE_SIZE counters
+    (scaled by a plain copy of known size), as recorded in profiles/hbm_bytes_<workload>.md,
+    or None when there is no record or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^sources-sha256 ([0-9a-f]{64})$", text, re.M)
+    if not m or m.group(1) != sources_sha256():
+        return None
+    m = re.search(rf"^traffic-bytes {re.escape(kernel)} (\d+)$", text, re.M)
+    return int(m.group(1)) if m else None
 
 
 def cpu_baseline(cfg, inp, budget_s=15.0):
@@ -92,6 +137,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (reference for HBM byte counters)")
@@ -106,7 +152,8 @@ def main():
     import combine_top_router_amd.lib as L
     from combine_top_router_amd.layer import MoeLayer
 
-    cfg = wl.CONFIGS[WORKLOAD]
+    cfg = wl.CONFIGS[args.workload]
+    mx = cfg.bwd == "mxfp8"
     inp = wl.make_inputs(cfg)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -114,7 +161,8 @@ def main():
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
     logits = torch.from_numpy(inp["logits"]).to(dev)
     x, wg, wu, wd, dy = t(inp["x"]), t(inp["w_gate"]), t(inp["w_up"]), t(inp["w_down"]), t(inp["dy"])
-    layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16, device=dev)
+    layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16,
+                     L.MOE_BWD_MXFP8 if mx else L.MOE_BWD_SAME, cfg.renorm, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -152,16 +200,25 @@ def main():
         kernels[name] = {"ms": round(avg, 4), "launches_per_step": len(v) // max(1, len(per["route_topk"])),
                          "GB/s": round(byts / avg / 1e6, 1) if byts else None,
                          "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None}
-    gemm = {n: kernels[n] for n in ("fwd_gateup", "fwd_down", "bwd_dA", "bwd_dWd", "bwd_dX", "bwd_dWgu")
-            if n in kernels}
+    gemm = {n: kernels[n] for n in GEMMS if n in kernels}
     dom = max(gemm, key=lambda n: gemm[n]["ms"])
     byts, flops = kernel_work(dom, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)
     avg_ms = gemm[dom]["ms"]
     achieved = byts / avg_ms / 1e6
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes": int(byts), "avg_ms": avg_ms,
-                "mfma_frac": round(flops / avg_ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    mfma_peak = FP8_PEAK_TFLOPS if dom.endswith("_mx") else BF16_PEAK_TFLOPS
+    # the roofline that bounds the kernel: HBM when its arithmetic intensity is below the ridge
+    hbm_bound = flops / byts < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = counted_traffic(args.workload, dom)
+    if hbm_bound:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        tf = flops / avg_ms / 1e9
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(tf, 1), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(tf / mfma_peak, 4), "traffic": traffic}
+    roofline.update({"algorithmic_bytes": int(byts), "algorithmic_flops": flops, "avg_ms": avg_ms,
+                     "mfma_frac": round(flops / avg_ms / 1e9 / mfma_peak, 4),
+                     "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)})
 
     flops_step = 18.0 * R * cfg.H * cfg.I
     fwd_names = ("route_topk", "index_hist", "index_scan", "index_rank", "tile_table", "fwd_gateup", "fwd_down",
@@ -175,13 +232,13 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Qwen3-30B-A3B MoE layer, one GPU: T=4096 H=2048 I=768 E=128 top-8, "
-                               "Gaussian router logits, bf16", "T": cfg.T, "H": cfg.H, "I": cfg.I,
+        "dtype": "bf16+mxfp8" if mx else "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "T": cfg.T, "H": cfg.H, "I": cfg.I,
                    "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
         "mfma_frac_step": round(flops_step / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "mfma_frac_gemms": round(flops_step / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "fwd_ms_kernels": round(fwd_ms, 4),
+        "hbm_frac_combine": round(kernels["combine"]["GB/s"] / HBM_PEAK_GBS, 4) if "combine" in kernels else None,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "kernels": kernels,
