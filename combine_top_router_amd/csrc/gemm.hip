@@ -6,18 +6,17 @@
 // GEMMs (Prime Mega MoE pages: one call fusing the linears, SwiGLU and combine, with
 // scratch buffers instead of intermediate tensors).
 //
-// Engine: persistent 512-thread workgroups (8 wave64, one workgroup per CU), 128x256
-// output tile, K step 64, each wave a 64x64 sub-tile as four v_mfma_f32_32x32x16_bf16
-// accumulators.  Operand tiles move global -> LDS with the gfx950 direct-to-LDS loads
-// (global_load_lds_dwordx4) into a three-stage LDS ring, issued two K steps ahead, one
-// barrier per K step.  An operand whose contraction axis is contiguous in memory
-// ("K-major") is stored [rows][64] and read with 16-byte LDS reads; an operand
-// contiguous along M or N ("MN-major": row-major weights as the B of x*W, and both
-// operands of the weight gradients, which contract over token rows) is stored
-// [64][width] and read with the transposing LDS read ds_read_b64_tr_b16, so no operand
-// is transposed in memory.  Both layouts are XOR-swizzled by 16-byte chunk against LDS
-// bank conflicts; the swizzle is applied by choosing which global chunk each lane of a
-// direct-to-LDS load fetches.
+// Engine (gemm_engine.h): persistent 768-thread workgroups (one per CU) of 8 compute
+// waves and 4 load waves, 128x256 output tile, K step 64, each compute wave a 64x64
+// sub-tile as four v_mfma_f32_32x32x16_bf16 accumulators.  The load waves move operand
+// tiles global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4)
+// into a three-stage LDS ring, two K steps ahead, one barrier per K step, and a
+// workgroup's tiles form one stream of K steps, so the next tile's loads fly while the
+// current tile's epilogue runs.  An operand whose contraction axis is contiguous in memory ("K-major") is
+// stored [rows][64] and read with 16-byte LDS reads; an operand contiguous along M or
+// N ("MN-major": row-major weights as the B of x*W, and both operands of the weight
+// gradients, which contract over token rows) is stored [64][width] and read with the
+// transposing LDS read ds_read_b64_tr_b16, so no operand is transposed in memory.
 //
 // Kernels:
 //   K1 fwd_gateup : G = Xp Wg, U = Xp Wu (dual B tile), epilogue saves G|U and A = silu(G) U
@@ -27,87 +26,127 @@
 //   B3 bwd_dX     : dXp = dG Wg^T + dU Wu^T (K = 2I)
 //   B2 bwd_dWd    : dWd[e] = (w A)_e^T dY'_e over the expert's rows
 //   B4 bwd_dWgu   : [dWg | dWu][e] = Xp_e^T [dG | dU]_e over the expert's rows
+#include <type_traits>
+
 #include "gemm_engine.h"
 
 namespace moe {
 
 namespace {
 
-// ---------------- K1: gate/up + SwiGLU ----------------
-struct PGateUp : Bf16Mma<PGateUp> {
-  static constexpr bool A_KMAJ = true, B_KMAJ = false;
-  static constexpr int NVMEM = LOADS;
-  // gate columns 0..127 and up columns 128..255 of the B tile; wave wn takes the same
-  // WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so
-  // G and U of one element share a lane
-  __device__ static int ncol(int wn, int ni) {
-    return (ni < NI / 2 ? 0 : 128) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
-  }
-  KRows<A_LOADS> a;
-  const bf16_t* b[B_LOADS];  // weight row k = 0 of the slot's column
-  size_t bstep;              // elements per K step of the weights (64 rows)
-  int wv;
-  __device__ void issue(int kt, bf16_t* st, int) const {
-    a.issue(kt, st, wv);
+// ---------------- shared pieces ----------------
+// What the compute waves of a row-tiled kernel know about a tile.
+struct RowTileInfo {
+  RowTile t;
+  int n0;
+  int nk;
+};
+
+// Row-tiled loader state common to every kernel.
+struct RowLd {
+  int nk;
+  int pw;
+  __device__ __forceinline__ void fetch(int, int) const {}
+};
+
+// K-major A rows of a row tile for load wave pw: the lane's chunk of each of its A_LP
+// rows, from a dense [rows, ld] buffer (dense != nullptr) or gathered through row_src.
+__device__ __forceinline__ void a_rows_kmaj(KRows& a, const bf16_t* dense, const bf16_t* gsrc,
+                                            const int32_t* row_src, int k, int ld, const RowTile& t, int pw,
+                                            int lane) {
+  int src[A_LP];
+  if (!dense) gather_rows_a(row_src, t, pw, lane, src);
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * bstep, st + A_ELEMS + (q * NW + wv) * 64 * 8);
+  for (int q = 0; q < A_LP; ++q) {
+    int r, c;
+    kmaj_slot(load_slot(q, pw, lane), r, c);
+    a.p[q] = (dense ? dense + (size_t)(t.rs + min(r, t.cnt - 1)) * ld : gsrc + (size_t)(src[q] / k) * ld) + c * 8;
+  }
+}
+
+__device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_t* offsets, int v, int NT, int nk,
+                                              int ntw, RowTileInfo& p) {
+  row_tile(tiles, offsets, v, NT, p.t);
+  p.n0 = p.t.nt * ntw;
+  p.nk = nk;
+}
+
+// ---------------- K1: gate/up + SwiGLU ----------------
+// B tile: gate columns 0..127 and up columns 128..255; compute wave wn takes the same
+// WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
+// and U of one element share a lane.
+struct LGateUp : RowLd {
+  static constexpr bool GATHER = false;
+  static constexpr int NVMEM = LOADS;
+  KRows a;
+  const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
+  size_t bstep;           // elements per K step of the weights (64 rows)
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
+    a.issue(kt, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
   }
 };
 
-__device__ __forceinline__ const bf16_t* a_row_ptr(const bf16_t* x, const bf16_t* xp, const int32_t* row_src,
-                                                   int k, int ld, int r) {
-  return xp ? xp + (size_t)r * ld : x + (size_t)(row_src[r] / k) * ld;
-}
-
-__global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  const int NT = (int)ceil_div(a.I, 128);
-  Sched sc(a.tiles[0] * NT);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-  for (; sc.more(); sc.next()) {
+struct JGateUp {
+  using Tile = RowTileInfo;
+  using Ld = LGateUp;
+  static constexpr bool A_KMAJ = true, B_KMAJ = false;
+  __device__ __forceinline__ static int ncol(int wn, int ni) {
+    return (ni < NI / 2 ? 0 : 128) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
+  }
+  FwdArgs a;
+  int NT;
+  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const {
+    row_tile_info(a.tiles, a.offsets, v, NT, a.H / BK, 128, p);
+  }
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int, f32x16 (&acc)[2][NI], int lane, int wm, int wn) const {
+    mma_stage<JGateUp>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
-    row_tile(a.tiles, a.offsets, sc.v, NT, t);
+    row_tile(a.tiles, a.offsets, v, NT, t);
     const int n0 = t.nt * 128;
-    PGateUp p;
-    p.wv = wv;
-#pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-      int r, c;
-      kmaj_slot(load_slot(q, wv, lane), r, c);
-      p.a.p[q] = a_row_ptr(a.x, a.xp, a.row_src, a.k, a.H, t.rs + min(r, t.cnt - 1)) + c * 8;
-    }
+    p.pw = pw;
+    p.nk = a.H / BK;
+    a_rows_kmaj(p.a, a.xp, a.x, a.row_src, a.k, a.H, t, pw, lane);
     const bf16_t* wg = a.wg + (size_t)t.e * a.H * a.I;
     const bf16_t* wu = a.wu + (size_t)t.e * a.H * a.I;
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
+    for (int q = 0; q < B_LP; ++q) {
       int r, c;
-      mnmaj_slot<BN>(load_slot(q, wv, lane), r, c);
+      mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
       int col = n0 + (c & 15) * 8;  // intermediate column; chunks 16..31 are W_up's
       if (col >= a.I) col = n0;      // tail columns: any valid address, results are discarded
       p.b[q] = (c < 16 ? wg : wu) + col + (size_t)r * a.I;
     }
     p.bstep = (size_t)BK * a.I;
-    f32x16 acc[2][NI];
-    mainloop(p, a.H / BK, lds, acc, wm * 64 < t.cnt);
-    // epilogue: lane takes 8 intermediate columns of one row, G from the gate blocks and
-    // U from the up blocks (same columns), and writes 16-byte chunks of G, U and A
-    constexpr int LPR = WCOLS / 16, RPP = 64 / LPR;
-    float* wsm = reinterpret_cast<float*>(lds) + wv * 32 * EP_LD;
+  }
+  // lane takes 8 intermediate columns of one row, G from the gate blocks and U from the
+  // up blocks (same columns), and writes 16-byte chunks of G, U and A
+  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+    constexpr int LPR = WCOLS / 16;
+    static_assert(64 / LPR == EP_ROWS, "one pass per staged quarter");
+    float* wsm = stage + wv * EP_ROWS * EP_LD;
     const size_t I2 = 2 * (size_t)a.I;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      stage_acc(wsm, acc, mi, lane);
-      __syncthreads();
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int j = 0; j < 32 / RPP; ++j) {
-        const int rr = lane / LPR + RPP * j, cc = (lane % LPR) * 8;
-        const int rt = wm * 64 + mi * 32 + rr;
+      for (int h = 0; h < 2; ++h) {
+        stage_quarter(wsm, acc, mi, h, lane);
+        const int rr = lane / LPR, cc = (lane % LPR) * 8;
+        const int rt = wm * 64 + mi * 32 + h * 16 + rr;
         float g[8], u[8], av[8];
         read8(wsm + rr * EP_LD + cc, g);
         read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
-        const int col = n0 + wn * (WCOLS / 2) + cc;
-        if (rt < t.cnt && col < a.I) {
-          const size_t r = (size_t)(t.rs + rt);
+        staging_done();
+        const int col = p.n0 + wn * (WCOLS / 2) + cc;
+        if (rt < p.t.cnt && col < a.I) {
+          const size_t r = (size_t)(p.t.rs + rt);
 #pragma unroll
           for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
           *reinterpret_cast<i32x4*>(a.gu + r * I2 + col) = pack8(g);
@@ -115,61 +154,67 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
           *reinterpret_cast<i32x4*>(a.a + r * a.I + col) = pack8(av);
         }
       }
-      __syncthreads();
-    }
-  }
-}
-
-// ---------------- K2: down projection * routing weight ----------------
-struct PMnB : Bf16Mma<PMnB> {
-  // K-major A rows, MN-major B (row-major weights [K, N])
-  static constexpr bool A_KMAJ = true, B_KMAJ = false;
-  static constexpr int NVMEM = LOADS;
-  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
-  KRows<A_LOADS> a;
-  const bf16_t* b[B_LOADS];
-  size_t bstep;
-  int wv;
-  __device__ void issue(int kt, bf16_t* st, int) const {
-    a.issue(kt, st, wv);
-#pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * bstep, st + A_ELEMS + (q * NW + wv) * 64 * 8);
   }
 };
 
-__global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  const int NT = (int)ceil_div(a.H, BN);
-  Sched sc(a.tiles[0] * NT);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1;
-  for (; sc.more(); sc.next()) {
-    RowTile t;
-    row_tile(a.tiles, a.offsets, sc.v, NT, t);
-    const int n0 = t.nt * BN;
-    PMnB p;
-    p.wv = wv;
+  JGateUp job{a, (int)ceil_div(a.I, 128)};
+  run_stream(job, lds);
+}
+
+// ---------------- K2: down projection * routing weight ----------------
+// K-major A rows, MN-major B (row-major weights [K, N])
+struct LMnB : RowLd {
+  static constexpr bool GATHER = false;
+  static constexpr int NVMEM = LOADS;
+  KRows a;
+  const bf16_t* b[B_LP];
+  size_t bstep;
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
+    a.issue(kt, st, pw);
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-      int r, c;
-      kmaj_slot(load_slot(q, wv, lane), r, c);
-      p.a.p[q] = a.a + (size_t)(t.rs + min(r, t.cnt - 1)) * a.I + c * 8;
-    }
+    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
+  }
+};
+
+struct JDown {
+  using Tile = RowTileInfo;
+  using Ld = LMnB;
+  static constexpr bool A_KMAJ = true, B_KMAJ = false;
+  __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+  FwdArgs a;
+  int NT;
+  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, a.I / BK, BN, p); }
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int, f32x16 (&acc)[2][NI], int lane, int wm, int wn) const {
+    mma_stage<JDown>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
+    RowTile t;
+    row_tile(a.tiles, a.offsets, v, NT, t);
+    const int n0 = t.nt * BN;
+    p.pw = pw;
+    p.nk = a.I / BK;
+    a_rows_kmaj(p.a, a.a, nullptr, nullptr, 1, a.I, t, pw, lane);
     const bf16_t* wd = a.wd + (size_t)t.e * a.I * a.H;
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
+    for (int q = 0; q < B_LP; ++q) {
       int r, c;
-      mnmaj_slot<BN>(load_slot(q, wv, lane), r, c);
+      mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
       int col = n0 + c * 8;
       if (col >= a.H) col = n0;  // tail columns: any valid address, results are discarded
       p.b[q] = wd + (size_t)r * a.H + col;
     }
     p.bstep = (size_t)BK * a.H;
-    f32x16 acc[2][NI];
-    mainloop(p, a.I / BK, lds, acc, wm * 64 < t.cnt);
-    epilogue_rows(lds, acc, [&](int rt, int ct, const float (&v)[8]) {
-      const int col = n0 + ct;
-      if (rt < t.cnt && col < a.H) {
-        const size_t r = (size_t)(t.rs + rt);
+  }
+  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&v)[8]) {
+      const int col = p.n0 + ct;
+      if (rt < p.t.cnt && col < a.H) {
+        const size_t r = (size_t)(p.t.rs + rt);
         const float w = a.topk_w[a.row_src[r]];
         float o[8];
 #pragma unroll
@@ -178,25 +223,29 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
       }
     });
   }
+};
+
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
+  JDown job{a, (int)ceil_div(a.H, BN)};
+  run_stream(job, lds);
 }
 
 // ---------------- B1 / B3: both operands K-major ----------------
-struct PKK : Bf16Mma<PKK> {
-  static constexpr bool A_KMAJ = true, B_KMAJ = true;
+struct LKK : RowLd {
+  static constexpr bool GATHER = false;
   static constexpr int NVMEM = LOADS;
-  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
-  KRows<A_LOADS> a;
-  const bf16_t* b[B_LOADS];   // B rows for K steps [0, ksplit)
-  const bf16_t* b2[B_LOADS];  // B3: W_up rows for K steps [ksplit, nk)
-  int ksplit;                 // B3: I / 64; B1: larger than any step count
-  int wv;
-  __device__ void issue(int kt, bf16_t* st, int) const {
-    a.issue(kt, st, wv);
+  KRows a;
+  const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
+  const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
+  int ksplit;              // B3: I / 64; B1: larger than any step count
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
+    a.issue(kt, st, pw);
     const bool second = kt >= ksplit;
     const int k0 = (second ? kt - ksplit : kt) * BK;
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q)
-      dma16((second ? b2[q] : b[q]) + k0, st + A_ELEMS + (q * NW + wv) * 64 * 8);
+    for (int q = 0; q < B_LP; ++q) dma16((second ? b2[q] : b[q]) + k0, b_dst(st, q, pw));
   }
 };
 
@@ -206,11 +255,14 @@ struct PKK : Bf16Mma<PKK> {
 // slots and swizzle are shared.  For v_mfma_scale_f32_32x32x64_f8f6f4 lane l of row
 // l & 31 holds codes 16 (l >> 5) .. +15 of each of the two 32-blocks of a 64-code
 // sub-step and supplies the scale of block l >> 5 of its row.  The scales of a step (4
-// bytes per row) come with one more direct-to-LDS load per thread into a small ring:
-// thread slot t < 128 carries A row t, 128 <= t < 384 B row t - 128.
+// bytes per row) come with two more direct-to-LDS loads per load wave into a small
+// ring: scale slot t < 128 carries A row t, 128 <= t < 384 B row t - 128 (slots
+// 384..511 repeat A row 0).
 constexpr int MX_STEP = 128;               // codes per K step
-constexpr int MX_SC_SLOT = NW * 64 * 4;    // scale bytes per stage
+constexpr int MX_SC_SLOT = 512 * 4;        // scale bytes per stage
+constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per load wave
 static_assert(MX_STEP == 2 * BK, "an fp8 step must span the bytes of a bf16 step");
+static_assert(MX_SC_LP * NP * 64 == 512, "scale slots");
 
 __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int lane) {
   const int c0 = kk * 4 + (lane >> 5);
@@ -222,121 +274,140 @@ __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int
   return out;
 }
 
-struct PMx {
-  static constexpr int NVMEM = LOADS + 1;
-  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
-  const uint8_t* a[A_LOADS];   // codes of the lane's slot at K step 0
-  const uint8_t* b[B_LOADS];
-  const uint8_t* sp;           // this thread's scale row at K step 0
-  uint8_t* scring;             // NSTAGE x MX_SC_SLOT bytes of LDS
-  int wv;
-  __device__ void issue(int kt, bf16_t* st, int slot) const {
+__device__ __forceinline__ int mx_ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+
+__device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, f32x16 (&acc)[2][NI], int lane,
+                                           int wm, int wn) {
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) dma16(a[q] + kt * MX_STEP, st + (q * NW + wv) * 64 * 8);
+  for (int kk = 0; kk < 2; ++kk) {
+    i32x8 af[2], bf[NI];
+    int sa[2], sb[NI];
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(b[q] + kt * MX_STEP, st + A_ELEMS + (q * NW + wv) * 64 * 8);
-    dma4(sp + kt * (MX_STEP / 32), scring + slot * MX_SC_SLOT + wv * 256);
-  }
-  __device__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm, int wn) const {
-    const uint8_t* sc = scring + slot * MX_SC_SLOT;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      i32x8 af[2], bf[NI];
-      int sa[2], sb[NI];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int r = wm * 64 + mi * 32 + (lane & 31);
-        af[mi] = frag_fp8(st, r, kk, lane);
-        sa[mi] = sc[r * 4 + kk * 2 + (lane >> 5)];
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int r = ncol(wn, ni) + (lane & 31);
-        bf[ni] = frag_fp8(st + A_ELEMS, r, kk, lane);
-        sb[ni] = sc[(BM + r) * 4 + kk * 2 + (lane >> 5)];
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], 0, 0, 0, sa[mi],
-                                                                       0, sb[ni]);
+    for (int mi = 0; mi < 2; ++mi) {
+      const int r = wm * 64 + mi * 32 + (lane & 31);
+      af[mi] = frag_fp8(st, r, kk, lane);
+      sa[mi] = sc[r * 4 + kk * 2 + (lane >> 5)];
     }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int r = mx_ncol(wn, ni) + (lane & 31);
+      bf[ni] = frag_fp8(st + A_ELEMS, r, kk, lane);
+      sb[ni] = sc[(BM + r) * 4 + kk * 2 + (lane >> 5)];
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0,
+                                                                     sb[ni]);
+  }
+}
+
+struct LMx {
+  static constexpr bool GATHER = false;
+  static constexpr int NVMEM = LOADS + MX_SC_LP;
+  int nk, pw;
+  const uint8_t* a[A_LP];       // codes of the lane's slot at K step 0
+  const uint8_t* b[B_LP];
+  const uint8_t* sp[MX_SC_LP];  // scale rows of the lane's scale slots at K step 0
+  uint8_t* scring;              // NSTAGE x MX_SC_SLOT bytes of LDS
+  __device__ __forceinline__ void fetch(int, int) const {}
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int slot, int, F&&) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) dma16(a[q] + kt * MX_STEP, a_dst(st, q, pw));
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * MX_STEP, b_dst(st, q, pw));
+#pragma unroll
+    for (int q = 0; q < MX_SC_LP; ++q)
+      dma4(sp[q] + kt * (MX_STEP / 32), scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256);
   }
   // operand rows: A row r (of tile) at a_base + ra(r) * lda, B row n at b_base + rb(n) * ldb;
   // both matrices' scales have row stride ld / 32 and start at s_a / s_b
   template <class RA, class RB>
-  __device__ void setup(const uint8_t* a_codes, const uint8_t* a_scales, int lda, RA ra, const uint8_t* b_codes,
-                        const uint8_t* b_scales, int ldb, RB rb, int k0, uint8_t* ring, int lane) {
-    wv = threadIdx.x >> 6;
+  __device__ __forceinline__ void setup(const uint8_t* a_codes, const uint8_t* a_scales, int lda, RA ra,
+                                        const uint8_t* b_codes, const uint8_t* b_scales, int ldb, RB rb, int k0,
+                                        uint8_t* ring, int lane) {
     scring = ring;
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
+    for (int q = 0; q < A_LP; ++q) {
       int r, c;
-      kmaj_slot(load_slot(q, wv, lane), r, c);
+      kmaj_slot(load_slot(q, pw, lane), r, c);
       a[q] = a_codes + (size_t)ra(r) * lda + k0 + c * 16;
     }
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
+    for (int q = 0; q < B_LP; ++q) {
       int r, c;
-      kmaj_slot(load_slot(q, wv, lane), r, c);
+      kmaj_slot(load_slot(q, pw, lane), r, c);
       b[q] = b_codes + (size_t)rb(r) * ldb + k0 + c * 16;
     }
-    const int t = wv * 64 + lane;
-    if (t < BM) sp = a_scales + (size_t)ra(t) * (lda / 32) + k0 / 32;
-    else if (t < BM + BN) sp = b_scales + (size_t)rb(t - BM) * (ldb / 32) + k0 / 32;
-    else sp = a_scales + (size_t)ra(0) * (lda / 32) + k0 / 32;   // unused slot, any valid row
+#pragma unroll
+    for (int q = 0; q < MX_SC_LP; ++q) {
+      const int t = load_slot(q, pw, lane);
+      if (t < BM) sp[q] = a_scales + (size_t)ra(t) * (lda / 32) + k0 / 32;
+      else if (t < BM + BN) sp[q] = b_scales + (size_t)rb(t - BM) * (ldb / 32) + k0 / 32;
+      else sp[q] = a_scales + (size_t)ra(0) * (lda / 32) + k0 / 32;   // unused slot, any valid row
+    }
   }
 };
+
+template <bool MX>
+using KKLd = typename std::conditional<MX, LMx, LKK>::type;
 
 // B1: dA' = dY' Wd^T.  Epilogue: SwiGLU backward on 8 columns per lane, w * A for B2, and
 // the rowdot of dA' and A over this wave's 64 columns, reduced across the 8 lanes of a row.
 // MX: both operands from the fp8 row-wise buffers (dY' rows, W_down rows along H), and
 // no w * A output (the MXFP8 dW_down quantises A and w * dY').
 template <bool MX>
-__global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, MxArgs m, int nparts) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
-  const int NT = (int)ceil_div(a.I, BN);
-  Sched sc(a.tiles[0] * NT);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-  for (; sc.more(); sc.next()) {
+struct JDa {
+  using Tile = RowTileInfo;
+  using Ld = KKLd<MX>;
+  static constexpr bool A_KMAJ = true, B_KMAJ = true;
+  __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+  BwdArgs a;
+  MxArgs m;
+  int NT, nparts;
+  uint8_t* scring;
+  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
+  __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm,
+                                          int wn) const {
+    if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    else mma_stage<JDa>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
-    row_tile(a.tiles, a.offsets, sc.v, NT, t);
+    row_tile(a.tiles, a.offsets, v, NT, t);
     const int n0 = t.nt * BN;
-    f32x16 acc[2][NI];
+    p.pw = pw;
+    p.nk = nk();
     if constexpr (MX) {
-      PMx p;
       p.setup(m.q_dy, m.s_dy, a.H, [&](int r) { return t.rs + min(r, t.cnt - 1); }, m.q_wd, m.s_wd, a.H,
               [&](int r) { return t.e * a.I + min(n0 + r, a.I - 1); }, 0, scring, lane);
-      mainloop(p, a.H / MX_STEP, lds, acc, wm * 64 < t.cnt);
     } else {
-      PKK p;
-      p.wv = wv;
       p.ksplit = 1 << 30;
-#pragma unroll
-      for (int q = 0; q < A_LOADS; ++q) {
-        int r, c;
-        kmaj_slot(load_slot(q, wv, lane), r, c);
-        p.a.p[q] = a.dy + (size_t)(a.row_src[t.rs + min(r, t.cnt - 1)] / a.k) * a.H + c * 8;
-      }
+      a_rows_kmaj(p.a, nullptr, a.dy, a.row_src, a.k, a.H, t, pw, lane);
       const bf16_t* wd = a.wd + (size_t)t.e * a.I * a.H;
 #pragma unroll
-      for (int q = 0; q < B_LOADS; ++q) {
+      for (int q = 0; q < B_LP; ++q) {
         int r, c;
-        kmaj_slot(load_slot(q, wv, lane), r, c);
+        kmaj_slot(load_slot(q, pw, lane), r, c);
         p.b[q] = wd + (size_t)min(n0 + r, a.I - 1) * a.H + c * 8;
         p.b2[q] = p.b[q];
       }
-      mainloop(p, a.H / BK, lds, acc, wm * 64 < t.cnt);
     }
+  }
+  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+    const int lane = threadIdx.x & 63, wn = threadIdx.x >> 7;
     const size_t I2 = 2 * (size_t)a.I;
-    epilogue_rows(lds, acc, [&](int rt, int ct, const float (&dap)[8]) {
-      const int col = n0 + ct;
-      const bool ok = rt < t.cnt && col < a.I;
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8]) {
+      const int col = p.n0 + ct;
+      const bool ok = rt < p.t.cnt && col < a.I;
       float part = 0.f;
       if (ok) {
-        const size_t r = (size_t)(t.rs + rt);
+        const size_t r = (size_t)(p.t.rs + rt);
         const float w = a.topk_w[a.row_src[r]];
         float g[8], u[8], av[8], dg[8], du[8], aw[8];
         unpack8(*reinterpret_cast<const i32x4*>(a.gu + r * I2 + col), g);
@@ -357,194 +428,259 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, MxArgs m, int npa
       }
 #pragma unroll
       for (int off = 1; off < EP_LPR; off <<= 1) part += __shfl_xor(part, off, 64);
-      if (rt < t.cnt && lane % EP_LPR == 0) a.dw_part[(size_t)(t.rs + rt) * nparts + t.nt * WN + wn] = part;
+      if (rt < p.t.cnt && lane % EP_LPR == 0) a.dw_part[(size_t)(p.t.rs + rt) * nparts + p.t.nt * WN + wn] = part;
     });
   }
+};
+
+template <bool MX>
+__global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, MxArgs m, int nparts) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
+  JDa<MX> job{a, m, (int)ceil_div(a.I, BN), nparts, scring};
+  run_stream(job, lds);
 }
 
 // B3: dXp = dG Wg^T + dU Wu^T, K = 2I: the first I/64 steps read W_gate rows, the rest W_up.
 // MX: dG|dU rows against the rows of the concatenated [W_gate | W_up] (both along 2I).
 template <bool MX>
-__global__ __launch_bounds__(NTHR, 1) void k_bwd_dx(BwdArgs a, MxArgs m) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
-  const int NT = (int)ceil_div(a.H, BN);
-  Sched sc(a.tiles[0] * NT);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1;
-  for (; sc.more(); sc.next()) {
+struct JDx {
+  using Tile = RowTileInfo;
+  using Ld = KKLd<MX>;
+  static constexpr bool A_KMAJ = true, B_KMAJ = true;
+  __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+  BwdArgs a;
+  MxArgs m;
+  int NT;
+  uint8_t* scring;
+  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
+  __device__ __forceinline__ int nk() const { return MX ? 2 * a.I / MX_STEP : 2 * a.I / BK; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm,
+                                          int wn) const {
+    if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    else mma_stage<JDx>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
-    row_tile(a.tiles, a.offsets, sc.v, NT, t);
+    row_tile(a.tiles, a.offsets, v, NT, t);
     const int n0 = t.nt * BN;
-    f32x16 acc[2][NI];
+    p.pw = pw;
+    p.nk = nk();
     if constexpr (MX) {
-      PMx p;
       p.setup(m.q_dgu, m.s_dgu, 2 * a.I, [&](int r) { return t.rs + min(r, t.cnt - 1); }, m.q_wg, m.s_wg, 2 * a.I,
               [&](int r) { return t.e * a.H + min(n0 + r, a.H - 1); }, 0, scring, lane);
-      mainloop(p, 2 * a.I / MX_STEP, lds, acc, wm * 64 < t.cnt);
     } else {
-      PKK p;
-      p.wv = wv;
       p.ksplit = a.I / BK;
-#pragma unroll
-      for (int q = 0; q < A_LOADS; ++q) {
-        int r, c;
-        kmaj_slot(load_slot(q, wv, lane), r, c);
-        p.a.p[q] = a.dgu + (size_t)(t.rs + min(r, t.cnt - 1)) * 2 * a.I + c * 8;
-      }
+      a_rows_kmaj(p.a, a.dgu, nullptr, nullptr, 1, 2 * a.I, t, pw, lane);
       const size_t woff = (size_t)t.e * a.H * a.I;
 #pragma unroll
-      for (int q = 0; q < B_LOADS; ++q) {
+      for (int q = 0; q < B_LP; ++q) {
         int r, c;
-        kmaj_slot(load_slot(q, wv, lane), r, c);
+        kmaj_slot(load_slot(q, pw, lane), r, c);
         const size_t n = (size_t)min(n0 + r, a.H - 1);
         p.b[q] = a.wg + woff + n * a.I + c * 8;
         p.b2[q] = a.wu + woff + n * a.I + c * 8;
       }
-      mainloop(p, 2 * a.I / BK, lds, acc, wm * 64 < t.cnt);
     }
-    epilogue_rows(lds, acc, [&](int rt, int ct, const float (&v)[8]) {
-      const int col = n0 + ct;
-      if (rt < t.cnt && col < a.H)
-        *reinterpret_cast<i32x4*>(a.dxp + (size_t)(t.rs + rt) * a.H + col) = pack8(v);
+  }
+  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&v)[8]) {
+      const int col = p.n0 + ct;
+      if (rt < p.t.cnt && col < a.H)
+        *reinterpret_cast<i32x4*>(a.dxp + (size_t)(p.t.rs + rt) * a.H + col) = pack8(v);
     });
   }
+};
+
+template <bool MX>
+__global__ __launch_bounds__(NTHR, 1) void k_bwd_dx(BwdArgs a, MxArgs m) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
+  JDx<MX> job{a, m, (int)ceil_div(a.H, BN), scring};
+  run_stream(job, lds);
 }
 
 // ---------------- weight gradients: contraction over an expert's rows ----------------
 // Both operands are MN-major tiles of 64 token rows; rows past the expert's end are
 // loaded from a zeroed scratch area.  For a gathered operand (rows of x or dy picked
-// by row_src) each wave also copies the 64 row_src entries of a K step into its own
-// LDS slot one step ahead, with one more direct-to-LDS load, so the vector memory
-// queue holds only direct-to-LDS loads and the counts stay exact.  Within issue(kt)
-// the index load of step kt + 1 goes first, and issue(kt + 1) waits for it with
-// vmcnt(LOADS): only the six operand loads of step kt may still be in flight.
+// by row_src) each load wave also copies the 64 row_src entries of a stream position
+// into its own LDS index slot one position ahead, with one more direct-to-LDS load, so
+// its vector memory queue holds only direct-to-LDS loads and the counts stay exact.
+// Within issue() the index load of the next position goes first, and the next issue()
+// waits for it with vmcnt(LOADS): only the operand loads may still be in flight.
 template <bool AG, bool BG>
-struct PWgrad : Bf16Mma<PWgrad<AG, BG>> {
-  static constexpr bool A_KMAJ = false, B_KMAJ = false;
+struct LWgrad {
   static constexpr bool GATHER = AG || BG;
   static constexpr int NVMEM = LOADS + (GATHER ? 1 : 0);
-  static constexpr int AR = 4, BR = 2;  // token rows per wave instruction of A and B
-  __device__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+  static constexpr int AR = 4, BR = 2;  // token rows per wave load of A and B
   const bf16_t* abase; int lda;
   const bf16_t* bbase; int ldb;
   const int32_t* row_src; const bf16_t* zeros; int k;
-  int rs, cnt, wv, lane;
-  int32_t* ids;                    // this wave's two LDS slots of BK row indices
-  int acol[A_LOADS], bcol[B_LOADS];  // element column of the lane's chunk
-  __device__ void fetch_ids(int kt) const {  // row_src of step kt -> slot kt & 1
-    dma4(row_src + rs + min(kt * BK + lane, cnt - 1), ids + (kt & 1) * IDS_SLOT);
+  int rs, cnt, pw, lane;
+  int nk;
+  int32_t* ids;                  // this wave's two LDS slots of BK row indices
+  int acol[A_LP], bcol[B_LP];    // element column of the lane's chunk
+  __device__ __forceinline__ void fetch(int kt, int par) const {  // row_src of step kt -> slot par
+    if (!GATHER) return;
+    const int32_t* src = cnt > 0 ? row_src + rs + min(kt * BK + lane, cnt - 1) : reinterpret_cast<const int32_t*>(zeros);
+    dma4(src, ids + par * IDS_SLOT);
   }
-  __device__ void issue(int kt, bf16_t* st, int) const {
-    const int32_t* my = ids + (kt & 1) * IDS_SLOT;
-    if (GATHER) {
-      if (kt == 0) {
-        fetch_ids(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
-      }
-    }
-    const bf16_t* ap[A_LOADS];
-    const bf16_t* bp[B_LOADS];
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int par, F&& fetch_next) const {
+    const int32_t* my = ids + par * IDS_SLOT;
+    if (GATHER) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
+    const bf16_t* ap[A_LP];
+    const bf16_t* bp[B_LP];
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-      const int kr = (q * NW + wv) * AR + (lane >> 4);
+    for (int q = 0; q < A_LP; ++q) {
+      const int kr = load_instr(q, pw) * AR + (lane >> 4);
       int row = rs + kt * BK + kr;
       if (AG) row = my[kr] / k;
       ap[q] = kt * BK + kr < cnt ? abase + (size_t)row * lda + acol[q] : zeros;
     }
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
-      const int kr = (q * NW + wv) * BR + (lane >> 5);
+    for (int q = 0; q < B_LP; ++q) {
+      const int kr = load_instr(q, pw) * BR + (lane >> 5);
       int row = rs + kt * BK + kr;
       if (BG) row = my[kr] / k;
       bp[q] = kt * BK + kr < cnt ? bbase + (size_t)row * ldb + bcol[q] : zeros;
     }
-    if (GATHER) fetch_ids(kt + 1);
+    if (GATHER) fetch_next();
 #pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) dma16(ap[q], st + (q * NW + wv) * 64 * 8);
+    for (int q = 0; q < A_LP; ++q) dma16(ap[q], a_dst(st, q, pw));
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) dma16(bp[q], st + A_ELEMS + (q * NW + wv) * 64 * 8);
+    for (int q = 0; q < B_LP; ++q) dma16(bp[q], b_dst(st, q, pw));
   }
 };
 
-template <int WHICH, bool AG, bool BG, bool MX>
-__device__ __forceinline__ void wgrad_tile(const BwdArgs& a, const MxArgs& m, bf16_t* lds, int32_t* ids,
-                                           uint8_t* scring, int e, int m0, int n0) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
-  f32x16 acc[2][NI];
-  if constexpr (MX) {
-    // transposed column-wise codes: rows are the output's M / N indices, K runs over
-    // the expert's padded row range [poff[e], poff[e + 1])
-    PMx p;
-    const int k0 = m.poff[e];
-    const int nk = (m.poff[e + 1] - k0) / MX_STEP;
-    auto ra = [&](int r) { return min(m0 + r, M - 1); };
-    auto rb = [&](int r) { return min(n0 + r, N - 1); };
-    if (WHICH == 0) p.setup(m.qt_a, m.st_a, m.Rp, ra, m.qt_dy, m.st_dy, m.Rp, rb, k0, scring, lane);
-    else p.setup(m.qt_x, m.st_x, m.Rp, ra, m.qt_dgu, m.st_dgu, m.Rp, rb, k0, scring, lane);
-    mainloop(p, nk, lds, acc, true);
-  } else {
-    PWgrad<AG, BG> p;
-    p.rs = a.offsets[e];
-    p.cnt = a.offsets[e + 1] - p.rs;
-    p.row_src = a.row_src; p.zeros = a.zeros; p.k = a.k;
-    p.wv = wv;
-    p.lane = lane;
-    p.ids = ids + wv * 2 * IDS_SLOT;
-    if (WHICH == 0) {
-      p.abase = a.aw; p.lda = a.I;
-      p.bbase = a.dy; p.ldb = a.H;
-    } else {
-      p.abase = AG ? a.x : a.xp; p.lda = a.H;
-      p.bbase = a.dgu; p.ldb = 2 * a.I;
-    }
-#pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-      int r, c;
-      mnmaj_slot<BM>(load_slot(q, wv, lane), r, c);
-      const int col = m0 + c * 8;
-      p.acol[q] = col < M ? col : m0;
-    }
-#pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
-      int r, c;
-      mnmaj_slot<BN>(load_slot(q, wv, lane), r, c);
-      const int col = n0 + c * 8;
-      p.bcol[q] = col < N ? col : n0;
-    }
-    mainloop(p, (p.cnt + BK - 1) / BK, lds, acc, true);
-  }
-  epilogue_rows(lds, acc, [&](int rt, int ct, const float (&vv)[8]) {
-    const int mm = m0 + rt, n = n0 + ct;
-    if (mm >= M || n >= N) return;
-    const i32x4 o = pack8(vv);
-    if (WHICH == 0) {
-      *reinterpret_cast<i32x4*>(a.dwd + ((size_t)e * a.I + mm) * a.H + n) = o;
-    } else if (n < a.I) {
-      *reinterpret_cast<i32x4*>(a.dwg + ((size_t)e * a.H + mm) * a.I + n) = o;
-    } else {
-      *reinterpret_cast<i32x4*>(a.dwu + ((size_t)e * a.H + mm) * a.I + (n - a.I)) = o;
-    }
-  });
-}
+struct WgradTile {
+  int e, m0, n0, nk;
+};
 
 // B2 (WHICH = 0): dWd[e] [I, H] = (w A)_e^T dY'_e (MX: Q(A)^T Q(w dY')).
 // B4 (WHICH = 1): [dWg | dWu][e] [H, 2I] = Xp_e^T [dG | dU]_e.
+template <int WHICH, bool AG, bool BG, bool MX>
+struct JWgrad {
+  using Tile = WgradTile;
+  using Ld = typename std::conditional<MX, LMx, LWgrad<AG, BG>>::type;
+  static constexpr bool A_KMAJ = false, B_KMAJ = false;
+  __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+  BwdArgs a;
+  MxArgs m;
+  int tm, tn;
+  int32_t* ids;
+  uint8_t* scring;
+  __device__ __forceinline__ int items() const { return a.El * tm * tn; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const {
+    p.e = uni(v / (tm * tn));
+    const int rem = uni(v - p.e * tm * tn);
+    p.m0 = uni(rem / tn) * BM;
+    p.n0 = uni(rem % tn) * BN;
+    if constexpr (MX) {
+      p.nk = uni((sload(m.poff + p.e + 1) - sload(m.poff + p.e)) / MX_STEP);
+    } else {
+      const int cnt = sload(a.offsets + p.e + 1) - sload(a.offsets + p.e);
+      p.nk = uni((cnt + BK - 1) / BK);
+    }
+  }
+  __device__ __forceinline__ bool active(const Tile&, int) const { return true; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm,
+                                          int wn) const {
+    if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    else mma_stage<JWgrad>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
+    const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
+    Tile t;
+    tile(v, t);
+    const int e = t.e, m0 = t.m0, n0 = t.n0;
+    p.pw = pw;
+    p.nk = t.nk;
+    if constexpr (MX) {
+      // transposed column-wise codes: rows are the output's M / N indices, K runs over
+      // the expert's padded row range [poff[e], poff[e + 1]); an expert without rows
+      // reads the zero area (its steps only keep the stream's counts)
+      const int k0 = sload(m.poff + e);
+      auto ra = [&](int r) { return min(m0 + r, M - 1); };
+      auto rb = [&](int r) { return min(n0 + r, N - 1); };
+      if (t.nk == 0) {
+        const uint8_t* z = reinterpret_cast<const uint8_t*>(a.zeros);
+        auto r0 = [](int) { return 0; };
+        p.setup(z, z, 0, r0, z, z, 0, r0, 0, scring, lane);
+      } else if (WHICH == 0) {
+        p.setup(m.qt_a, m.st_a, m.Rp, ra, m.qt_dy, m.st_dy, m.Rp, rb, k0, scring, lane);
+      } else {
+        p.setup(m.qt_x, m.st_x, m.Rp, ra, m.qt_dgu, m.st_dgu, m.Rp, rb, k0, scring, lane);
+      }
+    } else {
+      const int o0 = sload(a.offsets + e), o1 = sload(a.offsets + e + 1);
+      p.rs = o0;
+      p.cnt = uni(o1 - o0);
+      p.row_src = a.row_src; p.zeros = a.zeros; p.k = a.k;
+      p.lane = lane;
+      p.ids = ids + pw * 2 * IDS_SLOT;
+      if (WHICH == 0) {
+        p.abase = a.aw; p.lda = a.I;
+        p.bbase = a.dy; p.ldb = a.H;
+      } else {
+        p.abase = AG ? a.x : a.xp; p.lda = a.H;
+        p.bbase = a.dgu; p.ldb = 2 * a.I;
+      }
+#pragma unroll
+      for (int q = 0; q < A_LP; ++q) {
+        int r, c;
+        mnmaj_slot<BM>(load_slot(q, pw, lane), r, c);
+        const int col = m0 + c * 8;
+        p.acol[q] = col < M ? col : m0;
+      }
+#pragma unroll
+      for (int q = 0; q < B_LP; ++q) {
+        int r, c;
+        mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
+        const int col = n0 + c * 8;
+        p.bcol[q] = col < N ? col : n0;
+      }
+    }
+  }
+  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+    const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
+    const int e = p.e, m0 = p.m0, n0 = p.n0;
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&vv)[8]) {
+      const int mm = m0 + rt, n = n0 + ct;
+      if (mm >= M || n >= N) return;
+      const i32x4 o = pack8(vv);
+      if (WHICH == 0) {
+        *reinterpret_cast<i32x4*>(a.dwd + ((size_t)e * a.I + mm) * a.H + n) = o;
+      } else if (n < a.I) {
+        *reinterpret_cast<i32x4*>(a.dwg + ((size_t)e * a.H + mm) * a.I + n) = o;
+      } else {
+        *reinterpret_cast<i32x4*>(a.dwu + ((size_t)e * a.H + mm) * a.I + (n - a.I)) = o;
+      }
+    });
+  }
+};
+
 template <int WHICH, bool MX>
 __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int tm, int tn) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) int32_t ids[MX ? 4 : IDS_INTS];
   __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
-  for (Sched sc(a.El * tm * tn); sc.more(); sc.next()) {
-    const int e = sc.v / (tm * tn);
-    const int rem = sc.v - e * tm * tn;
-    const int mt = rem / tn, nt = rem - mt * tn;
-    if (MX) wgrad_tile<WHICH, false, false, true>(a, m, lds, ids, scring, e, mt * BM, nt * BN);
-    else if (WHICH == 0) wgrad_tile<0, false, true, false>(a, m, lds, ids, scring, e, mt * BM, nt * BN);
-    else if (a.xp) wgrad_tile<1, false, false, false>(a, m, lds, ids, scring, e, mt * BM, nt * BN);
-    else wgrad_tile<1, true, false, false>(a, m, lds, ids, scring, e, mt * BM, nt * BN);
+  if constexpr (MX) {
+    JWgrad<WHICH, false, false, true> job{a, m, tm, tn, ids, scring};
+    run_stream(job, lds);
+  } else if constexpr (WHICH == 0) {
+    JWgrad<0, false, true, false> job{a, m, tm, tn, ids, scring};
+    run_stream(job, lds);
+  } else {
+    if (a.xp) {
+      JWgrad<1, false, false, false> job{a, m, tm, tn, ids, scring};
+      run_stream(job, lds);
+    } else {
+      JWgrad<1, true, false, false> job{a, m, tm, tn, ids, scring};
+      run_stream(job, lds);
+    }
   }
 }
 

@@ -1,14 +1,23 @@
 // Shared GEMM engine of the bf16 and MXFP8 grouped GEMMs (internal header).
 //
-// Persistent 512-thread workgroups (8 wave64, one workgroup per CU), 128x256 output
-// tile, each wave a 64x64 sub-tile as 32x32 MFMA accumulator blocks.  Operand tiles
+// Persistent 768-thread workgroups (one per CU): 8 compute waves and 4 load waves.
+// 128x256 output tile, each compute wave a 64x64 sub-tile as 32x32 MFMA accumulator
+// blocks.  Operand tiles
 // move global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4)
-// into an LDS ring, issued DEPTH K steps ahead, one barrier per K step.  An operand
-// whose contraction axis is contiguous in memory ("K-major") is stored [rows][BK] and
-// read with 16-byte LDS reads; an operand contiguous along M or N ("MN-major") is
-// stored [BK][width] and read with the transposing LDS read ds_read_b64_tr_b16.  Both
-// layouts are XOR-swizzled by 16-byte chunk against LDS bank conflicts; the swizzle is
-// applied by choosing which global chunk each lane of a direct-to-LDS load fetches.
+// into a three-stage LDS ring, issued two K steps ahead, one barrier per K step.  An
+// operand whose contraction axis is contiguous in memory ("K-major") is stored
+// [rows][BK] and read with 16-byte LDS reads; an operand contiguous along M or N
+// ("MN-major") is stored [BK][width] and read with the transposing LDS read
+// ds_read_b64_tr_b16.  Both layouts are XOR-swizzled by 16-byte chunk against LDS bank
+// conflicts; the swizzle is applied by choosing which global chunk each lane of a
+// direct-to-LDS load fetches.
+//
+// A workgroup's tiles form one stream of K steps: the loads of the next tile's first
+// steps are issued while the current tile's last steps compute, and the current
+// tile's epilogue runs in the ring stage that its last step freed while those loads
+// are in flight.  Tile descriptors and gathered row indices are read with scalar
+// loads, so each load wave's vector memory counter holds only its own direct-to-LDS
+// loads and its waits stay exact.
 #pragma once
 
 #include "common.h"
@@ -16,29 +25,39 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 8
-#endif
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-constexpr int BM = 128, BN = 256, BK = MOE_GEMM_BK;
-constexpr int NSTAGE = BK == 64 ? 3 : 6;  // LDS ring stages (48 KB or 24 KB each)
-constexpr int DEPTH = NSTAGE - 1;         // K steps in flight ahead of the MFMAs
-constexpr int NW = MOE_GEMM_WAVES;   // waves per workgroup: 2 along M x NW/2 along N
-constexpr int NTHR = 64 * NW;
-constexpr int WN = NW / 2;           // waves along N
+constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int NSTAGE = 3;            // LDS ring stages (48 KB each)
+constexpr int DEPTH = NSTAGE - 1;    // K steps in flight ahead of the MFMAs
+constexpr int NW = 8;                // compute waves: 2 along M x 4 along N
+constexpr int NP = 8;                // load (producer) waves, two per SIMD
+constexpr int NTHR = 64 * (NW + NP);
+constexpr int WN = NW / 2;           // compute waves along N
 constexpr int NI = 8 / WN;           // 32-column accumulator blocks per wave
 constexpr int WCOLS = 32 * NI;       // columns per wave
 constexpr int A_ELEMS = BM * BK;                  // 8192 bf16
 constexpr int B_ELEMS = BN * BK;                  // 16384 bf16
 constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;    // 48 KB per stage
-constexpr int A_LOADS = A_ELEMS * 2 / 16 / NTHR;  // 16-byte loads per thread per stage
-constexpr int B_LOADS = B_ELEMS * 2 / 16 / NTHR;
-constexpr int LOADS = A_LOADS + B_LOADS;
+constexpr int A_INSTR = A_ELEMS * 2 / 1024;       // 1 KB wave loads per stage: 16 for A
+constexpr int B_INSTR = B_ELEMS * 2 / 1024;       // and 32 for B
+constexpr int A_LP = A_INSTR / NP;                // per load wave: 4 of A
+constexpr int B_LP = B_INSTR / NP;                // and 8 of B
+constexpr int LOADS = A_LP + B_LP;                // operand loads per load wave per stage
 constexpr int LDS_ELEMS = NSTAGE * STAGE_ELEMS;   // 144 KB
 constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
-constexpr int IDS_INTS = NW * 2 * IDS_SLOT;       // per wave, two K steps of gathered row indices
+constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per load wave, two positions of gathered row indices
+constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least
+
+// ---- scalar loads ----
+// A wave-uniform load through the scalar data cache (address space 4): it is counted
+// by lgkmcnt, not vmcnt.  The address is made wave-uniform.
+template <class T>
+__device__ __forceinline__ T sload(const T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return *(const __attribute__((address_space(4))) T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ---- LDS layouts (16-byte chunk granularity) ----
 // K-major [rows][BK]: CPR_K chunks per row, RPW rows per 256-byte bank window; chunk c
@@ -61,14 +80,15 @@ __device__ __forceinline__ void mnmaj_slot(int s, int& r, int& c) {
   c = mnmaj_chunk(r, s % CPR);
 }
 
-// Slot written by load q of this thread: each wave instruction fills 64 consecutive
-// slots (1 KB), lane l the l-th.
-__device__ __forceinline__ int load_slot(int q, int wv, int lane) { return (q * NW + wv) * 64 + lane; }
+// Wave load q of load wave pw is instruction q * NP + pw of its region; instruction I
+// fills slots 64 I .. 64 I + 63 (1 KB), lane l the l-th.
+__device__ __forceinline__ int load_instr(int q, int pw) { return q * NP + pw; }
+__device__ __forceinline__ int load_slot(int q, int pw, int lane) { return load_instr(q, pw) * 64 + lane; }
 
 // Direct-to-LDS loads, written as inline assembly: the wave's 64 lanes each fetch 16
 // (or 4) bytes from their own global address into consecutive LDS slots starting at
 // the wave-uniform base held in M0.  The compiler does not see these as LDS writes, so
-// it adds no waits of its own; the main loop orders them with explicit vmcnt waits.
+// it adds no waits of its own; the stream orders them with explicit vmcnt waits.
 // M0 is restored after each load.
 __device__ __forceinline__ void dma16(const void* g, bf16_t* lds_wave_base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((MOE_LDS void*)lds_wave_base));
@@ -82,6 +102,9 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(g), "s"(m) : "memory");
 }
+// LDS address of wave load q of load wave pw in the A or B region of a stage
+__device__ __forceinline__ bf16_t* a_dst(bf16_t* st, int q, int pw) { return st + load_instr(q, pw) * 512; }
+__device__ __forceinline__ bf16_t* b_dst(bf16_t* st, int q, int pw) { return st + A_ELEMS + load_instr(q, pw) * 512; }
 
 // MFMA 32x32x16 operand fragment: lane l gets 8 consecutive k of row/col (l & 31),
 // k = 8 * (l >> 5) .. +7 inside the 16-wide k sub-step kk.
@@ -111,7 +134,8 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const bf16_t* s, int base, int kk, 
   return out;
 }
 
-template <class P>
+// The bf16 MFMAs of one stage for a job J (J::A_KMAJ, J::B_KMAJ, J::ncol).
+template <class J>
 __device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][NI], int lane, int wm, int wn) {
   const bf16_t* As = st;
   const bf16_t* Bs = st + A_ELEMS;
@@ -120,10 +144,10 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][NI]
     bf16x8 af[2], bf[NI];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
-      af[mi] = P::A_KMAJ ? frag_kmaj(As, wm * 64 + mi * 32, kk, lane) : frag_mnmaj<BM>(As, wm * 64 + mi * 32, kk, lane);
+      af[mi] = J::A_KMAJ ? frag_kmaj(As, wm * 64 + mi * 32, kk, lane) : frag_mnmaj<BM>(As, wm * 64 + mi * 32, kk, lane);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
-      bf[ni] = P::B_KMAJ ? frag_kmaj(Bs, P::ncol(wn, ni), kk, lane) : frag_mnmaj<BN>(Bs, P::ncol(wn, ni), kk, lane);
+      bf[ni] = J::B_KMAJ ? frag_kmaj(Bs, J::ncol(wn, ni), kk, lane) : frag_mnmaj<BN>(Bs, J::ncol(wn, ni), kk, lane);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -132,64 +156,181 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][NI]
   }
 }
 
-// bf16 policies: the MFMAs of one stage
-template <class Derived>
-struct Bf16Mma {
-  __device__ void compute(const bf16_t* st, int, f32x16 (&acc)[2][NI], int lane, int wm, int wn) const {
-    mma_stage<Derived>(st, acc, lane, wm, wn);
-  }
-};
-
-// The main loop over nk K steps.  P::issue(kt, stage, slot) issues this thread's P::NVMEM
-// direct-to-LDS loads of K step kt and no other vector memory instruction.  Loads run
-// two steps ahead (the step index is clamped, so the count in flight is fixed); before
-// reading a stage each thread waits for its own loads of that stage, and the barrier
-// then makes every thread's loads visible and frees the stage the next loads
-// overwrite.  `active` is false for waves whose 64 rows all lie past the tile's valid
-// rows: they skip the MFMAs.
-template <class P>
-__device__ __forceinline__ void mainloop(P& p, int nk, bf16_t* lds, f32x16 (&acc)[2][NI], bool active) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][NI]) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
-  if (nk <= 0) return;
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) p.issue(min(d, nk - 1), lds + d * STAGE_ELEMS, d);
-  int cur = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // wait for this thread's loads of step kt (the DEPTH - 1 later steps may still
-    // fly) and its LDS reads of step kt - 1, then a plain barrier (__syncthreads()
-    // would also wait for every load in flight)
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((DEPTH - 1) * P::NVMEM) : "memory");
-    const int nxt = cur == 0 ? NSTAGE - 1 : cur - 1;  // (kt + DEPTH) % NSTAGE: the stage read in step kt - 1
-    p.issue(min(kt + DEPTH, nk - 1), lds + nxt * STAGE_ELEMS, nxt);
-    if (active) p.compute(lds + cur * STAGE_ELEMS, cur, acc, lane, wm, wn);
-    cur = cur == NSTAGE - 1 ? 0 : cur + 1;
+}
+
+// ---- persistent scheduling ----
+// Workgroup b runs on XCD b % 8.  The V work items are split into 8 contiguous
+// ranges, one per XCD, and the XCD's workgroups walk their range in order, so work
+// items sharing operands run together on one XCD and share its L2.
+struct Sched {
+  int v, hi, step;
+  __device__ explicit Sched(int V) {
+    const int x = blockIdx.x & 7;
+    const int lo = (int)(((int64_t)V * x) >> 3);
+    hi = (int)(((int64_t)V * (x + 1)) >> 3);
+    v = lo + (int)(blockIdx.x >> 3);
+    step = (int)(gridDim.x >> 3);
   }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // the trailing duplicate loads
+};
+
+// ---- the tile stream ----
+// A workgroup has NW compute waves and NP load waves.  Its tiles form one stream of K
+// steps ("positions"); every tile takes max(nk, MIN_STEPS) positions, positions past
+// nk repeating a valid step's loads and skipping the MFMAs.  At each position the
+// load waves wait for their own loads of that position, all waves meet at a barrier,
+// the load waves issue the loads of the position DEPTH ahead (possibly the next
+// tile's) into the stage read one position ago, and the compute waves run the MFMAs
+// of the position.  After a tile's last position all waves meet once more and the
+// compute waves run the tile's epilogue in the stage just read, while the load waves
+// wait at the next position's barrier with DEPTH positions in flight.  Load-issue
+// stalls (the vector memory queue of a CU drains at a fixed rate) hold only the load
+// waves, and the compute waves issue no loads of their own besides the epilogue's.
+//
+// A job J supplies: items(); steps(v) (K steps of item v; scalar loads only); the
+// compute side -- Tile, tile(v, Tile&) (what the epilogue needs, scalar loads only),
+// active(const Tile&, wm), compute(stage pointer, stage index, acc, lane, wm, wn) and
+// epilogue(const Tile&, acc, staging); and the load side -- Ld, setup(v, Ld&, pw,
+// lane) and Ld::NVMEM, Ld::GATHER, Ld::issue(kt, stage pointer, stage index, parity,
+// fetch_next) and Ld::fetch(kt, parity).  Each issue makes exactly NVMEM vector memory
+// instructions (fetch_next, when the loader calls it, is one of them: it fetches the
+// row indices of the next position into the other index slot), which keeps the vmcnt
+// waits exact.
+template <class J>
+__device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, Sched sc, int wv, int lane) {
+  using T = typename J::Tile;
+  const int wm = wv & 1, wn = wv >> 1;
+  T cur, nxt;
+  job.tile(sc.v, cur);
+  int v = sc.v;
+  f32x16 acc[2][NI];
+  zero_acc(acc);
+  int cs = 0;
+  for (;;) {
+    const int nk = cur.nk, len = max(nk, MIN_STEPS);
+    const bool more = v + sc.step < sc.hi;
+    const bool act = __builtin_amdgcn_readfirstlane((int)job.active(cur, wm)) != 0;
+    int done = 0;
+    for (int kc = 0; kc < len; ++kc) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kc < nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wm, wn);
+      if (kc == 0 && more) job.tile(v + sc.step, nxt);
+      done = cs;
+      cs = cs == NSTAGE - 1 ? 0 : cs + 1;
+    }
+    // every wave is done with the stage just read: stage the results there
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    job.epilogue(cur, acc, reinterpret_cast<float*>(lds + done * STAGE_ELEMS));
+    zero_acc(acc);
+    if (!more) break;
+    cur = nxt;
+    v += sc.step;
+  }
+}
+
+template <class J>
+__device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, Sched sc, int pw, int lane) {
+  using P = typename J::Ld;
+  P cur, nxt;
+  job.setup(sc.v, cur, pw, lane);
+  int vc = sc.v;                            // item of cur
+  int lc = max(cur.nk, MIN_STEPS), ln = 0;  // stream positions of cur and nxt
+  bool has_nxt = false, looked = false;     // nxt set up; the item after cur looked up
+  bool in_nxt = false;                      // the issue cursor is in nxt
+  int ik = 0;                               // issue cursor: step within its tile
+  int gpar = 0;                             // parity of the issue position
+  auto clampk = [](int kt, int nk) { return max(0, min(kt, nk - 1)); };
+  auto issue = [&](int stage) {
+    bf16_t* st = lds + stage * STAGE_ELEMS;
+    if (in_nxt) {
+      // never the last position of nxt: the compute cursor enters nxt first
+      const int k0 = ik;
+      nxt.issue(clampk(k0, nxt.nk), st, stage, gpar, [&] { nxt.fetch(k0 + 1, gpar ^ 1); });
+      ++ik;
+    } else {
+      const int k0 = ik;
+      const bool last = k0 >= lc - 1;
+      if (last && !looked) {
+        looked = true;
+        const int vn = vc + sc.step;
+        if (vn < sc.hi) {
+          job.setup(vn, nxt, pw, lane);
+          ln = max(nxt.nk, MIN_STEPS);
+          has_nxt = true;
+        }
+      }
+      cur.issue(clampk(k0, cur.nk), st, stage, gpar, [&] {
+        if (!last) cur.fetch(k0 + 1, gpar ^ 1);
+        else if (has_nxt) nxt.fetch(0, gpar ^ 1);
+        else cur.fetch(k0, gpar ^ 1);
+      });
+      if (!last) ++ik;
+      else if (has_nxt) { in_nxt = true; ik = 0; }
+    }
+    gpar ^= 1;
+  };
+  if (P::GATHER) {
+    cur.fetch(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d);
+  int cs = 0, kc = 0;
+  for (;;) {
+    // this wave's loads of the position have landed (the DEPTH - 1 later positions may
+    // still fly); the barrier then hands the stage to the compute waves and frees the
+    // stage they read one position ago
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"((DEPTH - 1) * P::NVMEM) : "memory");
+    issue(cs == 0 ? NSTAGE - 1 : cs - 1);  // (position + DEPTH) % NSTAGE
+    cs = cs == NSTAGE - 1 ? 0 : cs + 1;
+    if (++kc < lc) continue;
+    asm volatile("s_barrier" ::: "memory");  // the compute waves' epilogue barrier
+    if (!has_nxt) break;
+    cur = nxt;
+    vc += sc.step;
+    lc = ln;
+    has_nxt = looked = in_nxt = false;
+    kc = 0;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing repeated loads
+}
+
+template <class J>
+__device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6);
+  Sched sc(job.items());
+  if (sc.v >= sc.hi) return;
+  if (wv >= NW) load_stream(job, lds, sc, wv - NW, lane);
+  else compute_stream(job, lds, sc, wv, lane);
 }
 
 // ---- epilogue staging ----
-// After the main loop the LDS ring is free.  Each wave writes one 32-row half (mi) of
-// its 64 x WCOLS fp32 accumulator to its own [32][EP_LD] region, so that lanes can then
-// read 8 consecutive columns of one row and issue 16-byte global loads and stores.
+// Each wave stages 16-row quarters of its 64 x WCOLS fp32 accumulator in its own
+// [16][EP_LD] region of the free ring stage, so that lanes can then read 8 consecutive
+// columns of one row and issue 16-byte global loads and stores.  The regions are
+// private to their waves, so no workgroup barrier is needed between quarters.
 constexpr int EP_LD = WCOLS + 8;  // row stride in floats: rows r and r + 4 fall on disjoint banks
-static_assert(NW * 32 * EP_LD * 4 <= LDS_ELEMS * 2, "epilogue staging must fit in the LDS ring");
+constexpr int EP_ROWS = 16;
+static_assert(NW * EP_ROWS * EP_LD * 4 <= STAGE_ELEMS * 2, "epilogue staging must fit in one ring stage");
 
-__device__ __forceinline__ void stage_acc(float* wsm, const f32x16 (&acc)[2][NI], int mi, int lane) {
+// stage rows 16 h .. 16 h + 15 of accumulator block row mi (registers 8 h .. 8 h + 7)
+__device__ __forceinline__ void stage_quarter(float* wsm, const f32x16 (&acc)[2][NI], int mi, int h, int lane) {
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int r = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      wsm[r * EP_LD + ni * 32 + (lane & 31)] = acc[mi][ni][i];
+      wsm[r * EP_LD + ni * 32 + (lane & 31)] = acc[mi][ni][8 * h + i];
     }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
+__device__ __forceinline__ void staging_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -219,65 +360,69 @@ __device__ __forceinline__ void unpack8(i32x4 u, float (&v)[8]) {
 constexpr int EP_LPR = WCOLS / 8;      // lanes per row
 constexpr int EP_RPP = 64 / EP_LPR;    // rows per pass
 template <class F>
-__device__ __forceinline__ void epilogue_rows(bf16_t* lds, const f32x16 (&acc)[2][NI], F&& f) {
+__device__ __forceinline__ void epilogue_rows(float* stage, const f32x16 (&acc)[2][NI], F&& f) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
-  float* wsm = reinterpret_cast<float*>(lds) + wv * 32 * EP_LD;
+  float* wsm = stage + wv * EP_ROWS * EP_LD;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    stage_acc(wsm, acc, mi, lane);
-    __syncthreads();
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int j = 0; j < 32 / EP_RPP; ++j) {
-      const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
-      float v[8];
-      read8(wsm + rr * EP_LD + cc, v);
-      f(wm * 64 + mi * 32 + rr, wn * WCOLS + cc, v);
+    for (int h = 0; h < 2; ++h) {
+      stage_quarter(wsm, acc, mi, h, lane);
+#pragma unroll
+      for (int j = 0; j < EP_ROWS / EP_RPP; ++j) {
+        const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
+        float v[8];
+        read8(wsm + rr * EP_LD + cc, v);
+        f(wm * 64 + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v);
+      }
+      staging_done();
     }
-    __syncthreads();
-  }
 }
 
-// ---- persistent scheduling ----
-// Workgroup b runs on XCD b % 8.  The V work items are split into 8 contiguous
-// ranges, one per XCD, and the XCD's workgroups walk their range in order, so work
-// items sharing operands run together on one XCD and share its L2.
-struct Sched {
-  int v, hi, step;
-  __device__ explicit Sched(int V) {
-    const int x = blockIdx.x & 7;
-    const int lo = (int)(((int64_t)V * x) >> 3);
-    hi = (int)(((int64_t)V * (x + 1)) >> 3);
-    v = lo + (int)(blockIdx.x >> 3);
-    step = (int)(gridDim.x >> 3);
-  }
-  __device__ bool more() const { return v < hi; }
-  __device__ void next() { v += step; }
-};
-
 // Row-group tile: virtual item v -> expert, first row, valid rows and column tile, in
-// the expert-major order of the tile table (k_tile_table).
+// the expert-major order of the tile table (k_tile_table).  Scalar loads only.
 struct RowTile {
   int e, rs, cnt, nt;
 };
 __device__ __forceinline__ void row_tile(const int32_t* tiles, const int32_t* offsets, int v, int NT, RowTile& t) {
-  const int q = v / NT;
-  const i32x4 ent = *reinterpret_cast<const i32x4*>(tiles + 4 + 4 * q);
-  t.e = ent[0];
-  const int local = v - ent[1] * NT;
-  const int mt = local % ent[2];
-  t.nt = local / ent[2];
-  t.rs = offsets[t.e] + mt * BM;
-  t.cnt = min(BM, offsets[t.e + 1] - t.rs);
+  const int q = uni(v / NT);
+  const i32x4 ent = sload(reinterpret_cast<const i32x4*>(tiles + 4 + 4 * q));
+  t.e = uni(ent[0]);
+  const int local = uni(v - ent[1] * NT);
+  const int mt = uni(local % ent[2]);
+  t.nt = uni(local / ent[2]);
+  const int o0 = sload(offsets + t.e), o1 = sload(offsets + t.e + 1);
+  t.rs = uni(o0 + mt * BM);
+  t.cnt = uni(min(BM, o1 - t.rs));
 }
 
-// K-major operand with fixed rows: per load q, the row pointer (already offset by the
-// lane's chunk) of the slot it fills; step kt adds kt * 64 elements.
-template <int NL>
-struct KRows {
-  const bf16_t* p[NL];
-  __device__ void issue(int kt, bf16_t* tile, int wv) const {
+// Row-source indices of the A rows a load wave's K-major loads cover (load q fills rows
+// 8 I .. 8 I + 7 of the tile, I = q * NP + pw, lane l row 8 I + l / 8), clamped to the
+// tile's valid rows, read with scalar loads and selected per lane.
+__device__ __forceinline__ void gather_rows_a(const int32_t* row_src, const RowTile& t, int pw, int lane,
+                                              int (&src)[A_LP]) {
+  static_assert(CPR_K == 8, "a wave load covers 8 rows of 8 chunks");
+  const int j = lane >> 3;
 #pragma unroll
-    for (int q = 0; q < NL; ++q) dma16(p[q] + kt * BK, tile + (q * NW + wv) * 64 * 8);
+  for (int q = 0; q < A_LP; ++q) {
+    const int r0 = load_instr(q, pw) * 8;
+    int s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = sload(row_src + t.rs + min(r0 + i, t.cnt - 1));
+    const int lo = (j & 1) ? s[1] : s[0], lo2 = (j & 1) ? s[3] : s[2];
+    const int hi = (j & 1) ? s[5] : s[4], hi2 = (j & 1) ? s[7] : s[6];
+    const int a = (j & 2) ? lo2 : lo, b = (j & 2) ? hi2 : hi;
+    src[q] = (j & 4) ? b : a;
+  }
+}
+
+// K-major operand with fixed rows: per wave load q, the row pointer (already offset by
+// the lane's chunk) of the slot it fills; step kt adds kt * 64 elements.
+struct KRows {
+  const bf16_t* p[A_LP];
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int pw) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) dma16(p[q] + kt * BK, a_dst(st, q, pw));
   }
 };
 
@@ -301,7 +446,6 @@ inline int grid_for(int64_t work) {
   g = (g + 7) & ~7;
   return g < 8 ? 8 : g;
 }
-
 
 }  // namespace
 }  // namespace moe
