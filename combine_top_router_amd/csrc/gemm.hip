@@ -409,22 +409,36 @@ struct JDa {
       if (ok) {
         const size_t r = (size_t)(p.t.rs + rt);
         const float w = a.topk_w[a.row_src[r]];
-        float g[8], u[8], av[8], dg[8], du[8], aw[8];
-        unpack8(*reinterpret_cast<const i32x4*>(a.gu + r * I2 + col), g);
-        unpack8(*reinterpret_cast<const i32x4*>(a.gu + r * I2 + a.I + col), u);
-        unpack8(*reinterpret_cast<const i32x4*>(a.a + r * a.I + col), av);
+        // two columns at a time, straight from and back to packed bf16 pairs
+        __builtin_amdgcn_sched_barrier(0);
+        const i32x4 gw = *reinterpret_cast<const i32x4*>(a.gu + r * I2 + col);
+        const i32x4 uw = *reinterpret_cast<const i32x4*>(a.gu + r * I2 + a.I + col);
+        const i32x4 aw4 = *reinterpret_cast<const i32x4*>(a.a + r * a.I + col);
+        i32x4 dgo, duo, awo;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          part += dap[q] * av[q];
-          aw[q] = w * av[q];
-          const float da = w * dap[q];
-          const float sg = sigmoid_f(g[q]);
-          du[q] = da * g[q] * sg;
-          dg[q] = da * u[q] * sg * (1.f + g[q] * (1.f - sg));
+        for (int q = 0; q < 4; ++q) {
+          float dg2[2], du2[2], aw2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t gb = (uint32_t)gw[q], ub = (uint32_t)uw[q], ab = (uint32_t)aw4[q];
+            const float g = __uint_as_float(h ? gb & 0xffff0000u : gb << 16);
+            const float u = __uint_as_float(h ? ub & 0xffff0000u : ub << 16);
+            const float av = __uint_as_float(h ? ab & 0xffff0000u : ab << 16);
+            const float d = dap[2 * q + h];
+            part += d * av;
+            aw2[h] = w * av;
+            const float da = w * d;
+            const float sg = sigmoid_f(g);
+            du2[h] = da * g * sg;
+            dg2[h] = da * u * sg * (1.f + g * (1.f - sg));
+          }
+          dgo[q] = (int)((uint32_t)f2bf(dg2[0]) | ((uint32_t)f2bf(dg2[1]) << 16));
+          duo[q] = (int)((uint32_t)f2bf(du2[0]) | ((uint32_t)f2bf(du2[1]) << 16));
+          awo[q] = (int)((uint32_t)f2bf(aw2[0]) | ((uint32_t)f2bf(aw2[1]) << 16));
         }
-        *reinterpret_cast<i32x4*>(a.dgu + r * I2 + col) = pack8(dg);
-        *reinterpret_cast<i32x4*>(a.dgu + r * I2 + a.I + col) = pack8(du);
-        if (!MX) *reinterpret_cast<i32x4*>(a.aw + r * a.I + col) = pack8(aw);
+        *reinterpret_cast<i32x4*>(a.dgu + r * I2 + col) = dgo;
+        *reinterpret_cast<i32x4*>(a.dgu + r * I2 + a.I + col) = duo;
+        if (!MX) *reinterpret_cast<i32x4*>(a.aw + r * a.I + col) = awo;
       }
 #pragma unroll
       for (int off = 1; off < EP_LPR; off <<= 1) part += __shfl_xor(part, off, 64);

@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_combine<bf16_t>(const bf16_t* __restric
     for (int j = 0; j < 16; ++j) {
       const int r = rr[j];
       if (j >= k || r < 0) continue;
-      const i32x4 v = reinterpret_cast<const i32x4*>(rows + (size_t)r * H)[c];
+      const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(rows + (size_t)r * H) + c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += __uint_as_float(((uint32_t)v[q]) << 16);
