@@ -368,7 +368,7 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const f32x16 (&acc)[
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       stage_quarter(wsm, acc, mi, h, lane);
-#pragma unroll
+#pragma unroll 1
       for (int j = 0; j < EP_ROWS / EP_RPP; ++j) {
         const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
         float v[8];

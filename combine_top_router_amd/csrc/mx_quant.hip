@@ -95,18 +95,26 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
   }
 }
 
-// Column-wise, transposed: one workgroup per (padded 32-row block, 256 columns).  The
-// block's rows are staged in LDS as fp32 (after the optional gather and row scaling),
-// then thread t quantizes column n0 + t: 32 codes to qt[n][pb*32 ..] and one scale.
+// Column-wise, transposed: one workgroup per (padded 128-row chunk, 64 columns); a chunk
+// lies inside one expert's padded segment (segments are multiples of 128 rows).  The
+// chunk's row sources and weights are read once into LDS and its rows staged as fp32
+// (after the optional gather and row scaling); thread t quantizes the 32-row block
+// t / 64 of column t % 64 into LDS, and the workgroup then writes each column's 128
+// codes as one 128-byte line and its four scales as one word.
+constexpr int COL_ROWS = 128, COL_COLS = 64;
+static_assert(COL_ROWS == kMxRowPad, "a column chunk spans one padding unit");
 __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
                                                  const int32_t* __restrict__ row_src, int k,
                                                  const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ poff, int El, int N, int Rp,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ stt) {
-  __shared__ float tile[32][257];
-  const int pb = blockIdx.x;                 // padded block of 32 rows
-  const int pr0 = pb * 32;
+  __shared__ float tile[COL_ROWS][COL_COLS + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t codes[COL_COLS][COL_ROWS / 4];
+  __shared__ uint32_t scales[COL_COLS];
+  __shared__ int srow[COL_ROWS];
+  __shared__ float wrow[COL_ROWS];
+  const int pr0 = blockIdx.x * COL_ROWS;     // padded row of the chunk
   if (pr0 >= poff[El]) return;
   int lo = 0, hi = El - 1;                   // expert: last e with poff[e] <= pr0
   while (lo < hi) {
@@ -115,18 +123,31 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
   }
   const int e = lo;
   const int r0 = offsets[e] + (pr0 - poff[e]);
-  const int nrow = min(32, offsets[e + 1] - r0);   // may be <= 0 in an expert's padding
-  const int n0 = blockIdx.y * 256;
+  const int nrow = min(COL_ROWS, offsets[e + 1] - r0);   // may be <= 0 in an expert's padding
+  const int n0 = blockIdx.y * COL_COLS;
   const int tid = threadIdx.x;
-  // stage: 32 rows x 256 columns, 16-byte loads (4 per thread)
-  for (int i = tid; i < 32 * 32; i += 256) {
-    const int rr = i >> 5, cc = (i & 31) * 8;
+  if (tid < COL_ROWS) {
+    int sr = 0;
+    float w = 1.f;
+    if (tid < nrow) {
+      const int r = r0 + tid;
+      const int s = row_src ? row_src[r] : 0;
+      sr = row_src ? s / k : r;
+      if (topk_w) w = topk_w[s];
+    }
+    srow[tid] = sr;
+    wrow[tid] = w;
+  }
+  __syncthreads();
+  // stage: 128 rows x 64 columns, one 16-byte load per (row, 8 columns)
+#pragma unroll
+  for (int it = 0; it < COL_ROWS * (COL_COLS / 8) / 256; ++it) {
+    const int i = tid + 256 * it;
+    const int rr = i / (COL_COLS / 8), cc = (i % (COL_COLS / 8)) * 8;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (rr < nrow && n0 + cc < N) {
-      const int r = r0 + rr;
-      const int sr = row_src ? row_src[r] / k : r;
-      const i32x4 u = *reinterpret_cast<const i32x4*>(src + (size_t)sr * ld + n0 + cc);
-      const float w = topk_w ? topk_w[row_src[r]] : 1.f;
+      const i32x4 u = *reinterpret_cast<const i32x4*>(src + (size_t)srow[rr] * ld + n0 + cc);
+      const float w = wrow[rr];
 #pragma unroll
       for (int j = 0; j < 4; ++j) { v[2 * j] = bf_lo((uint32_t)u[j]) * w; v[2 * j + 1] = bf_hi((uint32_t)u[j]) * w; }
     }
@@ -134,24 +155,34 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
     for (int j = 0; j < 8; ++j) tile[rr][cc + j] = v[j];
   }
   __syncthreads();
-  const int n = n0 + tid;
-  if (n >= N) return;
-  float am = 0.f;
+  {
+    const int c = tid % COL_COLS, b = tid / COL_COLS;   // column, 32-row block
+    float am = 0.f;
 #pragma unroll
-  for (int rr = 0; rr < 32; ++rr) am = fmaxf(am, fabsf(tile[rr][tid]));
-  const int X = mx_scale_exp(am);
-  uint32_t w[8];
+    for (int rr = 0; rr < 32; ++rr) am = fmaxf(am, fabsf(tile[b * 32 + rr][c]));
+    const int X = mx_scale_exp(am);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t acc = 0;
+    for (int j = 0; j < 8; ++j) {
+      uint32_t acc = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc |= e4m3_code(tile[4 * j + b][tid], X) << (8 * b);
-    w[j] = acc;
+      for (int q = 0; q < 4; ++q) acc |= e4m3_code(tile[b * 32 + 4 * j + q][c], X) << (8 * q);
+      codes[c][b * 8 + j] = acc;
+    }
+    reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
   }
-  uint8_t* dst = qt + (size_t)n * Rp + pr0;
-  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-  stt[(size_t)n * (Rp / 32) + pb] = (uint8_t)(X + 127);
+  __syncthreads();
+  // write-out: 64 columns x 128 codes, eight lanes per 128-byte line
+#pragma unroll
+  for (int it = 0; it < COL_COLS * 8 / 256; ++it) {
+    const int i = tid + 256 * it;
+    const int c = i / 8, part = i % 8;
+    const int n = n0 + c;
+    if (n < N)
+      *reinterpret_cast<uint4*>(qt + (size_t)n * Rp + pr0 + part * 16) =
+          *reinterpret_cast<const uint4*>(&codes[c][part * 4]);
+  }
+  if (tid < COL_COLS && n0 + tid < N)
+    *reinterpret_cast<uint32_t*>(stt + (size_t)(n0 + tid) * (Rp / 32) + pr0 / 32) = scales[tid];
 }
 
 // padded offsets: every expert's rows rounded up to kMxRowPad
@@ -187,7 +218,8 @@ hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int
                           const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
                           uint8_t* stt, const char* name, hipStream_t st) {
   if (Rp <= 0) return hipSuccess;
-  MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / 32), (unsigned)ceil_div(N, 256)), dim3(256), 0, st, src, ld,
+  MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / COL_ROWS), (unsigned)ceil_div(N, COL_COLS)), dim3(256), 0, st,
+             src, ld,
              row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt);
   return hipGetLastError();
 }
