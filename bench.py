@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_30b", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of one captured HIP graph per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -174,16 +176,40 @@ def main():
     torch.cuda.synchronize()
     R = int(layer.offsets[-1].item())
 
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(stop) / args.steps
+    def timed(run):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            run()
+        stop.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
+    # the step's launches (no allocation, no host synchronisation inside) captured
+    # once as a HIP graph and replayed: the same kernels without per-launch gaps
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_on = lambda: (layer.forward(logits, x, wg, wu, wd), layer.backward(dy))
+            step_on()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer.forward(logits, x, wg, wu, wd)
+            layer.backward(dy)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    eager_ms, eager_wall = timed(step)
+    if graph is not None:
+        ms, wall = timed(graph.replay)
+    else:
+        ms, wall = eager_ms, eager_wall
 
     # per-kernel durations from HIP events recorded inside the library on the launch stream
     L.moe_timing_enable(True)
@@ -231,6 +257,8 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "launch": "eager" if graph is None else "hip_graph",
+        "eager_ms_per_step": round(eager_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16+mxfp8" if mx else "bf16", "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "T": cfg.T, "H": cfg.H, "I": cfg.I,
