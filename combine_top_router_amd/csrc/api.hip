@@ -47,7 +47,7 @@ struct Layout {
   // saved
   size_t off_gu, off_a, saved_bytes;
   // scratch
-  size_t off_tiles, off_zeros, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
+  size_t off_tiles, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
   // MXFP8 backward buffers (scratch), 0 when unused
   int64_t Rp;
   size_t off_mx[17];
@@ -90,7 +90,8 @@ void layout(const moe_shape& s, Layout& L) {
   const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
   L.off_tiles = 0;
   L.off_zeros = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
-  L.off_dgu = L.off_zeros + align_up(kZeroBytes);
+  L.off_order = L.off_zeros + align_up(kZeroBytes);
+  L.off_dgu = L.off_order + align_up((size_t)(El + 1) * 4);
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
   L.off_part = L.off_dxp + align_up(R * s.H * L.es);
   L.off_aw = L.off_part + align_up(R * L.nparts * 4);
@@ -269,7 +270,7 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
   hipError_t e;
   if (s.dtype == MOE_BF16) {
     int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    e = launch_tile_table(s, offsets, kGemmBM, tiles, nullptr, st);
+    e = launch_tile_table(s, offsets, kGemmBM, tiles, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     FwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
@@ -331,7 +332,8 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   hipError_t e;
   if (s.dtype == MOE_BF16) {
     int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    e = launch_tile_table(s, offsets, kGemmBM, tiles, at<int32_t>(scratch, L.off_zeros), st);
+    e = launch_tile_table(s, offsets, kGemmBM, tiles, at<int32_t>(scratch, L.off_zeros),
+                          at<int32_t>(scratch, L.off_order), st);
     if (e != hipSuccess) return hip_status(e, __func__);
     BwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
@@ -342,6 +344,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.dgu = at<bf16_t>(scratch, L.off_dgu); a.dxp = at<bf16_t>(scratch, L.off_dxp);
     a.dw_part = at<float>(scratch, L.off_part);
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
+    a.order = at<int32_t>(scratch, L.off_order);
     a.dwg = (bf16_t*)dw_gate; a.dwu = (bf16_t*)dw_up; a.dwd = (bf16_t*)dw_down;
     if (s.bwd == MOE_BWD_MXFP8) {
       MxArgs m{};

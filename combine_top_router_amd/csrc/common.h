@@ -71,7 +71,7 @@ hipError_t launch_route_bwd(const moe_shape& s, const float* logits, const int32
 hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                         int32_t* row_src, int32_t* row_of, int32_t* chunk_hist, hipStream_t st);
 hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
-                             int32_t* zeros, hipStream_t st);
+                             int32_t* zeros, int32_t* order, hipStream_t st);
 hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offsets,
                          const int32_t* row_src, void* xp, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
@@ -118,6 +118,7 @@ struct BwdArgs {
   float* dw_part;         // scratch [R_cap, nparts]
   bf16_t* aw;             // scratch [R_cap, I]: w * A
   const bf16_t* zeros;    // scratch: kZeroBytes of zeros
+  const int32_t* order;   // scratch [El + 1]: work order of the weight-gradient GEMMs (k_tile_table)
   bf16_t* dwg;            // [El, H, I]
   bf16_t* dwu;
   bf16_t* dwd;            // [El, I, H]

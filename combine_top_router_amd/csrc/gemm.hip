@@ -93,6 +93,8 @@ struct JGateUp {
   using Tile = RowTileInfo;
   using Ld = LGateUp;
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
+  static constexpr bool DYN = false;
+  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : 128) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
   }
@@ -183,6 +185,8 @@ struct JDown {
   using Tile = RowTileInfo;
   using Ld = LMnB;
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
+  static constexpr bool DYN = false;
+  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
   int NT;
@@ -363,6 +367,8 @@ struct JDa {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
+  static constexpr bool DYN = false;
+  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -462,6 +468,8 @@ struct JDx {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
+  static constexpr bool DYN = false;
+  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -580,6 +588,12 @@ struct JWgrad {
   using Tile = WgradTile;
   using Ld = typename std::conditional<MX, LMx, LWgrad<AG, BG>>::type;
   static constexpr bool A_KMAJ = false, B_KMAJ = false;
+  // items: position p in a.order, then the expert's tm x tn output tiles, m-major.
+  // a.order lists the experts by cost, most rows first, and a.order[El] = 1, when
+  // their loads are skewed enough for serpentine rounds to pay; else it is the
+  // identity, a.order[El] = 0, and the items go out in contiguous XCD ranges.
+  static constexpr bool DYN = true;
+  __device__ __forceinline__ bool serpentine() const { return sload(a.order + a.El) != 0; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -588,8 +602,9 @@ struct JWgrad {
   uint8_t* scring;
   __device__ __forceinline__ int items() const { return a.El * tm * tn; }
   __device__ __forceinline__ void tile(int v, Tile& p) const {
-    p.e = uni(v / (tm * tn));
-    const int rem = uni(v - p.e * tm * tn);
+    const int pos = uni(v / (tm * tn));
+    p.e = sload(a.order + pos);
+    const int rem = uni(v - pos * tm * tn);
     p.m0 = uni(rem / tn) * BM;
     p.n0 = uni(rem % tn) * BN;
     if constexpr (MX) {

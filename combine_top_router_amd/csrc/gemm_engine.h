@@ -166,17 +166,50 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][NI]) {
 }
 
 // ---- persistent scheduling ----
-// Workgroup b runs on XCD b % 8.  The V work items are split into 8 contiguous
-// ranges, one per XCD, and the XCD's workgroups walk their range in order, so work
-// items sharing operands run together on one XCD and share its L2.
+// Workgroup b runs on XCD b % 8.  Two orders of the V work items:
+// * contiguous: the items are split into 8 contiguous ranges, one per XCD, and the
+//   XCD's workgroups walk their range in order, so work items sharing operands run
+//   together on one XCD and share its L2 (what a job of equal-cost items wants);
+// * serpentine, for items sorted by cost, largest first: round r deals the G items
+//   [r G, r G + G) to the G workgroups, in ascending rank in even rounds and
+//   descending rank in odd ones, the rank being XCD-major (b % 8) * (G / 8) + b / 8.
+//   Every workgroup's sum of costs then stays within about one item of the mean, and
+//   each XCD still takes a contiguous block of G / 8 items per round, but one
+//   operand's items spread over more XCDs.
+// Jobs with DYN = true choose per launch (J::serpentine(), a uniform device flag).
+template <bool DYN>
 struct Sched {
-  int v, hi, step;
-  __device__ explicit Sched(int V) {
+  int v;        // the workgroup's current item; < 0: none
+  int hi;       // end of the items (contiguous: of the XCD's range)
+  int step;     // contiguous: stride
+  int w, g;     // serpentine: rank, grid size
+  bool serp;
+  __device__ Sched(int V, bool serpentine) {
     const int x = blockIdx.x & 7;
-    const int lo = (int)(((int64_t)V * x) >> 3);
-    hi = (int)(((int64_t)V * (x + 1)) >> 3);
-    v = lo + (int)(blockIdx.x >> 3);
-    step = (int)(gridDim.x >> 3);
+    serp = DYN && serpentine;
+    if (serp) {
+      g = (int)gridDim.x;
+      w = x * (g >> 3) + (int)(blockIdx.x >> 3);
+      hi = V;
+      v = w < V ? w : -1;
+    } else {
+      const int lo = (int)(((int64_t)V * x) >> 3);
+      hi = (int)(((int64_t)V * (x + 1)) >> 3);
+      step = (int)(gridDim.x >> 3);
+      v = lo + (int)(blockIdx.x >> 3);
+      if (v >= hi) v = -1;
+    }
+  }
+  // the item after u (an item of this workgroup), or -1
+  __device__ __forceinline__ int next(int u) const {
+    int n;
+    if (DYN && serp) {
+      const int r = u / g + 1;
+      n = r * g + ((r & 1) ? g - 1 - w : w);
+    } else {
+      n = u + step;
+    }
+    return n < hi ? n : -1;
   }
 };
 
@@ -202,8 +235,8 @@ struct Sched {
 // instructions (fetch_next, when the loader calls it, is one of them: it fetches the
 // row indices of the next position into the other index slot), which keeps the vmcnt
 // waits exact.
-template <class J>
-__device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, Sched sc, int wv, int lane) {
+template <class J, class S>
+__device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, S sc, int wv, int lane) {
   using T = typename J::Tile;
   const int wm = wv & 1, wn = wv >> 1;
   T cur, nxt;
@@ -214,13 +247,14 @@ __device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, Sched 
   int cs = 0;
   for (;;) {
     const int nk = cur.nk, len = max(nk, MIN_STEPS);
-    const bool more = v + sc.step < sc.hi;
+    const int vn = sc.next(v);
+    const bool more = vn >= 0;
     const bool act = __builtin_amdgcn_readfirstlane((int)job.active(cur, wm)) != 0;
     int done = 0;
     for (int kc = 0; kc < len; ++kc) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (kc < nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wm, wn);
-      if (kc == 0 && more) job.tile(v + sc.step, nxt);
+      if (kc == 0 && more) job.tile(vn, nxt);
       done = cs;
       cs = cs == NSTAGE - 1 ? 0 : cs + 1;
     }
@@ -230,16 +264,16 @@ __device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, Sched 
     zero_acc(acc);
     if (!more) break;
     cur = nxt;
-    v += sc.step;
+    v = vn;
   }
 }
 
-template <class J>
-__device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, Sched sc, int pw, int lane) {
+template <class J, class S>
+__device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int pw, int lane) {
   using P = typename J::Ld;
   P cur, nxt;
   job.setup(sc.v, cur, pw, lane);
-  int vc = sc.v;                            // item of cur
+  int vc = sc.v, vn = -1;                   // items of cur and nxt
   int lc = max(cur.nk, MIN_STEPS), ln = 0;  // stream positions of cur and nxt
   bool has_nxt = false, looked = false;     // nxt set up; the item after cur looked up
   bool in_nxt = false;                      // the issue cursor is in nxt
@@ -258,8 +292,8 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, Sched sc,
       const bool last = k0 >= lc - 1;
       if (last && !looked) {
         looked = true;
-        const int vn = vc + sc.step;
-        if (vn < sc.hi) {
+        vn = sc.next(vc);
+        if (vn >= 0) {
           job.setup(vn, nxt, pw, lane);
           ln = max(nxt.nk, MIN_STEPS);
           has_nxt = true;
@@ -293,7 +327,7 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, Sched sc,
     asm volatile("s_barrier" ::: "memory");  // the compute waves' epilogue barrier
     if (!has_nxt) break;
     cur = nxt;
-    vc += sc.step;
+    vc = vn;
     lc = ln;
     has_nxt = looked = in_nxt = false;
     kc = 0;
@@ -304,8 +338,8 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, Sched sc,
 template <class J>
 __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6);
-  Sched sc(job.items());
-  if (sc.v >= sc.hi) return;
+  Sched<J::DYN> sc(job.items(), job.serpentine());
+  if (sc.v < 0) return;
   if (wv >= NW) load_stream(job, lds, sc, wv - NW, lane);
   else compute_stream(job, lds, sc, wv, lane);
 }

@@ -118,15 +118,59 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, i
 // expert's first m-tile, number of m-tiles of the expert, 0}.  A GEMM with NT column
 // tiles enumerates its work as v = first * NT + (n-tile * tiles_of_e + m-tile in e), so
 // the m-tiles sharing one weight tile are adjacent and one expert's work is contiguous.
+// With order given, it also sets the work order of the weight-gradient GEMMs, whose
+// output tiles cost about c = max(ceil(rows / 64), 3) + 2 K steps: if one expert costs
+// over twice the mean, or the costliest of the 8 contiguous expert ranges of the XCDs
+// exceeds their mean by over 2 %, order[p] = the expert with the p-th most rows (ties:
+// lower index first) and order[El] = 1 (serpentine rounds); else order[e] = e and
+// order[El] = 0 (contiguous ranges, which keep each expert's tiles on one XCD's L2).
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
-                                                     int32_t* __restrict__ tiles, int32_t* __restrict__ zeros) {
+                                                     int32_t* __restrict__ tiles, int32_t* __restrict__ zeros,
+                                                     int32_t* __restrict__ order) {
   __shared__ int32_t buf[1024];
+  __shared__ int32_t rows[1024];
+  __shared__ int32_t xsum[8], cmax, serp;
   const int e = threadIdx.x;
   if (zeros && e < kZeroBytes / 4) zeros[e] = 0;
-  int n = 0;
-  if (e < El) n = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  if (e < 8) xsum[e] = 0;
+  if (e == 0) cmax = 0;
+  int n = 0, c = 0;
+  if (e < El) {
+    c = offsets[e + 1] - offsets[e];
+    n = (c + bm - 1) / bm;
+  }
   buf[e] = n;
+  rows[e] = c;
   __syncthreads();
+  if (order) {
+    if (e < El) {
+      const int cost = max((c + 63) / 64, 3) + 2;
+      atomicAdd(&xsum[(int)(((int64_t)e * 8) / El)], cost);
+      atomicMax(&cmax, cost);
+    }
+    __syncthreads();
+    if (e == 0) {
+      int64_t tot = 0, xm = 0;
+      for (int x = 0; x < 8; ++x) {
+        tot += xsum[x];
+        xm = max(xm, (int64_t)xsum[x]);
+      }
+      serp = (int64_t)cmax * El > 2 * tot || xm * 8 * 50 > tot * 51;
+      order[El] = serp;
+    }
+    __syncthreads();
+    if (e < El) {
+      int rank = e;
+      if (serp) {
+        rank = 0;
+        for (int j = 0; j < El; ++j) {
+          const int cj = rows[j];
+          rank += cj > c || (cj == c && j < e);
+        }
+      }
+      order[rank] = e;
+    }
+  }
   for (int off = 1; off < 1024; off <<= 1) {
     int v = e >= off ? buf[e - off] : 0;
     __syncthreads();
@@ -253,8 +297,8 @@ hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts,
 }
 
 hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
-                             int32_t* zeros, hipStream_t st) {
-  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles, zeros);
+                             int32_t* zeros, int32_t* order, hipStream_t st) {
+  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles, zeros, order);
   return hipGetLastError();
 }
 

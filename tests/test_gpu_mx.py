@@ -92,6 +92,7 @@ SMALL_MX = {
     # several 128-row tiles and a ragged tail per expert, I not a multiple of 128
     "ragged_mx": wl.MoeConfig("ragged_mx", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
     "ragged_mx_share": wl.MoeConfig("ragged_mx_share", 500, 384, 320, 10, 3, 4, 5, 9, bwd="mxfp8"),
+    "skew_mx": wl.MoeConfig("skew_mx", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf", bwd="mxfp8"),
 }
 
 

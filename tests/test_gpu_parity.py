@@ -24,6 +24,9 @@ SMALL = {
     "ragged_bf16": wl.MoeConfig("ragged_bf16", 700, 192, 192, 6, 2, 0, 6, 5),
     "ragged_bf16_share": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
     "ragged_f32": wl.MoeConfig("ragged_f32", 300, 96, 80, 6, 2, 0, 6, 7, dtype="f32"),
+    # Zipf-skewed loads with 8 empty experts; the weight gradients' 768 and 384 output
+    # tiles take several rounds of the persistent grid in cost order
+    "skew_bf16": wl.MoeConfig("skew_bf16", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf"),
 }
 
 
