@@ -6,17 +6,18 @@
 // GEMMs (Prime Mega MoE pages: one call fusing the linears, SwiGLU and combine, with
 // scratch buffers instead of intermediate tensors).
 //
-// Engine (gemm_engine.h): persistent 768-thread workgroups (one per CU) of 8 compute
-// waves and 4 load waves, 128x256 output tile, K step 64, each compute wave a 64x64
-// sub-tile as four v_mfma_f32_32x32x16_bf16 accumulators.  The load waves move operand
+// Engine (gemm_engine.h): persistent workgroups (one per CU) of 8 compute waves and
+// dedicated load waves, BM x 256 output tile, K step 64, each compute wave a (BM / 2) x
+// 64 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  The load waves move operand
 // tiles global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4)
-// into a three-stage LDS ring, two K steps ahead, one barrier per K step, and a
+// into a ring of LDS stages, DEPTH K steps ahead, one barrier per K step, and a
 // workgroup's tiles form one stream of K steps, so the next tile's loads fly while the
-// current tile's epilogue runs.  An operand whose contraction axis is contiguous in memory ("K-major") is
-// stored [rows][64] and read with 16-byte LDS reads; an operand contiguous along M or
-// N ("MN-major": row-major weights as the B of x*W, and both operands of the weight
-// gradients, which contract over token rows) is stored [64][width] and read with the
-// transposing LDS read ds_read_b64_tr_b16, so no operand is transposed in memory.
+// current tile's epilogue runs.  An operand whose contraction axis is contiguous in
+// memory ("K-major") is stored [rows][64] and read with 16-byte LDS reads; an operand
+// contiguous along M or N ("MN-major": row-major weights as the B of x*W, and both
+// operands of the weight gradients, which contract over token rows) is stored
+// [64][width] and read with the transposing LDS read ds_read_b64_tr_b16, so no operand
+// is transposed in memory.
 //
 // Kernels:
 //   K1 fwd_gateup : G = Xp Wg, U = Xp Wu (dual B tile), epilogue saves G|U and A = silu(G) U
@@ -72,7 +73,7 @@ __device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_
 }
 
 // ---------------- K1: gate/up + SwiGLU ----------------
-// B tile: gate columns 0..127 and up columns 128..255; compute wave wn takes the same
+// B tile: gate columns 0..BN/2-1 and up columns BN/2..BN-1; compute wave wn takes the same
 // WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
 // and U of one element share a lane.
 struct LGateUp : RowLd {
@@ -96,22 +97,22 @@ struct JGateUp {
   static constexpr bool DYN = false;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
-    return (ni < NI / 2 ? 0 : 128) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
+    return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
   }
   FwdArgs a;
   int NT;
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ void tile(int v, Tile& p) const {
-    row_tile_info(a.tiles, a.offsets, v, NT, a.H / BK, 128, p);
+    row_tile_info(a.tiles, a.offsets, v, NT, a.H / BK, BN / 2, p);
   }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int, f32x16 (&acc)[2][NI], int lane, int wm, int wn) const {
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int, Acc& acc, int lane, int wm, int wn) const {
     mma_stage<JGateUp>(st, acc, lane, wm, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
     row_tile(a.tiles, a.offsets, v, NT, t);
-    const int n0 = t.nt * 128;
+    const int n0 = t.nt * (BN / 2);
     p.pw = pw;
     p.nk = a.H / BK;
     a_rows_kmaj(p.a, a.xp, a.x, a.row_src, a.k, a.H, t, pw, lane);
@@ -121,27 +122,28 @@ struct JGateUp {
     for (int q = 0; q < B_LP; ++q) {
       int r, c;
       mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
-      int col = n0 + (c & 15) * 8;  // intermediate column; chunks 16..31 are W_up's
+      constexpr int HC = BN / 16;    // chunks per half: HC..2 HC - 1 are W_up's
+      int col = n0 + (c % HC) * 8;   // intermediate column
       if (col >= a.I) col = n0;      // tail columns: any valid address, results are discarded
-      p.b[q] = (c < 16 ? wg : wu) + col + (size_t)r * a.I;
+      p.b[q] = (c < HC ? wg : wu) + col + (size_t)r * a.I;
     }
     p.bstep = (size_t)BK * a.I;
   }
   // lane takes 8 intermediate columns of one row, G from the gate blocks and U from the
   // up blocks (same columns), and writes 16-byte chunks of G, U and A
-  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
     constexpr int LPR = WCOLS / 16;
     static_assert(64 / LPR == EP_ROWS, "one pass per staged quarter");
     float* wsm = stage + wv * EP_ROWS * EP_LD;
     const size_t I2 = 2 * (size_t)a.I;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         stage_quarter(wsm, acc, mi, h, lane);
         const int rr = lane / LPR, cc = (lane % LPR) * 8;
-        const int rt = wm * 64 + mi * 32 + h * 16 + rr;
+        const int rt = wm * WROWS + mi * 32 + h * 16 + rr;
         float g[8], u[8], av[8];
         read8(wsm + rr * EP_LD + cc, g);
         read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
@@ -161,7 +163,7 @@ struct JGateUp {
 
 __global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  JGateUp job{a, (int)ceil_div(a.I, 128)};
+  JGateUp job{a, (int)ceil_div(a.I, BN / 2)};
   run_stream(job, lds);
 }
 
@@ -192,8 +194,8 @@ struct JDown {
   int NT;
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, a.I / BK, BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int, f32x16 (&acc)[2][NI], int lane, int wm, int wn) const {
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int, Acc& acc, int lane, int wm, int wn) const {
     mma_stage<JDown>(st, acc, lane, wm, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
@@ -214,7 +216,7 @@ struct JDown {
     }
     p.bstep = (size_t)BK * a.H;
   }
-  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     epilogue_rows(stage, acc, [&](int rt, int ct, const float (&v)[8]) {
       const int col = p.n0 + ct;
       if (rt < p.t.cnt && col < a.H) {
@@ -259,14 +261,14 @@ struct LKK : RowLd {
 // slots and swizzle are shared.  For v_mfma_scale_f32_32x32x64_f8f6f4 lane l of row
 // l & 31 holds codes 16 (l >> 5) .. +15 of each of the two 32-blocks of a 64-code
 // sub-step and supplies the scale of block l >> 5 of its row.  The scales of a step (4
-// bytes per row) come with two more direct-to-LDS loads per load wave into a small
-// ring: scale slot t < 128 carries A row t, 128 <= t < 384 B row t - 128 (slots
-// 384..511 repeat A row 0).
+// bytes per row) come with 512 / (64 NP) more direct-to-LDS loads per load wave into a
+// small ring: scale slot t < BM carries A row t, BM <= t < BM + BN B row t - BM (the
+// slots past BM + BN repeat A row 0).
 constexpr int MX_STEP = 128;               // codes per K step
 constexpr int MX_SC_SLOT = 512 * 4;        // scale bytes per stage
 constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per load wave
 static_assert(MX_STEP == 2 * BK, "an fp8 step must span the bytes of a bf16 step");
-static_assert(MX_SC_LP * NP * 64 == 512, "scale slots");
+static_assert(MX_SC_LP * NP * 64 == 512 && BM + BN <= 512, "scale slots");
 
 __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int lane) {
   const int c0 = kk * 4 + (lane >> 5);
@@ -280,15 +282,15 @@ __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int
 
 __device__ __forceinline__ int mx_ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
 
-__device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, f32x16 (&acc)[2][NI], int lane,
+__device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, Acc& acc, int lane,
                                            int wm, int wn) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    i32x8 af[2], bf[NI];
-    int sa[2], sb[NI];
+    i32x8 af[MI], bf[NI];
+    int sa[MI], sb[NI];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int r = wm * 64 + mi * 32 + (lane & 31);
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = wm * WROWS + mi * 32 + (lane & 31);
       af[mi] = frag_fp8(st, r, kk, lane);
       sa[mi] = sc[r * 4 + kk * 2 + (lane >> 5)];
     }
@@ -299,7 +301,7 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
       sb[ni] = sc[(BM + r) * 4 + kk * 2 + (lane >> 5)];
     }
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0,
@@ -377,8 +379,8 @@ struct JDa {
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm,
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
                                           int wn) const {
     if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
     else mma_stage<JDa>(st, acc, lane, wm, wn);
@@ -405,8 +407,8 @@ struct JDa {
       }
     }
   }
-  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
-    const int lane = threadIdx.x & 63, wn = threadIdx.x >> 7;
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
+    const int lane = threadIdx.x & 63, wn = (int)((threadIdx.x >> 6) / WM);
     const size_t I2 = 2 * (size_t)a.I;
     epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8]) {
       const int col = p.n0 + ct;
@@ -478,8 +480,8 @@ struct JDx {
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? 2 * a.I / MX_STEP : 2 * a.I / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * 64 < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm,
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
                                           int wn) const {
     if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
     else mma_stage<JDx>(st, acc, lane, wm, wn);
@@ -507,7 +509,7 @@ struct JDx {
       }
     }
   }
-  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     epilogue_rows(stage, acc, [&](int rt, int ct, const float (&v)[8]) {
       const int col = p.n0 + ct;
       if (rt < p.t.cnt && col < a.H)
@@ -536,7 +538,7 @@ template <bool AG, bool BG>
 struct LWgrad {
   static constexpr bool GATHER = AG || BG;
   static constexpr int NVMEM = LOADS + (GATHER ? 1 : 0);
-  static constexpr int AR = 4, BR = 2;  // token rows per wave load of A and B
+  static constexpr int AR = 512 / BM, BR = 512 / BN;  // token rows per wave load of A and B
   const bf16_t* abase; int lda;
   const bf16_t* bbase; int ldb;
   const int32_t* row_src; const bf16_t* zeros; int k;
@@ -557,14 +559,14 @@ struct LWgrad {
     const bf16_t* bp[B_LP];
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) {
-      const int kr = load_instr(q, pw) * AR + (lane >> 4);
+      const int kr = load_instr(q, pw) * AR + (int)((unsigned)lane / (64 / AR));
       int row = rs + kt * BK + kr;
       if (AG) row = my[kr] / k;
       ap[q] = kt * BK + kr < cnt ? abase + (size_t)row * lda + acol[q] : zeros;
     }
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) {
-      const int kr = load_instr(q, pw) * BR + (lane >> 5);
+      const int kr = load_instr(q, pw) * BR + (int)((unsigned)lane / (64 / BR));
       int row = rs + kt * BK + kr;
       if (BG) row = my[kr] / k;
       bp[q] = kt * BK + kr < cnt ? bbase + (size_t)row * ldb + bcol[q] : zeros;
@@ -615,7 +617,7 @@ struct JWgrad {
     }
   }
   __device__ __forceinline__ bool active(const Tile&, int) const { return true; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, f32x16 (&acc)[2][NI], int lane, int wm,
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
                                           int wn) const {
     if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
     else mma_stage<JWgrad>(st, acc, lane, wm, wn);
@@ -673,7 +675,7 @@ struct JWgrad {
       }
     }
   }
-  __device__ __forceinline__ void epilogue(const Tile& p, const f32x16 (&acc)[2][NI], float* stage) const {
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
     const int e = p.e, m0 = p.m0, n0 = p.n0;
     epilogue_rows(stage, acc, [&](int rt, int ct, const float (&vv)[8]) {
@@ -717,7 +719,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int 
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
-  MOE_LAUNCH("fwd_gateup", k_fwd_gateup, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, 128))), dim3(NTHR), 0, st,
+  MOE_LAUNCH("fwd_gateup", k_fwd_gateup, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))), dim3(NTHR), 0, st,
              a);
   MOE_LAUNCH("fwd_down", k_fwd_down, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0, st, a);
   return hipGetLastError();

@@ -1,7 +1,7 @@
 // Shared GEMM engine of the bf16 and MXFP8 grouped GEMMs (internal header).
 //
-// Persistent 768-thread workgroups (one per CU): 8 compute waves and 4 load waves.
-// 128x256 output tile, each compute wave a 64x64 sub-tile as 32x32 MFMA accumulator
+// Persistent workgroups (one per CU) of NW compute waves and NP load waves.  BM x 256
+// output tile, each compute wave a (BM / 2) x 64 sub-tile as 32x32 MFMA accumulator
 // blocks.  Operand tiles
 // move global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4)
 // into a three-stage LDS ring, issued two K steps ahead, one barrier per K step.  An
@@ -31,18 +31,24 @@ constexpr int DEPTH = NSTAGE - 1;    // K steps in flight ahead of the MFMAs
 constexpr int NW = 8;                // compute waves: 2 along M x 4 along N
 constexpr int NP = 8;                // load (producer) waves, two per SIMD
 constexpr int NTHR = 64 * (NW + NP);
-constexpr int WN = NW / 2;           // compute waves along N
-constexpr int NI = 8 / WN;           // 32-column accumulator blocks per wave
+constexpr int WM = 2;                // compute waves along M
+constexpr int WN = NW / WM;          // compute waves along N
+constexpr int MI = BM / (32 * WM);   // 32-row accumulator blocks per wave
+constexpr int NI = BN / (32 * WN);   // 32-column accumulator blocks per wave
+constexpr int WROWS = 32 * MI;       // rows per wave
 constexpr int WCOLS = 32 * NI;       // columns per wave
-constexpr int A_ELEMS = BM * BK;                  // 8192 bf16
-constexpr int B_ELEMS = BN * BK;                  // 16384 bf16
-constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;    // 48 KB per stage
-constexpr int A_INSTR = A_ELEMS * 2 / 1024;       // 1 KB wave loads per stage: 16 for A
-constexpr int B_INSTR = B_ELEMS * 2 / 1024;       // and 32 for B
-constexpr int A_LP = A_INSTR / NP;                // per load wave: 4 of A
-constexpr int B_LP = B_INSTR / NP;                // and 8 of B
+constexpr int A_ELEMS = BM * BK;
+constexpr int B_ELEMS = BN * BK;
+constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
+constexpr int A_INSTR = A_ELEMS * 2 / 1024;       // 1 KB wave loads per stage, of A
+constexpr int B_INSTR = B_ELEMS * 2 / 1024;       // and of B
+constexpr int A_LP = A_INSTR / NP;                // per load wave
+constexpr int B_LP = B_INSTR / NP;
 constexpr int LOADS = A_LP + B_LP;                // operand loads per load wave per stage
-constexpr int LDS_ELEMS = NSTAGE * STAGE_ELEMS;   // 144 KB
+constexpr int LDS_ELEMS = NSTAGE * STAGE_ELEMS;
+using Acc = f32x16[MI][NI];                       // a compute wave's accumulators
+static_assert(MI * NI * 16 <= 128, "accumulators of one wave");
+static_assert(A_LP * NP == A_INSTR && B_LP * NP == B_INSTR, "wave loads divide among the load waves");
 constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
 constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per load wave, two positions of gathered row indices
 constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least
@@ -136,29 +142,30 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const bf16_t* s, int base, int kk, 
 
 // The bf16 MFMAs of one stage for a job J (J::A_KMAJ, J::B_KMAJ, J::ncol).
 template <class J>
-__device__ __forceinline__ void mma_stage(const bf16_t* st, f32x16 (&acc)[2][NI], int lane, int wm, int wn) {
+__device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, int wm, int wn) {
   const bf16_t* As = st;
   const bf16_t* Bs = st + A_ELEMS;
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 af[2], bf[NI];
+    bf16x8 af[MI], bf[NI];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-      af[mi] = J::A_KMAJ ? frag_kmaj(As, wm * 64 + mi * 32, kk, lane) : frag_mnmaj<BM>(As, wm * 64 + mi * 32, kk, lane);
+    for (int mi = 0; mi < MI; ++mi)
+      af[mi] = J::A_KMAJ ? frag_kmaj(As, wm * WROWS + mi * 32, kk, lane)
+                         : frag_mnmaj<BM>(As, wm * WROWS + mi * 32, kk, lane);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
       bf[ni] = J::B_KMAJ ? frag_kmaj(Bs, J::ncol(wn, ni), kk, lane) : frag_mnmaj<BN>(Bs, J::ncol(wn, ni), kk, lane);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][NI]) {
+__device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -238,11 +245,11 @@ struct Sched {
 template <class J, class S>
 __device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, S sc, int wv, int lane) {
   using T = typename J::Tile;
-  const int wm = wv & 1, wn = wv >> 1;
+  const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
   T cur, nxt;
   job.tile(sc.v, cur);
   int v = sc.v;
-  f32x16 acc[2][NI];
+  Acc acc;
   zero_acc(acc);
   int cs = 0;
   for (;;) {
@@ -345,7 +352,7 @@ __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
 }
 
 // ---- epilogue staging ----
-// Each wave stages 16-row quarters of its 64 x WCOLS fp32 accumulator in its own
+// Each wave stages 16-row pieces of its WROWS x WCOLS fp32 accumulator in its own
 // [16][EP_LD] region of the free ring stage, so that lanes can then read 8 consecutive
 // columns of one row and issue 16-byte global loads and stores.  The regions are
 // private to their waves, so no workgroup barrier is needed between quarters.
@@ -354,7 +361,7 @@ constexpr int EP_ROWS = 16;
 static_assert(NW * EP_ROWS * EP_LD * 4 <= STAGE_ELEMS * 2, "epilogue staging must fit in one ring stage");
 
 // stage rows 16 h .. 16 h + 15 of accumulator block row mi (registers 8 h .. 8 h + 7)
-__device__ __forceinline__ void stage_quarter(float* wsm, const f32x16 (&acc)[2][NI], int mi, int h, int lane) {
+__device__ __forceinline__ void stage_quarter(float* wsm, const Acc& acc, int mi, int h, int lane) {
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -394,11 +401,11 @@ __device__ __forceinline__ void unpack8(i32x4 u, float (&v)[8]) {
 constexpr int EP_LPR = WCOLS / 8;      // lanes per row
 constexpr int EP_RPP = 64 / EP_LPR;    // rows per pass
 template <class F>
-__device__ __forceinline__ void epilogue_rows(float* stage, const f32x16 (&acc)[2][NI], F&& f) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv & 1, wn = wv >> 1;
+__device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, F&& f) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
   float* wsm = stage + wv * EP_ROWS * EP_LD;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       stage_quarter(wsm, acc, mi, h, lane);
@@ -407,7 +414,7 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const f32x16 (&acc)[
         const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
         float v[8];
         read8(wsm + rr * EP_LD + cc, v);
-        f(wm * 64 + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v);
+        f(wm * WROWS + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v);
       }
       staging_done();
     }
