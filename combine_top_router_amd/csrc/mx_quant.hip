@@ -7,9 +7,9 @@
 //
 // Scale rule: X = the smallest integer with amax <= 448 * 2^X (so x / 2^X never
 // saturates), clamped to [-127, 127], X = 0 for an all-zero block.  Elements: x / 2^X
-// rounded to the nearest E4M3 value, ties to even, sign bit from x.  All of it is
-// exact integer/exponent arithmetic on the fp32 value, so identical inputs give
-// identical codes on any correct implementation.
+// rounded to the nearest E4M3 value, ties to even, sign bit from x.  The scale is exact
+// exponent arithmetic and the element conversion is correctly rounded, so identical
+// inputs give identical codes on any correct implementation.
 #include "common.h"
 
 namespace moe {
@@ -25,23 +25,13 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// E4M3 code of x * 2^-X (|x * 2^-X| <= 448 by the scale rule)
-__device__ __forceinline__ uint32_t e4m3_code(float x, int X) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = ldexpf(fabsf(x), -X);
-  uint32_t mag;
-  if (a >= 0.015625f) {                         // normal range: 3 mantissa bits
-    int e;
-    frexpf(a, &e);                              // a in [2^(e-1), 2^e)
-    const float q = rintf(ldexpf(a, 4 - e)) ;   // a / 2^(e-1-3), in [8, 16]
-    int ee = e - 1, mm = (int)q - 8;
-    if (mm == 8) { ee += 1; mm = 0; }           // rounded up into the next binade
-    mag = (uint32_t)(((ee + 7) << 3) | mm);
-  } else {                                      // subnormal: multiples of 2^-9
-    const float q = rintf(a * 512.f);           // 0..8
-    mag = (uint32_t)q;                          // 8 = 2^-6 = code 0x08, the smallest normal
-  }
-  return sign | mag;
+// E4M3 codes of x0..x3 * 2^-X packed little-endian (|x * 2^-X| <= 448 by the scale
+// rule).  The scaling by a power of two is exact; gfx950's v_cvt_pk_fp8_f32 converts to
+// the OCP E4M3 format rounding to nearest, ties to even (the default mode), with the
+// sign of the input, also for results that round to zero.
+__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3, int X) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x0, -X), ldexpf(x1, -X), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x2, -X), ldexpf(x3, -X), lo, true);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -84,11 +74,8 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
     am = fmaxf(am, __shfl_xor(am, 2, 64));
     if (ok) {
       const int X = mx_scale_exp(am);
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w0 |= e4m3_code(v[j], X) << (8 * j);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w1 |= e4m3_code(v[4 + j], X) << (8 * j);
+      const uint32_t w0 = e4m3_pack4(v[0], v[1], v[2], v[3], X);
+      const uint32_t w1 = e4m3_pack4(v[4], v[5], v[6], v[7], X);
       *reinterpret_cast<uint2*>(q + r * K + c) = make_uint2(w0, w1);
       if ((c & 31) == 0) s[r * (K / 32) + (c >> 5)] = (uint8_t)(X + 127);
     }
@@ -163,10 +150,8 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
     const int X = mx_scale_exp(am);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t acc = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc |= e4m3_code(tile[b * 32 + 4 * j + q][c], X) << (8 * q);
-      codes[c][b * 8 + j] = acc;
+      const float* t0 = &tile[b * 32 + 4 * j][c];
+      codes[c][b * 8 + j] = e4m3_pack4(t0[0], t0[COL_COLS + 1], t0[2 * (COL_COLS + 1)], t0[3 * (COL_COLS + 1)], X);
     }
     reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
   }
