@@ -389,6 +389,25 @@ int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint
                     __func__);
 }
 
+int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32_t groups, int64_t Rp,
+                         int32_t* poff, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (groups < 1 || groups > 1024) return fail(MOE_EINVAL, "groups = %d outside 1..1024", groups);
+  if (N <= 0 || N % 8 != 0) return fail(MOE_EINVAL, "N = %d must be a positive multiple of 8", N);
+  if (Rp < 0 || Rp % kMxRowPad != 0 || Rp > 0x7fffffffLL)
+    return fail(MOE_EINVAL, "Rp = %lld must be a multiple of %d in [0, 2^31)", (long long)Rp, kMxRowPad);
+  REQUIRE(offsets);
+  REQUIRE(poff);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_poff(offsets, groups, poff, st);
+  if (e != hipSuccess || Rp == 0) return hip_status(e, __func__);
+  REQUIRE(x);
+  REQUIRE(codes);
+  REQUIRE(scales);
+  return hip_status(launch_mx_cols((const bf16_t*)x, N, nullptr, 1, nullptr, offsets, poff, groups, N, (int)Rp, codes,
+                                   scales, "mx_quantize_cols", st),
+                    __func__);
+}
+
 int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
                        const float* topk_w, const float* d_topk_w, float* d_logits, void* stream) {
   int rc = check_shape(shape);

@@ -84,10 +84,11 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
 
 // Column-wise, transposed: one workgroup per (padded 128-row chunk, 64 columns); a chunk
 // lies inside one expert's padded segment (segments are multiples of 128 rows).  The
-// chunk's row sources and weights are read once into LDS and its rows staged as fp32
-// (after the optional gather and row scaling); thread t quantizes the 32-row block
-// t / 64 of column t % 64 into LDS, and the workgroup then writes each column's 128
-// codes as one 128-byte line and its four scales as one word.
+// chunk's row sources and weights are read once into LDS and its rows staged as bf16
+// (16 KB, so several workgroups share a CU); thread t takes the 32-row block t / 64 of
+// column t % 64 into registers (applying the optional row weight in fp32), quantizes
+// it into LDS, and the workgroup then writes each column's 128 codes as one 128-byte
+// line and its four scales as one word.
 constexpr int COL_ROWS = 128, COL_COLS = 64;
 static_assert(COL_ROWS == kMxRowPad, "a column chunk spans one padding unit");
 __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ poff, int El, int N, int Rp,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ stt) {
-  __shared__ float tile[COL_ROWS][COL_COLS + 1];
-  __shared__ __attribute__((aligned(16))) uint32_t codes[COL_COLS][COL_ROWS / 4];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[COL_ROWS][COL_COLS];
+  __shared__ __attribute__((aligned(16))) uint32_t codes[COL_COLS][COL_ROWS / 4 + 4];
   __shared__ uint32_t scales[COL_COLS];
   __shared__ int srow[COL_ROWS];
   __shared__ float wrow[COL_ROWS];
@@ -126,33 +127,39 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
     wrow[tid] = w;
   }
   __syncthreads();
-  // stage: 128 rows x 64 columns, one 16-byte load per (row, 8 columns)
+  // stage: 128 rows x 64 columns of bf16, one 16-byte load per (row, 8 columns)
+  {
+    constexpr int IT = COL_ROWS * (COL_COLS / 8) / 256;
+    i32x4 u[IT];
 #pragma unroll
-  for (int it = 0; it < COL_ROWS * (COL_COLS / 8) / 256; ++it) {
-    const int i = tid + 256 * it;
-    const int rr = i / (COL_COLS / 8), cc = (i % (COL_COLS / 8)) * 8;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (rr < nrow && n0 + cc < N) {
-      const i32x4 u = *reinterpret_cast<const i32x4*>(src + (size_t)srow[rr] * ld + n0 + cc);
-      const float w = wrow[rr];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { v[2 * j] = bf_lo((uint32_t)u[j]) * w; v[2 * j + 1] = bf_hi((uint32_t)u[j]) * w; }
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + 256 * it;
+      const int rr = i / (COL_COLS / 8), cc = (i % (COL_COLS / 8)) * 8;
+      u[it] = i32x4{0, 0, 0, 0};
+      if (rr < nrow && n0 + cc < N) u[it] = *reinterpret_cast<const i32x4*>(src + (size_t)srow[rr] * ld + n0 + cc);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[rr][cc + j] = v[j];
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + 256 * it;
+      const int rr = i / (COL_COLS / 8), cc = (i % (COL_COLS / 8)) * 8;
+      *reinterpret_cast<i32x4*>(&tile[rr][cc]) = u[it];
+    }
   }
   __syncthreads();
   {
     const int c = tid % COL_COLS, b = tid / COL_COLS;   // column, 32-row block
+    float v[32];
     float am = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 32; ++rr) am = fmaxf(am, fabsf(tile[b * 32 + rr][c]));
+    for (int rr = 0; rr < 32; ++rr) {
+      const int r = b * 32 + rr;
+      v[rr] = __uint_as_float((uint32_t)tile[r][c] << 16);
+      if (topk_w) v[rr] *= wrow[r];
+      am = fmaxf(am, fabsf(v[rr]));
+    }
     const int X = mx_scale_exp(am);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float* t0 = &tile[b * 32 + 4 * j][c];
-      codes[c][b * 8 + j] = e4m3_pack4(t0[0], t0[COL_COLS + 1], t0[2 * (COL_COLS + 1)], t0[3 * (COL_COLS + 1)], X);
-    }
+    for (int j = 0; j < 8; ++j) codes[c][b * 8 + j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
     reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
   }
   __syncthreads();

@@ -12,7 +12,7 @@ __all__ = [
     "MoeShape", "MoeError", "load", "lib_path", "EXPORTS",
     "moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_topk",
     "moe_dispatch", "moe_fwd", "moe_combine", "moe_bwd", "moe_route_topk_bwd",
-    "moe_mx_quantize", "moe_timing_enable", "moe_timing_read",
+    "moe_mx_quantize", "moe_mx_quantize_cols", "moe_timing_enable", "moe_timing_read",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
@@ -53,6 +53,7 @@ _SIG = {
     "moe_bwd": (ctypes.c_int, [_S] + [_P] * 18),
     "moe_route_topk_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
     "moe_mx_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    "moe_mx_quantize_cols": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P]),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
@@ -130,6 +131,11 @@ def moe_route_topk_bwd(shape, logits, topk_idx, topk_w, d_topk_w, d_logits, stre
 
 def moe_mx_quantize(x, rows, K, codes, scales, stream=0):
     _check(load().moe_mx_quantize(x, rows, K, codes, scales, stream), "moe_mx_quantize")
+
+
+def moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, stream=0):
+    _check(load().moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, stream),
+           "moe_mx_quantize_cols")
 
 
 def moe_timing_enable(on: bool = True):

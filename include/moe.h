@@ -157,6 +157,24 @@ int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_
  * quantises. */
 int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales, void* stream);
 
+/* Group-aware column-wise MXFP8 quantisation (NVIDIA article: the weight-gradient GEMMs
+ * contract over token rows, so their operands are quantised in blocks of 32 rows of one
+ * column, and a block never crosses from one expert's rows into the next's), exposed for
+ * tests and callers.  x: device bf16 [offsets[groups], N] row-major, N a multiple of 8;
+ * offsets: device int32 [groups + 1], non-decreasing from 0, 1 <= groups <= 1024.
+ * Group g's rows are placed at padded row poff[g] of a row space in which every group
+ * starts at a multiple of 128: poff (device int32 [groups + 1], written) = the exclusive
+ * prefix sum of the group sizes rounded up to 128.  Outputs are transposed: codes
+ * [N, Rp] E4M3 and scales [N, Rp / 32] e8m0 (same scale and rounding rule as
+ * moe_mx_quantize), column n's 32-row block j at codes[n][32 j .. 32 j + 31] and
+ * scales[n][j]; rows of a group's padding quantise as zeros (codes 0, scale 127).  Rp
+ * (a multiple of 128) bounds the padded row space: rows at or past Rp are not written,
+ * so Rp >= offsets[groups] + 127 * groups rounded up to 128 always suffices; rows from
+ * poff[groups] to Rp are left as they were.  Errors: MOE_EINVAL for bad sizes or NULL
+ * pointers. */
+int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32_t groups, int64_t Rp,
+                         int32_t* poff, uint8_t* codes, uint8_t* scales, void* stream);
+
 /* Opt-in kernel timing for profilers and benchmarks (no effect on results).
  * moe_timing_enable(1) makes every kernel that this host thread launches through the
  * calls above be bracketed by two HIP events recorded on the call's stream; (0) stops

@@ -88,3 +88,24 @@ def test_workspace_sizes_grow_with_the_layer():
     # saved holds G|U and A for every possible row
     R = 4096 * 8
     assert big[0] >= R * 3 * 768 * 2
+
+
+def test_quantizer_arguments_are_checked_before_launch():
+    L = _lib()
+    bad = [
+        dict(N=64, groups=0, Rp=128),      # no groups
+        dict(N=64, groups=1025, Rp=128),   # more than 1024 groups
+        dict(N=12, groups=2, Rp=128),      # N not a multiple of 8
+        dict(N=64, groups=2, Rp=100),      # Rp not a multiple of 128
+        dict(N=64, groups=2, Rp=-128),
+    ]
+    for kw in bad:
+        with pytest.raises(L.MoeError) as ei:
+            L.moe_mx_quantize_cols(8, kw["N"], 8, kw["groups"], kw["Rp"], 8, 8, 8)
+        assert ei.value.code == L.MOE_EINVAL, kw
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_mx_quantize_cols(8, 64, 0, 2, 128, 8, 8, 8)     # offsets NULL
+    assert ei.value.code == L.MOE_EINVAL
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_mx_quantize(8, 4, 48, 8, 8)                     # K not a multiple of 32
+    assert ei.value.code == L.MOE_EINVAL

@@ -1,7 +1,7 @@
 """Parity of the MXFP8 backward (fp8_bwd mode) with the oracle.
 
-The quantiser is compared code for code with the oracle's MX rule (integer work:
-bit-exact).  The layer: routing, index and the bf16 forward as in the bf16 runs
+The row-wise and the group-aware column-wise quantisers are compared code for code
+with the oracle's MX rule (integer work: bit-exact).  The layer: routing, index and the bf16 forward as in the bf16 runs
 (bit-exact integers, 1e-2 on y); the backward's outputs within a relative Frobenius
 error of 4e-2 of the oracle's MXFP8 backward, which quantises the same operands by
 the same rule in fp64.  Against the unquantised fp64 backward the error is the
@@ -76,6 +76,58 @@ def test_mx_quantize_empty_and_invalid():
     with pytest.raises(L.MoeError):
         L.moe_mx_quantize(xb.data_ptr(), 4, 48, buf.data_ptr(), buf.data_ptr(), 0)  # K % 32 != 0
     torch.cuda.synchronize()
+
+
+def _expected_cols(m, offsets, Rp):
+    """The oracle's codes for the group-aware column-wise layout: each group's 32-row
+    blocks (the last one zero-padded) quantised by quantize_blocks, placed from the
+    group's padded start; padding blocks up to the next multiple of 128 are zero."""
+    N = m.shape[1]
+    codes = np.zeros((N, Rp), dtype=np.uint8)
+    scales = np.full((N, Rp // 32), 127, dtype=np.uint8)
+    p = 0
+    for g in range(len(offsets) - 1):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        for j, r0 in enumerate(range(lo, hi, 32)):
+            blk = np.zeros((32, N))
+            blk[: min(32, hi - r0)] = m[r0:min(r0 + 32, hi)]
+            c, s, _ = omx.quantize_blocks(blk.T)
+            codes[:, p + 32 * j:p + 32 * j + 32] = c
+            scales[:, (p + 32 * j) // 32] = s
+        p += -(-(hi - lo) // 128) * 128
+    return codes, scales, p
+
+
+@pytest.mark.parametrize("sizes,N", [
+    ([200, 0, 1, 128, 129, 37], 64),     # ragged, an empty group, block and padding edges
+    ([1000], 192),                       # one group, N not a multiple of 64
+    ([31, 33, 0, 0, 300, 5], 8),         # narrowest N
+])
+def test_mx_quantize_cols_is_bit_exact(sizes, N):
+    import combine_top_router_amd.lib as L
+    rng = np.random.default_rng(len(sizes) * 1000 + N)
+    R = int(sum(sizes))
+    m = rng.standard_normal((R, N)) * np.exp2(rng.integers(-30, 30, size=(R, 1)))
+    m = m.astype(np.float32)
+    xb = torch.from_numpy(m).to("cuda").to(torch.bfloat16)
+    mb = xb.float().cpu().numpy().astype(np.float64)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    groups = len(sizes)
+    Rp = -(-(R + 127 * groups) // 128) * 128
+    off_d = torch.from_numpy(offsets).to("cuda")
+    poff = torch.full((groups + 1,), -1, dtype=torch.int32, device="cuda")
+    codes = torch.full((N, Rp), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((N, Rp // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    L.moe_mx_quantize_cols(xb.data_ptr(), N, off_d.data_ptr(), groups, Rp, poff.data_ptr(), codes.data_ptr(),
+                           scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rc, rs, used = _expected_cols(mb, offsets, Rp)
+    pad = np.concatenate([[0], np.cumsum([-(-n // 128) * 128 for n in sizes])])
+    assert np.array_equal(poff.cpu().numpy(), pad)
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(c[:, :used], rc[:, :used])
+    assert np.array_equal(s[:, :used // 32], rs[:, :used // 32])
+    assert np.all(c[:, used:] == 0x5A) and np.all(s[:, used // 32:] == 0x5A)   # past the groups: untouched
 
 
 def _oracle_mx(cfg, inp):
