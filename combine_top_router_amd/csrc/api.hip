@@ -390,11 +390,15 @@ int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint
 }
 
 int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32_t groups, int64_t Rp,
-                         int32_t* poff, uint8_t* codes, uint8_t* scales, void* stream) {
+                         int32_t* poff, uint8_t* codes, uint8_t* scales, uint8_t* row_codes,
+                         uint8_t* row_scales, void* stream) {
   if (groups < 1 || groups > 1024) return fail(MOE_EINVAL, "groups = %d outside 1..1024", groups);
   if (N <= 0 || N % 8 != 0) return fail(MOE_EINVAL, "N = %d must be a positive multiple of 8", N);
   if (Rp < 0 || Rp % kMxRowPad != 0 || Rp > 0x7fffffffLL)
     return fail(MOE_EINVAL, "Rp = %lld must be a multiple of %d in [0, 2^31)", (long long)Rp, kMxRowPad);
+  if ((row_codes == nullptr) != (row_scales == nullptr))
+    return fail(MOE_EINVAL, "row_codes and row_scales must both be given or both be NULL");
+  if (row_codes && N % 32 != 0) return fail(MOE_EINVAL, "row-wise output needs N = %d a multiple of 32", N);
   REQUIRE(offsets);
   REQUIRE(poff);
   hipStream_t st = (hipStream_t)stream;
@@ -404,7 +408,7 @@ int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32
   REQUIRE(codes);
   REQUIRE(scales);
   return hip_status(launch_mx_cols((const bf16_t*)x, N, nullptr, 1, nullptr, offsets, poff, groups, N, (int)Rp, codes,
-                                   scales, "mx_quantize_cols", st),
+                                   scales, "mx_quantize_cols", st, row_codes, row_scales),
                     __func__);
 }
 

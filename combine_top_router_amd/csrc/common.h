@@ -153,10 +153,12 @@ hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const i
                           const int32_t* offsets, int El, int64_t rows, int64_t rows_bound, int K, uint8_t* q,
                           uint8_t* s, const char* name, hipStream_t st);
 // column-wise, group-aware quantization into the padded transposed layout; optional row
-// gather (row_src / k) and per-row scaling by topk_w[row_src[r]]
+// gather (row_src / k) and per-row scaling by topk_w[row_src[r]]; with qr, also the
+// row-wise quantization of the same (gathered, unscaled) rows into qr [rows, N], sr
 hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int k, const float* topk_w,
                           const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
-                          uint8_t* stt, const char* name, hipStream_t st);
+                          uint8_t* stt, const char* name, hipStream_t st, uint8_t* qr = nullptr,
+                          uint8_t* sr = nullptr);
 hipError_t launch_poff(const int32_t* offsets, int El, int32_t* poff, hipStream_t st);
 hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
 

@@ -756,9 +756,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// MXFP8 backward.  Order: quantise the weights and dY' row-wise; B1 (fp8) writes dG|dU
-// (bf16); quantise dG|dU row-wise and, with A, w * dY' and Xp, column-wise per expert;
-// then B2, B3, B4 on fp8 operands.
+// MXFP8 backward.  Order: quantise the weights row-wise, and dY' row-wise together with
+// w * dY' column-wise per expert; B1 (fp8) writes dG|dU (bf16); quantise dG|dU row-wise
+// and column-wise in one pass, A and Xp column-wise; then B2, B3, B4 on fp8 operands.
 hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
   hipError_t e;
   const int El = a.El, H = a.H, I = a.I;
@@ -769,22 +769,20 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
                          "mx_q_wdown", st));
   MOE_TRY(launch_mx_rows(a.wg, a.wu, I, nullptr, 1, a.offsets, El, WgRows, WgRows, 2 * I, m.q_wg, m.s_wg,
                          "mx_q_wgateup", st));
-  MOE_TRY(launch_mx_rows(a.dy, nullptr, H, a.row_src, a.k, a.offsets, El, -1, m.R_cap, H, m.q_dy, m.s_dy, "mx_q_dy",
-                         st));
-  MOE_TRY(launch_bwd_gemms<true>(a, m, st));
-  MOE_TRY(launch_mx_rows(a.dgu, nullptr, 2 * I, nullptr, 1, a.offsets, El, -1, m.R_cap, 2 * I, m.q_dgu, m.s_dgu,
-                         "mx_q_dgu", st));
-  MOE_TRY(launch_mx_cols(a.a, I, nullptr, 1, nullptr, a.offsets, m.poff, El, I, m.Rp, m.qt_a, m.st_a, "mx_qt_a", st));
+  // dY' rows: row-wise for B1 and, from the same read, column-wise w * dY' for B2
   MOE_TRY(launch_mx_cols(a.dy, H, a.row_src, a.k, a.topk_w, a.offsets, m.poff, El, H, m.Rp, m.qt_dy, m.st_dy,
-                         "mx_qt_wdy", st));
+                         "mx_q_dy", st, m.q_dy, m.s_dy));
+  MOE_TRY(launch_bwd_gemms<true>(a, m, st));
+  // dG|dU: row-wise for B3 and column-wise for B4 in one pass
+  MOE_TRY(launch_mx_cols(a.dgu, 2 * I, nullptr, 1, nullptr, a.offsets, m.poff, El, 2 * I, m.Rp, m.qt_dgu, m.st_dgu,
+                         "mx_q_dgu", st, m.q_dgu, m.s_dgu));
+  MOE_TRY(launch_mx_cols(a.a, I, nullptr, 1, nullptr, a.offsets, m.poff, El, I, m.Rp, m.qt_a, m.st_a, "mx_qt_a", st));
   if (a.xp)
     MOE_TRY(launch_mx_cols(a.xp, H, nullptr, 1, nullptr, a.offsets, m.poff, El, H, m.Rp, m.qt_x, m.st_x, "mx_qt_x",
                            st));
   else
     MOE_TRY(launch_mx_cols(a.x, H, a.row_src, a.k, nullptr, a.offsets, m.poff, El, H, m.Rp, m.qt_x, m.st_x,
                            "mx_qt_x", st));
-  MOE_TRY(launch_mx_cols(a.dgu, 2 * I, nullptr, 1, nullptr, a.offsets, m.poff, El, 2 * I, m.Rp, m.qt_dgu, m.st_dgu,
-                         "mx_qt_dgu", st));
 #undef MOE_TRY
   {
     const int tm = (int)ceil_div(I, BM), tn = (int)ceil_div(H, BN);

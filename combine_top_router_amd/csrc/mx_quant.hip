@@ -88,7 +88,10 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
 // (16 KB, so several workgroups share a CU); thread t takes the 32-row block t / 64 of
 // column t % 64 into registers (applying the optional row weight in fp32), quantizes
 // it into LDS, and the workgroup then writes each column's 128 codes as one 128-byte
-// line and its four scales as one word.
+// line and its four scales as one word.  With qr given, the same staged tile also yields
+// the row-wise quantisation of the unweighted values (codes [rows, N] at the source's
+// dispatched row, scales [rows, N / 32]): thread t takes the 32 columns (t % 2) of
+// staged row t / 2, so a matrix that both layouts need is read once.
 constexpr int COL_ROWS = 128, COL_COLS = 64;
 static_assert(COL_ROWS == kMxRowPad, "a column chunk spans one padding unit");
 __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
@@ -96,7 +99,8 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
                                                  const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ poff, int El, int N, int Rp,
-                                                 uint8_t* __restrict__ qt, uint8_t* __restrict__ stt) {
+                                                 uint8_t* __restrict__ qt, uint8_t* __restrict__ stt,
+                                                 uint8_t* __restrict__ qr, uint8_t* __restrict__ sr) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[COL_ROWS][COL_COLS];
   __shared__ __attribute__((aligned(16))) uint32_t codes[COL_COLS][COL_ROWS / 4 + 4];
   __shared__ uint32_t scales[COL_COLS];
@@ -162,6 +166,35 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
     for (int j = 0; j < 8; ++j) codes[c][b * 8 + j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
     reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
   }
+  if (qr) {
+    const int rr = tid / 2, h = tid % 2;                // staged row, 32-column half
+    const int n = n0 + 32 * h;
+    if (rr < nrow && n < N) {
+      const i32x4* t4 = reinterpret_cast<const i32x4*>(&tile[rr][32 * h]);
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const i32x4 u = t4[q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * q + 2 * j] = bf_lo((uint32_t)u[j]);
+          v[8 * q + 2 * j + 1] = bf_hi((uint32_t)u[j]);
+        }
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(v[j]));
+      const int X = mx_scale_exp(am);
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
+      const size_t r = (size_t)(r0 + rr);
+      uint4* dst = reinterpret_cast<uint4*>(qr + r * N + n);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      sr[r * (N / 32) + n / 32] = (uint8_t)(X + 127);
+    }
+  }
   __syncthreads();
   // write-out: 64 columns x 128 codes, eight lanes per 128-byte line
 #pragma unroll
@@ -208,11 +241,10 @@ hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const i
 
 hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int k, const float* topk_w,
                           const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
-                          uint8_t* stt, const char* name, hipStream_t st) {
+                          uint8_t* stt, const char* name, hipStream_t st, uint8_t* qr, uint8_t* sr) {
   if (Rp <= 0) return hipSuccess;
   MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / COL_ROWS), (unsigned)ceil_div(N, COL_COLS)), dim3(256), 0, st,
-             src, ld,
-             row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt);
+             src, ld, row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt, qr, sr);
   return hipGetLastError();
 }
 

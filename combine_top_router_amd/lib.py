@@ -53,7 +53,8 @@ _SIG = {
     "moe_bwd": (ctypes.c_int, [_S] + [_P] * 18),
     "moe_route_topk_bwd": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
     "moe_mx_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
-    "moe_mx_quantize_cols": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P]),
+    "moe_mx_quantize_cols": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P,
+                                            _P, _P]),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
@@ -133,9 +134,9 @@ def moe_mx_quantize(x, rows, K, codes, scales, stream=0):
     _check(load().moe_mx_quantize(x, rows, K, codes, scales, stream), "moe_mx_quantize")
 
 
-def moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, stream=0):
-    _check(load().moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, stream),
-           "moe_mx_quantize_cols")
+def moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, row_codes=0, row_scales=0, stream=0):
+    _check(load().moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, row_codes, row_scales,
+                                       stream), "moe_mx_quantize_cols")
 
 
 def moe_timing_enable(on: bool = True):

@@ -170,10 +170,14 @@ int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint
  * scales[n][j]; rows of a group's padding quantise as zeros (codes 0, scale 127).  Rp
  * (a multiple of 128) bounds the padded row space: rows at or past Rp are not written,
  * so Rp >= offsets[groups] + 127 * groups rounded up to 128 always suffices; rows from
- * poff[groups] to Rp are left as they were.  Errors: MOE_EINVAL for bad sizes or NULL
- * pointers. */
+ * poff[groups] to Rp are left as they were.  With row_codes and row_scales both given
+ * (N then a multiple of 32), the same pass also writes the row-wise quantisation of the
+ * rows of x, as moe_mx_quantize would: row_codes [offsets[groups], N], row_scales
+ * [offsets[groups], N / 32] (the backward reads dY' and dG|dU once for both layouts).
+ * Errors: MOE_EINVAL for bad sizes or NULL pointers. */
 int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32_t groups, int64_t Rp,
-                         int32_t* poff, uint8_t* codes, uint8_t* scales, void* stream);
+                         int32_t* poff, uint8_t* codes, uint8_t* scales, uint8_t* row_codes,
+                         uint8_t* row_scales, void* stream);
 
 /* Opt-in kernel timing for profilers and benchmarks (no effect on results).
  * moe_timing_enable(1) makes every kernel that this host thread launches through the

@@ -98,10 +98,13 @@ def test_quantizer_arguments_are_checked_before_launch():
         dict(N=12, groups=2, Rp=128),      # N not a multiple of 8
         dict(N=64, groups=2, Rp=100),      # Rp not a multiple of 128
         dict(N=64, groups=2, Rp=-128),
+        dict(N=72, groups=2, Rp=128, rows=True),   # row-wise output needs N % 32 == 0
+        dict(N=64, groups=2, Rp=128, half=True),   # row codes without row scales
     ]
     for kw in bad:
         with pytest.raises(L.MoeError) as ei:
-            L.moe_mx_quantize_cols(8, kw["N"], 8, kw["groups"], kw["Rp"], 8, 8, 8)
+            rows = 8 if kw.get("rows") or kw.get("half") else 0
+            L.moe_mx_quantize_cols(8, kw["N"], 8, kw["groups"], kw["Rp"], 8, 8, 8, rows, 0 if kw.get("half") else rows)
         assert ei.value.code == L.MOE_EINVAL, kw
     with pytest.raises(L.MoeError) as ei:
         L.moe_mx_quantize_cols(8, 64, 0, 2, 128, 8, 8, 8)     # offsets NULL

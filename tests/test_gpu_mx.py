@@ -98,12 +98,13 @@ def _expected_cols(m, offsets, Rp):
     return codes, scales, p
 
 
-@pytest.mark.parametrize("sizes,N", [
-    ([200, 0, 1, 128, 129, 37], 64),     # ragged, an empty group, block and padding edges
-    ([1000], 192),                       # one group, N not a multiple of 64
-    ([31, 33, 0, 0, 300, 5], 8),         # narrowest N
+@pytest.mark.parametrize("sizes,N,rows", [
+    ([200, 0, 1, 128, 129, 37], 64, True),     # ragged, an empty group, block and padding edges
+    ([1000], 160, True),                       # one group, N not a multiple of 64
+    ([31, 33, 0, 0, 300, 5], 8, False),        # narrowest N
+    ([31, 33, 0, 0, 300, 5], 96, False),
 ])
-def test_mx_quantize_cols_is_bit_exact(sizes, N):
+def test_mx_quantize_cols_is_bit_exact(sizes, N, rows):
     import combine_top_router_amd.lib as L
     rng = np.random.default_rng(len(sizes) * 1000 + N)
     R = int(sum(sizes))
@@ -118,8 +119,11 @@ def test_mx_quantize_cols_is_bit_exact(sizes, N):
     poff = torch.full((groups + 1,), -1, dtype=torch.int32, device="cuda")
     codes = torch.full((N, Rp), 0x5A, dtype=torch.uint8, device="cuda")
     scales = torch.full((N, Rp // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    rq = torch.full((R, N), 0x5A, dtype=torch.uint8, device="cuda") if rows else None
+    rsc = torch.full((R, N // 32), 0x5A, dtype=torch.uint8, device="cuda") if rows else None
     L.moe_mx_quantize_cols(xb.data_ptr(), N, off_d.data_ptr(), groups, Rp, poff.data_ptr(), codes.data_ptr(),
-                           scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                           scales.data_ptr(), rq.data_ptr() if rows else 0, rsc.data_ptr() if rows else 0,
+                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     rc, rs, used = _expected_cols(mb, offsets, Rp)
     pad = np.concatenate([[0], np.cumsum([-(-n // 128) * 128 for n in sizes])])
@@ -128,6 +132,10 @@ def test_mx_quantize_cols_is_bit_exact(sizes, N):
     assert np.array_equal(c[:, :used], rc[:, :used])
     assert np.array_equal(s[:, :used // 32], rs[:, :used // 32])
     assert np.all(c[:, used:] == 0x5A) and np.all(s[:, used // 32:] == 0x5A)   # past the groups: untouched
+    if rows:
+        ec, es, _ = omx.quantize_blocks(mb.reshape(R, N // 32, 32))
+        assert np.array_equal(rq.cpu().numpy(), ec.reshape(R, N))
+        assert np.array_equal(rsc.cpu().numpy(), es)
 
 
 def _oracle_mx(cfg, inp):
