@@ -82,7 +82,7 @@ void layout(const moe_shape& s, Layout& L) {
   L.es = s.dtype == MOE_BF16 ? 2 : 4;
   L.max_tiles = (int)ceil_div(L.R_cap, kGemmBM) + El;
   L.nparts = s.dtype == MOE_BF16 ? bwd_bf16_nparts(s.I) : s.I;
-  L.nchunks = (int)ceil_div((int64_t)s.T * s.k, kSlotChunk);
+  L.nchunks = (int)ceil_div((int64_t)s.T * s.k, index_chunk((int64_t)s.T * s.k, El));
   const size_t R = (size_t)L.R_cap;
   L.off_gu = 0;
   L.off_a = align_up(R * 2 * s.I * L.es);

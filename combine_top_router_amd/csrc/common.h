@@ -44,7 +44,17 @@ __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __ex
 // Host-side: the launch configuration constants shared by the host code and kernels.
 constexpr int kGemmBM = 128;     // rows of one row-group GEMM tile (bf16 path)
 constexpr int kZeroBytes = 512;  // zeroed scratch area read in place of rows past a group's end
-constexpr int kSlotChunk = 4096; // (token, slot) pairs per histogram chunk
+// (token, slot) pairs per histogram chunk of the dispatch index: at least 1024, a
+// multiple of 256, and few enough chunks (<= 256 and <= 32768 / El) that every
+// workgroup can read the whole chunk-by-expert histogram
+inline int index_chunk(int64_t TK, int El) {
+  int64_t nmax = 32768 / El;
+  if (nmax > 256) nmax = 256;
+  if (nmax < 1) nmax = 1;
+  int64_t c = (TK + nmax - 1) / nmax;
+  c = (c + 255) / 256 * 256;
+  return (int)(c < 1024 ? 1024 : c);
+}
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -6,23 +6,24 @@
 // copy sits on the critical path (same article, "Optimization 1").
 //
 // The permutation is a stable counting sort of the (token, slot) ids by local expert:
-// 1) per-chunk expert histograms, 2) a column scan over chunks giving each chunk's
-// base position inside every expert group plus counts and offsets, 3) in-chunk ranks
-// from wavefront ballots (no atomic ordering), so the row order is deterministic:
-// expert-major, then token-ascending.
+// 1) per-chunk expert histograms; 2) in one more kernel, each chunk's workgroup sums
+// the histograms of the chunks before it and of all chunks (its base position inside
+// every expert group, and the counts and offsets), then ranks its slots with wavefront
+// ballots (no atomic ordering), so the row order is deterministic: expert-major, then
+// token-ascending.
 #include "common.h"
 
 namespace moe {
 
 namespace {
 
-__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ idx, int TK, int e_begin,
+__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ idx, int TK, int chunk, int e_begin,
                                               int El, int32_t* __restrict__ chunk_hist) {
   extern __shared__ int32_t hist[];
   for (int e = threadIdx.x; e < El; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int s0 = blockIdx.x * kSlotChunk;
-  const int s1 = min(TK, s0 + kSlotChunk);
+  const int s0 = blockIdx.x * chunk;
+  const int s1 = min(TK, s0 + chunk);
   for (int s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
     int e = idx[s] - e_begin;
     if (e >= 0 && e < El) atomicAdd(&hist[e], 1);
@@ -31,51 +32,68 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ idx, i
   for (int e = threadIdx.x; e < El; e += blockDim.x) chunk_hist[(size_t)blockIdx.x * El + e] = hist[e];
 }
 
-// One block of 1024 threads: column scan over chunks, counts and offsets.
-__global__ __launch_bounds__(1024) void k_scan(int nchunks, int El, int32_t* __restrict__ chunk_hist,
-                                               int32_t* __restrict__ counts,
-                                               int32_t* __restrict__ offsets) {
-  __shared__ int32_t buf[1024];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < El) {
-    for (int c = 0; c < nchunks; ++c) {
-      int v = chunk_hist[(size_t)c * El + e];
-      chunk_hist[(size_t)c * El + e] = total;
-      total += v;
-    }
-    counts[e] = total;
-  }
-  buf[e] = e < El ? total : 0;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    int v = e >= off ? buf[e - off] : 0;
-    __syncthreads();
-    buf[e] += v;
-    __syncthreads();
-  }
-  if (e < El) offsets[e + 1] = buf[e];
-  if (e == 0) offsets[0] = 0;
-}
-
-// Ranks within each chunk, 256 slots per step; wave w of the block takes slots
-// [64w, 64w + 64) of the step, and the waves' per-expert counts are combined in order.
-__global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, int TK, int e_begin,
-                                              int El, int ebits, const int32_t* __restrict__ chunk_hist,
-                                              const int32_t* __restrict__ offsets,
-                                              int32_t* __restrict__ row_src,
-                                              int32_t* __restrict__ row_of) {
+// One workgroup per chunk (at least one): expert totals and this chunk's prefix from the
+// chunk histograms, an exclusive scan of the totals (workgroup 0 writes counts and
+// offsets), then the chunk's slots in steps of 256; wave w of the workgroup takes
+// slots [64w, 64w + 64) of a step, and the waves' per-expert counts are combined in
+// order.
+__global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, int TK, int chunk, int nchunks,
+                                               int e_begin, int El, int ebits,
+                                               const int32_t* __restrict__ chunk_hist,
+                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ row_src, int32_t* __restrict__ row_of) {
   extern __shared__ int32_t sm[];
   int32_t* base = sm;            // [El]: next free row of expert e for this chunk
-  int32_t* cnt = sm + El;        // [4][El]: per-wave counts of the current step
+  int32_t* tot = sm + El;        // [El]: rows of expert e over all chunks
+  int32_t* cnt = sm + 2 * El;    // [4][El]: per-wave counts of the current step
+  __shared__ int32_t part[256];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int e = tid; e < El; e += 256) {
-    base[e] = offsets[e] + chunk_hist[(size_t)blockIdx.x * El + e];
+    base[e] = tot[e] = 0;
     cnt[e] = cnt[El + e] = cnt[2 * El + e] = cnt[3 * El + e] = 0;
   }
   __syncthreads();
-  const int s0 = blockIdx.x * kSlotChunk;
-  const int s1 = min(TK, s0 + kSlotChunk);
+  const int me = blockIdx.x;
+  for (int i = tid; i < nchunks * El; i += 256) {
+    const int c = i / El, e = i - c * El;
+    const int v = chunk_hist[i];
+    if (v) {
+      atomicAdd(&tot[e], v);
+      if (c < me) atomicAdd(&base[e], v);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of tot: thread t owns experts [t q, t q + q), q = ceil(El / 256)
+  const int q = (El + 255) / 256;
+  int mine = 0;
+  for (int j = 0; j < q; ++j) {
+    const int e = tid * q + j;
+    if (e < El) mine += tot[e];
+  }
+  part[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - mine;
+  for (int j = 0; j < q; ++j) {
+    const int e = tid * q + j;
+    if (e < El) {
+      if (me == 0) {
+        counts[e] = tot[e];
+        offsets[e] = run;
+      }
+      base[e] += run;
+      run += tot[e];
+    }
+  }
+  if (me == 0 && tid == 255) offsets[El] = part[255];
+  __syncthreads();
+  const int s0 = me * chunk;
+  const int s1 = min(TK, s0 + chunk);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int step = s0; step < s1; step += 256) {
     const int s = step + tid;
@@ -95,8 +113,8 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, i
       peers &= bit ? m : ~m;
     }
     const int rank = __popcll(peers & lt_mask);
-    const int tot = __popcll(peers);
-    if (valid && rank == 0) cnt[wv * El + e] = tot;
+    const int tot_w = __popcll(peers);
+    if (valid && rank == 0) cnt[wv * El + e] = tot_w;
     __syncthreads();
     if (valid) {
       int pos = base[e] + rank;
@@ -106,7 +124,7 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ idx, i
     }
     __syncthreads();
     if (valid && rank == 0) {
-      atomicAdd(&base[e], tot);
+      atomicAdd(&base[e], tot_w);
       cnt[wv * El + e] = 0;
     }
     __syncthreads();
@@ -283,16 +301,15 @@ hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts,
                         int32_t* row_src, int32_t* row_of, int32_t* chunk_hist, hipStream_t st) {
   const int TK = s.T * s.k;
   const int El = s.e_local;
-  const int nchunks = (int)ceil_div(TK, kSlotChunk);
+  const int chunk = index_chunk(TK, El);
+  const int nchunks = (int)ceil_div(TK, chunk);
   if (nchunks > 0)
-    MOE_LAUNCH("index_hist", k_hist, dim3(nchunks), dim3(256), El * sizeof(int32_t), st, idx, TK, s.e_begin, El,
-                       chunk_hist);
-  MOE_LAUNCH("index_scan", k_scan, dim3(1), dim3(1024), 0, st, nchunks, El, chunk_hist, counts, offsets);
+    MOE_LAUNCH("index_hist", k_hist, dim3(nchunks), dim3(256), El * sizeof(int32_t), st, idx, TK, chunk, s.e_begin,
+               El, chunk_hist);
   int ebits = 0;
   while ((1 << ebits) < El) ++ebits;
-  if (nchunks > 0)
-    MOE_LAUNCH("index_rank", k_rank, dim3(nchunks), dim3(256), 5 * El * sizeof(int32_t), st, idx, TK, s.e_begin,
-                       El, ebits, chunk_hist, offsets, row_src, row_of);
+  MOE_LAUNCH("index_place", k_place, dim3(nchunks > 0 ? nchunks : 1), dim3(256), 6 * El * sizeof(int32_t), st, idx,
+             TK, chunk, nchunks, s.e_begin, El, ebits, chunk_hist, counts, offsets, row_src, row_of);
   return hipGetLastError();
 }
 

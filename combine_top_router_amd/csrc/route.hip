@@ -1,4 +1,5 @@
-// Top-k softmax routing and its backward, one 64-lane wavefront per token.
+// Top-k softmax routing and its backward, one 64-lane wavefront per token (16 lanes per
+// token for the selection when E <= 256).
 //
 // Selection follows the top-K router of NVIDIA's DeepSeek-V3 MoE article ("What makes
 // MoE training hard": a learned router activates the top-K experts) at the Prime Mega
@@ -89,6 +90,73 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   }
 }
 
+// The same selection and weights with 16 lanes per token (four tokens per wavefront),
+// for E <= 256: VPL = E / 16 logits per lane, group reductions over 16 lanes.
+__device__ __forceinline__ Cand group16_argmax(Cand c) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    float ov = __shfl_xor(c.v, off, 16);
+    int oid = __shfl_xor(c.id, off, 16);
+    if (better(ov, oid, c.v, c.id)) { c.v = ov; c.id = oid; }
+  }
+  return c;
+}
+
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+  return v;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void k_route_topk16(const float* __restrict__ logits, int T, int E,
+                                                      int k, int renorm, int32_t* __restrict__ idx,
+                                                      float* __restrict__ w) {
+  const int sub = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (t >= T) return;   // a whole 16-lane group leaves together
+  const float* row = logits + (size_t)t * E;
+  float v[VPL];
+  bool taken[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = sub + 16 * i;
+    v[i] = e < E ? row[e] : -__builtin_inff();
+    taken[i] = e >= E;
+  }
+  float my_v = 0.f, top_v = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    Cand c{-__builtin_inff(), kPadId};
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = sub + 16 * i;
+      if (!taken[i] && better(v[i], e, c.v, c.id)) { c.v = v[i]; c.id = e; }
+    }
+    c = group16_argmax(c);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (sub + 16 * i == c.id) taken[i] = true;
+    if (j == 0) top_v = c.v;
+    if (sub == j) { my_v = c.v; my_id = c.id; }
+  }
+  const float z = sub < k ? expf(my_v - top_v) : 0.f;
+  float den;
+  if (renorm) {
+    den = group16_sum(z);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (sub + 16 * i < E) s += expf(v[i] - top_v);
+    den = group16_sum(s);
+  }
+  if (sub < k) {
+    idx[(size_t)t * k + sub] = my_id;
+    w[(size_t)t * k + sub] = z / den;
+  }
+}
+
 // d_logits through the softmax weights (the selection has no gradient).
 template <int VPL>
 __global__ __launch_bounds__(256) void k_route_bwd(const float* __restrict__ logits,
@@ -170,6 +238,18 @@ __global__ __launch_bounds__(256) void k_route_bwd(const float* __restrict__ log
 hipError_t launch_route_topk(const moe_shape& s, const float* logits, int32_t* idx, float* w,
                              hipStream_t st) {
   if (s.T == 0) return hipSuccess;
+  if (s.E <= 256) {
+    dim3 grid((unsigned)ceil_div(s.T, 16)), block(256);
+#define CALL16(V) \
+  MOE_LAUNCH("route_topk", k_route_topk16<V>, grid, block, 0, st, logits, s.T, s.E, s.k, s.renorm, idx, w)
+    if (s.E <= 16) CALL16(1);
+    else if (s.E <= 32) CALL16(2);
+    else if (s.E <= 64) CALL16(4);
+    else if (s.E <= 128) CALL16(8);
+    else CALL16(16);
+#undef CALL16
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)ceil_div(s.T, 4)), block(256);
 #define CALL(V) MOE_LAUNCH("route_topk", k_route_topk<V>, grid, block, 0, st, logits, s.T, s.E, s.k, s.renorm, idx, w)
   MOE_VPL_DISPATCH(s.E, CALL);
