@@ -43,11 +43,28 @@ struct RowTileInfo {
   int nk;
 };
 
-// Row-tiled loader state common to every kernel.
+// Row-tiled loader state common to every kernel.  These loaders stage through registers
+// (load / store of a Slot); issue() is the direct-to-LDS form of the same loads.
 struct RowLd {
+  static constexpr bool REG = true;
+  static constexpr int NLOAD = A_LP + B_LP;  // register loads per position
   int nk;
   int pw;
   __device__ __forceinline__ void fetch(int, int) const {}
+};
+struct RowSlot {
+  i32x4 a[A_LP];
+  i32x4 b[B_LP];
+  // wait until at most N of this wave's loads are in flight; the slot's registers are
+  // operands, so nothing reads them before the wait
+  template <int N>
+  __device__ __forceinline__ void ready() {
+    static_assert(A_LP == 2 && B_LP == 4, "operand list below");
+    asm volatile("s_waitcnt vmcnt(%6)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 : "n"(N)
+                 : "memory");
+  }
 };
 
 // K-major A rows of a row tile for load wave pw: the lane's chunk of each of its A_LP
@@ -87,6 +104,17 @@ struct LGateUp : RowLd {
     a.issue(kt, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
+  }
+  using Slot = RowSlot;
+  __device__ __forceinline__ void load(int kt, Slot& s) const {
+    a.load(kt, s.a);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
+  }
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st) const {
+    a.store(s.a, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
 };
 
@@ -181,6 +209,17 @@ struct LMnB : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
   }
+  using Slot = RowSlot;
+  __device__ __forceinline__ void load(int kt, Slot& s) const {
+    a.load(kt, s.a);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
+  }
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st) const {
+    a.store(s.a, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
+  }
 };
 
 struct JDown {
@@ -253,6 +292,19 @@ struct LKK : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16((second ? b2[q] : b[q]) + k0, b_dst(st, q, pw));
   }
+  using Slot = RowSlot;
+  __device__ __forceinline__ void load(int kt, Slot& s) const {
+    a.load(kt, s.a);
+    const bool second = kt >= ksplit;
+    const int k0 = (second ? kt - ksplit : kt) * BK;
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16((second ? b2[q] : b[q]) + k0);
+  }
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st) const {
+    a.store(s.a, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
+  }
 };
 
 // ---------------- MXFP8 operands (backward GEMMs in fp8_bwd mode) ----------------
@@ -310,6 +362,7 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
 }
 
 struct LMx {
+  static constexpr bool REG = false;
   static constexpr bool GATHER = false;
   static constexpr int NVMEM = LOADS + MX_SC_LP;
   int nk, pw;
@@ -536,6 +589,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dx(BwdArgs a, MxArgs m) {
 // waits for it with vmcnt(LOADS): only the operand loads may still be in flight.
 template <bool AG, bool BG>
 struct LWgrad {
+  static constexpr bool REG = false;
   static constexpr bool GATHER = AG || BG;
   static constexpr int NVMEM = LOADS + (GATHER ? 1 : 0);
   static constexpr int AR = 512 / BM, BR = 512 / BN;  // token rows per wave load of A and B

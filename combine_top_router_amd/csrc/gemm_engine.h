@@ -52,6 +52,7 @@ static_assert(A_LP * NP == A_INSTR && B_LP * NP == B_INSTR, "wave loads divide a
 constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
 constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per load wave, two positions of gathered row indices
 constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least
+constexpr int REG_AHEAD = 2;                      // register-staged loads: K steps held in registers
 
 // ---- scalar loads ----
 // A wave-uniform load through the scalar data cache (address space 4): it is counted
@@ -111,6 +112,20 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
 // LDS address of wave load q of load wave pw in the A or B region of a stage
 __device__ __forceinline__ bf16_t* a_dst(bf16_t* st, int q, int pw) { return st + load_instr(q, pw) * 512; }
 __device__ __forceinline__ bf16_t* b_dst(bf16_t* st, int q, int pw) { return st + A_ELEMS + load_instr(q, pw) * 512; }
+
+// Register-staged loads: a load wave reads its 16-byte chunks of a stage into
+// registers and later writes them to the same LDS slots a direct-to-LDS load would fill
+// (lane l at slot base + 16 l bytes).  The load is inline assembly, so the compiler
+// adds no wait of its own: the stream waits with an explicit vmcnt that also names the
+// registers (slot_ready), so no use of them can be placed before it.
+__device__ __forceinline__ i32x4 gload16(const bf16_t* p) {
+  i32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_put16(bf16_t* wave_base, i32x4 v) {
+  *reinterpret_cast<i32x4*>(wave_base + (threadIdx.x & 63) * 8) = v;
+}
 
 // MFMA 32x32x16 operand fragment: lane l gets 8 consecutive k of row/col (l & 31),
 // k = 8 * (l >> 5) .. +7 inside the 16-wide k sub-step kk.
@@ -342,13 +357,78 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing repeated loads
 }
 
+// The load side for jobs whose loaders stage through registers (J::Ld::REG) and whose
+// tiles all take the same number of K steps.  The load cursor runs DEPTH + REG_AHEAD
+// positions ahead of the MFMAs: at position c the load waves write the registers of
+// position c + DEPTH into the stage freed by the barrier and refill them with the loads
+// of position c + DEPTH + REG_AHEAD, so 2 + DEPTH K steps of operands are in flight
+// (the LDS ring alone holds DEPTH).  The compiler orders each LDS write after its loads.
+template <class J, class S>
+__device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc, int pw, int lane) {
+  using P = typename J::Ld;
+  using Slot = typename P::Slot;
+  static_assert(REG_AHEAD == 2, "the position loop is unrolled for two register slots");
+  int ntiles = 0;
+  for (int u = sc.v; u >= 0; u = sc.next(u)) ++ntiles;
+  P L;
+  int lv = sc.v;
+  job.setup(lv, L, pw, lane);
+  const int len = max(L.nk, MIN_STEPS);     // the same for every tile of the job
+  const int total = ntiles * len;           // stream positions of this workgroup
+  int lk = 0;                               // load cursor: step lk of item lv
+  // Every call issues its loads, also past the stream's end (then of the last tile,
+  // unused), so the two slots' loads alternate in a fixed order and the compiler's waits
+  // before each slot's LDS writes stay exact.
+  auto load_next = [&](Slot& t) {
+    L.load(min(lk, L.nk - 1), t);
+    if (lv >= 0 && ++lk == len) {
+      lk = 0;
+      const int nv = sc.next(lv);
+      lv = nv;
+      if (nv >= 0) job.setup(nv, L, pw, lane);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    Slot t;
+    load_next(t);
+    t.template ready<0>();
+    L.store(t, lds + d * STAGE_ELEMS);  // total >= MIN_STEPS > DEPTH
+  }
+  Slot s0, s1;
+  load_next(s0);  // position DEPTH
+  load_next(s1);  // position DEPTH + 1
+  auto position = [&](int c, Slot& t) {
+    if (c > 0 && c % len == 0) asm volatile("s_barrier" ::: "memory");  // the previous tile's epilogue barrier
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // t's loads are the older of the two slots': at most the other slot's may still fly
+    t.template ready<P::NLOAD>();
+    // past the stream's end (p >= total) this fills a stage no position reads any more
+    const int p = c + DEPTH;
+    L.store(t, lds + (p % NSTAGE) * STAGE_ELEMS);
+    load_next(t);  // position p + REG_AHEAD
+  };
+  for (int c = 0;; c += 2) {
+    position(c, s0);
+    if (c + 1 >= total) break;
+    position(c + 1, s1);
+    if (c + 2 >= total) break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads past the end
+  asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
+}
+
 template <class J>
 __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6);
   Sched<J::DYN> sc(job.items(), job.serpentine());
   if (sc.v < 0) return;
-  if (wv >= NW) load_stream(job, lds, sc, wv - NW, lane);
-  else compute_stream(job, lds, sc, wv, lane);
+  if (wv >= NW) {
+    if constexpr (J::Ld::REG) load_stream_reg(job, lds, sc, wv - NW, lane);
+    else load_stream(job, lds, sc, wv - NW, lane);
+  } else {
+    compute_stream(job, lds, sc, wv, lane);
+  }
 }
 
 // ---- epilogue staging ----
@@ -464,6 +544,14 @@ struct KRows {
   __device__ __forceinline__ void issue(int kt, bf16_t* st, int pw) const {
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) dma16(p[q] + kt * BK, a_dst(st, q, pw));
+  }
+  __device__ __forceinline__ void load(int kt, i32x4 (&v)[A_LP]) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) v[q] = gload16(p[q] + kt * BK);
+  }
+  __device__ __forceinline__ void store(const i32x4 (&v)[A_LP], bf16_t* st, int pw) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) lds_put16(a_dst(st, q, pw), v[q]);
   }
 };
 
