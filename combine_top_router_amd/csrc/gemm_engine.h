@@ -2,22 +2,22 @@
 //
 // Persistent workgroups (one per CU) of NW compute waves and NP load waves.  BM x 256
 // output tile, each compute wave a (BM / 2) x 64 sub-tile as 32x32 MFMA accumulator
-// blocks.  Operand tiles
-// move global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4)
-// into a three-stage LDS ring, issued two K steps ahead, one barrier per K step.  An
-// operand whose contraction axis is contiguous in memory ("K-major") is stored
-// [rows][BK] and read with 16-byte LDS reads; an operand contiguous along M or N
-// ("MN-major") is stored [BK][width] and read with the transposing LDS read
-// ds_read_b64_tr_b16.  Both layouts are XOR-swizzled by 16-byte chunk against LDS bank
-// conflicts; the swizzle is applied by choosing which global chunk each lane of a
-// direct-to-LDS load fetches.
+// blocks.  Operand tiles move global -> LDS into a three-stage LDS ring, one barrier per
+// K step, either with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4) issued
+// two K steps ahead, or (row-tiled jobs) through the load waves' registers, read four
+// K steps ahead and written to the ring two steps ahead.  An operand whose contraction
+// axis is contiguous in memory ("K-major") is stored [rows][BK] and read with 16-byte LDS
+// reads; an operand contiguous along M or N ("MN-major") is stored [BK][width] and read
+// with the transposing LDS read ds_read_b64_tr_b16.  Both layouts are XOR-swizzled by
+// 16-byte chunk against LDS bank conflicts; the swizzle is applied by choosing which
+// global chunk each lane of a load fetches.
 //
 // A workgroup's tiles form one stream of K steps: the loads of the next tile's first
 // steps are issued while the current tile's last steps compute, and the current
 // tile's epilogue runs in the ring stage that its last step freed while those loads
 // are in flight.  Tile descriptors and gathered row indices are read with scalar
-// loads, so each load wave's vector memory counter holds only its own direct-to-LDS
-// loads and its waits stay exact.
+// loads, so each load wave's vector memory counter holds only its own operand loads
+// and its waits stay exact.
 #pragma once
 
 #include "common.h"
