@@ -256,11 +256,19 @@ struct JDown {
     p.bstep = (size_t)BK * a.H;
   }
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&v)[8]) {
+    // the routing weights of the lane's rows, fetched before the staging starts
+    const int lane = threadIdx.x & 63, wm = (int)((unsigned)(threadIdx.x >> 6) % WM);
+    float wr[EP_LANE_ROWS];
+#pragma unroll
+    for (int i = 0; i < EP_LANE_ROWS; ++i) {
+      const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
+      wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
+    }
+    epilogue_rows<true>(stage, acc, [&](int rt, int ct, const float (&v)[8], int slot) {
       const int col = p.n0 + ct;
       if (rt < p.t.cnt && col < a.H) {
         const size_t r = (size_t)(p.t.rs + rt);
-        const float w = a.topk_w[a.row_src[r]];
+        const float w = wr[slot];
         float o[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) o[q] = w * v[q];
@@ -463,7 +471,7 @@ struct JDa {
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int lane = threadIdx.x & 63, wn = (int)((threadIdx.x >> 6) / WM);
     const size_t I2 = 2 * (size_t)a.I;
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8]) {
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int) {
       const int col = p.n0 + ct;
       const bool ok = rt < p.t.cnt && col < a.I;
       float part = 0.f;
@@ -563,7 +571,7 @@ struct JDx {
     }
   }
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&v)[8]) {
+    epilogue_rows<!MX>(stage, acc, [&](int rt, int ct, const float (&v)[8], int) {
       const int col = p.n0 + ct;
       if (rt < p.t.cnt && col < a.H)
         *reinterpret_cast<i32x4*>(a.dxp + (size_t)(p.t.rs + rt) * a.H + col) = pack8(v);
@@ -732,7 +740,7 @@ struct JWgrad {
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
     const int e = p.e, m0 = p.m0, n0 = p.n0;
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&vv)[8]) {
+    epilogue_rows<!MX>(stage, acc, [&](int rt, int ct, const float (&vv)[8], int) {
       const int mm = m0 + rt, n = n0 + ct;
       if (mm >= M || n >= N) return;
       const i32x4 o = pack8(vv);

@@ -476,11 +476,15 @@ __device__ __forceinline__ void unpack8(i32x4 u, float (&v)[8]) {
 }
 
 // Epilogue walk for the "wn * WCOLS + ni * 32" column mapping: calls
-// f(row_in_tile, col_in_tile, v[8]) for every 8-column chunk of this wave's sub-tile;
-// the EP_LPR lanes sharing a row are consecutive.
+// f(row_in_tile, col_in_tile, v[8], slot) for every 8-column chunk of this wave's
+// sub-tile (slot numbers the lane's rows, see ep_row); the EP_LPR lanes sharing a row
+// are consecutive.
 constexpr int EP_LPR = WCOLS / 8;      // lanes per row
 constexpr int EP_RPP = 64 / EP_LPR;    // rows per pass
-template <class F>
+// With UNROLL the row passes of a staged piece are unrolled, so their LDS reads and
+// global stores can overlap (jobs with small epilogues; the heavy ones keep them rolled
+// to stay within the register budget).
+template <bool UNROLL = false, class F>
 __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, F&& f) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
   float* wsm = stage + wv * EP_ROWS * EP_LD;
@@ -489,15 +493,33 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, F&& 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       stage_quarter(wsm, acc, mi, h, lane);
+      if constexpr (UNROLL) {
+        float v[EP_ROWS / EP_RPP][8];
+#pragma unroll
+        for (int j = 0; j < EP_ROWS / EP_RPP; ++j)
+          read8(wsm + (lane / EP_LPR + EP_RPP * j) * EP_LD + (lane % EP_LPR) * 8, v[j]);
+#pragma unroll
+        for (int j = 0; j < EP_ROWS / EP_RPP; ++j)
+          f(wm * WROWS + mi * 32 + h * 16 + lane / EP_LPR + EP_RPP * j, wn * WCOLS + (lane % EP_LPR) * 8, v[j],
+            (mi * 2 + h) * (EP_ROWS / EP_RPP) + j);
+      } else {
 #pragma unroll 1
-      for (int j = 0; j < EP_ROWS / EP_RPP; ++j) {
-        const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
-        float v[8];
-        read8(wsm + rr * EP_LD + cc, v);
-        f(wm * WROWS + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v);
+        for (int j = 0; j < EP_ROWS / EP_RPP; ++j) {
+          const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
+          float v[8];
+          read8(wsm + rr * EP_LD + cc, v);
+          f(wm * WROWS + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v, (mi * 2 + h) * (EP_ROWS / EP_RPP) + j);
+        }
       }
       staging_done();
     }
+}
+// The rows of the tile that epilogue_rows hands this lane, in call order (the f's last
+// argument): slot (mi * 2 + h) * (EP_ROWS / EP_RPP) + j.
+constexpr int EP_LANE_ROWS = MI * 2 * (EP_ROWS / EP_RPP);
+__device__ __forceinline__ int ep_row(int slot, int lane, int wm) {
+  const int j = slot % (EP_ROWS / EP_RPP), q = slot / (EP_ROWS / EP_RPP);
+  return wm * WROWS + q * 16 + lane / EP_LPR + EP_RPP * j;
 }
 
 // Row-group tile: virtual item v -> expert, first row, valid rows and column tile, in
