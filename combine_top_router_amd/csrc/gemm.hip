@@ -470,14 +470,22 @@ struct JDa {
   }
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int lane = threadIdx.x & 63, wn = (int)((threadIdx.x >> 6) / WM);
+    const int wm = (int)((unsigned)(threadIdx.x >> 6) % WM);
     const size_t I2 = 2 * (size_t)a.I;
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int) {
+    // the routing weights of the lane's rows, fetched before the staging starts
+    float wr[EP_LANE_ROWS];
+#pragma unroll
+    for (int i = 0; i < EP_LANE_ROWS; ++i) {
+      const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
+      wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
+    }
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int slot) {
       const int col = p.n0 + ct;
       const bool ok = rt < p.t.cnt && col < a.I;
       float part = 0.f;
       if (ok) {
         const size_t r = (size_t)(p.t.rs + rt);
-        const float w = a.topk_w[a.row_src[r]];
+        const float w = wr[slot];
         // two columns at a time, straight from and back to packed bf16 pairs
         __builtin_amdgcn_sched_barrier(0);
         const i32x4 gw = *reinterpret_cast<const i32x4*>(a.gu + r * I2 + col);
