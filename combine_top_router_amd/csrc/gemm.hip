@@ -46,7 +46,6 @@ struct RowTileInfo {
 // Row-tiled loader state common to every kernel.  These loaders stage through registers
 // (load / store of a Slot); issue() is the direct-to-LDS form of the same loads.
 struct RowLd {
-  static constexpr bool REG = true;
   static constexpr int NLOAD = A_LP + B_LP;  // register loads per position
   int nk;
   int pw;
@@ -111,8 +110,8 @@ struct LGateUp : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
   }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st) const {
-    a.store(s.a, st, pw);
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
+    a.put(s.a, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
@@ -122,7 +121,7 @@ struct JGateUp {
   using Tile = RowTileInfo;
   using Ld = LGateUp;
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
-  static constexpr bool DYN = false;
+  static constexpr bool DYN = false, REG = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
@@ -215,8 +214,8 @@ struct LMnB : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
   }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st) const {
-    a.store(s.a, st, pw);
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
+    a.put(s.a, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
@@ -226,7 +225,7 @@ struct JDown {
   using Tile = RowTileInfo;
   using Ld = LMnB;
   static constexpr bool A_KMAJ = true, B_KMAJ = false;
-  static constexpr bool DYN = false;
+  static constexpr bool DYN = false, REG = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
@@ -308,8 +307,8 @@ struct LKK : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) s.b[q] = gload16((second ? b2[q] : b[q]) + k0);
   }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st) const {
-    a.store(s.a, st, pw);
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
+    a.put(s.a, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
@@ -370,9 +369,22 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
 }
 
 struct LMx {
-  static constexpr bool REG = false;
   static constexpr bool GATHER = false;
   static constexpr int NVMEM = LOADS + MX_SC_LP;
+  static constexpr int NLOAD = NVMEM;  // register loads per position (row-tiled jobs)
+  struct Slot {
+    i32x4 a[A_LP];
+    i32x4 b[B_LP];
+    int s[MX_SC_LP];
+    template <int N>
+    __device__ __forceinline__ void ready() {
+      static_assert(A_LP == 2 && B_LP == 4 && MX_SC_LP == 1, "operand list below");
+      asm volatile("s_waitcnt vmcnt(%7)"
+                   : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(s[0])
+                   : "n"(N)
+                   : "memory");
+    }
+  };
   int nk, pw;
   const uint8_t* a[A_LP];       // codes of the lane's slot at K step 0
   const uint8_t* b[B_LP];
@@ -388,6 +400,23 @@ struct LMx {
 #pragma unroll
     for (int q = 0; q < MX_SC_LP; ++q)
       dma4(sp[q] + kt * (MX_STEP / 32), scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256);
+  }
+  __device__ __forceinline__ void load(int kt, Slot& t) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) t.a[q] = gload16(reinterpret_cast<const bf16_t*>(a[q] + kt * MX_STEP));
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) t.b[q] = gload16(reinterpret_cast<const bf16_t*>(b[q] + kt * MX_STEP));
+#pragma unroll
+    for (int q = 0; q < MX_SC_LP; ++q) t.s[q] = gload4(sp[q] + kt * (MX_STEP / 32));
+  }
+  __device__ __forceinline__ void store(const Slot& t, bf16_t* st, int slot) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) lds_put16(a_dst(st, q, pw), t.a[q]);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), t.b[q]);
+#pragma unroll
+    for (int q = 0; q < MX_SC_LP; ++q)
+      *reinterpret_cast<int*>(scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256 + (threadIdx.x & 63) * 4) = t.s[q];
   }
   // operand rows: A row r (of tile) at a_base + ra(r) * lda, B row n at b_base + rb(n) * ldb;
   // both matrices' scales have row stride ld / 32 and start at s_a / s_b
@@ -430,7 +459,7 @@ struct JDa {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
-  static constexpr bool DYN = false;
+  static constexpr bool DYN = false, REG = !MX;  // the fp8 B1 is faster with direct-to-LDS loads
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
@@ -539,7 +568,7 @@ struct JDx {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
-  static constexpr bool DYN = false;
+  static constexpr bool DYN = false, REG = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
@@ -605,7 +634,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dx(BwdArgs a, MxArgs m) {
 // waits for it with vmcnt(LOADS): only the operand loads may still be in flight.
 template <bool AG, bool BG>
 struct LWgrad {
-  static constexpr bool REG = false;
   static constexpr bool GATHER = AG || BG;
   static constexpr int NVMEM = LOADS + (GATHER ? 1 : 0);
   static constexpr int AR = 512 / BM, BR = 512 / BN;  // token rows per wave load of A and B
@@ -664,7 +692,7 @@ struct JWgrad {
   // a.order lists the experts by cost, most rows first, and a.order[El] = 1, when
   // their loads are skewed enough for serpentine rounds to pay; else it is the
   // identity, a.order[El] = 0, and the items go out in contiguous XCD ranges.
-  static constexpr bool DYN = true;
+  static constexpr bool DYN = true, REG = false;
   __device__ __forceinline__ bool serpentine() const { return sload(a.order + a.El) != 0; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;

@@ -126,6 +126,11 @@ __device__ __forceinline__ i32x4 gload16(const bf16_t* p) {
 __device__ __forceinline__ void lds_put16(bf16_t* wave_base, i32x4 v) {
   *reinterpret_cast<i32x4*>(wave_base + (threadIdx.x & 63) * 8) = v;
 }
+__device__ __forceinline__ int gload4(const void* p) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
 
 // MFMA 32x32x16 operand fragment: lane l gets 8 consecutive k of row/col (l & 31),
 // k = 8 * (l >> 5) .. +7 inside the 16-wide k sub-step kk.
@@ -357,7 +362,7 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing repeated loads
 }
 
-// The load side for jobs whose loaders stage through registers (J::Ld::REG) and whose
+// The load side for jobs whose loaders stage through registers (J::REG) and whose
 // tiles all take the same number of K steps.  The load cursor runs DEPTH + REG_AHEAD
 // positions ahead of the MFMAs: at position c the load waves write the registers of
 // position c + DEPTH into the stage freed by the barrier and refill them with the loads
@@ -393,7 +398,7 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
     Slot t;
     load_next(t);
     t.template ready<0>();
-    L.store(t, lds + d * STAGE_ELEMS);  // total >= MIN_STEPS > DEPTH
+    L.store(t, lds + d * STAGE_ELEMS, d);  // total >= MIN_STEPS > DEPTH
   }
   Slot s0, s1;
   load_next(s0);  // position DEPTH
@@ -405,7 +410,7 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
     t.template ready<P::NLOAD>();
     // past the stream's end (p >= total) this fills a stage no position reads any more
     const int p = c + DEPTH;
-    L.store(t, lds + (p % NSTAGE) * STAGE_ELEMS);
+    L.store(t, lds + (p % NSTAGE) * STAGE_ELEMS, p % NSTAGE);
     load_next(t);  // position p + REG_AHEAD
   };
   for (int c = 0;; c += 2) {
@@ -424,7 +429,7 @@ __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   Sched<J::DYN> sc(job.items(), job.serpentine());
   if (sc.v < 0) return;
   if (wv >= NW) {
-    if constexpr (J::Ld::REG) load_stream_reg(job, lds, sc, wv - NW, lane);
+    if constexpr (J::REG) load_stream_reg(job, lds, sc, wv - NW, lane);
     else load_stream(job, lds, sc, wv - NW, lane);
   } else {
     compute_stream(job, lds, sc, wv, lane);
@@ -571,7 +576,7 @@ struct KRows {
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) v[q] = gload16(p[q] + kt * BK);
   }
-  __device__ __forceinline__ void store(const i32x4 (&v)[A_LP], bf16_t* st, int pw) const {
+  __device__ __forceinline__ void put(const i32x4 (&v)[A_LP], bf16_t* st, int pw) const {
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) lds_put16(a_dst(st, q, pw), v[q]);
   }

@@ -156,3 +156,38 @@ def test_empty_expert_and_no_tokens():
     assert out0["y"].shape == (0, cfg.H)
     assert not out0["dw_gate"].any() and not out0["dw_down"].any()
     assert not out0["counts"].any() and not out0["offsets"].any()
+
+
+# Degenerate and boundary shapes of the method: a single expert choice (k = 1), every
+# expert chosen (k = E, where renorm = 1 equals the full softmax), one expert in all,
+# one local expert, the largest k, the full-softmax weights in bf16, the smallest H and I
+# the bf16 path takes (64) and an I that leaves a 64-column tail in every 256-wide tile.
+EDGE = {
+    "k1": wl.MoeConfig("k1", 300, 128, 64, 4, 1, 0, 4, 21),
+    "k_eq_E": wl.MoeConfig("k_eq_E", 200, 192, 128, 4, 4, 0, 4, 22),
+    "one_expert": wl.MoeConfig("one_expert", 150, 64, 64, 1, 1, 0, 1, 23),
+    "one_local": wl.MoeConfig("one_local", 256, 128, 192, 16, 4, 7, 1, 24),
+    "k16": wl.MoeConfig("k16", 64, 128, 64, 32, 16, 0, 32, 25),
+    "renorm0_bf16": wl.MoeConfig("renorm0_bf16", 256, 128, 128, 8, 3, 2, 5, 26, renorm=0),
+    "tail_cols": wl.MoeConfig("tail_cols", 333, 320, 320, 6, 2, 0, 6, 27),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_shapes(name):
+    cfg = EDGE[name]
+    print(f"[parity-edge] {name}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp)
+    ref = oracle_full(cfg, inp)
+    _check_ints(cfg, out, ref)
+    assert int(out["counts"].sum()) == int(out["offsets"][-1])
+    assert rel(out["topk_w"], ref["topk_w"]) < W_TOL
+    t = tol(cfg)
+    for key in ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits"):
+        err = rel(out[key], ref[key])
+        assert err < t, (key, err)
+    if cfg.k == cfg.E:
+        # every token reaches every expert: the counts are T, the weights sum to one
+        assert np.all(out["counts"] == cfg.T)
+        assert np.allclose(out["topk_w"].sum(axis=1), 1.0, atol=1e-5)
