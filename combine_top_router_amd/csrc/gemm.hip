@@ -780,12 +780,13 @@ struct JWgrad {
       const int mm = m0 + rt, n = n0 + ct;
       if (mm >= M || n >= N) return;
       const i32x4 o = pack8(vv);
+      // weight gradients are not read again by this pass: streaming stores
       if (WHICH == 0) {
-        *reinterpret_cast<i32x4*>(a.dwd + ((size_t)e * a.I + mm) * a.H + n) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(a.dwd + ((size_t)e * a.I + mm) * a.H + n));
       } else if (n < a.I) {
-        *reinterpret_cast<i32x4*>(a.dwg + ((size_t)e * a.H + mm) * a.I + n) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(a.dwg + ((size_t)e * a.H + mm) * a.I + n));
       } else {
-        *reinterpret_cast<i32x4*>(a.dwu + ((size_t)e * a.H + mm) * a.I + (n - a.I)) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(a.dwu + ((size_t)e * a.H + mm) * a.I + (n - a.I)));
       }
     });
   }
