@@ -372,7 +372,6 @@ template <class J, class S>
 __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc, int pw, int lane) {
   using P = typename J::Ld;
   using Slot = typename P::Slot;
-  static_assert(REG_AHEAD == 2, "the position loop is unrolled for two register slots");
   int ntiles = 0;
   for (int u = sc.v; u >= 0; u = sc.next(u)) ++ntiles;
   P L;
@@ -400,24 +399,29 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
     t.template ready<0>();
     L.store(t, lds + d * STAGE_ELEMS, d);  // total >= MIN_STEPS > DEPTH
   }
-  Slot s0, s1;
-  load_next(s0);  // position DEPTH
-  load_next(s1);  // position DEPTH + 1
+  Slot sl[REG_AHEAD];
+#pragma unroll
+  for (int r = 0; r < REG_AHEAD; ++r) load_next(sl[r]);  // positions DEPTH .. DEPTH + REG_AHEAD - 1
   auto position = [&](int c, Slot& t) {
     if (c > 0 && c % len == 0) asm volatile("s_barrier" ::: "memory");  // the previous tile's epilogue barrier
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // t's loads are the older of the two slots': at most the other slot's may still fly
-    t.template ready<P::NLOAD>();
+    // t's loads are the oldest in flight: the other slots' may still fly
+    t.template ready<(REG_AHEAD - 1) * P::NLOAD>();
     // past the stream's end (p >= total) this fills a stage no position reads any more
     const int p = c + DEPTH;
     L.store(t, lds + (p % NSTAGE) * STAGE_ELEMS, p % NSTAGE);
     load_next(t);  // position p + REG_AHEAD
   };
-  for (int c = 0;; c += 2) {
-    position(c, s0);
-    if (c + 1 >= total) break;
-    position(c + 1, s1);
-    if (c + 2 >= total) break;
+  for (int c = 0;; c += REG_AHEAD) {
+    bool end = false;
+#pragma unroll
+    for (int r = 0; r < REG_AHEAD; ++r) {
+      if (!end) {
+        position(c + r, sl[r]);
+        end = c + r + 1 >= total;
+      }
+    }
+    if (end) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads past the end
   asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
