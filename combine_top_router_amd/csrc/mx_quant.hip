@@ -82,19 +82,20 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
   }
 }
 
-// Column-wise, transposed: one workgroup per (padded 128-row chunk, 64 columns); a chunk
+// Column-wise, transposed: one workgroup per (padded 128-row chunk, 128 columns); a chunk
 // lies inside one expert's padded segment (segments are multiples of 128 rows).  The
 // chunk's row sources and weights are read once into LDS and its rows staged as bf16
-// (16 KB, so several workgroups share a CU); thread t takes the 32-row block t / 64 of
-// column t % 64 into registers (applying the optional row weight in fp32), quantizes
+// (32 KB, so several workgroups share a CU); thread t takes the 32-row block t / 128 of
+// column t % 128 into registers (applying the optional row weight in fp32), quantizes
 // it into LDS, and the workgroup then writes each column's 128 codes as one 128-byte
 // line and its four scales as one word.  With qr given, the same staged tile also yields
 // the row-wise quantisation of the unweighted values (codes [rows, N] at the source's
-// dispatched row, scales [rows, N / 32]): thread t takes the 32 columns (t % 2) of
-// staged row t / 2, so a matrix that both layouts need is read once.
-constexpr int COL_ROWS = 128, COL_COLS = 64;
+// dispatched row, scales [rows, N / 32]): thread t takes the 32 columns (t % 4) of
+// staged row t / 4, so a matrix that both layouts need is read once.
+constexpr int COL_ROWS = 128, COL_COLS = 128;
+constexpr int COL_THREADS = 4 * COL_COLS;   // one per (column, 32-row block)
 static_assert(COL_ROWS == kMxRowPad, "a column chunk spans one padding unit");
-__global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
+__global__ __launch_bounds__(COL_THREADS) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
                                                  const int32_t* __restrict__ row_src, int k,
                                                  const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ offsets,
@@ -133,18 +134,18 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
   __syncthreads();
   // stage: 128 rows x 64 columns of bf16, one 16-byte load per (row, 8 columns)
   {
-    constexpr int IT = COL_ROWS * (COL_COLS / 8) / 256;
+    constexpr int IT = COL_ROWS * (COL_COLS / 8) / COL_THREADS;
     i32x4 u[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int i = tid + 256 * it;
+      const int i = tid + COL_THREADS * it;
       const int rr = i / (COL_COLS / 8), cc = (i % (COL_COLS / 8)) * 8;
       u[it] = i32x4{0, 0, 0, 0};
       if (rr < nrow && n0 + cc < N) u[it] = *reinterpret_cast<const i32x4*>(src + (size_t)srow[rr] * ld + n0 + cc);
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int i = tid + 256 * it;
+      const int i = tid + COL_THREADS * it;
       const int rr = i / (COL_COLS / 8), cc = (i % (COL_COLS / 8)) * 8;
       *reinterpret_cast<i32x4*>(&tile[rr][cc]) = u[it];
     }
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
     reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
   }
   if (qr) {
-    const int rr = tid / 2, h = tid % 2;                // staged row, 32-column half
+    const int rr = tid / (COL_COLS / 32), h = tid % (COL_COLS / 32);   // staged row, 32-column block
     const int n = n0 + 32 * h;
     if (rr < nrow && n < N) {
       const i32x4* t4 = reinterpret_cast<const i32x4*>(&tile[rr][32 * h]);
@@ -196,10 +197,10 @@ __global__ __launch_bounds__(256) void k_mx_cols(const bf16_t* __restrict__ src,
     }
   }
   __syncthreads();
-  // write-out: 64 columns x 128 codes, eight lanes per 128-byte line
+  // write-out: COL_COLS columns x 128 codes, eight lanes per 128-byte line
 #pragma unroll
-  for (int it = 0; it < COL_COLS * 8 / 256; ++it) {
-    const int i = tid + 256 * it;
+  for (int it = 0; it < COL_COLS * 8 / COL_THREADS; ++it) {
+    const int i = tid + COL_THREADS * it;
     const int c = i / 8, part = i % 8;
     const int n = n0 + c;
     if (n < N)
@@ -243,7 +244,7 @@ hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int
                           const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
                           uint8_t* stt, const char* name, hipStream_t st, uint8_t* qr, uint8_t* sr) {
   if (Rp <= 0) return hipSuccess;
-  MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / COL_ROWS), (unsigned)ceil_div(N, COL_COLS)), dim3(256), 0, st,
+  MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / COL_ROWS), (unsigned)ceil_div(N, COL_COLS)), dim3(COL_THREADS), 0, st,
              src, ld, row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt, qr, sr);
   return hipGetLastError();
 }
