@@ -226,35 +226,49 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ rows, int
                                                  const int32_t* __restrict__ row_of,
                                                  T* __restrict__ out);
 
-template <>
-__global__ __launch_bounds__(256) void k_combine<bf16_t>(const bf16_t* __restrict__ rows, int T_, int H,
-                                                         int k, const int32_t* __restrict__ row_of,
-                                                         bf16_t* __restrict__ out) {
+// bf16 rows, KM >= k row slots per token
+template <int KM>
+__global__ __launch_bounds__(256) void k_combine_bf16(const bf16_t* __restrict__ rows, int T_, int H, int k,
+                                                     const int32_t* __restrict__ row_of, bf16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
   const int my_r = lane < k ? row_of[(size_t)t * k + lane] : -1;
-  int rr[16];  // the token's rows, broadcast while every lane is active (k <= 16)
+  int rr[KM];  // the token's rows, broadcast while every lane is active (k <= KM)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) rr[j] = __shfl(my_r, j, 64);
+  for (int j = 0; j < KM; ++j) rr[j] = __shfl(my_r, j, 64);
   const int nvec = H / 8;
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // two 16-byte columns per lane per pass: all of their row loads are issued before
+  // the sums that need them
+  for (int c0 = lane; c0 < nvec; c0 += 128) {
+    const bool two = c0 + 64 < nvec;
+    i32x4 v[2][KM];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < KM; ++j) {
       const int r = rr[j];
       if (j >= k || r < 0) continue;
-      const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(rows + (size_t)r * H) + c);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += __uint_as_float(((uint32_t)v[q]) << 16);
-        acc[2 * q + 1] += __uint_as_float(((uint32_t)v[q]) & 0xffff0000u);
-      }
+      const i32x4* p = reinterpret_cast<const i32x4*>(rows + (size_t)r * H) + c0;
+      v[0][j] = __builtin_nontemporal_load(p);
+      if (two) v[1][j] = __builtin_nontemporal_load(p + 64);
     }
-    i32x4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = (int)((uint32_t)f2bf(acc[2 * q]) | ((uint32_t)f2bf(acc[2 * q + 1]) << 16));
-    reinterpret_cast<i32x4*>(out + (size_t)t * H)[c] = o;
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && !two) break;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j >= k || rr[j] < 0) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += __uint_as_float(((uint32_t)v[h][j][q]) << 16);
+          acc[2 * q + 1] += __uint_as_float(((uint32_t)v[h][j][q]) & 0xffff0000u);
+        }
+      }
+      i32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = (int)((uint32_t)f2bf(acc[2 * q]) | ((uint32_t)f2bf(acc[2 * q + 1]) << 16));
+      reinterpret_cast<i32x4*>(out + (size_t)t * H)[c0 + 64 * h] = o;
+    }
   }
 }
 
@@ -337,12 +351,18 @@ hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* r
                           hipStream_t st, const char* name) {
   if (s.T == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(s.T, 4));
-  if (s.dtype == MOE_BF16)
-    MOE_LAUNCH(name, k_combine<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)rows, s.T, s.H, s.k, row_of,
-                       (bf16_t*)out);
-  else
+  if (s.dtype == MOE_BF16) {
+    if (s.k <= 8) {
+      MOE_LAUNCH(name, k_combine_bf16<8>, grid, dim3(256), 0, st, (const bf16_t*)rows, s.T, s.H, s.k, row_of,
+                 (bf16_t*)out);
+    } else {
+      MOE_LAUNCH(name, k_combine_bf16<16>, grid, dim3(256), 0, st, (const bf16_t*)rows, s.T, s.H, s.k, row_of,
+                 (bf16_t*)out);
+    }
+  } else {
     MOE_LAUNCH(name, k_combine<float>, grid, dim3(256), 0, st, (const float*)rows, s.T, s.H, s.k, row_of,
-                       (float*)out);
+               (float*)out);
+  }
   return hipGetLastError();
 }
 
