@@ -44,12 +44,11 @@ struct RowTileInfo {
 };
 
 // Row-tiled loader state common to every kernel.  These loaders stage through registers
-// (load / store of a Slot); issue() is the direct-to-LDS form of the same loads.
+// (load / store of a Slot).
 struct RowLd {
   static constexpr int NLOAD = A_LP + B_LP;  // register loads per position
   int nk;
   int pw;
-  __device__ __forceinline__ void fetch(int, int) const {}
 };
 struct RowSlot {
   i32x4 a[A_LP];
@@ -93,17 +92,9 @@ __device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_
 // WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
 // and U of one element share a lane.
 struct LGateUp : RowLd {
-  static constexpr bool GATHER = false;
-  static constexpr int NVMEM = LOADS;
   KRows a;
   const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
   size_t bstep;           // elements per K step of the weights (64 rows)
-  template <class F>
-  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
-    a.issue(kt, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
-  }
   using Slot = RowSlot;
   __device__ __forceinline__ void load(int kt, Slot& s) const {
     a.load(kt, s.a);
@@ -197,17 +188,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
 // ---------------- K2: down projection * routing weight ----------------
 // K-major A rows, MN-major B (row-major weights [K, N])
 struct LMnB : RowLd {
-  static constexpr bool GATHER = false;
-  static constexpr int NVMEM = LOADS;
   KRows a;
   const bf16_t* b[B_LP];
   size_t bstep;
-  template <class F>
-  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
-    a.issue(kt, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
-  }
   using Slot = RowSlot;
   __device__ __forceinline__ void load(int kt, Slot& s) const {
     a.load(kt, s.a);
@@ -285,20 +268,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
 
 // ---------------- B1 / B3: both operands K-major ----------------
 struct LKK : RowLd {
-  static constexpr bool GATHER = false;
-  static constexpr int NVMEM = LOADS;
   KRows a;
   const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
   const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
   int ksplit;              // B3: I / 64; B1: larger than any step count
-  template <class F>
-  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
-    a.issue(kt, st, pw);
-    const bool second = kt >= ksplit;
-    const int k0 = (second ? kt - ksplit : kt) * BK;
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) dma16((second ? b2[q] : b[q]) + k0, b_dst(st, q, pw));
-  }
   using Slot = RowSlot;
   __device__ __forceinline__ void load(int kt, Slot& s) const {
     a.load(kt, s.a);

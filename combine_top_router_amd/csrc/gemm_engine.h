@@ -572,10 +572,6 @@ __device__ __forceinline__ void gather_rows_a(const int32_t* row_src, const RowT
 // the lane's chunk) of the slot it fills; step kt adds kt * 64 elements.
 struct KRows {
   const bf16_t* p[A_LP];
-  __device__ __forceinline__ void issue(int kt, bf16_t* st, int pw) const {
-#pragma unroll
-    for (int q = 0; q < A_LP; ++q) dma16(p[q] + kt * BK, a_dst(st, q, pw));
-  }
   __device__ __forceinline__ void load(int kt, i32x4 (&v)[A_LP]) const {
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) v[q] = gload16(p[q] + kt * BK);
