@@ -176,6 +176,41 @@ def test_mx_layer_parity(name, fuse):
         assert e_plain < PLAIN_TOL, (key, e_plain)
 
 
+def _random_mx_configs(n, seed=4048):
+    """Seeded random small fp8_bwd layers: H a multiple of 128, I of 64, random E, k and
+    local range, both weight modes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 33))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        el = int(rng.integers(1, E + 1))
+        eb = int(rng.integers(0, E - el + 1))
+        out.append(wl.MoeConfig(f"rand_mx{i}", int(rng.integers(1, 400)), 128 * int(rng.integers(1, 4)),
+                                64 * int(rng.integers(1, 6)), E, k, eb, el, 200 + i, bwd="mxfp8",
+                                renorm=int(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_MX = {c.name: c for c in _random_mx_configs(6)}
+
+
+@pytest.mark.parametrize("name", list(RANDOM_MX))
+def test_mx_random_shapes(name):
+    cfg = RANDOM_MX[name]
+    print(f"[mx-parity-random] {cfg}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp)
+    idx, w, Y, ix, gmx, g = _oracle_mx(cfg, inp)
+    assert np.array_equal(out["topk_idx"], idx)
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    assert rel(out["y"], Y) < BF16_TOL
+    for key in GRADS:
+        e_mx = rel(out[key], gmx[key])
+        assert e_mx < MX_TOL, (key, e_mx)
+
+
 def test_mx_full_size_parity_sampled():
     """235B-A22B EP=8 share (16 of 128 experts, H=4096, I=1536, T=16384, top-8) in fp8_bwd
     mode: sampled tokens for dx and d_topk_w, sampled experts for the weight gradients,

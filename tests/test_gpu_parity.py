@@ -191,3 +191,38 @@ def test_edge_shapes(name):
         # every token reaches every expert: the counts are T, the weights sum to one
         assert np.all(out["counts"] == cfg.T)
         assert np.allclose(out["topk_w"].sum(axis=1), 1.0, atol=1e-5)
+
+
+def _random_configs(n, seed=2024):
+    """Seeded random small layers across the shape space the bf16 path accepts: H and I
+    multiples of 64, any E up to 40 with k <= min(E, 16), a random local expert range,
+    both weight modes; sized so the oracle finishes each in a few seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 41))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        el = int(rng.integers(1, E + 1))
+        eb = int(rng.integers(0, E - el + 1))
+        H = 64 * int(rng.integers(1, 7))
+        I = 64 * int(rng.integers(1, 7))
+        T = int(rng.integers(1, 400))
+        out.append(wl.MoeConfig(f"rand{i}", T, H, I, E, k, eb, el, 100 + i, renorm=int(rng.integers(0, 2))))
+    return out
+
+
+RANDOM = {c.name: c for c in _random_configs(10)}
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_random_shapes(name):
+    cfg = RANDOM[name]
+    print(f"[parity-random] {cfg}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp)
+    ref = oracle_full(cfg, inp)
+    _check_ints(cfg, out, ref)
+    assert rel(out["topk_w"], ref["topk_w"]) < W_TOL
+    for key in ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits"):
+        err = rel(out[key], ref[key])
+        assert err < BF16_TOL, (key, err)
