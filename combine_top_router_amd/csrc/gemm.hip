@@ -53,15 +53,15 @@ struct RowLd {
 struct RowSlot {
   i32x4 a[A_LP];
   i32x4 b[B_LP];
-  // wait until at most N of this wave's loads are in flight; the slot's registers are
-  // operands, so nothing reads them before the wait
+  // wait until at most N of this wave's loads are in flight; each register is then
+  // passed through an empty asm, so nothing reads it before the wait
   template <int N>
   __device__ __forceinline__ void ready() {
-    static_assert(A_LP == 2 && B_LP == 4, "operand list below");
-    asm volatile("s_waitcnt vmcnt(%6)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
-                 : "n"(N)
-                 : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) asm volatile("" : "+v"(a[q]));
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) asm volatile("" : "+v"(b[q]));
   }
 };
 
@@ -151,8 +151,8 @@ struct JGateUp {
   // up blocks (same columns), and writes 16-byte chunks of G, U and A
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
-    constexpr int LPR = WCOLS / 16;
-    static_assert(64 / LPR == EP_ROWS, "one pass per staged quarter");
+    constexpr int LPR = WCOLS / 16;          // lanes per row
+    constexpr int PASSES = EP_ROWS * LPR / 64;  // passes over a staged 16-row piece
     float* wsm = stage + wv * EP_ROWS * EP_LD;
     const size_t I2 = 2 * (size_t)a.I;
 #pragma unroll
@@ -160,20 +160,23 @@ struct JGateUp {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         stage_quarter(wsm, acc, mi, h, lane);
-        const int rr = lane / LPR, cc = (lane % LPR) * 8;
-        const int rt = wm * WROWS + mi * 32 + h * 16 + rr;
-        float g[8], u[8], av[8];
-        read8(wsm + rr * EP_LD + cc, g);
-        read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
-        staging_done();
-        const int col = p.n0 + wn * (WCOLS / 2) + cc;
-        if (rt < p.t.cnt && col < a.I) {
-          const size_t r = (size_t)(p.t.rs + rt);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
-          *reinterpret_cast<i32x4*>(a.gu + r * I2 + col) = pack8(g);
-          *reinterpret_cast<i32x4*>(a.gu + r * I2 + a.I + col) = pack8(u);
-          *reinterpret_cast<i32x4*>(a.a + r * a.I + col) = pack8(av);
+        for (int j = 0; j < PASSES; ++j) {
+          const int rr = lane / LPR + (64 / LPR) * j, cc = (lane % LPR) * 8;
+          const int rt = wm * WROWS + mi * 32 + h * 16 + rr;
+          float g[8], u[8], av[8];
+          read8(wsm + rr * EP_LD + cc, g);
+          read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
+          if (j == PASSES - 1) staging_done();
+          const int col = p.n0 + wn * (WCOLS / 2) + cc;
+          if (rt < p.t.cnt && col < a.I) {
+            const size_t r = (size_t)(p.t.rs + rt);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
+            *reinterpret_cast<i32x4*>(a.gu + r * I2 + col) = pack8(g);
+            *reinterpret_cast<i32x4*>(a.gu + r * I2 + a.I + col) = pack8(u);
+            *reinterpret_cast<i32x4*>(a.a + r * a.I + col) = pack8(av);
+          }
         }
       }
   }
@@ -351,11 +354,13 @@ struct LMx {
     int s[MX_SC_LP];
     template <int N>
     __device__ __forceinline__ void ready() {
-      static_assert(A_LP == 2 && B_LP == 4 && MX_SC_LP == 1, "operand list below");
-      asm volatile("s_waitcnt vmcnt(%7)"
-                   : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(s[0])
-                   : "n"(N)
-                   : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+#pragma unroll
+      for (int q = 0; q < A_LP; ++q) asm volatile("" : "+v"(a[q]));
+#pragma unroll
+      for (int q = 0; q < B_LP; ++q) asm volatile("" : "+v"(b[q]));
+#pragma unroll
+      for (int q = 0; q < MX_SC_LP; ++q) asm volatile("" : "+v"(s[q]));
     }
   };
   int nk, pw;
