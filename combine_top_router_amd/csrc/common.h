@@ -21,12 +21,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 pair (lo in bits 0..15), round to nearest even, with
+// gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
 }
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> struct elem;
 template <> struct elem<float> {
@@ -38,8 +43,9 @@ template <> struct elem<bf16_t> {
   __device__ static void store(bf16_t* p, float v) { *p = f2bf(v); }
 };
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// logistic function with the hardware reciprocal (v_rcp_f32, 1 ulp): exp(-g) = inf gives 0
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
 // Host-side: the launch configuration constants shared by the host code and kernels.
 constexpr int kGemmBM = 128;     // rows of one row-group GEMM tile (bf16 path)

@@ -516,9 +516,9 @@ struct JDa {
             du2[h] = da * g * sg;
             dg2[h] = da * u * sg * (1.f + g * (1.f - sg));
           }
-          dgo[q] = (int)((uint32_t)f2bf(dg2[0]) | ((uint32_t)f2bf(dg2[1]) << 16));
-          duo[q] = (int)((uint32_t)f2bf(du2[0]) | ((uint32_t)f2bf(du2[1]) << 16));
-          awo[q] = (int)((uint32_t)f2bf(aw2[0]) | ((uint32_t)f2bf(aw2[1]) << 16));
+          dgo[q] = (int)pk_bf16(dg2[0], dg2[1]);
+          duo[q] = (int)pk_bf16(du2[0], du2[1]);
+          awo[q] = (int)pk_bf16(aw2[0], aw2[1]);
         }
         *reinterpret_cast<i32x4*>(a.dgu + r * I2 + col) = dgo;
         *reinterpret_cast<i32x4*>(a.dgu + r * I2 + a.I + col) = duo;

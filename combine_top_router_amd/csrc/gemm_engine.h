@@ -472,7 +472,7 @@ __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
 __device__ __forceinline__ i32x4 pack8(const float (&v)[8]) {
   i32x4 o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = (int)((uint32_t)f2bf(v[2 * q]) | ((uint32_t)f2bf(v[2 * q + 1]) << 16));
+  for (int q = 0; q < 4; ++q) o[q] = (int)pk_bf16(v[2 * q], v[2 * q + 1]);
   return o;
 }
 

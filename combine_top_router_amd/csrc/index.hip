@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const bf16_t* __restrict__
       }
       i32x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = (int)((uint32_t)f2bf(acc[2 * q]) | ((uint32_t)f2bf(acc[2 * q + 1]) << 16));
+      for (int q = 0; q < 4; ++q) o[q] = (int)pk_bf16(acc[2 * q], acc[2 * q + 1]);
       reinterpret_cast<i32x4*>(out + (size_t)t * H)[c0 + 64 * h] = o;
     }
   }
