@@ -56,7 +56,8 @@ struct Layout {
 int check_shape(const moe_shape* s) {
   if (!s) return fail(MOE_EINVAL, "shape is NULL");
   if (s->T < 0) return fail(MOE_EINVAL, "T = %d < 0", s->T);
-  if (s->H <= 0 || s->I <= 0) return fail(MOE_EINVAL, "H = %d and I = %d must be > 0", s->H, s->I);
+  if (s->H <= 0 || s->I <= 0 || s->H > (1 << 20) || s->I > (1 << 20))
+    return fail(MOE_EINVAL, "H = %d and I = %d must lie in 1..2^20", s->H, s->I);
   if (s->E < 1 || s->E > 1024) return fail(MOE_EINVAL, "E = %d outside 1..1024", s->E);
   if (s->k < 1 || s->k > s->E || s->k > 16) return fail(MOE_EINVAL, "k = %d outside 1..min(E, 16)", s->k);
   if (s->e_local < 1 || s->e_begin < 0 || (int64_t)s->e_begin + s->e_local > s->E)

@@ -154,7 +154,10 @@ struct JGateUp {
     constexpr int LPR = WCOLS / 16;          // lanes per row
     constexpr int PASSES = EP_ROWS * LPR / 64;  // passes over a staged 16-row piece
     float* wsm = stage + wv * EP_ROWS * EP_LD;
-    const size_t I2 = 2 * (size_t)a.I;
+    const uint32_t I2 = 2u * (uint32_t)a.I;
+    // the tile's first row (uniform); lanes add 32-bit offsets
+    bf16_t* const gub = a.gu + (size_t)p.t.rs * I2;
+    bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -170,12 +173,12 @@ struct JGateUp {
           if (j == PASSES - 1) staging_done();
           const int col = p.n0 + wn * (WCOLS / 2) + cc;
           if (rt < p.t.cnt && col < a.I) {
-            const size_t r = (size_t)(p.t.rs + rt);
+            const uint32_t o = (uint32_t)rt * I2 + (uint32_t)col;
 #pragma unroll
             for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
-            *reinterpret_cast<i32x4*>(a.gu + r * I2 + col) = pack8(g);
-            *reinterpret_cast<i32x4*>(a.gu + r * I2 + a.I + col) = pack8(u);
-            *reinterpret_cast<i32x4*>(a.a + r * a.I + col) = pack8(av);
+            *reinterpret_cast<i32x4*>(gub + o) = pack8(g);
+            *reinterpret_cast<i32x4*>(gub + o + a.I) = pack8(u);
+            *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = pack8(av);
           }
         }
       }
@@ -249,15 +252,15 @@ struct JDown {
       const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
       wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
     }
+    bf16_t* const yb = a.yp + (size_t)p.t.rs * a.H;  // the tile's first row
     epilogue_rows<true>(stage, acc, [&](int rt, int ct, const float (&v)[8], int slot) {
       const int col = p.n0 + ct;
       if (rt < p.t.cnt && col < a.H) {
-        const size_t r = (size_t)(p.t.rs + rt);
         const float w = wr[slot];
         float o[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) o[q] = w * v[q];
-        *reinterpret_cast<i32x4*>(a.yp + r * a.H + col) = pack8(o);
+        *reinterpret_cast<i32x4*>(yb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = pack8(o);
       }
     });
   }
@@ -478,7 +481,12 @@ struct JDa {
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int lane = threadIdx.x & 63, wn = (int)((threadIdx.x >> 6) / WM);
     const int wm = (int)((unsigned)(threadIdx.x >> 6) % WM);
-    const size_t I2 = 2 * (size_t)a.I;
+    const uint32_t I2 = 2u * (uint32_t)a.I;
+    // the tile's first row (uniform); lanes add 32-bit offsets
+    const bf16_t* const gub = a.gu + (size_t)p.t.rs * I2;
+    const bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
+    bf16_t* const dgub = a.dgu + (size_t)p.t.rs * I2;
+    bf16_t* const awb = a.aw + (size_t)p.t.rs * a.I;
     // the routing weights of the lane's rows, fetched before the staging starts
     float wr[EP_LANE_ROWS];
 #pragma unroll
@@ -491,13 +499,13 @@ struct JDa {
       const bool ok = rt < p.t.cnt && col < a.I;
       float part = 0.f;
       if (ok) {
-        const size_t r = (size_t)(p.t.rs + rt);
+        const uint32_t og = (uint32_t)rt * I2 + (uint32_t)col, oa = (uint32_t)rt * (uint32_t)a.I + (uint32_t)col;
         const float w = wr[slot];
         // two columns at a time, straight from and back to packed bf16 pairs
         __builtin_amdgcn_sched_barrier(0);
-        const i32x4 gw = *reinterpret_cast<const i32x4*>(a.gu + r * I2 + col);
-        const i32x4 uw = *reinterpret_cast<const i32x4*>(a.gu + r * I2 + a.I + col);
-        const i32x4 aw4 = *reinterpret_cast<const i32x4*>(a.a + r * a.I + col);
+        const i32x4 gw = *reinterpret_cast<const i32x4*>(gub + og);
+        const i32x4 uw = *reinterpret_cast<const i32x4*>(gub + og + a.I);
+        const i32x4 aw4 = *reinterpret_cast<const i32x4*>(ab + oa);
         i32x4 dgo, duo, awo;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -520,9 +528,9 @@ struct JDa {
           duo[q] = (int)pk_bf16(du2[0], du2[1]);
           awo[q] = (int)pk_bf16(aw2[0], aw2[1]);
         }
-        *reinterpret_cast<i32x4*>(a.dgu + r * I2 + col) = dgo;
-        *reinterpret_cast<i32x4*>(a.dgu + r * I2 + a.I + col) = duo;
-        if (!MX) *reinterpret_cast<i32x4*>(a.aw + r * a.I + col) = awo;
+        *reinterpret_cast<i32x4*>(dgub + og) = dgo;
+        *reinterpret_cast<i32x4*>(dgub + og + a.I) = duo;
+        if (!MX) *reinterpret_cast<i32x4*>(awb + oa) = awo;
       }
 #pragma unroll
       for (int off = 1; off < EP_LPR; off <<= 1) part += __shfl_xor(part, off, 64);
@@ -586,10 +594,11 @@ struct JDx {
     }
   }
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
+    bf16_t* const xb = a.dxp + (size_t)p.t.rs * a.H;  // the tile's first row
     epilogue_rows<!MX>(stage, acc, [&](int rt, int ct, const float (&v)[8], int) {
       const int col = p.n0 + ct;
       if (rt < p.t.cnt && col < a.H)
-        *reinterpret_cast<i32x4*>(a.dxp + (size_t)(p.t.rs + rt) * a.H + col) = pack8(v);
+        *reinterpret_cast<i32x4*>(xb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = pack8(v);
     });
   }
 };
@@ -754,18 +763,18 @@ struct JWgrad {
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
     const int e = p.e, m0 = p.m0, n0 = p.n0;
+    // the tile's first output row in dW_down, or in dW_gate and dW_up (uniform); a lane's
+    // columns are the same in every row it writes, so its matrix is chosen once
+    const uint32_t ld = WHICH == 0 ? (uint32_t)a.H : (uint32_t)a.I;
+    const size_t row0 = ((size_t)e * M + m0) * ld;
+    const int lane = threadIdx.x & 63, wn = (int)((threadIdx.x >> 6) / WM);
+    const int nl = n0 + wn * WCOLS + (lane % EP_LPR) * 8;
+    bf16_t* const lb = WHICH == 0 ? a.dwd + row0 + nl : (nl < a.I ? a.dwg + row0 + nl : a.dwu + row0 + (nl - a.I));
     epilogue_rows<!MX>(stage, acc, [&](int rt, int ct, const float (&vv)[8], int) {
       const int mm = m0 + rt, n = n0 + ct;
       if (mm >= M || n >= N) return;
-      const i32x4 o = pack8(vv);
       // weight gradients are not read again by this pass: streaming stores
-      if (WHICH == 0) {
-        __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(a.dwd + ((size_t)e * a.I + mm) * a.H + n));
-      } else if (n < a.I) {
-        __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(a.dwg + ((size_t)e * a.H + mm) * a.I + n));
-      } else {
-        __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(a.dwu + ((size_t)e * a.H + mm) * a.I + (n - a.I)));
-      }
+      __builtin_nontemporal_store(pack8(vv), reinterpret_cast<i32x4*>(lb + (uint32_t)rt * ld));
     });
   }
 };

@@ -63,8 +63,8 @@ typedef enum { MOE_BWD_SAME = 0, MOE_BWD_MXFP8 = 1 } moe_bwd_prec;
 
 typedef struct {
   int32_t T;        /* tokens, >= 0 */
-  int32_t H;        /* hidden size, > 0, multiple of 64 for MOE_BF16 */
-  int32_t I;        /* expert intermediate size, > 0, multiple of 64 for MOE_BF16 */
+  int32_t H;        /* hidden size, 1..2^20, multiple of 64 for MOE_BF16 */
+  int32_t I;        /* expert intermediate size, 1..2^20, multiple of 64 for MOE_BF16 */
   int32_t E;        /* routed experts, 1..1024 */
   int32_t k;        /* experts per token, 1..min(E, 16) */
   int32_t e_begin;  /* first local expert */
