@@ -47,6 +47,7 @@ BAD = [
     (dict(k=9), -1), (dict(k=17, E=32), -1), (dict(e_local=0), -1), (dict(e_begin=5, e_local=4), -1),
     (dict(e_begin=-1), -1), (dict(dtype=7), -1), (dict(bwd=3), -1), (dict(renorm=2), -1),
     (dict(H=100), -1), (dict(I=96), -1), (dict(dtype=0, H=130), -1),
+    (dict(H=(1 << 20) + 64), -1), (dict(I=(1 << 20) + 64), -1),
     (dict(dtype=0, bwd=1), -2),
 ]
 
