@@ -359,8 +359,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     } else {
       e = launch_bwd_bf16(a, st);
     }
-    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st);
-    if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
+    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st, "combine", a.dw_part, L.nparts, d_topk_w);
   } else {
     BwdArgsF32 a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;

@@ -90,8 +90,10 @@ hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm,
                              int32_t* zeros, int32_t* order, hipStream_t st);
 hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offsets,
                          const int32_t* row_src, void* xp, hipStream_t st);
+// bf16 with part != null: also d_topk_w from the partial row-dots (the dX combine)
 hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
-                          hipStream_t st, const char* name = "combine");
+                          hipStream_t st, const char* name = "combine", const float* part = nullptr,
+                          int nparts = 0, float* d_topk_w = nullptr);
 hipError_t launch_dtopk(const moe_shape& s, const float* dw_part, int nparts, const int32_t* row_of,
                         float* d_topk_w, hipStream_t st);
 

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, 
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
                                                      int32_t* __restrict__ tiles, int32_t* __restrict__ zeros,
                                                      int32_t* __restrict__ order) {
-  __shared__ int32_t buf[1024];
+  __shared__ int32_t buf[16];  // wave totals of the scan
   __shared__ int32_t rows[1024];
   __shared__ int32_t xsum[8], cmax, serp;
   const int e = threadIdx.x;
@@ -157,7 +157,6 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
     c = offsets[e + 1] - offsets[e];
     n = (c + bm - 1) / bm;
   }
-  buf[e] = n;
   rows[e] = c;
   __syncthreads();
   if (order) {
@@ -189,18 +188,26 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
       order[rank] = e;
     }
   }
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = e >= off ? buf[e - off] : 0;
-    __syncthreads();
-    buf[e] += v;
-    __syncthreads();
+  // inclusive scan of the tile counts: within each wave by shuffles, then over the
+  // sixteen wave totals
+  const int lane = e & 63, wv = e >> 6;
+  int incl = n;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  const int start = buf[e] - n;
+  if (lane == 63) buf[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wv; ++w) before += buf[w];
+  incl += before;
+  const int start = incl - n;
   for (int j = 0; j < n; ++j) {
     i32x4 ent = {e, start, n, 0};
     *reinterpret_cast<i32x4*>(tiles + 4 + 4 * (start + j)) = ent;
   }
-  if (e == 1023) tiles[0] = buf[1023];
+  if (e == 1023) tiles[0] = incl;
 }
 
 // xp[r] = x[row_src[r] / k]: one wave per row, 16-byte vectors.
@@ -226,14 +233,24 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ rows, int
                                                  const int32_t* __restrict__ row_of,
                                                  T* __restrict__ out);
 
-// bf16 rows, KM >= k row slots per token
+// bf16 rows, KM >= k row slots per token.  With part (the backward's dX combine), also
+// d_topk_w of the token's slots: each the sum, in part order, of its row's nparts partial
+// row-dots (0 for a slot without a local row).
 template <int KM>
 __global__ __launch_bounds__(256) void k_combine_bf16(const bf16_t* __restrict__ rows, int T_, int H, int k,
-                                                     const int32_t* __restrict__ row_of, bf16_t* __restrict__ out) {
+                                                     const int32_t* __restrict__ row_of, bf16_t* __restrict__ out,
+                                                     const float* __restrict__ part, int nparts,
+                                                     float* __restrict__ d_topk_w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
   const int my_r = lane < k ? row_of[(size_t)t * k + lane] : -1;
+  if (part && lane < k) {
+    float acc = 0.f;
+    if (my_r >= 0)
+      for (int p = 0; p < nparts; ++p) acc += part[(size_t)my_r * nparts + p];
+    d_topk_w[(size_t)t * k + lane] = acc;
+  }
   int rr[KM];  // the token's rows, broadcast while every lane is active (k <= KM)
 #pragma unroll
   for (int j = 0; j < KM; ++j) rr[j] = __shfl(my_r, j, 64);
@@ -348,16 +365,16 @@ hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offse
 }
 
 hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
-                          hipStream_t st, const char* name) {
+                          hipStream_t st, const char* name, const float* part, int nparts, float* d_topk_w) {
   if (s.T == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(s.T, 4));
   if (s.dtype == MOE_BF16) {
     if (s.k <= 8) {
       MOE_LAUNCH(name, k_combine_bf16<8>, grid, dim3(256), 0, st, (const bf16_t*)rows, s.T, s.H, s.k, row_of,
-                 (bf16_t*)out);
+                 (bf16_t*)out, part, nparts, d_topk_w);
     } else {
       MOE_LAUNCH(name, k_combine_bf16<16>, grid, dim3(256), 0, st, (const bf16_t*)rows, s.T, s.H, s.k, row_of,
-                 (bf16_t*)out);
+                 (bf16_t*)out, part, nparts, d_topk_w);
     }
   } else {
     MOE_LAUNCH(name, k_combine<float>, grid, dim3(256), 0, st, (const float*)rows, s.T, s.H, s.k, row_of,
