@@ -33,6 +33,11 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 // fp32 -> bf16, round to nearest even.
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
+// x / k for 0 <= x < 2^31 and 1 <= k <= 16, given inv_k = 1.0 / k: (x + 1/2) / k lies at
+// least 1 / (2k) from an integer, far more than the double product's rounding error
+// (below 2^-20 here), so truncating it gives the exact quotient in three instructions.
+__device__ __forceinline__ int div_k(int x, double inv_k) { return (int)(((double)x + 0.5) * inv_k); }
+
 template <typename T> struct elem;
 template <> struct elem<float> {
   __device__ static float load(const float* p) { return *p; }

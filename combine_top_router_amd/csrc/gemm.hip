@@ -626,7 +626,7 @@ struct LWgrad {
   static constexpr int AR = 512 / BM, BR = 512 / BN;  // token rows per wave load of A and B
   const bf16_t* abase; int lda;
   const bf16_t* bbase; int ldb;
-  const int32_t* row_src; const bf16_t* zeros; int k;
+  const int32_t* row_src; const bf16_t* zeros; double inv_k;  // 1 / top-k
   int rs, cnt, pw, lane;
   int nk;
   int32_t* ids;                  // this wave's two LDS slots of BK row indices
@@ -646,14 +646,14 @@ struct LWgrad {
     for (int q = 0; q < A_LP; ++q) {
       const int kr = load_instr(q, pw) * AR + (int)((unsigned)lane / (64 / AR));
       int row = rs + kt * BK + kr;
-      if (AG) row = my[kr] / k;
+      if (AG) row = div_k(my[kr], inv_k);
       ap[q] = kt * BK + kr < cnt ? abase + (size_t)row * lda + acol[q] : zeros;
     }
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) {
       const int kr = load_instr(q, pw) * BR + (int)((unsigned)lane / (64 / BR));
       int row = rs + kt * BK + kr;
-      if (BG) row = my[kr] / k;
+      if (BG) row = div_k(my[kr], inv_k);
       bp[q] = kt * BK + kr < cnt ? bbase + (size_t)row * ldb + bcol[q] : zeros;
     }
     if (GATHER) fetch_next();
@@ -734,7 +734,7 @@ struct JWgrad {
       const int o0 = sload(a.offsets + e), o1 = sload(a.offsets + e + 1);
       p.rs = o0;
       p.cnt = uni(o1 - o0);
-      p.row_src = a.row_src; p.zeros = a.zeros; p.k = a.k;
+      p.row_src = a.row_src; p.zeros = a.zeros; p.inv_k = 1.0 / a.k;
       p.lane = lane;
       p.ids = ids + pw * 2 * IDS_SLOT;
       if (WHICH == 0) {

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -113,3 +114,15 @@ def test_quantizer_arguments_are_checked_before_launch():
     with pytest.raises(L.MoeError) as ei:
         L.moe_mx_quantize(8, 4, 48, 8, 8)                     # K not a multiple of 32
     assert ei.value.code == L.MOE_EINVAL
+
+
+def test_quotient_by_top_k_through_double_is_exact():
+    """The kernels divide a row_src entry x (0 <= x < 2^31) by k (1..16) as
+    trunc((x + 0.5) * (1.0 / k)) in double precision; check it against integer division on
+    the residues next to every multiple of k near the ends of the range."""
+    for k in range(1, 17):
+        inv = 1.0 / k
+        base = np.concatenate([np.arange(0, 4096), np.arange(2**31 - 4096 * k, 2**31 - 1, k)])
+        x = np.unique(np.clip((base[:, None] // k * k + np.arange(-1, k + 1)[None, :]).ravel(), 0, 2**31 - 1))
+        q = np.trunc((x.astype(np.float64) + 0.5) * inv).astype(np.int64)
+        assert np.array_equal(q, x // k), k
