@@ -642,18 +642,27 @@ struct LWgrad {
     if (GATHER) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
     const bf16_t* ap[A_LP];
     const bf16_t* bp[B_LP];
+    // all gathered indices are read (the slot holds valid entries for every row) before
+    // any address is formed, so their LDS reads go out together and are waited for once
+    int ia[A_LP], ib[B_LP];
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) ia[q] = AG ? my[load_instr(q, pw) * AR + (int)((unsigned)lane / (64 / AR))] : 0;
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) ib[q] = BG ? my[load_instr(q, pw) * BR + (int)((unsigned)lane / (64 / BR))] : 0;
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) asm volatile("" : "+v"(ia[q]));
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) asm volatile("" : "+v"(ib[q]));
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) {
       const int kr = load_instr(q, pw) * AR + (int)((unsigned)lane / (64 / AR));
-      int row = rs + kt * BK + kr;
-      if (AG) row = div_k(my[kr], inv_k);
+      const int row = AG ? div_k(ia[q], inv_k) : rs + kt * BK + kr;
       ap[q] = kt * BK + kr < cnt ? abase + (size_t)row * lda + acol[q] : zeros;
     }
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) {
       const int kr = load_instr(q, pw) * BR + (int)((unsigned)lane / (64 / BR));
-      int row = rs + kt * BK + kr;
-      if (BG) row = div_k(my[kr], inv_k);
+      const int row = BG ? div_k(ib[q], inv_k) : rs + kt * BK + kr;
       bp[q] = kt * BK + kr < cnt ? bbase + (size_t)row * ldb + bcol[q] : zeros;
     }
     if (GATHER) fetch_next();
