@@ -54,12 +54,20 @@ __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, 
   }
   __syncthreads();
   const int me = blockIdx.x;
-  for (int i = tid; i < nchunks * El; i += 256) {
-    const int c = i / El, e = i - c * El;
-    const int v = chunk_hist[i];
-    if (v) {
-      atomicAdd(&tot[e], v);
-      if (c < me) atomicAdd(&base[e], v);
+  // eight histogram loads in flight per thread before their sums
+  constexpr int HU = 8;
+  const int nh = nchunks * El;
+  for (int i0 = tid; i0 < nh; i0 += 256 * HU) {
+    int v[HU];
+#pragma unroll
+    for (int u = 0; u < HU; ++u) v[u] = i0 + 256 * u < nh ? chunk_hist[i0 + 256 * u] : 0;
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+      if (v[u]) {
+        const int i = i0 + 256 * u, c = i / El, e = i - c * El;
+        atomicAdd(&tot[e], v[u]);
+        if (c < me) atomicAdd(&base[e], v[u]);
+      }
     }
   }
   __syncthreads();
