@@ -1,9 +1,10 @@
-"""fp64 oracle of the MXFP8 backward: E4M3 elements with one e8m0 scale per 32.
+"""fp64 oracle of the MXFP8 GEMMs: E4M3 elements with one e8m0 scale per 32.
 
 The pages name the formats only: MXFP8 block scaling for the expert GEMMs and a
 group-aware MXFP8 quantisation (NVIDIA article, "Optimization 1" and its list of
 Transformer Engine building blocks), and an fp8_bwd mode with a bf16 forward and an
-fp8 backward (Prime Mega MoE pages).  The element and scale encodings are the OCP
+fp8 backward, and an mxfp8 mode that runs the expert GEMMs in MXFP8 (Prime Mega
+MoE pages: precision bf16, mxfp8, fp8 or fp8_bwd).  The element and scale encodings are the OCP
 Microscaling (MX) v1.0 ones: E4M3 "FN" (bias 7, max 448, no infinities, 0x7F/0xFF
 NaN) and E8M0 (2^(code-127)).
 
@@ -19,6 +20,12 @@ Readings:
   (A and w*dY' for dW_down; X and dG, dU for dW_gate, dW_up).
 * B1 quantises the unweighted dY' and applies w after the GEMM; B2 quantises w*dY'.
   dG and dU are quantised from their unrounded values.  Outputs stay unquantised.
+* mxfp8 forward: the two forward GEMMs take MXFP8 operands along their contraction
+  axes: the gate/up GEMM quantises the rows of X along H and W_gate, W_up in blocks
+  of 32 consecutive rows (h) of each column; the down GEMM quantises the rows of A
+  along I and W_down in blocks of 32 consecutive rows (i) of each column.  A is
+  quantised from its unrounded value and the routing weight applies after the GEMM.
+  G, U and A (what the backward reads) are the unquantised results of these GEMMs.
 """
 from __future__ import annotations
 
@@ -30,7 +37,7 @@ E4M3_MAX = 448.0
 BLOCK = 32
 
 __all__ = ["e4m3_decode", "e4m3_round", "e4m3_encode", "e8m0_exponent", "quantize_blocks",
-           "qdq_rows", "qdq_cols_grouped", "layer_backward_mx"]
+           "qdq_rows", "qdq_cols_grouped", "layer_forward_mx", "layer_backward_mx"]
 
 
 def e4m3_decode(code):
@@ -114,6 +121,37 @@ def qdq_cols_grouped(m, offsets):
             _, _, deq = quantize_blocks(blk.T)          # [N, 32]
             out[r0:r1] = deq.T[: r1 - r0]
     return out
+
+
+def layer_forward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, topk_w, index=None):
+    """The forward with the four forward-GEMM operands quantize-dequantized to MXFP8
+    (module docstring, mxfp8 forward); fp64 everywhere else.  Returns Y [T,H] and the
+    saved rows (G, U, A, Yp) in the same form as the plain oracle's forward."""
+    if index is None:
+        index = build_index(topk_idx, e_begin, e_local)
+    x = _f64(inp["x"])
+    T, H = x.shape
+    I = inp["w_gate"].shape[2]
+    R = index["row_src"].shape[0]
+    wflat = _f64(topk_w).reshape(-1)
+    G = np.zeros((R, I)); U = np.zeros((R, I)); A = np.zeros((R, I)); Yp = np.zeros((R, H))
+    Y = np.zeros((T, H))
+    for e in range(e_local):
+        lo, hi = int(index["offsets"][e]), int(index["offsets"][e + 1])
+        if hi == lo:
+            continue
+        rows = index["row_src"][lo:hi]
+        tok = rows // k
+        # gate/up GEMM: Q(X rows along H) against Q(W columns along H)
+        qx = qdq_rows(x[tok])
+        g = qx @ qdq_cols_grouped(inp["w_gate"][e], np.array([0, H]))
+        u = qx @ qdq_cols_grouped(inp["w_up"][e], np.array([0, H]))
+        a = silu(g) * u
+        # down GEMM: Q(A rows along I) against Q(W_down columns along I), then w
+        yp = wflat[rows][:, None] * (qdq_rows(a) @ qdq_cols_grouped(inp["w_down"][e], np.array([0, I])))
+        G[lo:hi], U[lo:hi], A[lo:hi], Yp[lo:hi] = g, u, a, yp
+        Y[tok] += yp                                  # tokens are distinct within one expert
+    return Y, {"G": G, "U": U, "A": A, "Yp": Yp, "index": index}
 
 
 def layer_backward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, topk_w, saved):

@@ -92,3 +92,90 @@ def test_mx_backward_is_close_to_exact_backward():
     for key in ("dx", "dw_gate", "dw_up", "dw_down", "d_topk_w"):
         rel = np.linalg.norm(gq[key] - g[key]) / np.linalg.norm(g[key])
         assert 1e-3 < rel < 8e-2, (key, rel)
+
+
+def _on_grid_rows(rng, n, K, xlo=-9, xhi=-5):
+    """[n, K] values on the MX grid of their own 32-element row blocks: each block has
+    a random exponent X, E4M3 grid values times 2^X, and its amax pinned to 448 * 2^X,
+    so row-wise quantisation returns them unchanged.  Neighbouring rows get unrelated
+    exponents, so the same values are off the grid of column blocks."""
+    codes = rng.integers(0, 0x7E, size=(n, K))
+    sgn = np.where(rng.integers(0, 2, size=(n, K)) == 1, -1.0, 1.0)
+    X = rng.integers(xlo, xhi, size=(n, K // 32))
+    m = sgn * mx.e4m3_decode(codes) * np.repeat(np.exp2(X), 32, axis=1)
+    m[:, ::32] = 448.0 * np.exp2(X)
+    return m
+
+
+def _mx_fwd_case(seed, grid):
+    """Tiny layer (E = 4, k = 2) whose X rows are on their row-block grid and whose
+    W_gate, W_up, W_down columns are on their column-block grid (grid=True).
+
+    E4M3 keeps 3 mantissa bits at every scale down to 2^-15 below a block's maximum,
+    so the block axis only shows on values that far below their block's largest:
+    token rows are scaled by 2^-8, 1 or 2^8 (A's rows then span 2^32), which a
+    column block of A cannot hold but a row block can."""
+    cfg = wl.MoeConfig("mxf", 48, 64, 64, 4, 2, 0, 4, seed, bwd="mxfp8")
+    inp = wl.make_inputs(cfg)
+    if grid:
+        rng = np.random.default_rng(seed)
+        inp["x"] = _on_grid_rows(rng, 48, 64) * np.exp2(8.0 * rng.integers(-1, 2, size=(48, 1)))
+        for w in ("w_gate", "w_up", "w_down"):
+            inp[w] = np.stack([_on_grid_rows(rng, 64, 64, -12, -8).T for _ in range(4)])
+    idx, w = om.route_topk(inp["logits"], cfg.k)
+    return cfg, inp, idx, w
+
+
+def test_mx_forward_quantises_along_the_contraction_axes():
+    # X and the weights lie on the grid of the blocks the mxfp8 forward uses (X rows
+    # along H, weight columns along H or I), so the gate/up GEMM is exact: G and U
+    # equal the exact oracle's.  Quantising along the other axis would change them.
+    cfg, inp, idx, w = _mx_fwd_case(31, grid=True)
+    _, sx = om.layer_forward(inp, cfg.k, 0, cfg.e_local, idx, w)
+    _, sq = mx.layer_forward_mx(inp, cfg.k, 0, cfg.e_local, idx, w)
+    assert np.array_equal(sx["index"]["row_src"], sq["index"]["row_src"])
+    assert np.allclose(sq["G"], sx["G"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(sq["U"], sx["U"], rtol=1e-12, atol=1e-12)
+    assert not np.allclose(mx.qdq_rows(inp["w_gate"][0]), inp["w_gate"][0])   # the wrong axis is lossy
+    assert not np.allclose(mx.qdq_cols_grouped(inp["x"], np.array([0, 48])), inp["x"])
+    # W_down is exact too, so only A's row-wise quantisation (along I) remains in Yp
+    wf = w.reshape(-1)
+    ri = sx["index"]["row_src"]
+    off = sx["index"]["offsets"]
+    for e in range(cfg.e_local):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        ref = wf[ri[lo:hi]][:, None] * (mx.qdq_rows(sx["A"][lo:hi]) @ inp["w_down"][e])
+        assert np.allclose(sq["Yp"][lo:hi], ref, rtol=1e-12, atol=1e-12)
+        exact = sx["Yp"][lo:hi]
+        rowrel = lambda a: np.max(np.linalg.norm(a - ref, axis=1) / np.linalg.norm(ref, axis=1))
+        assert rowrel(exact) > 1e-3                                                    # A's quantisation is seen
+        wrong = wf[ri[lo:hi]][:, None] * (mx.qdq_cols_grouped(sx["A"][lo:hi], np.array([0, hi - lo]))
+                                          @ inp["w_down"][e])
+        assert rowrel(wrong) > 1e-1                                                    # and its axis matters
+
+
+def test_mx_forward_is_close_to_exact_forward():
+    # Gaussian data: each E4M3 quantisation adds a relative error of a few percent at
+    # most (3 mantissa bits), and the results stay within that of the exact forward.
+    cfg, inp, idx, w = _mx_fwd_case(32, grid=False)
+    Y, sx = om.layer_forward(inp, cfg.k, 0, cfg.e_local, idx, w)
+    Yq, sq = mx.layer_forward_mx(inp, cfg.k, 0, cfg.e_local, idx, w)
+    for a, b in ((Yq, Y), (sq["G"], sx["G"]), (sq["U"], sx["U"]), (sq["A"], sx["A"])):
+        rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+        assert 1e-3 < rel < 8e-2, rel
+    # combine: Y is the sum of each token's weighted rows
+    Ysum = np.zeros_like(Yq)
+    np.add.at(Ysum, sq["index"]["row_src"] // cfg.k, sq["Yp"])
+    assert np.allclose(Ysum, Yq)
+
+
+def test_mx_forward_power_of_two_equivariance():
+    # MX quantisation commutes with scaling by a power of two (the block exponent moves,
+    # the codes stay): 4 W_up and W_down / 2 give exactly 2 Y.
+    cfg, inp, idx, w = _mx_fwd_case(33, grid=False)
+    Y, _ = mx.layer_forward_mx(inp, cfg.k, 0, cfg.e_local, idx, w)
+    inp2 = dict(inp, w_up=inp["w_up"] * 4.0, w_down=inp["w_down"] * 0.5)
+    Y2, _ = mx.layer_forward_mx(inp2, cfg.k, 0, cfg.e_local, idx, w)
+    assert np.array_equal(Y2, 2.0 * Y)
