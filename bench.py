@@ -10,7 +10,8 @@ the R routed rows; tile padding is not counted).
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 [--workload NAME]: the default is the Qwen3-30B-A3B layer; the other names time the
-235B-A22B EP=8 share, the Zipf-skewed routing and the fp8_bwd mode for the design notes.
+235B-A22B EP=8 share, the Zipf-skewed routing, the fp8_bwd mode and the mxfp8 mode
+(MXFP8 forward and backward GEMMs) for the design notes.
 """
 from __future__ import annotations
 
@@ -37,9 +38,11 @@ WORKLOADS = {
                       "top-8, Gaussian router logits, bf16",
     "skew_zipf": "Zipf(1.2)-skewed routing at the 30B shape: T=16384 H=2048 I=768 E=128 top-8, 8 experts empty, bf16",
     "qwen3_235b_ep8_fp8bwd": "fp8_bwd mode at the 235B-A22B EP=8 share: bf16 forward, MXFP8 backward GEMMs",
+    "qwen3_235b_ep8_mxfp8": "mxfp8 mode at the 235B-A22B EP=8 share: MXFP8 forward and backward GEMMs",
+    "qwen3_30b_mxfp8": "mxfp8 mode at the Qwen3-30B-A3B layer: MXFP8 forward and backward GEMMs",
 }
 GEMMS = ("fwd_gateup", "fwd_down", "bwd_dA", "bwd_dWd", "bwd_dX", "bwd_dWgu",
-         "bwd_dA_mx", "bwd_dWd_mx", "bwd_dX_mx", "bwd_dWgu_mx")
+         "fwd_gateup_mx", "fwd_down_mx", "bwd_dA_mx", "bwd_dWd_mx", "bwd_dX_mx", "bwd_dWgu_mx")
 
 
 def kernel_work(name, T, H, I, k, R, El):
@@ -62,7 +65,9 @@ def kernel_work(name, T, H, I, k, R, El):
         "gather": (T * H * b + row_h, 0.0),
         "combine": (row_h + T * H * b, 0.0),
         "unpermute_dx": (row_h + T * H * b, 0.0),
-        # MXFP8 backward: fp8 operands, bf16 side inputs and outputs
+        # MXFP8 GEMMs: fp8 operands, bf16 side inputs and outputs
+        "fwd_gateup_mx": ((row_h + W_gu) / b * q + row_2i + row_i, 4.0 * R * H * I),
+        "fwd_down_mx": ((row_i + W_d) / b * q + row_h, 2.0 * R * H * I),
         "bwd_dA_mx": ((row_h + W_d) / b * q + row_2i + row_i + row_2i, 2.0 * R * H * I),
         "bwd_dWd_mx": ((row_i + row_h) / b * q + W_d, 2.0 * R * H * I),
         "bwd_dX_mx": ((row_2i + W_gu) / b * q + row_h, 4.0 * R * H * I),
@@ -156,6 +161,7 @@ def main():
 
     cfg = wl.CONFIGS[args.workload]
     mx = cfg.bwd == "mxfp8"
+    mxf = cfg.fwd == "mxfp8"
     inp = wl.make_inputs(cfg)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -164,7 +170,8 @@ def main():
     logits = torch.from_numpy(inp["logits"]).to(dev)
     x, wg, wu, wd, dy = t(inp["x"]), t(inp["w_gate"]), t(inp["w_up"]), t(inp["w_down"]), t(inp["dy"])
     layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16,
-                     L.MOE_BWD_MXFP8 if mx else L.MOE_BWD_SAME, cfg.renorm, device=dev)
+                     L.MOE_BWD_MXFP8 if mx else L.MOE_BWD_SAME, cfg.renorm, device=dev,
+                     fwd=L.MOE_FWD_MXFP8 if mxf else L.MOE_FWD_SAME)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -247,9 +254,13 @@ def main():
                      "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)})
 
     flops_step = 18.0 * R * cfg.H * cfg.I
-    fwd_names = ("route_topk", "index_hist", "index_scan", "index_rank", "tile_table", "fwd_gateup", "fwd_down",
-                 "combine")
-    fwd_ms = sum(v["ms"] * v["launches_per_step"] for n, v in kernels.items() if n in fwd_names)
+    fwd_names = ("route_topk", "index_hist", "index_place", "tile_table", "fwd_gateup", "fwd_down", "combine",
+                 "fwd_gateup_mx", "fwd_down_mx", "mx_goff", "mx_qt_wgate", "mx_qt_wup", "mx_qt_wdown", "mx_q_x",
+                 "mx_q_a")
+    # the forward's share: one of the two tile-table builds and the y combine (the other
+    # combine is the backward's dx)
+    fwd_ms = sum(v["ms"] * (1 if n in ("tile_table", "combine") else v["launches_per_step"])
+                 for n, v in kernels.items() if n in fwd_names)
     gemm_ms = sum(v["ms"] * v["launches_per_step"] for n, v in gemm.items())
     out = {
         "metric": "MoE layer fwd+bwd ms & TFLOPS at Qwen3-30B-A3B shape, 1 MI355X; % MFMA peak",
@@ -260,7 +271,8 @@ def main():
         "launch": "eager" if graph is None else "hip_graph",
         "eager_ms_per_step": round(eager_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16+mxfp8" if mx else "bf16", "data": "synthetic",
+        "dtype": ("mxfp8" if mxf and mx else "mxfp8+bf16" if mxf else "bf16+mxfp8" if mx else "bf16"),
+        "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "T": cfg.T, "H": cfg.H, "I": cfg.I,
                    "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
         "mfma_frac_step": round(flops_step / ms / 1e9 / BF16_PEAK_TFLOPS, 4),

@@ -51,6 +51,8 @@ struct Layout {
   // MXFP8 backward buffers (scratch), 0 when unused
   int64_t Rp;
   size_t off_mx[17];
+  // MXFP8 forward buffers (scratch, after the tile table), 0 when unused
+  size_t off_mxf[10];
 };
 
 int check_shape(const moe_shape* s) {
@@ -74,6 +76,12 @@ int check_shape(const moe_shape* s) {
     return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs bf16 data");
   if (s->bwd == MOE_BWD_MXFP8 && s->H % 128 != 0)
     return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs H a multiple of 128 (H = %d)", s->H);
+  if (s->fwd != MOE_FWD_SAME && s->fwd != MOE_FWD_MXFP8) return fail(MOE_EINVAL, "fwd = %d", s->fwd);
+  if (s->fwd == MOE_FWD_MXFP8) {  // e_local * H <= 2^30 by the limits above: int column strides
+    if (s->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the MXFP8 forward needs bf16 data");
+    if (s->H % 128 != 0 || s->I % 128 != 0)
+      return fail(MOE_EUNSUPPORTED, "the MXFP8 forward needs H and I multiples of 128 (H = %d, I = %d)", s->H, s->I);
+  }
   return MOE_OK;
 }
 
@@ -116,6 +124,19 @@ void layout(const moe_shape& s, Layout& L) {
     bwd_bytes = off;
   }
   L.scratch_bytes = bwd_bytes > dispatch_bytes ? bwd_bytes : dispatch_bytes;
+  for (int i = 0; i < 10; ++i) L.off_mxf[i] = 0;
+  if (s.fwd == MOE_FWD_MXFP8) {
+    const size_t H = (size_t)s.H, I = (size_t)s.I, Eh = (size_t)El * s.H, Ei = (size_t)El * s.I;
+    // codes then scales of: Xp rows, A rows, [W_gate | W_up]^T, W_down^T; the group offsets
+    const size_t sizes[10] = {R * H, R * H / 32, R * I, R * I / 32, 2 * I * Eh, 2 * I * Eh / 32, H * Ei, H * Ei / 32,
+                              (size_t)(El + 1) * 4, (size_t)(El + 1) * 4};
+    size_t off = L.off_dgu;  // the tile table and the zeroed area stay in front
+    for (int i = 0; i < 10; ++i) {
+      L.off_mxf[i] = off;
+      off += align_up(sizes[i]);
+    }
+    if (off > L.scratch_bytes) L.scratch_bytes = off;
+  }
 }
 
 template <typename T>
@@ -279,7 +300,17 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
     a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up; a.wd = (const bf16_t*)w_down;
     a.tiles = tiles; a.max_tiles = L.max_tiles;
     a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a); a.yp = (bf16_t*)yp;
-    e = launch_fwd_bf16(a, st);
+    if (s.fwd == MOE_FWD_MXFP8) {
+      MxFwdArgs m{};
+      uint8_t** bufs[8] = {&m.q_x, &m.s_x, &m.q_a, &m.s_a, &m.qt_wgu, &m.st_wgu, &m.qt_wd, &m.st_wd};
+      for (int i = 0; i < 8; ++i) *bufs[i] = at<uint8_t>(scratch, L.off_mxf[i]);
+      m.goff_h = at<int32_t>(scratch, L.off_mxf[8]);
+      m.goff_i = at<int32_t>(scratch, L.off_mxf[9]);
+      m.R_cap = L.R_cap;
+      e = launch_fwd_mx(a, m, st);
+    } else {
+      e = launch_fwd_bf16(a, st);
+    }
   } else {
     FwdArgsF32 a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;

@@ -52,6 +52,27 @@ template <> struct elem<bf16_t> {
 __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
+// MX scale exponent of a 32-element block with absolute maximum amax (E4M3 elements,
+// e8m0 scale 2^X): the smallest X with amax <= 448 * 2^X, clamped to [-127, 127]; 0 for
+// an all-zero block.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  const float m = frexpf(amax, &e);    // amax = m * 2^e, m in [0.5, 1)
+  // amax in [2^(e-1), 2^e): X = e - 9, plus one if amax > 1.75 * 2^(e-1) = 448 * 2^(e-9)
+  int X = e - 9 + (m > 0.875f ? 1 : 0);
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// E4M3 codes of x0..x3 * 2^-X packed little-endian (|x * 2^-X| <= 448 by the scale
+// rule).  The scaling by a power of two is exact; gfx950's v_cvt_pk_fp8_f32 converts to
+// the OCP E4M3 format rounding to nearest, ties to even (the default mode), with the
+// sign of the input, also for results that round to zero.
+__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3, int X) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x0, -X), ldexpf(x1, -X), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x2, -X), ldexpf(x3, -X), lo, true);
+}
+
 // Host-side: the launch configuration constants shared by the host code and kernels.
 constexpr int kGemmBM = 128;     // rows of one row-group GEMM tile (bf16 path)
 constexpr int kZeroBytes = 512;  // zeroed scratch area read in place of rows past a group's end
@@ -184,6 +205,23 @@ hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int
                           uint8_t* sr = nullptr);
 hipError_t launch_poff(const int32_t* offsets, int El, int32_t* poff, hipStream_t st);
 hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
+// out[e] = e * step for e = 0..n (the group offsets of n equal weight matrices)
+hipError_t launch_mx_iota(int32_t* out, int n, int step, hipStream_t st);
+
+// MXFP8 forward operands (scratch).  The weights are quantised column-wise into the
+// transposed layout of launch_mx_cols with one group per expert: column n of expert e's
+// matrix at codes[n * Rp + e * K .. + K - 1] (K = H for W_gate / W_up, I for W_down,
+// both multiples of 128, so the groups need no padding and Rp = El * K).
+struct MxFwdArgs {
+  uint8_t* q_x; uint8_t* s_x;        // row-wise Xp along H               [R_cap, H]
+  uint8_t* q_a; uint8_t* s_a;        // row-wise A along I                [R_cap, I]
+  uint8_t* qt_wgu; uint8_t* st_wgu;  // column-wise [W_gate | W_up] along H, transposed [2I, El*H]
+  uint8_t* qt_wd; uint8_t* st_wd;    // column-wise W_down along I, transposed          [H, El*I]
+  int32_t* goff_h;                   // [El + 1]: e * H
+  int32_t* goff_i;                   // [El + 1]: e * I
+  int64_t R_cap;
+};
+hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st);
 
 // fp32 (SIMT) grouped GEMMs: the same chain in fp32 arithmetic
 struct FwdArgsF32 {

@@ -87,213 +87,7 @@ __device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_
   p.nk = nk;
 }
 
-// ---------------- K1: gate/up + SwiGLU ----------------
-// B tile: gate columns 0..BN/2-1 and up columns BN/2..BN-1; compute wave wn takes the same
-// WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
-// and U of one element share a lane.
-struct LGateUp : RowLd {
-  KRows a;
-  const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
-  size_t bstep;           // elements per K step of the weights (64 rows)
-  using Slot = RowSlot;
-  __device__ __forceinline__ void load(int kt, Slot& s) const {
-    a.load(kt, s.a);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
-  }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
-    a.put(s.a, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
-  }
-};
-
-struct JGateUp {
-  using Tile = RowTileInfo;
-  using Ld = LGateUp;
-  static constexpr bool A_KMAJ = true, B_KMAJ = false;
-  static constexpr bool DYN = false, REG = true;
-  __device__ __forceinline__ bool serpentine() const { return false; }
-  __device__ __forceinline__ static int ncol(int wn, int ni) {
-    return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
-  }
-  FwdArgs a;
-  int NT;
-  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
-  __device__ __forceinline__ void tile(int v, Tile& p) const {
-    row_tile_info(a.tiles, a.offsets, v, NT, a.H / BK, BN / 2, p);
-  }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int, Acc& acc, int lane, int wm, int wn) const {
-    mma_stage<JGateUp>(st, acc, lane, wm, wn);
-  }
-  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
-    RowTile t;
-    row_tile(a.tiles, a.offsets, v, NT, t);
-    const int n0 = t.nt * (BN / 2);
-    p.pw = pw;
-    p.nk = a.H / BK;
-    a_rows_kmaj(p.a, a.xp, a.x, a.row_src, a.k, a.H, t, pw, lane);
-    const bf16_t* wg = a.wg + (size_t)t.e * a.H * a.I;
-    const bf16_t* wu = a.wu + (size_t)t.e * a.H * a.I;
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) {
-      int r, c;
-      mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
-      constexpr int HC = BN / 16;    // chunks per half: HC..2 HC - 1 are W_up's
-      int col = n0 + (c % HC) * 8;   // intermediate column
-      if (col >= a.I) col = n0;      // tail columns: any valid address, results are discarded
-      p.b[q] = (c < HC ? wg : wu) + col + (size_t)r * a.I;
-    }
-    p.bstep = (size_t)BK * a.I;
-  }
-  // lane takes 8 intermediate columns of one row, G from the gate blocks and U from the
-  // up blocks (same columns), and writes 16-byte chunks of G, U and A
-  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
-    constexpr int LPR = WCOLS / 16;          // lanes per row
-    constexpr int PASSES = EP_ROWS * LPR / 64;  // passes over a staged 16-row piece
-    float* wsm = stage + wv * EP_ROWS * EP_LD;
-    const uint32_t I2 = 2u * (uint32_t)a.I;
-    // the tile's first row (uniform); lanes add 32-bit offsets
-    bf16_t* const gub = a.gu + (size_t)p.t.rs * I2;
-    bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        stage_quarter(wsm, acc, mi, h, lane);
-#pragma unroll
-        for (int j = 0; j < PASSES; ++j) {
-          const int rr = lane / LPR + (64 / LPR) * j, cc = (lane % LPR) * 8;
-          const int rt = wm * WROWS + mi * 32 + h * 16 + rr;
-          float g[8], u[8], av[8];
-          read8(wsm + rr * EP_LD + cc, g);
-          read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
-          if (j == PASSES - 1) staging_done();
-          const int col = p.n0 + wn * (WCOLS / 2) + cc;
-          if (rt < p.t.cnt && col < a.I) {
-            const uint32_t o = (uint32_t)rt * I2 + (uint32_t)col;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
-            *reinterpret_cast<i32x4*>(gub + o) = pack8(g);
-            *reinterpret_cast<i32x4*>(gub + o + a.I) = pack8(u);
-            *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = pack8(av);
-          }
-        }
-      }
-  }
-};
-
-__global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  JGateUp job{a, (int)ceil_div(a.I, BN / 2)};
-  run_stream(job, lds);
-}
-
-// ---------------- K2: down projection * routing weight ----------------
-// K-major A rows, MN-major B (row-major weights [K, N])
-struct LMnB : RowLd {
-  KRows a;
-  const bf16_t* b[B_LP];
-  size_t bstep;
-  using Slot = RowSlot;
-  __device__ __forceinline__ void load(int kt, Slot& s) const {
-    a.load(kt, s.a);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
-  }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
-    a.put(s.a, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
-  }
-};
-
-struct JDown {
-  using Tile = RowTileInfo;
-  using Ld = LMnB;
-  static constexpr bool A_KMAJ = true, B_KMAJ = false;
-  static constexpr bool DYN = false, REG = true;
-  __device__ __forceinline__ bool serpentine() const { return false; }
-  __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
-  FwdArgs a;
-  int NT;
-  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
-  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, a.I / BK, BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int, Acc& acc, int lane, int wm, int wn) const {
-    mma_stage<JDown>(st, acc, lane, wm, wn);
-  }
-  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
-    RowTile t;
-    row_tile(a.tiles, a.offsets, v, NT, t);
-    const int n0 = t.nt * BN;
-    p.pw = pw;
-    p.nk = a.I / BK;
-    a_rows_kmaj(p.a, a.a, nullptr, nullptr, 1, a.I, t, pw, lane);
-    const bf16_t* wd = a.wd + (size_t)t.e * a.I * a.H;
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) {
-      int r, c;
-      mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
-      int col = n0 + c * 8;
-      if (col >= a.H) col = n0;  // tail columns: any valid address, results are discarded
-      p.b[q] = wd + (size_t)r * a.H + col;
-    }
-    p.bstep = (size_t)BK * a.H;
-  }
-  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
-    // the routing weights of the lane's rows, fetched before the staging starts
-    const int lane = threadIdx.x & 63, wm = (int)((unsigned)(threadIdx.x >> 6) % WM);
-    float wr[EP_LANE_ROWS];
-#pragma unroll
-    for (int i = 0; i < EP_LANE_ROWS; ++i) {
-      const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
-      wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
-    }
-    bf16_t* const yb = a.yp + (size_t)p.t.rs * a.H;  // the tile's first row
-    epilogue_rows<true>(stage, acc, [&](int rt, int ct, const float (&v)[8], int slot) {
-      const int col = p.n0 + ct;
-      if (rt < p.t.cnt && col < a.H) {
-        const float w = wr[slot];
-        float o[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = w * v[q];
-        *reinterpret_cast<i32x4*>(yb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = pack8(o);
-      }
-    });
-  }
-};
-
-__global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
-  JDown job{a, (int)ceil_div(a.H, BN)};
-  run_stream(job, lds);
-}
-
-// ---------------- B1 / B3: both operands K-major ----------------
-struct LKK : RowLd {
-  KRows a;
-  const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
-  const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
-  int ksplit;              // B3: I / 64; B1: larger than any step count
-  using Slot = RowSlot;
-  __device__ __forceinline__ void load(int kt, Slot& s) const {
-    a.load(kt, s.a);
-    const bool second = kt >= ksplit;
-    const int k0 = (second ? kt - ksplit : kt) * BK;
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16((second ? b2[q] : b[q]) + k0);
-  }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
-    a.put(s.a, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
-  }
-};
-
-// ---------------- MXFP8 operands (backward GEMMs in fp8_bwd mode) ----------------
+// ---------------- MXFP8 operands (mxfp8 forward, fp8_bwd / mxfp8 backward) ----------------
 // Both operands K-major E4M3 codes [rows][K] with e8m0 scales [rows][K/32].  One K step
 // is 128 codes: the same 128 bytes per row as a bf16 step of 64, so the LDS ring,
 // slots and swizzle are shared.  For v_mfma_scale_f32_32x32x64_f8f6f4 lane l of row
@@ -318,8 +112,8 @@ __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int
   return out;
 }
 
-__device__ __forceinline__ int mx_ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
-
+// The scaled MFMAs of one stage for a job J: B rows J::ncol(wn, ni) as in mma_stage.
+template <class J>
 __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, Acc& acc, int lane,
                                            int wm, int wn) {
 #pragma unroll
@@ -334,7 +128,7 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int r = mx_ncol(wn, ni) + (lane & 31);
+      const int r = J::ncol(wn, ni) + (lane & 31);
       bf[ni] = frag_fp8(st + A_ELEMS, r, kk, lane);
       sb[ni] = sc[(BM + r) * 4 + kk * 2 + (lane >> 5)];
     }
@@ -428,6 +222,274 @@ struct LMx {
   }
 };
 
+// ---------------- K1: gate/up + SwiGLU ----------------
+// B tile: gate columns 0..BN/2-1 and up columns BN/2..BN-1; compute wave wn takes the same
+// WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
+// and U of one element share a lane.
+struct LGateUp : RowLd {
+  KRows a;
+  const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
+  size_t bstep;           // elements per K step of the weights (64 rows)
+  using Slot = RowSlot;
+  __device__ __forceinline__ void load(int kt, Slot& s) const {
+    a.load(kt, s.a);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
+  }
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
+    a.put(s.a, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
+  }
+};
+
+// MX: Xp rows (row-wise codes along H) against the transposed column-wise codes of
+// [W_gate | W_up] (rows n < I gate, I + n up; expert e's K range starts at e * H).
+template <bool MX>
+struct JGateUp {
+  using Tile = RowTileInfo;
+  using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
+  static constexpr bool A_KMAJ = true, B_KMAJ = MX;
+  static constexpr bool DYN = false, REG = true;
+  __device__ __forceinline__ bool serpentine() const { return false; }
+  __device__ __forceinline__ static int ncol(int wn, int ni) {
+    return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
+  }
+  FwdArgs a;
+  MxFwdArgs m;
+  int NT;
+  uint8_t* scring;
+  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
+  __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const {
+    row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN / 2, p);
+  }
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm, int wn) const {
+    if constexpr (MX) mx_compute<JGateUp>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    else mma_stage<JGateUp>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
+    RowTile t;
+    row_tile(a.tiles, a.offsets, v, NT, t);
+    const int n0 = t.nt * (BN / 2);
+    p.pw = pw;
+    p.nk = nk();
+    if constexpr (MX) {
+      const size_t ldw = (size_t)a.El * a.H;  // codes per transposed weight column
+      const size_t eoff = (size_t)t.e * a.H;
+      // B tile row r: gate column n0 + r for r < BN / 2, else up column n0 + r - BN / 2;
+      // tail columns read any valid column (their results are discarded)
+      p.setup(m.q_x, m.s_x, a.H, [&](int r) { return t.rs + min(r, t.cnt - 1); }, m.qt_wgu + eoff,
+              m.st_wgu + eoff / 32, (int)ldw,
+              [&](int r) { return (r < BN / 2 ? 0 : a.I) + min(n0 + r % (BN / 2), a.I - 1); }, 0, scring, lane);
+    } else {
+      setup_bf16(t, n0, p, pw, lane);
+    }
+  }
+  __device__ __forceinline__ void setup_bf16(const RowTile& t, int n0, LGateUp& p, int pw, int lane) const {
+    a_rows_kmaj(p.a, a.xp, a.x, a.row_src, a.k, a.H, t, pw, lane);
+    const bf16_t* wg = a.wg + (size_t)t.e * a.H * a.I;
+    const bf16_t* wu = a.wu + (size_t)t.e * a.H * a.I;
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) {
+      int r, c;
+      mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
+      constexpr int HC = BN / 16;    // chunks per half: HC..2 HC - 1 are W_up's
+      int col = n0 + (c % HC) * 8;   // intermediate column
+      if (col >= a.I) col = n0;      // tail columns: any valid address, results are discarded
+      p.b[q] = (c < HC ? wg : wu) + col + (size_t)r * a.I;
+    }
+    p.bstep = (size_t)BK * a.I;
+  }
+  // lane takes 8 intermediate columns of one row, G from the gate blocks and U from the
+  // up blocks (same columns), and writes 16-byte chunks of G, U and A
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+    constexpr int LPR = WCOLS / 16;          // lanes per row
+    constexpr int PASSES = EP_ROWS * LPR / 64;  // passes over a staged 16-row piece
+    static_assert(!MX || LPR * 8 == 32, "the lanes of a row span one MX block of A");
+    float* wsm = stage + wv * EP_ROWS * EP_LD;
+    const uint32_t I2 = 2u * (uint32_t)a.I;
+    // the tile's first row (uniform); lanes add 32-bit offsets
+    bf16_t* const gub = a.gu + (size_t)p.t.rs * I2;
+    bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        stage_quarter(wsm, acc, mi, h, lane);
+#pragma unroll
+        for (int j = 0; j < PASSES; ++j) {
+          const int rr = lane / LPR + (64 / LPR) * j, cc = (lane % LPR) * 8;
+          const int rt = wm * WROWS + mi * 32 + h * 16 + rr;
+          float g[8], u[8], av[8];
+          read8(wsm + rr * EP_LD + cc, g);
+          read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
+          if (j == PASSES - 1) staging_done();
+          const int col = p.n0 + wn * (WCOLS / 2) + cc;
+          if constexpr (MX) {
+            // the down GEMM's row-wise codes of A, quantised here from the fp32 values: the
+            // LPR lanes of a row hold one 32-column block (all of it inside or outside I)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
+            float am = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(av[q]));
+#pragma unroll
+            for (int off = 1; off < LPR; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+            const int X = mx_scale_exp(am);
+            if (rt < p.t.cnt && col < a.I) {
+              const size_t r = (size_t)(p.t.rs + rt);
+              *reinterpret_cast<uint2*>(m.q_a + r * a.I + col) =
+                  make_uint2(e4m3_pack4(av[0], av[1], av[2], av[3], X), e4m3_pack4(av[4], av[5], av[6], av[7], X));
+              if (lane % LPR == 0) m.s_a[r * (a.I / 32) + col / 32] = (uint8_t)(X + 127);
+            }
+          }
+          if (rt < p.t.cnt && col < a.I) {
+            const uint32_t o = (uint32_t)rt * I2 + (uint32_t)col;
+            if constexpr (!MX) {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
+            }
+            *reinterpret_cast<i32x4*>(gub + o) = pack8(g);
+            *reinterpret_cast<i32x4*>(gub + o + a.I) = pack8(u);
+            *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = pack8(av);
+          }
+        }
+      }
+  }
+};
+
+template <bool MX>
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a, MxFwdArgs m) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
+  JGateUp<MX> job{a, m, (int)ceil_div(a.I, BN / 2), scring};
+  run_stream(job, lds);
+}
+
+// ---------------- K2: down projection * routing weight ----------------
+// K-major A rows, MN-major B (row-major weights [K, N])
+struct LMnB : RowLd {
+  KRows a;
+  const bf16_t* b[B_LP];
+  size_t bstep;
+  using Slot = RowSlot;
+  __device__ __forceinline__ void load(int kt, Slot& s) const {
+    a.load(kt, s.a);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
+  }
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
+    a.put(s.a, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
+  }
+};
+
+// MX: A rows (row-wise codes along I) against the transposed column-wise codes of
+// W_down (row n = hidden column n; expert e's K range starts at e * I).
+template <bool MX>
+struct JDown {
+  using Tile = RowTileInfo;
+  using Ld = typename std::conditional<MX, LMx, LMnB>::type;
+  static constexpr bool A_KMAJ = true, B_KMAJ = MX;
+  static constexpr bool DYN = false, REG = true;
+  __device__ __forceinline__ bool serpentine() const { return false; }
+  __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
+  FwdArgs a;
+  MxFwdArgs m;
+  int NT;
+  uint8_t* scring;
+  __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
+  __device__ __forceinline__ int nk() const { return MX ? a.I / MX_STEP : a.I / BK; }
+  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
+  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm, int wn) const {
+    if constexpr (MX) mx_compute<JDown>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    else mma_stage<JDown>(st, acc, lane, wm, wn);
+  }
+  __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
+    RowTile t;
+    row_tile(a.tiles, a.offsets, v, NT, t);
+    const int n0 = t.nt * BN;
+    p.pw = pw;
+    p.nk = nk();
+    if constexpr (MX) {
+      const size_t ldw = (size_t)a.El * a.I;
+      const size_t eoff = (size_t)t.e * a.I;
+      p.setup(m.q_a, m.s_a, a.I, [&](int r) { return t.rs + min(r, t.cnt - 1); }, m.qt_wd + eoff, m.st_wd + eoff / 32,
+              (int)ldw, [&](int r) { return min(n0 + r, a.H - 1); }, 0, scring, lane);
+    } else {
+      setup_bf16(t, n0, p, pw, lane);
+    }
+  }
+  __device__ __forceinline__ void setup_bf16(const RowTile& t, int n0, LMnB& p, int pw, int lane) const {
+    a_rows_kmaj(p.a, a.a, nullptr, nullptr, 1, a.I, t, pw, lane);
+    const bf16_t* wd = a.wd + (size_t)t.e * a.I * a.H;
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) {
+      int r, c;
+      mnmaj_slot<BN>(load_slot(q, pw, lane), r, c);
+      int col = n0 + c * 8;
+      if (col >= a.H) col = n0;  // tail columns: any valid address, results are discarded
+      p.b[q] = wd + (size_t)r * a.H + col;
+    }
+    p.bstep = (size_t)BK * a.H;
+  }
+  __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
+    // the routing weights of the lane's rows, fetched before the staging starts
+    const int lane = threadIdx.x & 63, wm = (int)((unsigned)(threadIdx.x >> 6) % WM);
+    float wr[EP_LANE_ROWS];
+#pragma unroll
+    for (int i = 0; i < EP_LANE_ROWS; ++i) {
+      const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
+      wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
+    }
+    bf16_t* const yb = a.yp + (size_t)p.t.rs * a.H;  // the tile's first row
+    epilogue_rows<true>(stage, acc, [&](int rt, int ct, const float (&v)[8], int slot) {
+      const int col = p.n0 + ct;
+      if (rt < p.t.cnt && col < a.H) {
+        const float w = wr[slot];
+        float o[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = w * v[q];
+        *reinterpret_cast<i32x4*>(yb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = pack8(o);
+      }
+    });
+  }
+};
+
+template <bool MX>
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a, MxFwdArgs m) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
+  JDown<MX> job{a, m, (int)ceil_div(a.H, BN), scring};
+  run_stream(job, lds);
+}
+
+// ---------------- B1 / B3: both operands K-major ----------------
+struct LKK : RowLd {
+  KRows a;
+  const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
+  const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
+  int ksplit;              // B3: I / 64; B1: larger than any step count
+  using Slot = RowSlot;
+  __device__ __forceinline__ void load(int kt, Slot& s) const {
+    a.load(kt, s.a);
+    const bool second = kt >= ksplit;
+    const int k0 = (second ? kt - ksplit : kt) * BK;
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16((second ? b2[q] : b[q]) + k0);
+  }
+  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
+    a.put(s.a, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
+  }
+};
+
 template <bool MX>
 using KKLd = typename std::conditional<MX, LMx, LKK>::type;
 
@@ -453,7 +515,7 @@ struct JDa {
   __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
                                           int wn) const {
-    if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    if constexpr (MX) mx_compute<JDa>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
     else mma_stage<JDa>(st, acc, lane, wm, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
@@ -567,7 +629,7 @@ struct JDx {
   __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
                                           int wn) const {
-    if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    if constexpr (MX) mx_compute<JDx>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
     else mma_stage<JDx>(st, acc, lane, wm, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
@@ -713,7 +775,7 @@ struct JWgrad {
   __device__ __forceinline__ bool active(const Tile&, int) const { return true; }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
                                           int wn) const {
-    if constexpr (MX) mx_compute(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
+    if constexpr (MX) mx_compute<JWgrad>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
     else mma_stage<JWgrad>(st, acc, lane, wm, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
@@ -814,9 +876,41 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int 
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
-  MOE_LAUNCH("fwd_gateup", k_fwd_gateup, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))), dim3(NTHR), 0, st,
-             a);
-  MOE_LAUNCH("fwd_down", k_fwd_down, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0, st, a);
+  MxFwdArgs m{};
+  MOE_LAUNCH("fwd_gateup", k_fwd_gateup<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))),
+             dim3(NTHR), 0, st, a, m);
+  MOE_LAUNCH("fwd_down", k_fwd_down<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0,
+             st, a, m);
+  return hipGetLastError();
+}
+
+// MXFP8 forward.  Order: quantise W_gate, W_up and W_down column-wise (one group per
+// expert) and the Xp rows row-wise; K1 on fp8 operands writes G|U and A (bf16) and the
+// row-wise codes of A (from its fp32 values); K2 on fp8 operands.
+hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
+  if (a.max_tiles == 0) return hipSuccess;
+  hipError_t e;
+  const int El = a.El, H = a.H, I = a.I;
+  const int RpH = El * H, RpI = El * I;
+#define MOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+  MOE_TRY(launch_mx_iota(m.goff_h, El, H, st));
+  MOE_TRY(launch_mx_iota(m.goff_i, El, I, st));
+  MOE_TRY(launch_mx_cols(a.wg, I, nullptr, 1, nullptr, m.goff_h, m.goff_h, El, I, RpH, m.qt_wgu, m.st_wgu,
+                         "mx_qt_wgate", st));
+  MOE_TRY(launch_mx_cols(a.wu, I, nullptr, 1, nullptr, m.goff_h, m.goff_h, El, I, RpH, m.qt_wgu + (size_t)I * RpH,
+                         m.st_wgu + (size_t)I * (RpH / 32), "mx_qt_wup", st));
+  MOE_TRY(launch_mx_cols(a.wd, H, nullptr, 1, nullptr, m.goff_i, m.goff_i, El, H, RpI, m.qt_wd, m.st_wd,
+                         "mx_qt_wdown", st));
+  if (a.xp)
+    MOE_TRY(launch_mx_rows(a.xp, nullptr, H, nullptr, 1, a.offsets, El, -1, m.R_cap, H, m.q_x, m.s_x, "mx_q_x", st));
+  else
+    MOE_TRY(launch_mx_rows(a.x, nullptr, H, a.row_src, a.k, a.offsets, El, -1, m.R_cap, H, m.q_x, m.s_x, "mx_q_x",
+                           st));
+  MOE_LAUNCH("fwd_gateup_mx", k_fwd_gateup<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(I, BN / 2))),
+             dim3(NTHR), 0, st, a, m);
+#undef MOE_TRY
+  MOE_LAUNCH("fwd_down_mx", k_fwd_down<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(H, BN))), dim3(NTHR), 0,
+             st, a, m);
   return hipGetLastError();
 }
 

@@ -16,24 +16,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-  if (!(amax > 0.f)) return 0;
-  int e;
-  const float m = frexpf(amax, &e);    // amax = m * 2^e, m in [0.5, 1)
-  // amax in [2^(e-1), 2^e): X = e - 9, plus one if amax > 1.75 * 2^(e-1) = 448 * 2^(e-9)
-  int X = e - 9 + (m > 0.875f ? 1 : 0);
-  return X < -127 ? -127 : (X > 127 ? 127 : X);
-}
-
-// E4M3 codes of x0..x3 * 2^-X packed little-endian (|x * 2^-X| <= 448 by the scale
-// rule).  The scaling by a power of two is exact; gfx950's v_cvt_pk_fp8_f32 converts to
-// the OCP E4M3 format rounding to nearest, ties to even (the default mode), with the
-// sign of the input, also for results that round to zero.
-__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3, int X) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x0, -X), ldexpf(x1, -X), 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x2, -X), ldexpf(x3, -X), lo, true);
-}
-
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
@@ -228,7 +210,17 @@ __global__ __launch_bounds__(1024) void k_poff(const int32_t* __restrict__ offse
   if (e == 0) poff[0] = 0;
 }
 
+__global__ __launch_bounds__(256) void k_iota(int32_t* __restrict__ out, int n, int step) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e <= n) out[e] = e * step;
+}
+
 }  // namespace
+
+hipError_t launch_mx_iota(int32_t* out, int n, int step, hipStream_t st) {
+  MOE_LAUNCH("mx_goff", k_iota, dim3((unsigned)ceil_div(n + 1, 256)), dim3(256), 0, st, out, n, step);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const int32_t* row_src, int k,
                           const int32_t* offsets, int El, int64_t rows, int64_t rows_bound, int K, uint8_t* q,

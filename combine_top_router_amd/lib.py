@@ -8,7 +8,7 @@ import os
 
 __all__ = [
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
-    "MOE_F32", "MOE_BF16", "MOE_BWD_SAME", "MOE_BWD_MXFP8",
+    "MOE_F32", "MOE_BF16", "MOE_BWD_SAME", "MOE_BWD_MXFP8", "MOE_FWD_SAME", "MOE_FWD_MXFP8",
     "MoeShape", "MoeError", "load", "lib_path", "EXPORTS",
     "moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_topk",
     "moe_dispatch", "moe_fwd", "moe_combine", "moe_bwd", "moe_route_topk_bwd",
@@ -18,6 +18,7 @@ __all__ = [
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_BWD_SAME, MOE_BWD_MXFP8 = 0, 1
+MOE_FWD_SAME, MOE_FWD_MXFP8 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -28,7 +29,7 @@ def lib_path() -> str:
 
 class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "H", "I", "E", "k", "e_begin", "e_local", "dtype", "bwd", "renorm")]
+                ("T", "H", "I", "E", "k", "e_begin", "e_local", "dtype", "bwd", "renorm", "fwd")]
 
     def __repr__(self):
         return "MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"

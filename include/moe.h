@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -60,6 +60,7 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_BWD_SAME = 0, MOE_BWD_MXFP8 = 1 } moe_bwd_prec;
+typedef enum { MOE_FWD_SAME = 0, MOE_FWD_MXFP8 = 1 } moe_fwd_prec;
 
 typedef struct {
   int32_t T;        /* tokens, >= 0 */
@@ -72,7 +73,10 @@ typedef struct {
   int32_t dtype;    /* moe_dtype */
   int32_t bwd;      /* moe_bwd_prec: MOE_BWD_MXFP8 needs MOE_BF16 */
   int32_t renorm;   /* 1: weights = softmax over the k selected logits; 0: softmax over all E */
+  int32_t fwd;      /* moe_fwd_prec: MOE_FWD_MXFP8 needs MOE_BF16 (added in ABI version 2) */
 } moe_shape;
+/* The pages' precision modes map onto (fwd, bwd): bf16 = (SAME, SAME) with MOE_BF16,
+ * fp8_bwd = (SAME, MXFP8), mxfp8 = (MXFP8, MXFP8). */
 
 /* MOE_ABI_VERSION of the built library. */
 int moe_abi_version(void);
@@ -112,7 +116,15 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
  *   g = x[t] W_gate[e], u = x[t] W_up[e], a = silu(g) * u,
  *   yp[r] = topk_w[t, j] * (a W_down[e])          ([R_cap, H])
  * g, u and a are kept in `saved` for moe_bwd.  xp may be NULL (rows read from x
- * through row_src) or the buffer filled by moe_dispatch.  Needs saved and scratch. */
+ * through row_src) or the buffer filled by moe_dispatch.  Needs saved and scratch.
+ * shape.fwd == MOE_FWD_MXFP8 (the pages' mxfp8 mode) runs both GEMMs on MXFP8 operands
+ * quantised in the call, blocks of 32 along each GEMM's contraction axis, with the
+ * scale and rounding rule of moe_mx_quantize: the rows of x along H and each column of
+ * W_gate[e], W_up[e] in blocks of 32 consecutive h; then the rows of a along I
+ * (quantised from its fp32 value, before the rounding of the saved bf16 a) and each
+ * column of W_down[e] in blocks of 32 consecutive i.  g, u and a are still the bf16-rounded GEMM results, and the routing
+ * weight still applies after the down GEMM.  Needs H and I multiples of 128
+ * (MOE_EUNSUPPORTED otherwise). */
 int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t* offsets,
             const int32_t* row_src, const float* topk_w, const void* w_gate, const void* w_up,
             const void* w_down, void* yp, void* saved, void* scratch, void* stream);

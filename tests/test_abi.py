@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(L.lib_path())
     for n in _declared():
         assert hasattr(raw, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def _shape(L, **kw):
@@ -50,6 +50,8 @@ BAD = [
     (dict(H=100), -1), (dict(I=96), -1), (dict(dtype=0, H=130), -1),
     (dict(H=(1 << 20) + 64), -1), (dict(I=(1 << 20) + 64), -1),
     (dict(dtype=0, bwd=1), -2),
+    # MXFP8 forward: an unknown value, fp32 data, H or I not a multiple of 128
+    (dict(fwd=2), -1), (dict(dtype=0, fwd=1), -2), (dict(fwd=1), -2), (dict(fwd=1, I=128, H=192), -2),
 ]
 
 

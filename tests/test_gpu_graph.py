@@ -18,6 +18,7 @@ CASES = {
     "tiny_bf16": wl.CONFIGS["tiny_bf16"],
     "ragged_bf16_share": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
     "ragged_mx": wl.MoeConfig("ragged_mx", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
+    "ragged_mxfp8": wl.MoeConfig("ragged_mxfp8", 700, 256, 256, 6, 2, 0, 6, 8, bwd="mxfp8", fwd="mxfp8"),
     "tiny_f32": wl.CONFIGS["tiny_f32"],
 }
 
@@ -39,7 +40,8 @@ def test_graph_replays_match_eager(name):
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local,
                      L.MOE_F32 if cfg.dtype == "f32" else L.MOE_BF16,
-                     L.MOE_BWD_MXFP8 if cfg.bwd == "mxfp8" else L.MOE_BWD_SAME, cfg.renorm)
+                     L.MOE_BWD_MXFP8 if cfg.bwd == "mxfp8" else L.MOE_BWD_SAME, cfg.renorm,
+                     fwd=L.MOE_FWD_MXFP8 if cfg.fwd == "mxfp8" else L.MOE_FWD_SAME)
     logits = torch.from_numpy(np.ascontiguousarray(inp["logits"])).cuda()
     x, wg, wu, wd, dy = (to_dev(inp[k], dt) for k in ("x", "w_gate", "w_up", "w_down", "dy"))
 

@@ -1,4 +1,5 @@
-"""Parity of the MXFP8 backward (fp8_bwd mode) with the oracle.
+"""Parity of the MXFP8 backward (fp8_bwd mode) and of the MXFP8 forward and backward
+(mxfp8 mode) with the oracle.
 
 The row-wise and the group-aware column-wise quantisers are compared code for code
 with the oracle's MX rule (integer work: bit-exact).  The layer: routing, index and the bf16 forward as in the bf16 runs
@@ -6,7 +7,15 @@ with the oracle's MX rule (integer work: bit-exact).  The layer: routing, index 
 error of 4e-2 of the oracle's MXFP8 backward, which quantises the same operands by
 the same rule in fp64.  Against the unquantised fp64 backward the error is the
 quantisation's own (E4M3 keeps 3 mantissa bits; dx passes two quantised GEMMs, about
-5%): checked only against the looser bound PLAIN_TOL, to catch gross mistakes."""
+5%): checked only against the looser bound PLAIN_TOL, to catch gross mistakes.
+
+mxfp8 mode: y within 1e-2 of the oracle's MXFP8 forward.  Both sides quantise the
+same operands by the same rule (A from its unrounded value), so what differs is the
+fp32 accumulation and the bf16 rounding of Yp and y, as in the bf16 runs.  Were A
+quantised after its bf16 rounding instead, a code would move by one E4M3 step wherever
+that rounding crosses an E4M3 rounding boundary (about one element in 2^5) and y would
+differ by about 1.6e-2.  The gradients: 4e-2 of the oracle's MXFP8 backward run on the
+oracle's MXFP8 forward."""
 import numpy as np
 import pytest
 
@@ -243,7 +252,7 @@ def test_mx_full_size_parity_sampled():
         assert err < MX_TOL, (key, err)
 
 
-def _expert_subset(cfg, idx, w, inp, experts):
+def _expert_subset(cfg, idx, w, inp, experts, fwd_mx=False):
     """The oracle's MXFP8 backward of the layer restricted to the given local experts
     (renumbered 0..n-1; slots routed elsewhere dropped).  Their row groups, and so their
     column-wise blocks, are unchanged, and the row-wise blocks are per row, so their
@@ -261,6 +270,88 @@ def _expert_subset(cfg, idx, w, inp, experts):
         loc[k_] = inp[k_][np.asarray(experts)]
     idx_s, w_s = mapped[tok], np.where(keep[tok], w[tok], 0.0)
     n = len(experts)
-    Y, saved = om.layer_forward(loc, cfg.k, 0, n, idx_s, w_s)
+    fwd = omx.layer_forward_mx if fwd_mx else om.layer_forward
+    Y, saved = fwd(loc, cfg.k, 0, n, idx_s, w_s)
     gmx = omx.layer_backward_mx(loc, cfg.k, 0, n, idx_s, w_s, saved)
+    gmx["y"] = Y
     return gmx, tok, whole
+
+
+# ---------------- mxfp8 mode: MXFP8 forward and backward ----------------
+def _oracle_mxf(cfg, inp):
+    idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
+    Yq, saved_q = omx.layer_forward_mx(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w)
+    gmx = omx.layer_backward_mx(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w, saved_q)
+    Y, saved = om.layer_forward(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w)
+    g = om.layer_backward(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w, saved)
+    return idx, w, Yq, Y, saved["index"], gmx, g
+
+
+SMALL_MXF = {
+    "tiny_mxf": wl.MoeConfig("tiny_mxf", 64, 128, 128, 8, 2, 0, 8, 0, bwd="mxfp8", fwd="mxfp8"),
+    # several 128-row tiles and ragged tails, I = 384 (three gate/up column tiles), H = 384
+    # (a 128-column tail in the down GEMM)
+    "ragged_mxf": wl.MoeConfig("ragged_mxf", 700, 384, 384, 6, 2, 0, 6, 12, bwd="mxfp8", fwd="mxfp8"),
+    "share_mxf": wl.MoeConfig("share_mxf", 500, 256, 256, 10, 3, 4, 5, 13, bwd="mxfp8", fwd="mxfp8"),
+    "skew_mxf": wl.MoeConfig("skew_mxf", 1024, 512, 384, 64, 4, 0, 64, 14, routing="zipf", bwd="mxfp8",
+                             fwd="mxfp8"),
+    # MXFP8 forward with the bf16 backward
+    "fwd_only_mxf": wl.MoeConfig("fwd_only_mxf", 300, 256, 128, 5, 2, 0, 5, 15, fwd="mxfp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_MXF))
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused_gather", "xp"])
+def test_mxfp8_layer_parity(name, fuse):
+    cfg = SMALL_MXF[name]
+    print(f"[mxfp8-parity] {name} fuse={fuse}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp, fuse_gather=fuse)
+    idx, w, Yq, Y, ix, gmx, g = _oracle_mxf(cfg, inp)
+    assert np.array_equal(out["topk_idx"], idx)
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    assert rel(out["topk_w"], w) < W_TOL
+    e_q, e_plain = rel(out["y"], Yq), rel(out["y"], Y)
+    print(f"  y: vs mx oracle {e_q:.3e}, vs unquantised {e_plain:.3e}", flush=True)
+    assert e_q < BF16_TOL, e_q
+    assert e_plain < PLAIN_TOL, e_plain
+    if cfg.bwd != "mxfp8":
+        return
+    for key in GRADS:
+        e_mx, e_pl = rel(out[key], gmx[key]), rel(out[key], g[key])
+        print(f"  {key}: vs mx oracle {e_mx:.3e}, vs unquantised {e_pl:.3e}", flush=True)
+        assert e_mx < MX_TOL, (key, e_mx)
+        assert e_pl < PLAIN_TOL, (key, e_pl)
+
+
+def test_mxfp8_full_size_parity_sampled():
+    """235B-A22B EP=8 share in mxfp8 mode: y, dx and d_topk_w of sampled tokens and the
+    weight gradients of sampled experts against the oracle's MXFP8 forward and backward
+    restricted to those experts (the row-wise blocks are per row and the weights' and
+    the gradients' column-wise blocks per expert, so the restriction changes nothing)."""
+    cfg = wl.CONFIGS["qwen3_235b_ep8_mxfp8"]
+    print(f"[mxfp8-parity-full] {cfg.name}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp)
+    idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
+    assert np.array_equal(out["topk_idx"], idx)
+    ix = om.build_index(idx, cfg.e_begin, cfg.e_local)
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    rng = np.random.default_rng(322)
+    experts = np.sort(rng.choice(cfg.e_local, size=3, replace=False))
+    sub, tok, whole = _expert_subset(cfg, idx, w, inp, experts, fwd_mx=True)
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        for j, e in enumerate(experts):
+            err = rel(out[key][e], sub[key][j])
+            print(f"  {key}[{e}]: {err:.3e}", flush=True)
+            assert err < MX_TOL, (key, e, err)
+    assert whole.sum() > 100
+    err = rel(out["y"][tok[whole]], sub["y"][whole])
+    print(f"  y ({int(whole.sum())} tokens): {err:.3e}", flush=True)
+    assert err < BF16_TOL, err
+    for key in ("dx", "d_topk_w"):
+        err = rel(out[key][tok[whole]], sub[key][whole])
+        print(f"  {key} ({int(whole.sum())} tokens): {err:.3e}", flush=True)
+        assert err < MX_TOL, (key, err)

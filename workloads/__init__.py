@@ -38,6 +38,7 @@ class MoeConfig:
     seed: int
     dtype: str = "bf16"      # "bf16" or "f32": x, weights, dY
     bwd: str = "bf16"        # "bf16" or "mxfp8" backward GEMMs
+    fwd: str = "bf16"        # "bf16" or "mxfp8" forward GEMMs
     routing: str = "gauss"   # "gauss": N(0,1) logits; "zipf": biased Gumbel logits
     renorm: int = 1          # 1: softmax over the k selected logits; 0: over all E
 
@@ -62,6 +63,10 @@ CONFIGS = {
     # the 235B share with an MXFP8 backward
     "qwen3_235b_ep8_fp8bwd": MoeConfig("qwen3_235b_ep8_fp8bwd", 16384, 4096, 1536, 128, 8, 0, 16, 2,
                                        bwd="mxfp8"),
+    # the pages' mxfp8 mode (MXFP8 forward and backward GEMMs) at both layer shapes
+    "qwen3_235b_ep8_mxfp8": MoeConfig("qwen3_235b_ep8_mxfp8", 16384, 4096, 1536, 128, 8, 0, 16, 2,
+                                      bwd="mxfp8", fwd="mxfp8"),
+    "qwen3_30b_mxfp8": MoeConfig("qwen3_30b_mxfp8", 4096, 2048, 768, 128, 8, 0, 128, 1, bwd="mxfp8", fwd="mxfp8"),
 }
 
 
