@@ -46,6 +46,10 @@ struct Layout {
   int nchunks;
   // saved
   size_t off_gu, off_a, saved_bytes;
+  // mxfp8 mode (MXFP8 forward and backward): the backward's row-wise weight codes, written
+  // by the forward's weight passes into saved (codes, scales of W_down, [W_gate | W_up])
+  bool wrows_saved;
+  size_t off_wrows[4];
   // scratch
   size_t off_tiles, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
   // MXFP8 backward buffers (scratch), 0 when unused
@@ -96,6 +100,16 @@ void layout(const moe_shape& s, Layout& L) {
   L.off_gu = 0;
   L.off_a = align_up(R * 2 * s.I * L.es);
   L.saved_bytes = L.off_a + align_up(R * s.I * L.es);
+  L.wrows_saved = s.fwd == MOE_FWD_MXFP8 && s.bwd == MOE_BWD_MXFP8;
+  for (int i = 0; i < 4; ++i) L.off_wrows[i] = 0;
+  if (L.wrows_saved) {
+    const size_t Eh = (size_t)El * s.H, Ei = (size_t)El * s.I;
+    const size_t sizes[4] = {Ei * s.H, Ei * s.H / 32, Eh * 2 * s.I, Eh * 2 * s.I / 32};
+    for (int i = 0; i < 4; ++i) {
+      L.off_wrows[i] = L.saved_bytes;
+      L.saved_bytes += align_up(sizes[i]);
+    }
+  }
   const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
   L.off_tiles = 0;
   L.off_zeros = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
@@ -113,9 +127,11 @@ void layout(const moe_shape& s, Layout& L) {
     const size_t Rp = (size_t)L.Rp;
     // codes then scales of: dY' rows, W_down rows, dG|dU rows, [W_gate|W_up] rows,
     // A^T, (w dY')^T, Xp^T, (dG|dU)^T; then the padded offsets
-    const size_t sizes[17] = {R * H, R * H / 32, Ei * H, Ei * H / 32, R * 2 * I, R * 2 * I / 32, Eh * 2 * I,
-                              Eh * 2 * I / 32, I * Rp, I * Rp / 32, H * Rp, H * Rp / 32, H * Rp, H * Rp / 32,
-                              2 * I * Rp, 2 * I * Rp / 32, (size_t)(El + 1) * 4};
+    // (the weights' row-wise codes live in saved in mxfp8 mode)
+    const size_t wsz = L.wrows_saved ? 0 : 1;
+    const size_t sizes[17] = {R * H, R * H / 32, wsz * Ei * H, wsz * Ei * H / 32, R * 2 * I, R * 2 * I / 32,
+                              wsz * Eh * 2 * I, wsz * Eh * 2 * I / 32, I * Rp, I * Rp / 32, H * Rp, H * Rp / 32,
+                              H * Rp, H * Rp / 32, 2 * I * Rp, 2 * I * Rp / 32, (size_t)(El + 1) * 4};
     size_t off = bwd_bytes;
     for (int i = 0; i < 17; ++i) {
       L.off_mx[i] = off;
@@ -307,6 +323,12 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
       m.goff_h = at<int32_t>(scratch, L.off_mxf[8]);
       m.goff_i = at<int32_t>(scratch, L.off_mxf[9]);
       m.R_cap = L.R_cap;
+      if (L.wrows_saved) {
+        m.q_wd_rows = at<uint8_t>(saved, L.off_wrows[0]);
+        m.s_wd_rows = at<uint8_t>(saved, L.off_wrows[1]);
+        m.q_wgu_rows = at<uint8_t>(saved, L.off_wrows[2]);
+        m.s_wgu_rows = at<uint8_t>(saved, L.off_wrows[3]);
+      }
       e = launch_fwd_mx(a, m, st);
     } else {
       e = launch_fwd_bf16(a, st);
@@ -386,6 +408,14 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
       m.poff = at<int32_t>(scratch, L.off_mx[16]);
       m.Rp = (int)L.Rp;
       m.R_cap = L.R_cap;
+      m.w_ready = L.wrows_saved;
+      if (L.wrows_saved) {  // written by moe_fwd's weight passes
+        uint8_t* saved_w = const_cast<uint8_t*>(at<uint8_t>(saved, 0));
+        m.q_wd = saved_w + L.off_wrows[0];
+        m.s_wd = saved_w + L.off_wrows[1];
+        m.q_wg = saved_w + L.off_wrows[2];
+        m.s_wg = saved_w + L.off_wrows[3];
+      }
       e = launch_bwd_mx(a, m, st);
     } else {
       e = launch_bwd_bf16(a, st);

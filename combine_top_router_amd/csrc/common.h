@@ -186,6 +186,7 @@ struct MxArgs {
   int32_t* poff;                     // [El + 1] padded row offsets
   int Rp;                            // padded row capacity (multiple of kMxRowPad)
   int64_t R_cap;                     // row capacity of the row-wise activation buffers
+  bool w_ready;                      // q_wd / q_wg already hold the weights' codes (mxfp8 forward)
 };
 inline int64_t mx_rp_cap(int64_t R_cap, int El) { return ceil_div(R_cap + (int64_t)(kMxRowPad - 1) * El, kMxRowPad) * kMxRowPad; }
 
@@ -198,11 +199,12 @@ hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const i
                           uint8_t* s, const char* name, hipStream_t st);
 // column-wise, group-aware quantization into the padded transposed layout; optional row
 // gather (row_src / k) and per-row scaling by topk_w[row_src[r]]; with qr, also the
-// row-wise quantization of the same (gathered, unscaled) rows into qr [rows, N], sr
+// row-wise quantization of the same (gathered, unscaled) rows into qr [rows, ldr], sr
+// [rows, ldr / 32] (ldr <= 0: ldr = N)
 hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int k, const float* topk_w,
                           const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
                           uint8_t* stt, const char* name, hipStream_t st, uint8_t* qr = nullptr,
-                          uint8_t* sr = nullptr);
+                          uint8_t* sr = nullptr, int ldr = 0);
 hipError_t launch_poff(const int32_t* offsets, int El, int32_t* poff, hipStream_t st);
 hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
 // out[e] = e * step for e = 0..n (the group offsets of n equal weight matrices)
@@ -220,6 +222,10 @@ struct MxFwdArgs {
   int32_t* goff_h;                   // [El + 1]: e * H
   int32_t* goff_i;                   // [El + 1]: e * I
   int64_t R_cap;
+  // optional (an MXFP8 backward follows): the same passes also write the backward's
+  // row-wise weight codes, W_down along H [El*I, H] and [W_gate | W_up] along I [El*H, 2I]
+  uint8_t* q_wd_rows; uint8_t* s_wd_rows;
+  uint8_t* q_wgu_rows; uint8_t* s_wgu_rows;
 };
 hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st);
 

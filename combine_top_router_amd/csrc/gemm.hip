@@ -895,12 +895,15 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
 #define MOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
   MOE_TRY(launch_mx_iota(m.goff_h, El, H, st));
   MOE_TRY(launch_mx_iota(m.goff_i, El, I, st));
+  // with q_wgu_rows, gate and up codes sit side by side in rows of 2I codes
+  const bool rows = m.q_wgu_rows != nullptr;
   MOE_TRY(launch_mx_cols(a.wg, I, nullptr, 1, nullptr, m.goff_h, m.goff_h, El, I, RpH, m.qt_wgu, m.st_wgu,
-                         "mx_qt_wgate", st));
+                         "mx_qt_wgate", st, m.q_wgu_rows, m.s_wgu_rows, 2 * I));
   MOE_TRY(launch_mx_cols(a.wu, I, nullptr, 1, nullptr, m.goff_h, m.goff_h, El, I, RpH, m.qt_wgu + (size_t)I * RpH,
-                         m.st_wgu + (size_t)I * (RpH / 32), "mx_qt_wup", st));
+                         m.st_wgu + (size_t)I * (RpH / 32), "mx_qt_wup", st, rows ? m.q_wgu_rows + I : nullptr,
+                         rows ? m.s_wgu_rows + I / 32 : nullptr, 2 * I));
   MOE_TRY(launch_mx_cols(a.wd, H, nullptr, 1, nullptr, m.goff_i, m.goff_i, El, H, RpI, m.qt_wd, m.st_wd,
-                         "mx_qt_wdown", st));
+                         "mx_qt_wdown", st, m.q_wd_rows, m.s_wd_rows, H));
   if (a.xp)
     MOE_TRY(launch_mx_rows(a.xp, nullptr, H, nullptr, 1, a.offsets, El, -1, m.R_cap, H, m.q_x, m.s_x, "mx_q_x", st));
   else
@@ -945,7 +948,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// MXFP8 backward.  Order: quantise the weights row-wise, and dY' row-wise together with
+// MXFP8 backward.  Order: quantise the weights row-wise (unless the MXFP8 forward left
+// their codes in the saved buffer), and dY' row-wise together with
 // w * dY' column-wise per expert; B1 (fp8) writes dG|dU (bf16); quantise dG|dU row-wise
 // and column-wise in one pass, A and Xp column-wise; then B2, B3, B4 on fp8 operands.
 hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
@@ -954,10 +958,12 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
 #define MOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
   MOE_TRY(launch_poff(a.offsets, El, m.poff, st));
   const int64_t WdRows = (int64_t)El * I, WgRows = (int64_t)El * H;
-  MOE_TRY(launch_mx_rows(a.wd, nullptr, H, nullptr, 1, a.offsets, El, WdRows, WdRows, H, m.q_wd, m.s_wd,
-                         "mx_q_wdown", st));
-  MOE_TRY(launch_mx_rows(a.wg, a.wu, I, nullptr, 1, a.offsets, El, WgRows, WgRows, 2 * I, m.q_wg, m.s_wg,
-                         "mx_q_wgateup", st));
+  if (!m.w_ready) {
+    MOE_TRY(launch_mx_rows(a.wd, nullptr, H, nullptr, 1, a.offsets, El, WdRows, WdRows, H, m.q_wd, m.s_wd,
+                           "mx_q_wdown", st));
+    MOE_TRY(launch_mx_rows(a.wg, a.wu, I, nullptr, 1, a.offsets, El, WgRows, WgRows, 2 * I, m.q_wg, m.s_wg,
+                           "mx_q_wgateup", st));
+  }
   // dY' rows: row-wise for B1 and, from the same read, column-wise w * dY' for B2
   MOE_TRY(launch_mx_cols(a.dy, H, a.row_src, a.k, a.topk_w, a.offsets, m.poff, El, H, m.Rp, m.qt_dy, m.st_dy,
                          "mx_q_dy", st, m.q_dy, m.s_dy));

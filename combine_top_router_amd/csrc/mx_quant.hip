@@ -71,9 +71,9 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
 // column t % 128 into registers (applying the optional row weight in fp32), quantizes
 // it into LDS, and the workgroup then writes each column's 128 codes as one 128-byte
 // line and its four scales as one word.  With qr given, the same staged tile also yields
-// the row-wise quantisation of the unweighted values (codes [rows, N] at the source's
-// dispatched row, scales [rows, N / 32]): thread t takes the 32 columns (t % 4) of
-// staged row t / 4, so a matrix that both layouts need is read once.
+// the row-wise quantisation of the unweighted values (codes at qr[r * ldr + n] for the
+// dispatched row r, scales at sr[r * (ldr / 32) + n / 32]): thread t takes the 32
+// columns (t % 4) of staged row t / 4, so a matrix that both layouts need is read once.
 constexpr int COL_ROWS = 128, COL_COLS = 128;
 constexpr int COL_THREADS = 4 * COL_COLS;   // one per (column, 32-row block)
 static_assert(COL_ROWS == kMxRowPad, "a column chunk spans one padding unit");
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(COL_THREADS) void k_mx_cols(const bf16_t* __restric
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ poff, int El, int N, int Rp,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ stt,
-                                                 uint8_t* __restrict__ qr, uint8_t* __restrict__ sr) {
+                                                 uint8_t* __restrict__ qr, uint8_t* __restrict__ sr, int ldr) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[COL_ROWS][COL_COLS];
   __shared__ __attribute__((aligned(16))) uint32_t codes[COL_COLS][COL_ROWS / 4 + 4];
   __shared__ uint32_t scales[COL_COLS];
@@ -172,10 +172,10 @@ __global__ __launch_bounds__(COL_THREADS) void k_mx_cols(const bf16_t* __restric
 #pragma unroll
       for (int j = 0; j < 8; ++j) w[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
       const size_t r = (size_t)(r0 + rr);
-      uint4* dst = reinterpret_cast<uint4*>(qr + r * N + n);
+      uint4* dst = reinterpret_cast<uint4*>(qr + r * ldr + n);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      sr[r * (N / 32) + n / 32] = (uint8_t)(X + 127);
+      sr[r * (ldr / 32) + n / 32] = (uint8_t)(X + 127);
     }
   }
   __syncthreads();
@@ -234,10 +234,10 @@ hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const i
 
 hipError_t launch_mx_cols(const bf16_t* src, int ld, const int32_t* row_src, int k, const float* topk_w,
                           const int32_t* offsets, const int32_t* poff, int El, int N, int Rp, uint8_t* qt,
-                          uint8_t* stt, const char* name, hipStream_t st, uint8_t* qr, uint8_t* sr) {
+                          uint8_t* stt, const char* name, hipStream_t st, uint8_t* qr, uint8_t* sr, int ldr) {
   if (Rp <= 0) return hipSuccess;
   MOE_LAUNCH(name, k_mx_cols, dim3((unsigned)(Rp / COL_ROWS), (unsigned)ceil_div(N, COL_COLS)), dim3(COL_THREADS), 0, st,
-             src, ld, row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt, qr, sr);
+             src, ld, row_src, k, topk_w, offsets, poff, El, N, Rp, qt, stt, qr, sr, ldr > 0 ? ldr : N);
   return hipGetLastError();
 }
 

@@ -85,7 +85,9 @@ int moe_abi_version(void);
 const char* moe_last_error(void);
 
 /* Byte sizes of the two caller-owned workspaces for `shape`:
- *  saved   -- written by moe_fwd, read by moe_bwd (the saved G, U and A rows);
+ *  saved   -- written by moe_fwd, read by moe_bwd (the saved G, U and A rows; in
+ *             mxfp8 mode, fwd and bwd both MOE_*_MXFP8, also the backward's row-wise
+ *             MXFP8 codes of the weights, which the forward's weight passes produce);
  *  scratch -- temporary space of moe_dispatch, moe_fwd and moe_bwd; its contents do
  *             not need to survive between calls.
  * Both pointers must be non-NULL.  Returns MOE_EINVAL for an invalid shape. */
