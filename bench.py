@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of one captured HIP graph per step")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation checkpointing: the forward keeps nothing, the backward recomputes the "
+                         "gate/up GEMM (value still counts the 18RHI of the layer, not the 4RHI recomputed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -171,7 +174,7 @@ def main():
     x, wg, wu, wd, dy = t(inp["x"]), t(inp["w_gate"]), t(inp["w_up"]), t(inp["w_down"]), t(inp["dy"])
     layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16,
                      L.MOE_BWD_MXFP8 if mx else L.MOE_BWD_SAME, cfg.renorm, device=dev,
-                     fwd=L.MOE_FWD_MXFP8 if mxf else L.MOE_FWD_SAME)
+                     fwd=L.MOE_FWD_MXFP8 if mxf else L.MOE_FWD_SAME, recompute=int(args.recompute))
     stream = torch.cuda.current_stream()
 
     def step():
@@ -221,10 +224,15 @@ def main():
     # per-kernel durations from HIP events recorded inside the library on the launch stream
     L.moe_timing_enable(True)
     per = {}
-    for _ in range(max(3, min(args.steps, 10))):
-        step()
-        for name, kms in L.moe_timing_read():
-            per.setdefault(name, []).append(kms)
+    nrep = max(3, min(args.steps, 10))
+    part_ms = {"fwd": 0.0, "bwd": 0.0}
+    for _ in range(nrep):
+        for part, run in (("fwd", lambda: layer.forward(logits, x, wg, wu, wd, stream)),
+                          ("bwd", lambda: layer.backward(dy, stream))):
+            run()
+            for name, kms in L.moe_timing_read():
+                per.setdefault(name, []).append(kms)
+                part_ms[part] += kms / nrep
     L.moe_timing_enable(False)
     kernels = {}
     for name, v in per.items():
@@ -254,13 +262,7 @@ def main():
                      "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)})
 
     flops_step = 18.0 * R * cfg.H * cfg.I
-    fwd_names = ("route_topk", "index_hist", "index_place", "tile_table", "fwd_gateup", "fwd_down", "combine",
-                 "fwd_gateup_mx", "fwd_down_mx", "mx_goff", "mx_qt_wgate", "mx_qt_wup", "mx_qt_wdown", "mx_q_x",
-                 "mx_q_a")
-    # the forward's share: one of the two tile-table builds and the y combine (the other
-    # combine is the backward's dx)
-    fwd_ms = sum(v["ms"] * (1 if n in ("tile_table", "combine") else v["launches_per_step"])
-                 for n, v in kernels.items() if n in fwd_names)
+    fwd_ms, bwd_ms = part_ms["fwd"], part_ms["bwd"]
     gemm_ms = sum(v["ms"] * v["launches_per_step"] for n, v in gemm.items())
     out = {
         "metric": "MoE layer fwd+bwd ms & TFLOPS at Qwen3-30B-A3B shape, 1 MI355X; % MFMA peak",
@@ -273,11 +275,13 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": ("mxfp8" if mxf and mx else "mxfp8+bf16" if mxf else "bf16+mxfp8" if mx else "bf16"),
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "T": cfg.T, "H": cfg.H, "I": cfg.I,
-                   "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
+        "config": {"workload": WORKLOADS[args.workload] + (", activation checkpointing (backward recomputes "
+                                                            "the gate/up GEMM)" if args.recompute else ""),
+                   "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
         "mfma_frac_step": round(flops_step / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "mfma_frac_gemms": round(flops_step / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "fwd_ms_kernels": round(fwd_ms, 4),
+        "bwd_ms_kernels": round(bwd_ms, 4),
         "hbm_frac_combine": round(kernels["combine"]["GB/s"] / HBM_PEAK_GBS, 4) if "combine" in kernels else None,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,

@@ -50,6 +50,8 @@ struct Layout {
   // by the forward's weight passes into saved (codes, scales of W_down, [W_gate | W_up])
   bool wrows_saved;
   size_t off_wrows[4];
+  // recompute: G|U and A in scratch, behind every other scratch buffer
+  size_t off_rgu, off_ra;
   // scratch
   size_t off_tiles, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
   // MXFP8 backward buffers (scratch), 0 when unused
@@ -81,6 +83,8 @@ int check_shape(const moe_shape* s) {
   if (s->bwd == MOE_BWD_MXFP8 && s->H % 128 != 0)
     return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs H a multiple of 128 (H = %d)", s->H);
   if (s->fwd != MOE_FWD_SAME && s->fwd != MOE_FWD_MXFP8) return fail(MOE_EINVAL, "fwd = %d", s->fwd);
+  if (s->recompute != 0 && s->recompute != 1) return fail(MOE_EINVAL, "recompute = %d", s->recompute);
+  if (s->recompute && s->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "recompute needs bf16 data");
   if (s->fwd == MOE_FWD_MXFP8) {  // e_local * H <= 2^30 by the limits above: int column strides
     if (s->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the MXFP8 forward needs bf16 data");
     if (s->H % 128 != 0 || s->I % 128 != 0)
@@ -99,8 +103,8 @@ void layout(const moe_shape& s, Layout& L) {
   const size_t R = (size_t)L.R_cap;
   L.off_gu = 0;
   L.off_a = align_up(R * 2 * s.I * L.es);
-  L.saved_bytes = L.off_a + align_up(R * s.I * L.es);
-  L.wrows_saved = s.fwd == MOE_FWD_MXFP8 && s.bwd == MOE_BWD_MXFP8;
+  L.saved_bytes = s.recompute ? 0 : L.off_a + align_up(R * s.I * L.es);
+  L.wrows_saved = s.fwd == MOE_FWD_MXFP8 && s.bwd == MOE_BWD_MXFP8 && !s.recompute;
   for (int i = 0; i < 4; ++i) L.off_wrows[i] = 0;
   if (L.wrows_saved) {
     const size_t Eh = (size_t)El * s.H, Ei = (size_t)El * s.I;
@@ -152,6 +156,12 @@ void layout(const moe_shape& s, Layout& L) {
       off += align_up(sizes[i]);
     }
     if (off > L.scratch_bytes) L.scratch_bytes = off;
+  }
+  L.off_rgu = L.off_ra = 0;
+  if (s.recompute) {
+    L.off_rgu = L.scratch_bytes;
+    L.off_ra = L.off_rgu + align_up(R * 2 * s.I * L.es);
+    L.scratch_bytes = L.off_ra + align_up(R * s.I * L.es);
   }
 }
 
@@ -295,7 +305,7 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
   REQUIRE(w_gate);
   REQUIRE(w_up);
   REQUIRE(w_down);
-  REQUIRE_WS(saved);
+  if (!s.recompute) REQUIRE_WS(saved);
   REQUIRE_WS(scratch);
   if (s.T == 0) return MOE_OK;
   REQUIRE(row_src);
@@ -316,6 +326,10 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
     a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up; a.wd = (const bf16_t*)w_down;
     a.tiles = tiles; a.max_tiles = L.max_tiles;
     a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a); a.yp = (bf16_t*)yp;
+    if (s.recompute) {  // nothing kept: the down GEMM's A in scratch, no G|U
+      a.gu = nullptr;
+      a.a = at<bf16_t>(scratch, L.off_ra);
+    }
     if (s.fwd == MOE_FWD_MXFP8) {
       MxFwdArgs m{};
       uint8_t** bufs[8] = {&m.q_x, &m.s_x, &m.q_a, &m.s_a, &m.qt_wgu, &m.st_wgu, &m.qt_wd, &m.st_wd};
@@ -369,7 +383,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   REQUIRE(dw_gate);
   REQUIRE(dw_up);
   REQUIRE(dw_down);
-  REQUIRE_WS(saved);
+  if (!s.recompute) REQUIRE_WS(saved);
   REQUIRE_WS(scratch);
   if (s.T > 0) {
     REQUIRE(dy);
@@ -400,6 +414,29 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
     a.order = at<int32_t>(scratch, L.off_order);
     a.dwg = (bf16_t*)dw_gate; a.dwu = (bf16_t*)dw_up; a.dwd = (bf16_t*)dw_down;
+    if (s.recompute) {  // G|U and A again, by the forward's gate/up GEMM, into scratch
+      bf16_t* const rgu = at<bf16_t>(scratch, L.off_rgu);
+      bf16_t* const ra = at<bf16_t>(scratch, L.off_ra);
+      a.gu = rgu;
+      a.a = ra;
+      FwdArgs f{};
+      f.T = s.T; f.H = s.H; f.I = s.I; f.k = s.k; f.El = s.e_local;
+      f.x = a.x; f.xp = a.xp; f.offsets = offsets; f.row_src = row_src; f.topk_w = topk_w;
+      f.wg = a.wg; f.wu = a.wu; f.wd = a.wd; f.tiles = tiles; f.max_tiles = L.max_tiles;
+      f.gu = rgu; f.a = ra; f.yp = nullptr;
+      if (s.fwd == MOE_FWD_MXFP8) {
+        MxFwdArgs m{};
+        uint8_t** bufs[8] = {&m.q_x, &m.s_x, &m.q_a, &m.s_a, &m.qt_wgu, &m.st_wgu, &m.qt_wd, &m.st_wd};
+        for (int i = 0; i < 8; ++i) *bufs[i] = at<uint8_t>(scratch, L.off_mxf[i]);
+        m.goff_h = at<int32_t>(scratch, L.off_mxf[8]);
+        m.goff_i = at<int32_t>(scratch, L.off_mxf[9]);
+        m.R_cap = L.R_cap;
+        e = launch_fwd_mx(f, m, st, true);
+      } else {
+        e = launch_fwd_gateup_bf16(f, st);
+      }
+      if (e != hipSuccess) return hip_status(e, __func__);
+    }
     if (s.bwd == MOE_BWD_MXFP8) {
       MxArgs m{};
       uint8_t** bufs[16] = {&m.q_dy, &m.s_dy, &m.q_wd, &m.s_wd, &m.q_dgu, &m.s_dgu, &m.q_wg, &m.s_wg,

@@ -136,11 +136,12 @@ struct FwdArgs {
   const bf16_t* wd;       // [El, I, H]
   const int32_t* tiles;   // row-group tile table
   int max_tiles;
-  bf16_t* gu;             // [R_cap, 2I]  (g | u)
+  bf16_t* gu;             // [R_cap, 2I]  (g | u), or null: not kept
   bf16_t* a;              // [R_cap, I]
   bf16_t* yp;             // [R_cap, H]
 };
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st);  // K1 only
 
 struct BwdArgs {
   int T, H, I, k, El;
@@ -227,7 +228,8 @@ struct MxFwdArgs {
   uint8_t* q_wd_rows; uint8_t* s_wd_rows;
   uint8_t* q_wgu_rows; uint8_t* s_wgu_rows;
 };
-hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st);
+// k1_only: the gate/up GEMM and what it needs (the backward's recompute)
+hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, bool k1_only = false);
 
 // fp32 (SIMT) grouped GEMMs: the same chain in fp32 arithmetic
 struct FwdArgsF32 {

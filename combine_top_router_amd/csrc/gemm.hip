@@ -311,8 +311,10 @@ struct JGateUp {
     static_assert(!MX || LPR * 8 == 32, "the lanes of a row span one MX block of A");
     float* wsm = stage + wv * EP_ROWS * EP_LD;
     const uint32_t I2 = 2u * (uint32_t)a.I;
-    // the tile's first row (uniform); lanes add 32-bit offsets
-    bf16_t* const gub = a.gu + (size_t)p.t.rs * I2;
+    // the tile's first row (uniform); lanes add 32-bit offsets.  G|U is not kept when the
+    // backward recomputes it.
+    const bool keep_gu = a.gu != nullptr;
+    bf16_t* const gub = keep_gu ? a.gu + (size_t)p.t.rs * I2 : nullptr;
     bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -352,8 +354,10 @@ struct JGateUp {
 #pragma unroll
               for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
             }
-            *reinterpret_cast<i32x4*>(gub + o) = pack8(g);
-            *reinterpret_cast<i32x4*>(gub + o + a.I) = pack8(u);
+            if (keep_gu) {
+              *reinterpret_cast<i32x4*>(gub + o) = pack8(g);
+              *reinterpret_cast<i32x4*>(gub + o + a.I) = pack8(u);
+            }
             *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = pack8(av);
           }
         }
@@ -874,6 +878,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int 
 
 }  // namespace
 
+hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st) {
+  if (a.max_tiles == 0) return hipSuccess;
+  MxFwdArgs m{};
+  MOE_LAUNCH("fwd_gateup", k_fwd_gateup<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))),
+             dim3(NTHR), 0, st, a, m);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
@@ -887,7 +899,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
 // MXFP8 forward.  Order: quantise W_gate, W_up and W_down column-wise (one group per
 // expert) and the Xp rows row-wise; K1 on fp8 operands writes G|U and A (bf16) and the
 // row-wise codes of A (from its fp32 values); K2 on fp8 operands.
-hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
+hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, bool k1_only) {
   if (a.max_tiles == 0) return hipSuccess;
   hipError_t e;
   const int El = a.El, H = a.H, I = a.I;
@@ -902,8 +914,9 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
   MOE_TRY(launch_mx_cols(a.wu, I, nullptr, 1, nullptr, m.goff_h, m.goff_h, El, I, RpH, m.qt_wgu + (size_t)I * RpH,
                          m.st_wgu + (size_t)I * (RpH / 32), "mx_qt_wup", st, rows ? m.q_wgu_rows + I : nullptr,
                          rows ? m.s_wgu_rows + I / 32 : nullptr, 2 * I));
-  MOE_TRY(launch_mx_cols(a.wd, H, nullptr, 1, nullptr, m.goff_i, m.goff_i, El, H, RpI, m.qt_wd, m.st_wd,
-                         "mx_qt_wdown", st, m.q_wd_rows, m.s_wd_rows, H));
+  if (!k1_only)
+    MOE_TRY(launch_mx_cols(a.wd, H, nullptr, 1, nullptr, m.goff_i, m.goff_i, El, H, RpI, m.qt_wd, m.st_wd,
+                           "mx_qt_wdown", st, m.q_wd_rows, m.s_wd_rows, H));
   if (a.xp)
     MOE_TRY(launch_mx_rows(a.xp, nullptr, H, nullptr, 1, a.offsets, El, -1, m.R_cap, H, m.q_x, m.s_x, "mx_q_x", st));
   else
@@ -912,6 +925,7 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
   MOE_LAUNCH("fwd_gateup_mx", k_fwd_gateup<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(I, BN / 2))),
              dim3(NTHR), 0, st, a, m);
 #undef MOE_TRY
+  if (k1_only) return hipGetLastError();
   MOE_LAUNCH("fwd_down_mx", k_fwd_down<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(H, BN))), dim3(NTHR), 0,
              st, a, m);
   return hipGetLastError();

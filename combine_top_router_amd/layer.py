@@ -22,14 +22,15 @@ class MoeLayer:
     """One GPU's share of a dropless MoE layer: experts [e_begin, e_begin + e_local) of E.
 
     ``forward`` runs route -> dispatch -> expert MLP -> combine and ``backward`` runs the
-    expert backward and the router backward.  With ``fuse_gather`` the token rows are
+    expert backward and the router backward.  ``recompute=1`` keeps nothing between the two
+    (activation checkpointing: the backward recomputes the gate/up GEMM).  With ``fuse_gather`` the token rows are
     read from x through row_src inside the GEMMs instead of a gathered copy xp.
     """
 
     def __init__(self, T, H, I, E, k, e_begin=0, e_local=None, dtype=L.MOE_BF16, bwd=L.MOE_BWD_SAME,
-                 renorm=1, device="cuda", fuse_gather=True, fwd=L.MOE_FWD_SAME):
+                 renorm=1, device="cuda", fuse_gather=True, fwd=L.MOE_FWD_SAME, recompute=0):
         e_local = E if e_local is None else e_local
-        self.shape = L.MoeShape(T, H, I, E, k, e_begin, e_local, dtype, bwd, renorm, fwd)
+        self.shape = L.MoeShape(T, H, I, E, k, e_begin, e_local, dtype, bwd, renorm, fwd, recompute)
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -46,7 +47,8 @@ class MoeLayer:
         self.xp = None if fuse_gather else torch.empty(self.R_cap, H, dtype=self.dtype, device=dev)
         self.yp = torch.empty(max(self.R_cap, 1), H, dtype=self.dtype, device=dev)
         self.y = torch.empty(T, H, dtype=self.dtype, device=dev)
-        self.saved = torch.empty(max(saved_b, 256), dtype=torch.uint8, device=dev)
+        # with recompute nothing is kept between forward and backward: no saved buffer at all
+        self.saved = None if recompute else torch.empty(max(saved_b, 256), dtype=torch.uint8, device=dev)
         self.scratch = torch.empty(max(scratch_b, 256), dtype=torch.uint8, device=dev)
         self.dx = torch.empty(T, H, dtype=self.dtype, device=dev)
         self.dw_gate = torch.empty(e_local, H, I, dtype=self.dtype, device=dev)

@@ -29,7 +29,7 @@ def lib_path() -> str:
 
 class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "H", "I", "E", "k", "e_begin", "e_local", "dtype", "bwd", "renorm", "fwd")]
+                ("T", "H", "I", "E", "k", "e_begin", "e_local", "dtype", "bwd", "renorm", "fwd", "recompute")]
 
     def __repr__(self):
         return "MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"

@@ -74,6 +74,7 @@ typedef struct {
   int32_t bwd;      /* moe_bwd_prec: MOE_BWD_MXFP8 needs MOE_BF16 */
   int32_t renorm;   /* 1: weights = softmax over the k selected logits; 0: softmax over all E */
   int32_t fwd;      /* moe_fwd_prec: MOE_FWD_MXFP8 needs MOE_BF16 (added in ABI version 2) */
+  int32_t recompute;/* 1: activation checkpointing, see moe_bwd; needs MOE_BF16 (ABI version 2) */
 } moe_shape;
 /* The pages' precision modes map onto (fwd, bwd): bf16 = (SAME, SAME) with MOE_BF16,
  * fp8_bwd = (SAME, MXFP8), mxfp8 = (MXFP8, MXFP8). */
@@ -90,7 +91,8 @@ const char* moe_last_error(void);
  *             MXFP8 codes of the weights, which the forward's weight passes produce);
  *  scratch -- temporary space of moe_dispatch, moe_fwd and moe_bwd; its contents do
  *             not need to survive between calls.
- * Both pointers must be non-NULL.  Returns MOE_EINVAL for an invalid shape. */
+ * Both pointers must be non-NULL.  Returns MOE_EINVAL for an invalid shape.  With
+ * shape.recompute = 1 saved_bytes is 0: nothing is kept between the two calls. */
 int moe_workspace_bytes(const moe_shape* shape, size_t* saved_bytes, size_t* scratch_bytes);
 
 /* Top-k routing (NVIDIA article: a learned router activates the top-K experts;
@@ -144,7 +146,13 @@ int moe_combine(const moe_shape* shape, const void* yp, const int32_t* row_of, v
  * shape.bwd == MOE_BWD_MXFP8 runs the four backward GEMMs on MXFP8 operands (E4M3
  * values with one e8m0 scale per 32 along each GEMM's contraction axis, column-wise
  * blocks of 32 rows never crossing an expert group).  `saved` must hold what moe_fwd
- * wrote for the same inputs.  Needs scratch. */
+ * wrote for the same inputs.  Needs scratch.
+ * shape.recompute = 1 (activation checkpointing; Prime Mega MoE pages: the layers are
+ * timed with full activation checkpointing, a full layer being two forwards and one
+ * backward): moe_fwd keeps g, u, a only in scratch and moe_bwd recomputes them from the
+ * same inputs with the same gate/up GEMM (in the forward's precision) before the backward
+ * GEMMs, so `saved` may be NULL in both calls and every output is bit-identical to
+ * recompute = 0.  In mxfp8 mode the backward then quantises its weights itself. */
 int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* xp,
             const int32_t* offsets, const int32_t* row_src, const int32_t* row_of,
             const float* topk_w, const void* w_gate, const void* w_up, const void* w_down,

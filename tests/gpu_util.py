@@ -36,7 +36,7 @@ def host(t):
     return t.detach().float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
 
 
-def run_layer(cfg, inp, fuse_gather=True, scale_up=1.0):
+def run_layer(cfg, inp, fuse_gather=True, scale_up=1.0, recompute=0):
     """Forward + backward on the GPU; returns host copies of every output."""
     from combine_top_router_amd.layer import MoeLayer
     import combine_top_router_amd.lib as L
@@ -44,7 +44,9 @@ def run_layer(cfg, inp, fuse_gather=True, scale_up=1.0):
     layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local,
                      L.MOE_F32 if cfg.dtype == "f32" else L.MOE_BF16,
                      L.MOE_BWD_MXFP8 if cfg.bwd == "mxfp8" else L.MOE_BWD_SAME, cfg.renorm,
-                     fuse_gather=fuse_gather, fwd=L.MOE_FWD_MXFP8 if cfg.fwd == "mxfp8" else L.MOE_FWD_SAME)
+                     fuse_gather=fuse_gather, fwd=L.MOE_FWD_MXFP8 if cfg.fwd == "mxfp8" else L.MOE_FWD_SAME,
+                     recompute=recompute)
+    assert (layer.saved is None) == bool(recompute)
     logits = torch.from_numpy(np.ascontiguousarray(inp["logits"])).cuda()
     x = to_dev(inp["x"], dt)
     wg = to_dev(inp["w_gate"], dt)

@@ -52,6 +52,8 @@ BAD = [
     (dict(dtype=0, bwd=1), -2),
     # MXFP8 forward: an unknown value, fp32 data, H or I not a multiple of 128
     (dict(fwd=2), -1), (dict(dtype=0, fwd=1), -2), (dict(fwd=1), -2), (dict(fwd=1, I=128, H=192), -2),
+    # recompute: an unknown value, fp32 data
+    (dict(recompute=2), -1), (dict(dtype=0, recompute=1), -2),
 ]
 
 
@@ -92,6 +94,16 @@ def test_workspace_sizes_grow_with_the_layer():
     # saved holds G|U and A for every possible row
     R = 4096 * 8
     assert big[0] >= R * 3 * 768 * 2
+    # recompute keeps nothing between the calls; the backward's recomputed G|U and A live
+    # in scratch instead
+    ck = L.moe_workspace_bytes(_shape(L, T=4096, H=2048, I=768, E=128, k=8, e_local=128, recompute=1))
+    assert ck[0] == 0 and ck[1] >= big[1] + R * 3 * 768 * 2
+    # mxfp8: saved also holds the backward's row-wise weight codes (with their scales),
+    # unless recompute is on
+    mx = dict(T=4096, H=2048, I=768, E=128, k=8, e_local=128, fwd=1, bwd=1)
+    wcodes = 128 * 3 * 2048 * 768 * (1 + 1 / 32)
+    assert L.moe_workspace_bytes(_shape(L, **mx))[0] >= big[0] + wcodes
+    assert L.moe_workspace_bytes(_shape(L, **mx, recompute=1))[0] == 0
 
 
 def test_quantizer_arguments_are_checked_before_launch():

@@ -1,0 +1,47 @@
+"""Activation checkpointing (recompute = 1): the forward keeps nothing for the backward
+(no saved buffer is allocated or passed) and the backward recomputes G|U and A with the
+forward's own gate/up GEMM.  The kernels are deterministic, so every output must equal
+the outputs of the saved-activation path bit for bit; that path's parity with the
+oracle is tested elsewhere, so this also holds the recompute path to the oracle.  Each
+precision mode (bf16, fp8_bwd, mxfp8), both weight modes, a local share, a skewed layer
+and the full Qwen3-30B-A3B layer."""
+import numpy as np
+import pytest
+
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from gpu_util import inputs, run_layer  # noqa: E402
+
+CASES = {
+    "tiny_bf16": wl.CONFIGS["tiny_bf16"],
+    "ragged_bf16_share": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
+    "skew_bf16": wl.MoeConfig("skew_bf16", 1024, 256, 192, 64, 4, 0, 64, 16, routing="zipf"),
+    "ragged_fp8bwd": wl.MoeConfig("ragged_fp8bwd", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
+    "ragged_mxfp8_share": wl.MoeConfig("ragged_mxfp8_share", 500, 256, 256, 10, 3, 4, 5, 13, bwd="mxfp8",
+                                       fwd="mxfp8"),
+}
+KEYS = ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits", "topk_idx", "row_src")
+
+
+def _check_equal(cfg, fuse):
+    inp = inputs(cfg)
+    ref = run_layer(cfg, inp, fuse_gather=fuse, recompute=0)
+    got = run_layer(cfg, inp, fuse_gather=fuse, recompute=1)
+    for key in KEYS:
+        assert np.array_equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused_gather", "xp"])
+def test_recompute_equals_saved_path(name, fuse):
+    print(f"[recompute] {name} fuse={fuse}", flush=True)
+    _check_equal(CASES[name], fuse)
+
+
+def test_recompute_full_size_30b():
+    cfg = wl.CONFIGS["qwen3_30b"]
+    print(f"[recompute-full] {cfg.name}", flush=True)
+    _check_equal(cfg, True)
