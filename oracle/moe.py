@@ -19,6 +19,10 @@ Readings (the pages name the steps but print no formula):
   with no local slot gets Y = 0 (the partial sum another rank would complete).
 * Backward -- the chain rule of the forward above (dA', d_w, SwiGLU backward, dX,
   dW_gate, dW_up, dW_down) and of the softmax weights (router backward).
+* Router GEMM -- NVIDIA article, "Optimization 2" (fused router kernels assign each
+  token to its experts): the plainest learned router is one linear map without bias,
+  logits = X W_r with W_r [H, E] (every expert, not only the local ones), followed by
+  the routing above.  Its backward: dX gains d_logits W_r^T, dW_r = X^T d_logits.
 
 Everything is evaluated in fp64 from the (bf16- or fp32-valued) inputs, with no
 intermediate rounding.
@@ -29,7 +33,8 @@ import numpy as np
 
 __all__ = [
     "route_topk", "build_index", "silu", "layer_forward", "layer_backward",
-    "router_backward", "brute_force", "token_sample", "expert_sample",
+    "router_backward", "router_logits", "router_gemm_backward", "brute_force", "token_sample",
+    "expert_sample",
 ]
 
 
@@ -186,6 +191,18 @@ def router_backward(logits, topk_idx, topk_w, d_topk_w, renorm: int = 1):
         s = np.sum(w * dw, axis=1, keepdims=True)     # w_j = p[S_j]
         out = p * (gsel - s)
     return out
+
+
+def router_logits(x, w_r):
+    """Router GEMM: logits [T,E] = x [T,H] W_r [H,E] (fp64)."""
+    return _f64(x) @ _f64(w_r)
+
+
+def router_gemm_backward(x, w_r, d_logits):
+    """Backward of the router GEMM: (d loss/d x [T,H], d loss/d W_r [H,E]) for the
+    upstream d_logits [T,E]."""
+    dl = _f64(d_logits)
+    return dl @ _f64(w_r).T, _f64(x).T @ dl
 
 
 def brute_force(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, topk_w):

@@ -133,3 +133,83 @@ def test_round_trip_permute_unpermute_is_multiplicity():
                 back[s // k] += xp[r]
                 n[s // k] += 1
         assert np.array_equal(back, n[:, None] * x)
+
+
+def _router_case(seed=5):
+    """Tiny fp64 layer whose logits come from a router GEMM x W_r (E = 8, k = 2)."""
+    cfg = wl.CONFIGS["tiny_f32"].replace(seed=seed)
+    inp = wl.make_inputs(cfg)
+    inp = {kk: np.asarray(v, dtype=np.float64) for kk, v in inp.items()}
+    rng = np.random.default_rng(seed)
+    w_r = rng.standard_normal((cfg.H, cfg.E)) / np.sqrt(cfg.H)
+    return cfg, inp, w_r
+
+
+def _router_loss(cfg, inp, w_r, x=None):
+    """<dY, Y> with logits = x W_r feeding the routing; x also feeds the experts."""
+    x = inp["x"] if x is None else x
+    lg = om.router_logits(x, w_r)
+    idx, w = om.route_topk(lg, cfg.k, cfg.renorm)
+    Y, _ = om.layer_forward(dict(inp, x=x), cfg.k, cfg.e_begin, cfg.e_local, idx, w)
+    return float(np.sum(inp["dy"] * Y)), lg
+
+
+def _router_grads(cfg, inp, w_r):
+    lg = om.router_logits(inp["x"], w_r)
+    idx, w = om.route_topk(lg, cfg.k, cfg.renorm)
+    Y, saved = om.layer_forward(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w)
+    g = om.layer_backward(inp, cfg.k, cfg.e_begin, cfg.e_local, idx, w, saved)
+    dl = om.router_backward(lg, idx, w, g["d_topk_w"], cfg.renorm)
+    dx_r, dw_r = om.router_gemm_backward(inp["x"], w_r, dl)
+    return lg, dl, g, dx_r, dw_r
+
+
+def _margin(lg, k):
+    s = np.sort(lg, axis=1)[:, ::-1]
+    return float(np.min(s[:, k - 1] - s[:, k]))
+
+
+def test_router_gemm_backward_by_finite_differences():
+    # the whole chain logits = x W_r -> top-k softmax -> layer: central differences of
+    # <dY, Y> on W_r entries, and on x entries where x feeds both the router and the
+    # experts (dX = the experts' dX + d_logits W_r^T)
+    cfg, inp, w_r = _router_case()
+    lg, dl, g, dx_r, dw_r = _router_grads(cfg, inp, w_r)
+    rng = np.random.default_rng(9)
+    h = 1e-6
+    checked = 0
+    for _ in range(12):
+        pos = (int(rng.integers(0, cfg.H)), int(rng.integers(0, cfg.E)))
+        wp = w_r.copy(); wp[pos] += h
+        wm = w_r.copy(); wm[pos] -= h
+        (lp, lgp), (lm, lgm) = _router_loss(cfg, inp, wp), _router_loss(cfg, inp, wm)
+        if min(_margin(lgp, cfg.k), _margin(lgm, cfg.k)) < 1e-4:
+            continue      # the selection would change inside the difference
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - dw_r[pos]) <= 1e-5 * max(1.0, abs(fd)), (pos, fd, dw_r[pos])
+        checked += 1
+    dx = g["dx"] + dx_r
+    for _ in range(12):
+        pos = (int(rng.integers(0, cfg.T)), int(rng.integers(0, cfg.H)))
+        xp = inp["x"].copy(); xp[pos] += h
+        xm = inp["x"].copy(); xm[pos] -= h
+        (lp, lgp), (lm, lgm) = _router_loss(cfg, inp, w_r, xp), _router_loss(cfg, inp, w_r, xm)
+        if min(_margin(lgp, cfg.k), _margin(lgm, cfg.k)) < 1e-4:
+            continue
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - dx[pos]) <= 1e-5 * max(1.0, abs(fd)), (pos, fd, dx[pos])
+        checked += 1
+    assert checked >= 16
+    # the router's own share of dX is not negligible, so a dropped term would show
+    assert np.linalg.norm(dx_r) > 1e-2 * np.linalg.norm(g["dx"])
+
+
+def test_router_gemm_euler_identities():
+    # logits are linear in W_r and in x (for the router path): <dW_r, W_r> = <dx_r, x> =
+    # <d_logits, logits>
+    cfg, inp, w_r = _router_case(6)
+    lg, dl, g, dx_r, dw_r = _router_grads(cfg, inp, w_r)
+    ref = float(np.sum(dl * lg))
+    assert abs(ref) > 1e-3
+    assert abs(float(np.sum(dw_r * w_r)) - ref) <= 1e-10 * max(1.0, abs(ref))
+    assert abs(float(np.sum(dx_r * inp["x"])) - ref) <= 1e-10 * max(1.0, abs(ref))
