@@ -52,6 +52,7 @@ struct Layout {
   size_t off_wrows[4];
   // recompute: G|U and A in scratch, behind every other scratch buffer
   size_t off_rgu, off_ra;
+  size_t off_router_part;
   // scratch
   size_t off_tiles, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
   // MXFP8 backward buffers (scratch), 0 when unused
@@ -157,6 +158,12 @@ void layout(const moe_shape& s, Layout& L) {
     }
     if (off > L.scratch_bytes) L.scratch_bytes = off;
   }
+  // the router GEMM's scratch (a separate call: overlaps everything above): W_r^T, then the
+  // fp32 partial sums of dW_r
+  L.off_router_part = align_up((size_t)s.E * s.H * 2);
+  const size_t router_bytes = L.off_router_part +
+                              align_up((size_t)router_dw_slices(s.T, s.H, s.E) * s.H * s.E * 4);
+  if (router_bytes > L.scratch_bytes) L.scratch_bytes = router_bytes;
   L.off_rgu = L.off_ra = 0;
   if (s.recompute) {
     L.off_rgu = L.scratch_bytes;
@@ -473,6 +480,50 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
   }
   return hip_status(e, __func__);
+}
+
+int moe_router_fwd(const moe_shape* shape, const void* x, const void* w_r, float* logits, int32_t* topk_idx,
+                   float* topk_w, void* scratch, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the router GEMM needs bf16 data");
+  if (s.E % 8 != 0) return fail(MOE_EUNSUPPORTED, "the router GEMM needs E a multiple of 8 (E = %d)", s.E);
+  REQUIRE(w_r);
+  REQUIRE_WS(scratch);
+  if (s.T > 0) {
+    REQUIRE(x);
+    REQUIRE(logits);
+    REQUIRE(topk_idx);
+    REQUIRE(topk_w);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_router_fwd(s, (const bf16_t*)x, (const bf16_t*)w_r, at<bf16_t>(scratch, 0), logits, st);
+  if (e == hipSuccess && s.T > 0) e = launch_route_topk(s, logits, topk_idx, topk_w, st);
+  return hip_status(e, __func__);
+}
+
+int moe_router_bwd(const moe_shape* shape, const void* x, const void* w_r, const float* d_logits,
+                   const void* dx_in, void* dx, void* dw_r, void* scratch, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the router GEMM needs bf16 data");
+  if (s.E % 8 != 0) return fail(MOE_EUNSUPPORTED, "the router GEMM needs E a multiple of 8 (E = %d)", s.E);
+  REQUIRE(w_r);
+  REQUIRE(dw_r);
+  REQUIRE_WS(scratch);
+  if (s.T > 0) {
+    REQUIRE(x);
+    REQUIRE(d_logits);
+    REQUIRE(dx);
+  }
+  Layout L;
+  layout(s, L);
+  return hip_status(launch_router_bwd(s, (const bf16_t*)x, (const bf16_t*)w_r, d_logits, (const bf16_t*)dx_in,
+                                      (bf16_t*)dx, (bf16_t*)dw_r, at<float>(scratch, L.off_router_part),
+                                      (hipStream_t)stream),
+                    __func__);
 }
 
 int moe_mx_quantize(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales, void* stream) {

@@ -120,6 +120,13 @@ hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offse
 hipError_t launch_combine(const moe_shape& s, const void* rows, const int32_t* row_of, void* out,
                           hipStream_t st, const char* name = "combine", const float* part = nullptr,
                           int nparts = 0, float* d_topk_w = nullptr);
+// router GEMM (router_gemm.hip): wt = W_r^T scratch [E, H]; part = fp32 partial dW_r
+// [router_dw_slices(T, H, E), H, E]
+int router_dw_slices(int T, int H, int E);
+hipError_t launch_router_fwd(const moe_shape& s, const bf16_t* x, const bf16_t* w, bf16_t* wt, float* logits,
+                             hipStream_t st);
+hipError_t launch_router_bwd(const moe_shape& s, const bf16_t* x, const bf16_t* w, const float* dl,
+                             const bf16_t* dx_in, bf16_t* dx, bf16_t* dw, float* part, hipStream_t st);
 hipError_t launch_dtopk(const moe_shape& s, const float* dw_part, int nparts, const int32_t* row_of,
                         float* d_topk_w, hipStream_t st);
 

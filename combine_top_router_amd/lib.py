@@ -13,6 +13,7 @@ __all__ = [
     "moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_topk",
     "moe_dispatch", "moe_fwd", "moe_combine", "moe_bwd", "moe_route_topk_bwd",
     "moe_mx_quantize", "moe_mx_quantize_cols", "moe_timing_enable", "moe_timing_read",
+    "moe_router_fwd", "moe_router_bwd",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
@@ -56,6 +57,8 @@ _SIG = {
     "moe_mx_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     "moe_mx_quantize_cols": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P,
                                             _P, _P]),
+    "moe_router_fwd": (ctypes.c_int, [_S] + [_P] * 7),
+    "moe_router_bwd": (ctypes.c_int, [_S] + [_P] * 8),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
@@ -138,6 +141,16 @@ def moe_mx_quantize(x, rows, K, codes, scales, stream=0):
 def moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, row_codes=0, row_scales=0, stream=0):
     _check(load().moe_mx_quantize_cols(x, N, offsets, groups, Rp, poff, codes, scales, row_codes, row_scales,
                                        stream), "moe_mx_quantize_cols")
+
+
+def moe_router_fwd(shape, x, w_r, logits, topk_idx, topk_w, scratch, stream=0):
+    _check(load().moe_router_fwd(ctypes.byref(shape), x, w_r, logits, topk_idx, topk_w, scratch, stream),
+           "moe_router_fwd")
+
+
+def moe_router_bwd(shape, x, w_r, d_logits, dx_in, dx, dw_r, scratch, stream=0):
+    _check(load().moe_router_bwd(ctypes.byref(shape), x, w_r, d_logits, dx_in, dx, dw_r, scratch, stream),
+           "moe_router_bwd")
 
 
 def moe_timing_enable(on: bool = True):

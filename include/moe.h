@@ -168,6 +168,25 @@ int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_
                        const float* topk_w, const float* d_topk_w, float* d_logits,
                        void* stream);
 
+/* Router GEMM with the routing (NVIDIA article, "Optimization 2": fused router kernels
+ * assign each token to its experts before dispatch).  The router is one linear map
+ * without bias over all E experts (not only the local ones):
+ *   logits [T, E] fp32 = x [T, H] w_r [H, E]   (bf16 x and w_r, fp32 accumulation),
+ * then the top-k softmax routing of moe_route_topk on these logits (topk_idx, topk_w).
+ * Needs MOE_BF16, E a multiple of 8 (MOE_EUNSUPPORTED otherwise) and scratch. */
+int moe_router_fwd(const moe_shape* shape, const void* x, const void* w_r, float* logits, int32_t* topk_idx,
+                   float* topk_w, void* scratch, void* stream);
+
+/* Backward of the router GEMM for the upstream d_logits [T, E] fp32 (what
+ * moe_route_topk_bwd writes): dx [T, H] = dx_in + d_logits w_r^T and dw_r [H, E] =
+ * x^T d_logits, both bf16.  dx_in may be NULL (taken as 0) or equal to dx (e.g. the dx
+ * that moe_bwd wrote, so that dx becomes the whole input gradient: x feeds both the
+ * router and the experts).  d_logits enters the bf16 MFMAs rounded to bf16 and the sums
+ * run in fp32; dw_r sums deterministic token slices in a fixed order.  Needs MOE_BF16,
+ * E a multiple of 8 and scratch. */
+int moe_router_bwd(const moe_shape* shape, const void* x, const void* w_r, const float* d_logits,
+                   const void* dx_in, void* dx, void* dw_r, void* scratch, void* stream);
+
 /* MXFP8 quantisation of the backward (NVIDIA article: group-aware MXFP8 quantisation
  * for the MXFP8 grouped GEMMs; Prime Mega MoE pages: fp8_bwd mode), exposed for tests
  * and for callers that keep quantised weights: quantises `rows` rows of K bf16 values

@@ -140,3 +140,28 @@ def test_quotient_by_top_k_through_double_is_exact():
         x = np.unique(np.clip((base[:, None] // k * k + np.arange(-1, k + 1)[None, :]).ravel(), 0, 2**31 - 1))
         q = np.trunc((x.astype(np.float64) + 0.5) * inv).astype(np.int64)
         assert np.array_equal(q, x // k), k
+
+
+def test_router_arguments_are_checked_before_launch():
+    L = _lib()
+    cases = [
+        (dict(dtype=0), L.MOE_EUNSUPPORTED),   # fp32 data
+        (dict(E=12, k=2), L.MOE_EUNSUPPORTED),  # E not a multiple of 8
+    ]
+    for kw, code in cases:
+        for call in (lambda s: L.moe_router_fwd(s, 8, 8, 8, 8, 8, 8),
+                     lambda s: L.moe_router_bwd(s, 8, 8, 8, 0, 8, 8, 8)):
+            with pytest.raises(L.MoeError) as ei:
+                call(_shape(L, **kw))
+            assert ei.value.code == code
+    s = _shape(L)
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_router_fwd(s, 8, 0, 8, 8, 8, 8)       # w_r is NULL
+    assert ei.value.code == L.MOE_EINVAL
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_router_bwd(s, 8, 8, 8, 0, 8, 8, 0)    # scratch is NULL
+    assert ei.value.code == L.MOE_EWORKSPACE
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_router_bwd(s, 8, 8, 0, 0, 8, 8, 8)    # d_logits is NULL
+    assert ei.value.code == L.MOE_EINVAL
+

@@ -10,8 +10,9 @@ table: "1 node, 8xH200, EP=8, 128 experts, top-8, random routing").  Hidden size
 are not on the pages; they come from the public Qwen3 model shapes
 (H=2048/I=768 and H=4096/I=1536).
 
-Streams (numpy PCG64 through ``SeedSequence(seed).spawn(8)``):
-0 logits, 1 x, 2 W_gate, 3 W_up, 4 W_down, 5 dY, 6 skew permutation, 7 Gumbel noise.
+Streams (numpy PCG64 through ``SeedSequence(seed).spawn(9)``; child i does not depend
+on how many are spawned): 0 logits, 1 x, 2 W_gate, 3 W_up, 4 W_down, 5 dY, 6 skew
+permutation, 7 Gumbel noise, 8 router weight W_r (N(0,1)/sqrt(H), [H, E]).
 x and dY are N(0,1); W_gate/W_up are N(0,1)/sqrt(H); W_down is N(0,1)/sqrt(I);
 logits are N(0,1) fp32, or Zipf-biased Gumbel logits for the skewed workload.
 """
@@ -22,7 +23,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["MoeConfig", "CONFIGS", "make_inputs", "bf16_round", "bf16_bits", "bits_to_f32"]
+__all__ = ["MoeConfig", "CONFIGS", "make_inputs", "make_router_weight", "bf16_round", "bf16_bits", "bits_to_f32"]
 
 
 @dataclass(frozen=True)
@@ -130,3 +131,10 @@ def make_inputs(cfg: MoeConfig, with_weights: bool = True, with_dy: bool = True)
     if with_dy:
         out["dy"] = rnd(_normal(rng[5], (cfg.T, cfg.H)))
     return out
+
+
+def make_router_weight(cfg: MoeConfig) -> np.ndarray:
+    """Router weight W_r [H, E] of ``cfg`` (all E experts), rounded like the other inputs."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(cfg.seed).spawn(9)[8]))
+    w = _normal(rng, (cfg.H, cfg.E), 1.0 / np.sqrt(cfg.H))
+    return bf16_round(w) if cfg.dtype == "bf16" else w
