@@ -45,7 +45,7 @@ GEMMS = ("fwd_gateup", "fwd_down", "bwd_dA", "bwd_dWd", "bwd_dX", "bwd_dWgu",
          "fwd_gateup_mx", "fwd_down_mx", "bwd_dA_mx", "bwd_dWd_mx", "bwd_dX_mx", "bwd_dWgu_mx")
 
 
-def kernel_work(name, T, H, I, k, R, El):
+def kernel_work(name, T, H, I, k, R, El, E_all=0):
     """Algorithmic bytes and flops of one launch of a hot-path kernel (bf16 data).
 
     Per routed row and per expert weights, as in the design notes: each kernel's
@@ -63,6 +63,9 @@ def kernel_work(name, T, H, I, k, R, El):
         "bwd_dX": (row_2i + W_gu + row_h, 4.0 * R * H * I),
         "bwd_dWgu": (row_h + row_2i + W_gu, 4.0 * R * H * I),
         "gather": (T * H * b + row_h, 0.0),
+        # router GEMM (E = all experts): x, W_r, fp32 logits / d_logits
+        "router_logits": (T * H * b + H * E_all * b + T * E_all * 4, 2.0 * T * H * E_all),
+        "router_dx": (T * E_all * 4 + H * E_all * b + 2 * T * H * b, 2.0 * T * H * E_all),
         "combine": (row_h + T * H * b, 0.0),
         "unpermute_dx": (row_h + T * H * b, 0.0),
         # MXFP8 GEMMs: fp8 operands, bf16 side inputs and outputs
@@ -149,6 +152,8 @@ def main():
     ap.add_argument("--recompute", action="store_true",
                     help="activation checkpointing: the forward keeps nothing, the backward recomputes the "
                          "gate/up GEMM (value still counts the 18RHI of the layer, not the 4RHI recomputed)")
+    ap.add_argument("--router", action="store_true",
+                    help="logits from the router GEMM x W_r inside the step (and its backward into dx and dW_r)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -160,7 +165,7 @@ def main():
     import torch
     import workloads as wl
     import combine_top_router_amd.lib as L
-    from combine_top_router_amd.layer import MoeLayer
+    from combine_top_router_amd.layer import MoeLayer, stream_handle
 
     cfg = wl.CONFIGS[args.workload]
     mx = cfg.bwd == "mxfp8"
@@ -176,10 +181,34 @@ def main():
                      L.MOE_BWD_MXFP8 if mx else L.MOE_BWD_SAME, cfg.renorm, device=dev,
                      fwd=L.MOE_FWD_MXFP8 if mxf else L.MOE_FWD_SAME, recompute=int(args.recompute))
     stream = torch.cuda.current_stream()
+    if args.router:
+        w_r = t(wl.make_router_weight(cfg))
+        router_logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
+        dw_r = torch.empty(cfg.H, cfg.E, dtype=bf, device=dev)
+        sh, scr = layer.shape, layer.scratch.data_ptr()
+
+    def fwd(st=None):
+        if not args.router:
+            return layer.forward(logits, x, wg, wu, wd, st)
+        h = stream_handle(st)
+        L.moe_router_fwd(sh, x.data_ptr(), w_r.data_ptr(), router_logits.data_ptr(), layer.topk_idx.data_ptr(),
+                         layer.topk_w.data_ptr(), scr, h)
+        layer.inputs = (router_logits, x, wg, wu, wd)
+        layer.dispatch(x, st)
+        layer.experts(x, wg, wu, wd, st)
+        layer.combine(st)
+        return layer.y
+
+    def bwd(st=None):
+        g = layer.backward(dy, st)
+        if args.router:   # x feeds the router too: dx += d_logits W_r^T, and dW_r
+            L.moe_router_bwd(sh, x.data_ptr(), w_r.data_ptr(), layer.d_logits.data_ptr(), layer.dx.data_ptr(),
+                             layer.dx.data_ptr(), dw_r.data_ptr(), scr, stream_handle(st))
+        return g
 
     def step():
-        layer.forward(logits, x, wg, wu, wd, stream)
-        layer.backward(dy, stream)
+        fwd(stream)
+        bwd(stream)
 
     for _ in range(args.warmup):
         step()
@@ -204,14 +233,14 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step_on = lambda: (layer.forward(logits, x, wg, wu, wd), layer.backward(dy))
+            step_on = lambda: (fwd(), bwd())
             step_on()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            layer.forward(logits, x, wg, wu, wd)
-            layer.backward(dy)
+            fwd()
+            bwd()
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -226,18 +255,23 @@ def main():
     per = {}
     nrep = max(3, min(args.steps, 10))
     part_ms = {"fwd": 0.0, "bwd": 0.0}
+    # one untimed step counts the forward's launches; then each step is read once (no host
+    # wait between its forward and backward) and split at that count
+    fwd(stream)
+    n_fwd = len(L.moe_timing_read())
+    bwd(stream)
+    L.moe_timing_read()
     for _ in range(nrep):
-        for part, run in (("fwd", lambda: layer.forward(logits, x, wg, wu, wd, stream)),
-                          ("bwd", lambda: layer.backward(dy, stream))):
-            run()
-            for name, kms in L.moe_timing_read():
-                per.setdefault(name, []).append(kms)
-                part_ms[part] += kms / nrep
+        fwd(stream)
+        bwd(stream)
+        for i, (name, kms) in enumerate(L.moe_timing_read()):
+            per.setdefault(name, []).append(kms)
+            part_ms["fwd" if i < n_fwd else "bwd"] += kms / nrep
     L.moe_timing_enable(False)
     kernels = {}
     for name, v in per.items():
         avg = float(np.mean(v))
-        byts, flops = kernel_work(name, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)
+        byts, flops = kernel_work(name, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local, cfg.E)
         kernels[name] = {"ms": round(avg, 4), "launches_per_step": len(v) // max(1, len(per["route_topk"])),
                          "GB/s": round(byts / avg / 1e6, 1) if byts else None,
                          "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None}
@@ -261,7 +295,7 @@ def main():
                      "mfma_frac": round(flops / avg_ms / 1e9 / mfma_peak, 4),
                      "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)})
 
-    flops_step = 18.0 * R * cfg.H * cfg.I
+    flops_step = 18.0 * R * cfg.H * cfg.I + (6.0 * cfg.T * cfg.H * cfg.E if args.router else 0.0)
     fwd_ms, bwd_ms = part_ms["fwd"], part_ms["bwd"]
     gemm_ms = sum(v["ms"] * v["launches_per_step"] for n, v in gemm.items())
     out = {
@@ -276,7 +310,8 @@ def main():
         "dtype": ("mxfp8" if mxf and mx else "mxfp8+bf16" if mxf else "bf16+mxfp8" if mx else "bf16"),
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (", activation checkpointing (backward recomputes "
-                                                            "the gate/up GEMM)" if args.recompute else ""),
+                                                            "the gate/up GEMM)" if args.recompute else "")
+                   + (", router GEMM x W_r in the step" if args.router else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
         "mfma_frac_step": round(flops_step / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
         "mfma_frac_gemms": round(flops_step / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
