@@ -7,11 +7,13 @@
 // and gives dW_r = x^T d_logits.  The work is small (2 T H E flops, x read once), so the
 // kernels aim at reading x once from HBM with enough waves in flight, not at a deep
 // LDS pipeline:
-//   logits : each workgroup a 32-row x 64-expert tile, 8 waves = 2 column blocks x 4
+//   logits : each workgroup a 32-row x 64-expert tile, 16 waves = 2 column blocks x 8
 //            slices of H, slices summed through LDS; A and B fragments straight from
 //            global memory (x rows and a transposed copy of W_r, both K-contiguous).
-//   dx     : each wave a 32 x 32 block of dX over K = E; d_logits rounded to bf16 as it
-//            is loaded, W_r rows already K-contiguous; adds dx_in in fp32.
+//   dx     : each workgroup a 128-token x 256-column tile (so W_r is read T / 128 times
+//            and d_logits H / 256 times), each wave 32 x 128 of it over K = E, its
+//            d_logits fragments (rounded to bf16 as they are loaded) read once for four
+//            32-column blocks; W_r rows are already K-contiguous; adds dx_in in fp32.
 //   dW_r   : 64 x 64 tiles over a slice of the tokens, x and d_logits staged transposed
 //            in LDS (token-contiguous) for 16-byte fragment reads; the slices' fp32
 //            partial sums reduced in a fixed order by a second kernel (deterministic).
@@ -64,11 +66,12 @@ __global__ __launch_bounds__(256) void k_router_wt(const bf16_t* __restrict__ w,
   }
 }
 
-constexpr int LG_KSPLIT = 4;   // slices of H per logits tile
+constexpr int LG_KSPLIT = 8;   // slices of H per logits tile
 constexpr int LG_COLS = 64;    // experts per logits tile
 
-// logits [T, E] = x [T, H] W_r [H, E]; H % (16 * LG_KSPLIT) == 0
-__global__ __launch_bounds__(512) void k_router_logits(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wt,
+// logits [T, E] = x [T, H] W_r [H, E]; H % 64 == 0 (a slice of H is a multiple of 8 and
+// the loop steps 16 with the last half step masked)
+__global__ __launch_bounds__(1024) void k_router_logits(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wt,
                                                        int T, int H, int E, float* __restrict__ logits) {
   __shared__ f32x16 red[LG_KSPLIT - 1][2][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -81,8 +84,13 @@ __global__ __launch_bounds__(512) void k_router_logits(const bf16_t* __restrict_
   f32x16 acc;
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  const bool k16 = kl % 16 == 0;               // uniform: no masked half step
 #pragma unroll 8
-  for (int k = 0; k < kl; k += 16) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load8(pa + k), load8(pb + k), acc, 0, 0, 0);
+  for (int k = 0; k < kl; k += 16) {
+    const bool in = k16 || k + (lane >> 5) * 8 < kl;   // kl % 8 == 0: a lane's 8 indices all in or all out
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(in ? load8(pa + k) : zero8(), in ? load8(pb + k) : zero8(), acc, 0,
+                                                   0, 0);
+  }
   if (ks > 0) red[ks - 1][cb][lane] = acc;
   __syncthreads();
   if (ks == 0) {
@@ -101,30 +109,60 @@ __global__ __launch_bounds__(512) void k_router_logits(const bf16_t* __restrict_
   }
 }
 
-// dx [T, H] = dx_in + d_logits [T, E] W_r^T; E % 8 == 0.  Each wave a 32 x 32 block.
+constexpr int DX_BLOCKS = 4;                  // 32-column blocks of dX per wave
+constexpr int DX_ROWS = 128;                  // tokens per workgroup: 4 row blocks of waves
+constexpr int DX_COLS = 2 * 32 * DX_BLOCKS;   // columns per workgroup: 2 column halves of waves
+
+// dx [T, H] = dx_in + d_logits [T, E] W_r^T; E % 8 == 0 (E16: E % 16 == 0, no masked
+// half step).  Wave wv: rows 32 (wv % 4), columns 128 (wv / 4) of the workgroup's tile.
+template <bool E16>
 __global__ __launch_bounds__(512) void k_router_dx(const float* __restrict__ dl, const bf16_t* __restrict__ w, int T,
                                                    int H, int E, const bf16_t* dx_in, bf16_t* dx) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * 32, c0 = blockIdx.y * 256 + wv * 32;
-  if (c0 >= H) return;
-  const int row = min(r0 + (lane & 31), T - 1), col = min(c0 + (lane & 31), H - 1);
+  const int r0 = blockIdx.x * DX_ROWS + (wv & 3) * 32, c0 = blockIdx.y * DX_COLS + (wv >> 2) * 32 * DX_BLOCKS;
+  if (c0 >= H || r0 >= T) return;
+  const int row = min(r0 + (lane & 31), T - 1);
   const float* pa = dl + (size_t)row * E + (lane >> 5) * 8;
-  const bf16_t* pb = w + (size_t)col * E + (lane >> 5) * 8;
-  f32x16 acc;
+  const bf16_t* pb[DX_BLOCKS];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int b = 0; b < DX_BLOCKS; ++b) pb[b] = w + (size_t)min(c0 + 32 * b + (lane & 31), H - 1) * E + (lane >> 5) * 8;
+  f32x16 acc[DX_BLOCKS];
+#pragma unroll
+  for (int b = 0; b < DX_BLOCKS; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[b][j] = 0.f;
+#pragma unroll 2
   for (int k = 0; k < E; k += 16) {
-    const bool in = k + (lane >> 5) * 8 < E;   // E % 8 == 0: a lane's 8 indices are all in or all out
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(in ? cvt8(pa + k) : zero8(), in ? load8(pb + k) : zero8(), acc, 0,
-                                                   0, 0);
-  }
-  const int c = c0 + (lane & 31);
+    // E % 8 == 0: a lane's 8 indices are all in or all out
+    const bool in = E16 || k + (lane >> 5) * 8 < E;
+    const rbf16x8 a = in ? cvt8(pa + k) : zero8();
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = r0 + acc_row(j, lane);
-    if (r < T && c < H) {
-      const size_t o = (size_t)r * H + c;
-      dx[o] = f2bf((dx_in ? bf2f(dx_in[o]) : 0.f) + acc[j]);
+    for (int b = 0; b < DX_BLOCKS; ++b)
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, in ? load8(pb[b] + k) : zero8(), acc[b], 0, 0, 0);
+  }
+  // dx_in may be dx itself: every dx_in value of the lane is loaded before the first store,
+  // so the loads are issued together instead of one after each store
+  if (dx_in) {
+    bf16_t din[DX_BLOCKS][16];
+#pragma unroll
+    for (int b = 0; b < DX_BLOCKS; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = min(r0 + acc_row(j, lane), T - 1), c = min(c0 + 32 * b + (lane & 31), H - 1);
+        din[b][j] = dx_in[(size_t)r * H + c];
+      }
+#pragma unroll
+    for (int b = 0; b < DX_BLOCKS; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[b][j] += bf2f(din[b][j]);
+  }
+#pragma unroll
+  for (int b = 0; b < DX_BLOCKS; ++b) {
+    const int c = c0 + 32 * b + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = r0 + acc_row(j, lane);
+      if (r < T && c < H) dx[(size_t)r * H + c] = f2bf(acc[b][j]);
     }
   }
 }
@@ -217,16 +255,20 @@ hipError_t launch_router_fwd(const moe_shape& s, const bf16_t* x, const bf16_t* 
              st, w, s.H, s.E, wt);
   if (s.T == 0) return hipGetLastError();
   MOE_LAUNCH("router_logits", k_router_logits, dim3((unsigned)ceil_div(s.T, 32), (unsigned)ceil_div(s.E, LG_COLS)),
-             dim3(512), 0, st, x, wt, s.T, s.H, s.E, logits);
+             dim3(1024), 0, st, x, wt, s.T, s.H, s.E, logits);
   return hipGetLastError();
 }
 
 hipError_t launch_router_bwd(const moe_shape& s, const bf16_t* x, const bf16_t* w, const float* dl,
                              const bf16_t* dx_in, bf16_t* dx, bf16_t* dw, float* part, hipStream_t st) {
   const int64_t n = (int64_t)s.H * s.E;
-  if (s.T > 0)
-    MOE_LAUNCH("router_dx", k_router_dx, dim3((unsigned)ceil_div(s.T, 32), (unsigned)ceil_div(s.H, 256)), dim3(512), 0,
-               st, dl, w, s.T, s.H, s.E, dx_in, dx);
+  {
+    const dim3 grid((unsigned)ceil_div(s.T, DX_ROWS), (unsigned)ceil_div(s.H, DX_COLS));
+    if (s.T > 0 && s.E % 16 == 0)
+      MOE_LAUNCH("router_dx", k_router_dx<true>, grid, dim3(512), 0, st, dl, w, s.T, s.H, s.E, dx_in, dx);
+    else if (s.T > 0)
+      MOE_LAUNCH("router_dx", k_router_dx<false>, grid, dim3(512), 0, st, dl, w, s.T, s.H, s.E, dx_in, dx);
+  }
   const int slices = router_dw_slices(s.T, s.H, s.E);
   const int tslice = (int)(ceil_div(ceil_div(s.T, slices), DW_CHUNK) * DW_CHUNK);
   MOE_LAUNCH("router_dw", k_router_dw,
