@@ -20,6 +20,9 @@ CASES = {
     "ragged_mx": wl.MoeConfig("ragged_mx", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
     "ragged_mxfp8": wl.MoeConfig("ragged_mxfp8", 700, 256, 256, 6, 2, 0, 6, 8, bwd="mxfp8", fwd="mxfp8"),
     "tiny_f32": wl.CONFIGS["tiny_f32"],
+    # activation checkpointing: the backward's recompute of G|U and A is captured too
+    "ragged_bf16_share_recompute": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
+    "ragged_mxfp8_recompute": wl.MoeConfig("ragged_mxfp8", 700, 256, 256, 6, 2, 0, 6, 8, bwd="mxfp8", fwd="mxfp8"),
 }
 
 
@@ -41,7 +44,8 @@ def test_graph_replays_match_eager(name):
     layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local,
                      L.MOE_F32 if cfg.dtype == "f32" else L.MOE_BF16,
                      L.MOE_BWD_MXFP8 if cfg.bwd == "mxfp8" else L.MOE_BWD_SAME, cfg.renorm,
-                     fwd=L.MOE_FWD_MXFP8 if cfg.fwd == "mxfp8" else L.MOE_FWD_SAME)
+                     fwd=L.MOE_FWD_MXFP8 if cfg.fwd == "mxfp8" else L.MOE_FWD_SAME,
+                     recompute=int(name.endswith("_recompute")))
     logits = torch.from_numpy(np.ascontiguousarray(inp["logits"])).cuda()
     x, wg, wu, wd, dy = (to_dev(inp[k], dt) for k in ("x", "w_gate", "w_up", "w_down", "dy"))
 

@@ -88,3 +88,51 @@ def test_router_no_tokens():
     L.moe_router_bwd(s, 0, w.data_ptr(), 0, 0, 0, dw.data_ptr(), scratch.data_ptr(), stream)
     torch.cuda.synchronize()
     assert not dw.float().abs().sum().item()
+
+
+def test_router_graph_replays_match_eager():
+    """moe_router_fwd + moe_router_bwd captured as one HIP graph: every replay, with eager
+    work and a host wait between replays, reproduces the eager outputs bit for bit."""
+    import combine_top_router_amd.lib as L
+    cfg = CASES["ragged"]
+    inp = wl.make_inputs(cfg, with_weights=False, with_dy=False)
+    s = _shape(cfg)
+    _, scratch_b = L.moe_workspace_bytes(s)
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    x, w = to_dev(inp["x"], torch.bfloat16), to_dev(wl.make_router_weight(cfg), torch.bfloat16)
+    dl = torch.from_numpy(np.random.default_rng(5).standard_normal((T, E)).astype(np.float32)).cuda()
+    outs = {"logits": torch.empty(T, E, dtype=torch.float32, device="cuda"),
+            "idx": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+            "w": torch.empty(T, k, dtype=torch.float32, device="cuda"),
+            "dx": torch.empty(T, H, dtype=torch.bfloat16, device="cuda"),
+            "dw": torch.empty(H, E, dtype=torch.bfloat16, device="cuda")}
+    scratch = torch.empty(scratch_b, dtype=torch.uint8, device="cuda")
+
+    def run():
+        st = torch.cuda.current_stream().cuda_stream
+        L.moe_router_fwd(s, x.data_ptr(), w.data_ptr(), outs["logits"].data_ptr(), outs["idx"].data_ptr(),
+                         outs["w"].data_ptr(), scratch.data_ptr(), st)
+        L.moe_router_bwd(s, x.data_ptr(), w.data_ptr(), dl.data_ptr(), 0, outs["dx"].data_ptr(),
+                         outs["dw"].data_ptr(), scratch.data_ptr(), st)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    junk = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        for t in outs.values():
+            t.fill_(3)
+        junk.add_(1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t, ref[n]), (rep, n)
+
