@@ -325,6 +325,41 @@ def test_mxfp8_layer_parity(name, fuse):
         assert e_pl < PLAIN_TOL, (key, e_pl)
 
 
+def _random_mxf_configs(n, seed=4049):
+    """Seeded random small mxfp8 layers: H and I multiples of 128, random E, k, local
+    range and renorm, some with recompute."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 33))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        el = int(rng.integers(1, E + 1))
+        eb = int(rng.integers(0, E - el + 1))
+        out.append((wl.MoeConfig(f"rand_mxf{i}", int(rng.integers(1, 400)), 128 * int(rng.integers(1, 4)),
+                                 128 * int(rng.integers(1, 4)), E, k, eb, el, 300 + i, bwd="mxfp8", fwd="mxfp8",
+                                 renorm=int(rng.integers(0, 2))), int(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_MXF = {c.name: (c, rc) for c, rc in _random_mxf_configs(6)}
+
+
+@pytest.mark.parametrize("name", list(RANDOM_MXF))
+def test_mxfp8_random_shapes(name):
+    cfg, recompute = RANDOM_MXF[name]
+    print(f"[mxfp8-parity-random] {cfg} recompute={recompute}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp, recompute=recompute)
+    idx, w, Yq, Y, ix, gmx, g = _oracle_mxf(cfg, inp)
+    assert np.array_equal(out["topk_idx"], idx)
+    assert np.array_equal(out["offsets"], ix["offsets"])
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    assert rel(out["y"], Yq) < BF16_TOL
+    for key in GRADS:
+        e_mx = rel(out[key], gmx[key])
+        assert e_mx < MX_TOL, (key, e_mx)
+
+
 def test_mxfp8_full_size_parity_sampled():
     """235B-A22B EP=8 share in mxfp8 mode: y, dx and d_topk_w of sampled tokens and the
     weight gradients of sampled experts against the oracle's MXFP8 forward and backward
