@@ -134,10 +134,12 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
         if ctx is not None:
             ctx.__exit__(None, None, None)
     flops = 18.0 * rows_done * cfg.H * cfg.I
+    mx = " (the unquantised oracle; the MXFP8 modes' oracle adds the quantise-dequantise passes)" \
+        if "mxfp8" in (cfg.fwd, cfg.bwd) else ""
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or 1, "kind": "oracle",
             "sample": f"fp64 numpy oracle: routing + index of all {cfg.T} tokens, then forward+backward of "
                       f"{n_exp} of {cfg.e_local} experts ({rows_done} of {int(ix['counts'].sum())} rows) "
-                      f"in {dt:.1f} s"}
+                      f"in {dt:.1f} s{mx}"}
 
 
 def main():
