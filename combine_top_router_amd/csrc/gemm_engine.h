@@ -423,7 +423,11 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
     }
     if (end) break;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads past the end
+  // the loads past the end: waited for with their registers still live (read and
+  // written after the wait), so no register of an in-flight load is given to other
+  // values before the load has landed
+#pragma unroll
+  for (int r = 0; r < REG_AHEAD; ++r) sl[r].template ready<0>();
   asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
 }
 
