@@ -5,8 +5,8 @@ exact, the GPU sums in fp32); the routing is an integer decision taken in fp32, 
 topk_idx must equal the oracle's routing applied to the GPU's own fp32 logits, bit for
 bit, and the weights match within 2e-6.  Backward: dx (= dx_in + d_logits W_r^T) and
 dW_r within 1e-2 of the fp64 results (d_logits enters the bf16 MFMAs rounded to bf16), with dx_in absent,
-given, and the same buffer as dx.  Small ragged shapes, the tiny layer and the full
-Qwen3-30B-A3B router (T=4096, H=2048, E=128)."""
+given, and the same buffer as dx.  Small ragged shapes, the tiny layer, routers over 512 and
+1024 experts and the full Qwen3-30B-A3B router (T=4096, H=2048, E=128)."""
 import numpy as np
 import pytest
 
@@ -22,6 +22,9 @@ CASES = {
     "tiny": wl.CONFIGS["tiny_bf16"],
     "ragged": wl.MoeConfig("ragged_router", 700, 192, 64, 40, 3, 0, 40, 21),
     "one_token": wl.MoeConfig("one_token_router", 1, 64, 64, 16, 4, 0, 16, 22),
+    # wide routers: E past the 16-lane routing kernel's 256 and at the ABI's 1024
+    "wide_512": wl.MoeConfig("wide_router", 100, 128, 64, 512, 8, 0, 512, 23),
+    "wide_1024_k16": wl.MoeConfig("wide_router_k16", 50, 64, 64, 1024, 16, 0, 1024, 24, renorm=0),
     "qwen3_30b": wl.CONFIGS["qwen3_30b"],
 }
 
