@@ -1,4 +1,4 @@
-// bf16 MFMA grouped GEMMs of the expert MLP, forward and backward, for gfx950.
+// bf16 and MXFP8 MFMA grouped GEMMs of the expert MLP, forward and backward, for gfx950.
 //
 // Grouped GEMM over each expert's real row count in one launch, shapes read on the
 // device (NVIDIA DeepSeek-V3 MoE article, "Optimization 1"); the two expert linear
@@ -27,6 +27,8 @@
 //   B3 bwd_dX     : dXp = dG Wg^T + dU Wu^T (K = 2I)
 //   B2 bwd_dWd    : dWd[e] = (w A)_e^T dY'_e over the expert's rows
 //   B4 bwd_dWgu   : [dWg | dWu][e] = Xp_e^T [dG | dU]_e over the expert's rows
+// Each has an MXFP8 variant on v_mfma_scale_f32_32x32x64_f8f6f4 over E4M3 codes with e8m0
+// scales per 32 along K (the fp8 forward's K1 also writes A's row-wise codes).
 #include <type_traits>
 
 #include "gemm_engine.h"
