@@ -252,7 +252,7 @@ struct JGateUp {
   using Tile = RowTileInfo;
   using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
-  static constexpr bool DYN = false, REG = true;
+  static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
@@ -401,7 +401,7 @@ struct JDown {
   using Tile = RowTileInfo;
   using Ld = typename std::conditional<MX, LMx, LMnB>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
-  static constexpr bool DYN = false, REG = true;
+  static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
