@@ -94,7 +94,7 @@ __global__ __launch_bounds__(1024) void k_router_logits(const bf16_t* __restrict
   if (ks > 0) red[ks - 1][cb][lane] = acc;
   __syncthreads();
   if (ks == 0) {
-#pragma unroll
+#pragma unroll 1
     for (int s = 0; s < LG_KSPLIT - 1; ++s) {
       const f32x16 o = red[s][cb][lane];
 #pragma unroll
