@@ -3,8 +3,8 @@
 forward's own gate/up GEMM.  The kernels are deterministic, so every output must equal
 the outputs of the saved-activation path bit for bit; that path's parity with the
 oracle is tested elsewhere, so this also holds the recompute path to the oracle.  Each
-precision mode (bf16, fp8_bwd, mxfp8), both weight modes, a local share, a skewed layer
-and the full Qwen3-30B-A3B layer."""
+precision mode (bf16, fp8_bwd, mxfp8, MXFP8 forward with a bf16 backward), both weight
+modes, a local share, a skewed layer and the full Qwen3-30B-A3B layer."""
 import numpy as np
 import pytest
 
@@ -22,6 +22,8 @@ CASES = {
     "ragged_fp8bwd": wl.MoeConfig("ragged_fp8bwd", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
     "ragged_mxfp8_share": wl.MoeConfig("ragged_mxfp8_share", 500, 256, 256, 10, 3, 4, 5, 13, bwd="mxfp8",
                                        fwd="mxfp8"),
+    # MXFP8 forward with the bf16 backward: the recompute runs the fp8 gate/up chain
+    "ragged_mxfp8_fwd_only": wl.MoeConfig("ragged_mxfp8_fwd_only", 300, 256, 128, 5, 2, 0, 5, 15, fwd="mxfp8"),
 }
 KEYS = ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits", "topk_idx", "row_src")
 
