@@ -89,8 +89,8 @@ const char* moe_last_error(void);
  *  saved   -- written by moe_fwd, read by moe_bwd (the saved G, U and A rows; in
  *             mxfp8 mode, fwd and bwd both MOE_*_MXFP8, also the backward's row-wise
  *             MXFP8 codes of the weights, which the forward's weight passes produce);
- *  scratch -- temporary space of moe_dispatch, moe_fwd and moe_bwd; its contents do
- *             not need to survive between calls.
+ *  scratch -- temporary space of moe_dispatch, moe_fwd, moe_bwd, moe_router_fwd and
+ *             moe_router_bwd; its contents do not need to survive between calls.
  * Both pointers must be non-NULL.  Returns MOE_EINVAL for an invalid shape.  With
  * shape.recompute = 1 saved_bytes is 0: nothing is kept between the two calls. */
 int moe_workspace_bytes(const moe_shape* shape, size_t* saved_bytes, size_t* scratch_bytes);
