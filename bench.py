@@ -290,7 +290,7 @@ def main():
     for name, v in per.items():
         avg = float(np.mean(v))
         byts, flops = kernel_work(name, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local, cfg.E)
-        kernels[name] = {"ms": round(avg, 4), "launches_per_step": len(v) // max(1, len(per["route_topk"])),
+        kernels[name] = {"ms": round(avg, 4), "launches_per_step": len(v) // nrep,
                          "GB/s": round(byts / avg / 1e6, 1) if byts else None,
                          "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None}
     gemm = {n: kernels[n] for n in GEMMS if n in kernels}
