@@ -360,12 +360,14 @@ def test_mxfp8_random_shapes(name):
         assert e_mx < MX_TOL, (key, e_mx)
 
 
-def test_mxfp8_full_size_parity_sampled():
-    """235B-A22B EP=8 share in mxfp8 mode: y, dx and d_topk_w of sampled tokens and the
-    weight gradients of sampled experts against the oracle's MXFP8 forward and backward
-    restricted to those experts (the row-wise blocks are per row and the weights' and
-    the gradients' column-wise blocks per expert, so the restriction changes nothing)."""
-    cfg = wl.CONFIGS["qwen3_235b_ep8_mxfp8"]
+@pytest.mark.parametrize("wname", ["qwen3_235b_ep8_mxfp8", "qwen3_30b_mxfp8"])
+def test_mxfp8_full_size_parity_sampled(wname):
+    """The 235B-A22B EP=8 share and the 30B-A3B layer in mxfp8 mode: y, dx and d_topk_w of
+    sampled tokens and the weight gradients of sampled experts against the oracle's MXFP8
+    forward and backward restricted to those experts (the row-wise blocks are per row and
+    the weights' and the gradients' column-wise blocks per expert, so the restriction
+    changes nothing)."""
+    cfg = wl.CONFIGS[wname]
     print(f"[mxfp8-parity-full] {cfg.name}", flush=True)
     inp = inputs(cfg)
     out = run_layer(cfg, inp)
@@ -382,6 +384,11 @@ def test_mxfp8_full_size_parity_sampled():
             err = rel(out[key][e], sub[key][j])
             print(f"  {key}[{e}]: {err:.3e}", flush=True)
             assert err < MX_TOL, (key, e, err)
+    if cfg.e_local == cfg.E:
+        # every slot is local (the 30B layer): a token's y and dx need all 8 of its
+        # experts, which three sampled experts almost never cover; the weight gradients
+        # above are the full-size check there
+        return
     assert whole.sum() > 100
     err = rel(out["y"][tok[whole]], sub["y"][whole])
     print(f"  y ({int(whole.sum())} tokens): {err:.3e}", flush=True)
