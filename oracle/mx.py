@@ -37,7 +37,7 @@ E4M3_MAX = 448.0
 BLOCK = 32
 
 __all__ = ["e4m3_decode", "e4m3_round", "e4m3_encode", "e8m0_exponent", "quantize_blocks",
-           "qdq_rows", "qdq_cols_grouped", "layer_forward_mx", "layer_backward_mx"]
+           "qdq_rows", "qdq_cols_grouped", "layer_forward_mx", "layer_backward_mx", "BWD_POINTS"]
 
 
 def e4m3_decode(code):
@@ -154,9 +154,54 @@ def layer_forward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, to
     return Y, {"G": G, "U": U, "A": A, "Yp": Yp, "index": index}
 
 
-def layer_backward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, topk_w, saved):
+def _b1_dy(dye, we):
+    """B1's dY' operand: the unweighted gathered rows, row-wise along H."""
+    return qdq_rows(dye)
+
+
+def _b2_dy(dye, we, seg):
+    """B2's dY' operand: w * dY', column-wise in group-aware 32-row blocks."""
+    return qdq_cols_grouped(we[:, None] * dye, seg)
+
+
+def _rows_w(w):
+    """A weight matrix quantised row-wise (W_down [I, H] along H for B1; W_gate and
+    W_up [H, I] along I for B3)."""
+    return qdq_rows(w)
+
+
+def _rows_act(m, seg):
+    """An activation operand quantised row-wise (dG and dU along I for B3)."""
+    return qdq_rows(m)
+
+
+def _cols_act(m, seg):
+    """An activation operand quantised column-wise in group-aware 32-row blocks (A for
+    B2; Xp, dG and dU for B4)."""
+    return qdq_cols_grouped(m, seg)
+
+
+# The eight quantisation points of the MXFP8 backward (module docstring, "Blocks lie along
+# each backward GEMM's contraction axis" and "B1 quantises the unweighted dY'").  Each entry
+# is the quantise-dequantise applied at that point.  layer_backward_mx takes the table as
+# an argument only so that the tests can move one point at a time and show that a pin fails.
+BWD_POINTS = {
+    "b1_dy": _b1_dy,        # (dY' rows, w) -> Q_rows(dY')
+    "b1_wd": _rows_w,       # W_down [I, H] -> Q along H
+    "b2_a": _cols_act,      # (A, seg) -> Q_cols(A)
+    "b2_dy": _b2_dy,        # (dY' rows, w, seg) -> Q_cols(w dY')
+    "b3_dgu": _rows_act,    # (dG or dU, seg) -> Q along I
+    "b3_w": _rows_w,        # W_gate / W_up [H, I] -> Q along I
+    "b4_x": _cols_act,      # (Xp, seg) -> Q_cols(Xp)
+    "b4_dgu": _cols_act,    # (dG or dU, seg) -> Q_cols
+}
+
+
+def layer_backward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, topk_w, saved, points=None):
     """The backward with the eight backward-GEMM operands quantize-dequantized to
-    MXFP8 at the points listed in the module docstring; fp64 everywhere else."""
+    MXFP8 at the points listed in the module docstring (the table BWD_POINTS, which
+    `points` may override entry by entry); fp64 everywhere else."""
+    q = dict(BWD_POINTS, **(points or {}))
     index = saved["index"]
     x = _f64(inp["x"]); dy = _f64(inp["dy"])
     T, H = x.shape
@@ -176,21 +221,21 @@ def layer_backward_mx(inp: dict, k: int, e_begin: int, e_local: int, topk_idx, t
         wg = _f64(inp["w_gate"][e]); wu = _f64(inp["w_up"][e]); wd = _f64(inp["w_down"][e])
         xe, dye = x[tok], dy[tok]
         seg = np.array([0, hi - lo])
-        # B1: dA' = Q(dY') Q(Wd)^T, both row-wise along H
-        dap = qdq_rows(dye) @ qdq_rows(wd).T
+        # B1: dA' = Q(dY') Q(Wd)^T, both row-wise along H; w applies after the GEMM
+        dap = q["b1_dy"](dye, we) @ q["b1_wd"](wd).T
         d_w = np.sum(dap * a, axis=1)
         da = we[:, None] * dap
         s = sigmoid(g)
         du = da * g * s
         dg = da * u * s * (1.0 + g * (1.0 - s))
         # B2: dWd = Q_col(A)^T Q_col(w dY')
-        dWd[e] = qdq_cols_grouped(a, seg).T @ qdq_cols_grouped(we[:, None] * dye, seg)
+        dWd[e] = q["b2_a"](a, seg).T @ q["b2_dy"](dye, we, seg)
         # B3: dXp = Q(dG) Q(Wg)^T + Q(dU) Q(Wu)^T, row-wise along I
-        dxe = qdq_rows(dg) @ qdq_rows(wg).T + qdq_rows(du) @ qdq_rows(wu).T
+        dxe = q["b3_dgu"](dg, seg) @ q["b3_w"](wg).T + q["b3_dgu"](du, seg) @ q["b3_w"](wu).T
         # B4: dWg = Q_col(X)^T Q_col(dG), dWu = Q_col(X)^T Q_col(dU)
-        qx = qdq_cols_grouped(xe, seg)
-        dWg[e] = qx.T @ qdq_cols_grouped(dg, seg)
-        dWu[e] = qx.T @ qdq_cols_grouped(du, seg)
+        qx = q["b4_x"](xe, seg)
+        dWg[e] = qx.T @ q["b4_dgu"](dg, seg)
+        dWu[e] = qx.T @ q["b4_dgu"](du, seg)
         dX[tok] += dxe
         d_topk_w[rows] = d_w
     return {"dx": dX, "dw_gate": dWg, "dw_up": dWu, "dw_down": dWd,
