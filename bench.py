@@ -49,7 +49,9 @@ def kernel_work(name, T, H, I, k, R, El, E_all=0):
     """Algorithmic bytes and flops of one launch of a hot-path kernel (bf16 data).
 
     Per routed row and per expert weights, as in the design notes: each kernel's
-    bytes are the operands it must read and the results it must write once."""
+    bytes are the operands it must read and the results it must write once.  The dX
+    unpermute also reads the row-dot partials of d_topk_w (WN = 4 per 256 columns of I,
+    fp32) and writes d_topk_w."""
     b = 2
     W_gu = 2 * El * H * I * b
     W_d = El * I * H * b
@@ -67,7 +69,7 @@ def kernel_work(name, T, H, I, k, R, El, E_all=0):
         "router_logits": (T * H * b + H * E_all * b + T * E_all * 4, 2.0 * T * H * E_all),
         "router_dx": (T * E_all * 4 + H * E_all * b + 2 * T * H * b, 2.0 * T * H * E_all),
         "combine": (row_h + T * H * b, 0.0),
-        "unpermute_dx": (row_h + T * H * b, 0.0),
+        "unpermute_dx": (row_h + T * H * b + R * 4 * ((I + 255) // 256) * 4 + T * k * 4, 0.0),
         # MXFP8 GEMMs: fp8 operands, bf16 side inputs and outputs
         "fwd_gateup_mx": ((row_h + W_gu) / b * q + row_2i + row_i, 4.0 * R * H * I),
         "fwd_down_mx": ((row_i + W_d) / b * q + row_h, 2.0 * R * H * I),
@@ -104,14 +106,16 @@ def counted_traffic(workload, kernel):
     return int(m.group(1)) if m else None
 
 
-def cpu_baseline(cfg, inp, budget_s=15.0):
+def cpu_baseline(cfg, inp, budget_s=20.0):
     """The oracle as it stands, on the host cores, over a bounded sample: routing and
-    index for all tokens, then forward + backward of whole experts (all their rows) in
-    order until the time budget is spent."""
+    index of all tokens, then the forward of the first n local experts (all their rows),
+    then their backward, each timed on its own; n is the whole layer when a first pass
+    over one expert says it fits the time budget, else the share that does."""
     from oracle import moe as om
     threads = None
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
+        # one GPU's share of the host: 16 threads (the OMP_NUM_THREADS of one-GPU jobs)
         limit = min(16, os.cpu_count() or 1)
         ctx = threadpool_limits(limits=limit)
         threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
@@ -121,25 +125,35 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
         t0 = time.perf_counter()
         idx, w = om.route_topk(inp["logits"], cfg.k, cfg.renorm)
         ix = om.build_index(idx, cfg.e_begin, cfg.e_local)
-        rows_done = 0
-        n_exp = 0
-        for e in range(cfg.e_local):
-            om.expert_sample(inp, cfg.k, ix, w, [e])        # forward + backward of expert e
-            rows_done += int(ix["counts"][e])
-            n_exp += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        dt = time.perf_counter() - t0
+        t_route = time.perf_counter() - t0
+        rel = np.asarray(idx) - cfg.e_begin
+
+        def run(n):
+            sub = dict(inp, w_gate=inp["w_gate"][:n], w_up=inp["w_up"][:n], w_down=inp["w_down"][:n])
+            f0 = time.perf_counter()
+            _, saved = om.layer_forward(sub, cfg.k, 0, n, rel, w)
+            f1 = time.perf_counter()
+            om.layer_backward(sub, cfg.k, 0, n, rel, w, saved)
+            f2 = time.perf_counter()
+            return f1 - f0, f2 - f1, int(saved["index"]["offsets"][-1])
+
+        tf1, tb1, r1 = run(1)
+        n = cfg.e_local if (tf1 + tb1) * cfg.e_local < budget_s else max(1, int(budget_s / (tf1 + tb1)))
+        tf, tb, rows = run(n) if n > 1 else (tf1, tb1, r1)
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    flops = 18.0 * rows_done * cfg.H * cfg.I
+    hi = cfg.H * cfg.I
     mx = " (the unquantised oracle; the MXFP8 modes' oracle adds the quantise-dequantise passes)" \
         if "mxfp8" in (cfg.fwd, cfg.bwd) else ""
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or 1, "kind": "oracle",
-            "sample": f"fp64 numpy oracle: routing + index of all {cfg.T} tokens, then forward+backward of "
-                      f"{n_exp} of {cfg.e_local} experts ({rows_done} of {int(ix['counts'].sum())} rows) "
-                      f"in {dt:.1f} s{mx}"}
+    return {"value": 18.0 * rows * hi / (tf + tb) / 1e12, "unit": "TFLOP/s", "cores": threads or 1,
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "fwd_TFLOP/s": 6.0 * rows * hi / tf / 1e12, "bwd_TFLOP/s": 12.0 * rows * hi / tb / 1e12,
+            "fwd_s": round(tf, 2), "bwd_s": round(tb, 2), "route_index_s": round(t_route, 2),
+            "sample": f"fp64 numpy oracle on {threads or 1} BLAS threads of {os.cpu_count()} host CPUs: routing + "
+                      f"index of all {cfg.T} tokens, then the forward ({tf:.1f} s) and the backward ({tb:.1f} s) of "
+                      f"{n} of {cfg.e_local} local experts ({rows} of {int(ix['counts'].sum())} rows), timed "
+                      f"apart{mx}"}
 
 
 def main():
@@ -294,6 +308,11 @@ def main():
                          "GB/s": round(byts / avg / 1e6, 1) if byts else None,
                          "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None}
     gemm = {n: kernels[n] for n in GEMMS if n in kernels}
+    # each GEMM against the dense MFMA peak of its own operand type (bf16 or MXFP8)
+    gemm_flops = sum(kernel_work(n, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)[1] * v["launches_per_step"]
+                     for n, v in gemm.items())
+    gemm_peak_ms = sum(v["ms"] * v["launches_per_step"] * (FP8_PEAK_TFLOPS if n.endswith("_mx") else BF16_PEAK_TFLOPS)
+                       for n, v in gemm.items())
     dom = max(gemm, key=lambda n: gemm[n]["ms"])
     byts, flops = kernel_work(dom, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)
     avg_ms = gemm[dom]["ms"]
@@ -315,7 +334,6 @@ def main():
 
     flops_step = 18.0 * R * cfg.H * cfg.I + (6.0 * cfg.T * cfg.H * cfg.E if args.router else 0.0)
     fwd_ms, bwd_ms = part_ms["fwd"], part_ms["bwd"]
-    gemm_ms = sum(v["ms"] * v["launches_per_step"] for n, v in gemm.items())
     out = {
         "metric": "MoE layer fwd+bwd ms & TFLOPS at Qwen3-30B-A3B shape, 1 MI355X; % MFMA peak",
         "value": round(flops_step / ms / 1e9, 2),
@@ -332,11 +350,19 @@ def main():
                                                             "the gate/up GEMM)" if args.recompute else "")
                    + (", router GEMM x W_r in the step" if args.router else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
+        # the layer's algorithmic flops (router GEMM included with --router) over the step
+        # time, against the dense bf16 peak
         "mfma_frac_step": round(flops_step / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-        "mfma_frac_gemms": round(flops_step / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+        # the expert GEMMs only: their flops over the sum of their kernel times, each kernel
+        # against its own operand type's dense peak (bf16 2.5, MXFP8 5.0 PFLOP/s)
+        "mfma_frac_gemms": round(gemm_flops / gemm_peak_ms / 1e9, 4),
+        "kernel_timing": "HIP events recorded by the library on the launch stream around each kernel of "
+                         f"{nrep} eagerly launched steps (mean per launch); ms_per_step is the graph replay",
         "fwd_ms_kernels": round(fwd_ms, 4),
         "bwd_ms_kernels": round(bwd_ms, 4),
         "hbm_frac_combine": round(kernels["combine"]["GB/s"] / HBM_PEAK_GBS, 4) if "combine" in kernels else None,
+        "hbm_frac_unpermute_dx": (round(kernels["unpermute_dx"]["GB/s"] / HBM_PEAK_GBS, 4)
+                                  if "unpermute_dx" in kernels else None),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "kernels": kernels,

@@ -77,12 +77,20 @@ int check_shape(const moe_shape* s) {
   if (s->renorm != 0 && s->renorm != 1) return fail(MOE_EINVAL, "renorm = %d", s->renorm);
   if ((int64_t)s->T * s->k > 0x7fffffffLL) return fail(MOE_EINVAL, "T * k exceeds 2^31 - 1");
   if (s->dtype == MOE_BF16 && (s->H % 64 != 0 || s->I % 64 != 0))
-    return fail(MOE_EINVAL, "bf16 needs H and I multiples of 64 (H = %d, I = %d)", s->H, s->I);
-  if (s->dtype == MOE_F32 && s->H % 4 != 0) return fail(MOE_EINVAL, "fp32 needs H a multiple of 4 (H = %d)", s->H);
+    return fail(MOE_EUNSUPPORTED, "bf16 needs H and I multiples of 64 (H = %d, I = %d)", s->H, s->I);
+  if (s->dtype == MOE_F32 && s->H % 4 != 0)
+    return fail(MOE_EUNSUPPORTED, "fp32 needs H a multiple of 4 (H = %d)", s->H);
   if (s->bwd == MOE_BWD_MXFP8 && s->dtype != MOE_BF16)
     return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs bf16 data");
   if (s->bwd == MOE_BWD_MXFP8 && s->H % 128 != 0)
     return fail(MOE_EUNSUPPORTED, "the MXFP8 backward needs H a multiple of 128 (H = %d)", s->H);
+  if (s->bwd == MOE_BWD_MXFP8) {  // the kernels index the padded row space with int
+    const int64_t R_cap = (int64_t)s->T * (s->k < s->e_local ? s->k : s->e_local);
+    const int64_t Rp = mx_rp_cap(R_cap, s->e_local);
+    if (Rp > 0x7fffffffLL)
+      return fail(MOE_EUNSUPPORTED, "the MXFP8 backward's padded row space (%lld rows) exceeds 2^31 - 1",
+                  (long long)Rp);
+  }
   if (s->fwd != MOE_FWD_SAME && s->fwd != MOE_FWD_MXFP8) return fail(MOE_EINVAL, "fwd = %d", s->fwd);
   if (s->recompute != 0 && s->recompute != 1) return fail(MOE_EINVAL, "recompute = %d", s->recompute);
   if (s->recompute && s->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "recompute needs bf16 data");
@@ -182,19 +190,15 @@ struct TimingRec {
   const char* name;
   int e0, e1;
 };
+// The events are created once, by moe_timing_enable, so that no hot-path call creates
+// one; a kernel launched when the pool is used up is not recorded.
+constexpr int kTimingEvents = 4096;
 struct Timing {
   bool on = false;
   std::vector<hipEvent_t> pool;
   int used = 0;
   std::vector<TimingRec> recs;
-  hipEvent_t next() {
-    if (used == (int)pool.size()) {
-      hipEvent_t ev = nullptr;
-      if (hipEventCreate(&ev) != hipSuccess) return nullptr;
-      pool.push_back(ev);
-    }
-    return pool[used++];
-  }
+  hipEvent_t next() { return used < (int)pool.size() ? pool[used++] : nullptr; }
 };
 thread_local Timing g_timing;
 
@@ -206,9 +210,8 @@ thread_local Timing g_timing;
 namespace moe {
 void ktimer_begin(const char* name, hipStream_t st) {
   Timing& T = g_timing;
-  if (!T.on) return;
+  if (!T.on || T.used + 2 > (int)T.pool.size()) return;
   hipEvent_t ev = T.next();
-  if (!ev) return;
   hipEventRecord(ev, st);
   T.recs.push_back({name, T.used - 1, -1});
 }
@@ -225,9 +228,19 @@ void ktimer_end(hipStream_t st) {
 extern "C" {
 
 int moe_timing_enable(int on) {
-  g_timing.on = on != 0;
-  g_timing.used = 0;
-  g_timing.recs.clear();
+  Timing& T = g_timing;
+  T.on = false;
+  T.used = 0;
+  T.recs.clear();
+  if (on) {
+    while ((int)T.pool.size() < kTimingEvents) {
+      hipEvent_t ev = nullptr;
+      const hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) return hip_status(e, __func__);
+      T.pool.push_back(ev);
+    }
+    T.on = true;
+  }
   return MOE_OK;
 }
 
@@ -464,7 +477,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     } else {
       e = launch_bwd_bf16(a, st);
     }
-    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st, "combine", a.dw_part, L.nparts, d_topk_w);
+    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st, "unpermute_dx", a.dw_part, L.nparts, d_topk_w);
   } else {
     BwdArgsF32 a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
@@ -476,7 +489,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.dw_part = at<float>(scratch, L.off_part);
     a.dwg = (float*)dw_gate; a.dwu = (float*)dw_up; a.dwd = (float*)dw_down;
     e = launch_bwd_f32(a, st);
-    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st);
+    if (e == hipSuccess && s.T > 0) e = launch_combine(s, a.dxp, row_of, dx, st, "unpermute_dx");
     if (e == hipSuccess && s.T > 0) e = launch_dtopk(s, a.dw_part, L.nparts, row_of, d_topk_w, st);
   }
   return hip_status(e, __func__);

@@ -36,9 +36,11 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ idx, i
 // chunk histograms, an exclusive scan of the totals (workgroup 0 writes counts and
 // offsets), then the chunk's slots in steps of 256; wave w of the workgroup takes
 // slots [64w, 64w + 64) of a step, and the waves' per-expert counts are combined in
-// order.
+// order.  Rows are kept only below R_cap: a token whose ids repeat a local expert could
+// otherwise give more than T * min(k, El) rows; the rows past R_cap in the expert-major
+// order get no row (row_of = -1) and counts / offsets stop at R_cap.
 __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, int TK, int chunk, int nchunks,
-                                               int e_begin, int El, int ebits,
+                                               int e_begin, int El, int ebits, int R_cap,
                                                const int32_t* __restrict__ chunk_hist,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ row_src, int32_t* __restrict__ row_of) {
@@ -91,14 +93,15 @@ __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, 
     const int e = tid * q + j;
     if (e < El) {
       if (me == 0) {
-        counts[e] = tot[e];
-        offsets[e] = run;
+        const int o0 = min(run, R_cap), o1 = min(run + tot[e], R_cap);
+        counts[e] = o1 - o0;
+        offsets[e] = o0;
       }
       base[e] += run;
       run += tot[e];
     }
   }
-  if (me == 0 && tid == 255) offsets[El] = part[255];
+  if (me == 0 && tid == 255) offsets[El] = min(part[255], R_cap);
   __syncthreads();
   const int s0 = me * chunk;
   const int s1 = min(TK, s0 + chunk);
@@ -127,8 +130,8 @@ __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, 
     if (valid) {
       int pos = base[e] + rank;
       for (int w2 = 0; w2 < wv; ++w2) pos += cnt[w2 * El + e];
-      row_src[pos] = s;
-      row_of[s] = pos;
+      if (pos < R_cap) row_src[pos] = s;
+      row_of[s] = pos < R_cap ? pos : -1;
     }
     __syncthreads();
     if (valid && rank == 0) {
@@ -347,8 +350,9 @@ hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts,
                El, chunk_hist);
   int ebits = 0;
   while ((1 << ebits) < El) ++ebits;
+  const int R_cap = s.T * (s.k < El ? s.k : El);
   MOE_LAUNCH("index_place", k_place, dim3(nchunks > 0 ? nchunks : 1), dim3(256), 6 * El * sizeof(int32_t), st, idx,
-             TK, chunk, nchunks, s.e_begin, El, ebits, chunk_hist, counts, offsets, row_src, row_of);
+             TK, chunk, nchunks, s.e_begin, El, ebits, R_cap, chunk_hist, counts, offsets, row_src, row_of);
   return hipGetLastError();
 }
 

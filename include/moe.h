@@ -5,9 +5,10 @@
  * (token, slot) pairs into ragged per-expert row groups, a grouped gate/up GEMM with
  * SwiGLU, a grouped down GEMM scaled by the routing weight, and the weighted combine
  * back to token order; plus the whole backward.  Sources: the Prime Mega MoE pages
- * (DeepSeek's fused Mega MoE chain "EP dispatch, two expert linear layers, SwiGLU,
- * combine" and Prime Intellect's added backward, precision modes bf16 and fp8_bwd)
- * and NVIDIA's DeepSeek-V3 MoE article (dropless MoE; "Optimization 1": grouped GEMM
+ * (the aisight.pl article, opening section: DeepSeek's fused Mega MoE kernel runs the
+ * expert-parallel dispatch, both expert linear layers with SwiGLU between them, and the
+ * combine as one chain, and Prime Intellect added its backward; precision modes bf16 and
+ * fp8_bwd) and NVIDIA's DeepSeek-V3 MoE article (dropless MoE; "Optimization 1": grouped GEMM
  * over each expert's real token count with device-resident shapes; "Optimization 2":
  * dispatch permutes tokens by expert, combine restores token order and accumulates
  * the per-expert outputs; group-aware MXFP8 quantisation).
@@ -53,7 +54,9 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* a size, range or enum value is invalid, or a required pointer is NULL */
-  MOE_EUNSUPPORTED = -2, /* a valid but unsupported combination (e.g. MXFP8 with fp32 data) */
+  MOE_EUNSUPPORTED = -2, /* a valid but unsupported combination: H or I not a multiple of 64 in
+                            bf16 (H of 4 in fp32), MXFP8 with fp32 data or H, I not multiples of
+                            128, an MXFP8 padded row space past 2^31 - 1 rows */
   MOE_EWORKSPACE = -3,   /* a required workspace pointer (saved / scratch) is NULL */
   MOE_EHIP = -4          /* the HIP runtime reported an error at launch */
 } moe_status;
@@ -64,8 +67,8 @@ typedef enum { MOE_FWD_SAME = 0, MOE_FWD_MXFP8 = 1 } moe_fwd_prec;
 
 typedef struct {
   int32_t T;        /* tokens, >= 0 */
-  int32_t H;        /* hidden size, 1..2^20, multiple of 64 for MOE_BF16 */
-  int32_t I;        /* expert intermediate size, 1..2^20, multiple of 64 for MOE_BF16 */
+  int32_t H;        /* hidden size, 1..2^20; MOE_BF16 supports multiples of 64, MOE_F32 of 4 */
+  int32_t I;        /* expert intermediate size, 1..2^20; MOE_BF16 supports multiples of 64 */
   int32_t E;        /* routed experts, 1..1024 */
   int32_t k;        /* experts per token, 1..min(E, 16) */
   int32_t e_begin;  /* first local expert */
@@ -109,7 +112,12 @@ int moe_route_topk(const moe_shape* shape, const float* logits, int32_t* topk_id
  * its inverse row_of [T*k] (slot -> row, or -1 if the slot's expert is not local,
  * including ids outside [0, E)).  If xp is non-NULL, also gathers xp[r] = x[row_src[r]/k]
  * ([R_cap, H]); with xp == NULL the gather is left to moe_fwd / moe_bwd, which then
- * read x through row_src.  x may be NULL when xp is NULL.  Needs scratch. */
+ * read x through row_src.  x may be NULL when xp is NULL.  Needs scratch.
+ * The k ids of a token must be distinct (moe_route_topk's always are).  If they are not
+ * and e_local < k, R could exceed R_cap: the kernel then keeps the first R_cap rows of
+ * the expert-major order, gives the later slots no row (row_of = -1, so they contribute
+ * nothing and get d_topk_w = 0) and stops counts and offsets at R_cap, so that no write
+ * leaves the R_cap-sized buffers of this or any later call. */
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                  int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* row_of,
                  void* xp, void* scratch, void* stream);
@@ -159,11 +167,15 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
             const void* saved, void* dx, void* dw_gate, void* dw_up, void* dw_down,
             float* d_topk_w, void* scratch, void* stream);
 
-/* Router backward through the routing weights: d_logits [T, E] fp32.  renorm = 1:
+/* Router backward through the routing weights (NVIDIA article, "What makes MoE training
+ * hard": a learned router scores the experts and the top-K are kept, so the loss reaches
+ * the router through the softmax weights of the kept experts; Prime Mega MoE pages: the
+ * backward of the fused chain).  Writes d_logits [T, E] fp32.  renorm = 1:
  * d_logits[t, S_j] = w_j (d_w_j - sum_i w_i d_w_i) and 0 for unselected experts;
  * renorm = 0 (needs logits): d_logits[t, e] = p_e (g_e - sum_j p_{S_j} d_w_j) with
  * p = softmax(logits[t]) and g_e = d_w of the slot selecting e, else 0.  The top-k
- * selection itself is piecewise constant and contributes no gradient. */
+ * selection itself is piecewise constant and contributes no gradient.  logits is read
+ * only for renorm = 0 (the full softmax) and may be NULL for renorm = 1. */
 int moe_route_topk_bwd(const moe_shape* shape, const float* logits, const int32_t* topk_idx,
                        const float* topk_w, const float* d_topk_w, float* d_logits,
                        void* stream);
@@ -227,7 +239,9 @@ int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32
  * recorded event, writes up to `capacity` kernel names (static strings owned by the
  * library) and elapsed milliseconds in launch order, sets *count to the number of
  * kernels recorded since the last read or enable, and discards the records.  The
- * events are library-owned, reused, and live until the process ends. */
+ * events (a pool of 4096 per host thread) are created by moe_timing_enable(1), so the
+ * calls above never create one; they are reused and live until the process ends.  Kernels
+ * launched after the pool is used up (without a read in between) are not recorded. */
 int moe_timing_enable(int on);
 int moe_timing_read(int capacity, const char** names, float* ms, int* count);
 

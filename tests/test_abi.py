@@ -47,9 +47,12 @@ BAD = [
     (dict(T=-1), -1), (dict(H=0), -1), (dict(E=0), -1), (dict(E=2000), -1), (dict(k=0), -1),
     (dict(k=9), -1), (dict(k=17, E=32), -1), (dict(e_local=0), -1), (dict(e_begin=5, e_local=4), -1),
     (dict(e_begin=-1), -1), (dict(dtype=7), -1), (dict(bwd=3), -1), (dict(renorm=2), -1),
-    (dict(H=100), -1), (dict(I=96), -1), (dict(dtype=0, H=130), -1),
+    # valid sizes the kernels do not support: bf16 H or I off a multiple of 64, fp32 H of 4
+    (dict(H=100), -2), (dict(I=96), -2), (dict(dtype=0, H=130), -2),
     (dict(H=(1 << 20) + 64), -1), (dict(I=(1 << 20) + 64), -1),
     (dict(dtype=0, bwd=1), -2),
+    # MXFP8 backward whose padded row space (R_cap plus 127 rows per expert) passes 2^31 - 1
+    (dict(T=(2 ** 31 - 1) // 8, k=8, E=1024, e_local=1024, bwd=1), -2),
     # MXFP8 forward: an unknown value, fp32 data, H or I not a multiple of 128
     (dict(fwd=2), -1), (dict(dtype=0, fwd=1), -2), (dict(fwd=1), -2), (dict(fwd=1, I=128, H=192), -2),
     # recompute: an unknown value, fp32 data

@@ -185,6 +185,23 @@ def test_mx_layer_parity(name, fuse):
         assert e_plain < PLAIN_TOL, (key, e_plain)
 
 
+@pytest.mark.parametrize("name", ["tiny_bf16_mx", "ragged_mx_share", "skew_mx"])
+def test_mx_layer_parity_recompute(name):
+    """fp8_bwd with activation checkpointing (the backward recomputes G|U and A with the
+    bf16 gate/up GEMM) against the oracle's MXFP8 backward."""
+    cfg = SMALL_MX[name]
+    print(f"[mx-parity-recompute] {name}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp, recompute=1)
+    idx, w, Y, ix, gmx, g = _oracle_mx(cfg, inp)
+    assert np.array_equal(out["topk_idx"], idx)
+    assert np.array_equal(out["row_src"], ix["row_src"])
+    assert rel(out["y"], Y) < BF16_TOL
+    for key in GRADS:
+        e_mx = rel(out[key], gmx[key])
+        assert e_mx < MX_TOL, (key, e_mx)
+
+
 def _random_mx_configs(n, seed=4048):
     """Seeded random small fp8_bwd layers: H a multiple of 128, I of 64, random E, k and
     local range, both weight modes."""

@@ -57,6 +57,26 @@ def test_small_layer_parity(name, fuse):
         assert np.array_equal(out["xp"], inp["x"][ix_tok(ref, cfg)])
 
 
+RECOMPUTE = [n for n, c in SMALL.items() if c.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("name", RECOMPUTE)
+def test_small_layer_parity_recompute(name):
+    """Activation checkpointing (the pages time their layers with full activation
+    checkpointing: the forward keeps nothing and the backward recomputes G|U and A)
+    against the oracle, every output element by element."""
+    cfg = SMALL[name]
+    print(f"[parity-recompute] {name}", flush=True)
+    inp = inputs(cfg)
+    out = run_layer(cfg, inp, recompute=1)
+    ref = oracle_full(cfg, inp)
+    _check_ints(cfg, out, ref)
+    assert rel(out["topk_w"], ref["topk_w"]) < W_TOL
+    for key in ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits"):
+        err = rel(out[key], ref[key])
+        assert err < BF16_TOL, (key, err)
+
+
 def ix_tok(ref, cfg):
     return ref["index"]["row_src"] // cfg.k
 
@@ -83,8 +103,13 @@ def test_full_size_parity_sampled(name):
     for key in ("y", "dx", "d_topk_w"):
         err = rel(out[key][toks], s[key])
         assert err < BF16_TOL, (key, err)
+    # the router backward on the GPU's own d_topk_w (the kernel alone, fp32) and on the
+    # oracle's d_topk_w (the whole chain)
     dl = om.router_backward(inp["logits"][toks], idx[toks], w[toks], out["d_topk_w"][toks], cfg.renorm)
     assert rel(out["d_logits"][toks], dl) < 1e-5
+    dl_chain = om.router_backward(inp["logits"][toks], idx[toks], w[toks], s["d_topk_w"], cfg.renorm)
+    err = rel(out["d_logits"][toks], dl_chain)
+    assert err < BF16_TOL, ("d_logits", err)
     counts = ix["counts"]
     experts = sorted({int(np.argmax(counts)), int(np.argmin(counts)), int(rng.integers(cfg.e_local))})
     es = om.expert_sample(inp, cfg.k, ix, w, experts)
@@ -226,3 +251,37 @@ def test_random_shapes(name):
     for key in ("y", "dx", "dw_gate", "dw_up", "dw_down", "d_topk_w", "d_logits"):
         err = rel(out[key], ref[key])
         assert err < BF16_TOL, (key, err)
+
+
+def test_repeated_ids_stay_within_r_cap():
+    """A token's k ids must be distinct; if they repeat a local expert while e_local < k,
+    the dispatch keeps the first R_cap rows of the expert-major order and gives the later
+    slots no row.  Every token here picks experts [0, 0, 1, 1] of the local pair, so
+    expert 0 alone fills R_cap = 2T rows: counts [2T, 0], offsets stop at R_cap, expert 1's
+    slots get row_of = -1, and nothing is written past R_cap (guard entries untouched)."""
+    import combine_top_router_amd.lib as L
+    T, H, E, k = 64, 128, 8, 4
+    s = L.MoeShape(T, H, 64, E, k, 0, 2, L.MOE_BF16, 0, 1, 0, 0)
+    R_cap, G = T * 2, 256
+    dev = "cuda"
+    topk = torch.tensor([[0, 0, 1, 1]] * T, dtype=torch.int32, device=dev)
+    x = torch.randn(T, H, device=dev).to(torch.bfloat16)
+    counts = torch.full((2,), -7, dtype=torch.int32, device=dev)
+    offsets = torch.full((3,), -7, dtype=torch.int32, device=dev)
+    row_src = torch.full((R_cap + G,), -7, dtype=torch.int32, device=dev)
+    row_of = torch.full((T * k,), -7, dtype=torch.int32, device=dev)
+    xp = torch.full((R_cap + 8, H), 5.0, dtype=torch.bfloat16, device=dev)
+    _, scratch_b = L.moe_workspace_bytes(s)
+    scratch = torch.empty(max(scratch_b, 256), dtype=torch.uint8, device=dev)
+    L.moe_dispatch(s, topk.data_ptr(), x.data_ptr(), counts.data_ptr(), offsets.data_ptr(), row_src.data_ptr(),
+                   row_of.data_ptr(), xp.data_ptr(), scratch.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    slots = np.arange(T * k).reshape(T, k)
+    assert counts.cpu().tolist() == [R_cap, 0]
+    assert offsets.cpu().tolist() == [0, R_cap, R_cap]
+    assert np.array_equal(row_src[:R_cap].cpu().numpy(), slots[:, :2].reshape(-1))
+    assert np.all(row_src[R_cap:].cpu().numpy() == -7)
+    ro = row_of.cpu().numpy().reshape(T, k)
+    assert np.array_equal(ro[:, :2].reshape(-1), np.arange(R_cap)) and np.all(ro[:, 2:] == -1)
+    assert torch.equal(xp[:R_cap], x.repeat_interleave(2, dim=0))
+    assert torch.all(xp[R_cap:] == 5.0)

@@ -78,6 +78,50 @@ def test_router_parity(name):
         assert err_dx < BF16_TOL and err_dw < BF16_TOL, (mode, err_dx, err_dw)
 
 
+@pytest.mark.parametrize("name", ["ragged", "wide_512", "qwen3_30b"])
+def test_router_end_to_end_from_fp64_logits(name):
+    """The whole forward chain against the oracle's: the GPU's top-k ids and weights from
+    its own router GEMM against the oracle's routing of the fp64 logits x W_r.  The fp32
+    sums carry rounding errors of at most 2^-24 of each partial sum; their total stays
+    within b = sqrt(H) 2^-24 sum_h |x_h w_he| (a random walk of H such errors; the test
+    checks that the GPU's logits do), so a token whose k-th and (k+1)-th fp64 logits lie
+    closer than 2b may legitimately pick either: such tokens are skipped and counted
+    (there must be few)."""
+    import combine_top_router_amd.lib as L
+    cfg = CASES[name]
+    print(f"[router-e2e] {name}", flush=True)
+    inp = wl.make_inputs(cfg, with_weights=False, with_dy=False)
+    w_r = wl.make_router_weight(cfg)
+    s = _shape(cfg)
+    _, scratch_b = L.moe_workspace_bytes(s)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    x, w = to_dev(inp["x"], torch.bfloat16), to_dev(w_r, torch.bfloat16)
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    scratch = torch.empty(scratch_b, dtype=torch.uint8, device="cuda")
+    L.moe_router_fwd(s, x.data_ptr(), w.data_ptr(), logits.data_ptr(), idx.data_ptr(), tw.data_ptr(),
+                     scratch.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    L64 = om.router_logits(inp["x"], w_r)
+    ridx, rw = om.route_topk(L64, k, cfg.renorm)
+    bound = np.sqrt(cfg.H) * 2.0 ** -24 * (np.abs(inp["x"].astype(np.float64)) @ np.abs(w_r.astype(np.float64)))
+    assert np.all(np.abs(logits.cpu().numpy() - L64) <= bound)
+    srt = np.sort(L64, axis=1)[:, ::-1]
+    gap = srt[:, k - 1] - srt[:, k] if k < E else np.full(T, np.inf)
+    ok = gap > 2.0 * bound.max(axis=1)
+    skipped = int((~ok).sum())
+    print(f"  tokens {T}, skipped near ties {skipped}", flush=True)
+    assert skipped <= max(2, T // 100)
+    gi, gw = idx.cpu().numpy()[ok], tw.cpu().numpy()[ok]
+    ri, rwk = ridx[ok], rw[ok]
+    # the selected set; within it two slots may swap places where their logits lie within
+    # the fp32 error of each other, so weights are compared expert by expert
+    og, orf = np.argsort(gi, axis=1), np.argsort(ri, axis=1)
+    assert np.array_equal(np.take_along_axis(gi, og, 1), np.take_along_axis(ri, orf, 1))
+    assert rel(np.take_along_axis(gw, og, 1), np.take_along_axis(rwk, orf, 1)) < 1e-5
+
+
 def test_router_no_tokens():
     import combine_top_router_amd.lib as L
     cfg = wl.CONFIGS["tiny_bf16"].replace(T=0)
