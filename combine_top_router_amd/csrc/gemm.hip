@@ -138,8 +138,10 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0,
-                                                                     sb[ni]);
+        acc[mi][ni] = J::TRANS ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[ni], af[mi], acc[mi][ni], 0, 0, 0,
+                                                                                sb[ni], 0, sa[mi])
+                               : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], 0, 0, 0,
+                                                                                sa[mi], 0, sb[ni]);
   }
 }
 
@@ -253,6 +255,7 @@ struct JGateUp {
   using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
+  static constexpr bool TRANS = false, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
@@ -402,6 +405,7 @@ struct JDown {
   using Ld = typename std::conditional<MX, LMx, LMnB>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
+  static constexpr bool TRANS = false, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
@@ -509,6 +513,7 @@ struct JDa {
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, REG = !MX;  // the fp8 B1 is faster with direct-to-LDS loads
+  static constexpr bool TRANS = false, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
@@ -623,6 +628,7 @@ struct JDx {
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, REG = true;
+  static constexpr bool TRANS = false, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
@@ -756,7 +762,8 @@ struct JWgrad {
   // a.order lists the experts by cost, most rows first, and a.order[El] = 1, when
   // their loads are skewed enough for serpentine rounds to pay; else it is the
   // identity, a.order[El] = 0, and the items go out in contiguous XCD ranges.
-  static constexpr bool DYN = true, REG = false;
+  // the accumulators hold C^T; the epilogue writes them as bf16 row bands (band_store)
+  static constexpr bool DYN = true, REG = false, TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return sload(a.order + a.El) != 0; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
@@ -837,22 +844,30 @@ struct JWgrad {
       }
     }
   }
+  // The transposed accumulator blocks become bf16 row chunks (trans_chunks) and leave
+  // through the wave's LDS band (band_store), 8 lanes to a 128-byte row segment.
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
     const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
-    const int e = p.e, m0 = p.m0, n0 = p.n0;
-    // the tile's first output row in dW_down, or in dW_gate and dW_up (uniform); a lane's
-    // columns are the same in every row it writes, so its matrix is chosen once
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+    // the tile's first output row in dW_down, or in dW_gate and dW_up (uniform)
     const uint32_t ld = WHICH == 0 ? (uint32_t)a.H : (uint32_t)a.I;
-    const size_t row0 = ((size_t)e * M + m0) * ld;
-    const int lane = threadIdx.x & 63, wn = (int)((threadIdx.x >> 6) / WM);
-    const int nl = n0 + wn * WCOLS + (lane % EP_LPR) * 8;
-    bf16_t* const lb = WHICH == 0 ? a.dwd + row0 + nl : (nl < a.I ? a.dwg + row0 + nl : a.dwu + row0 + (nl - a.I));
-    epilogue_rows<!MX>(stage, acc, [&](int rt, int ct, const float (&vv)[8], int) {
-      const int mm = m0 + rt, n = n0 + ct;
-      if (mm >= M || n >= N) return;
-      // weight gradients are not read again by this pass: streaming stores
-      __builtin_nontemporal_store(pack8(vv), reinterpret_cast<i32x4*>(lb + (uint32_t)rt * ld));
-    });
+    const size_t row0 = ((size_t)p.e * M + p.m0) * ld;
+    bf16_t* const wreg = reinterpret_cast<bf16_t*>(stage) + wv * BAND_ELEMS;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      i32x4 ch[NI][2];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) trans_chunks(acc[mi][ni], ch[ni]);
+      const int rb = wm * WROWS + mi * 32;   // the band's first row in the tile
+      band_store(wreg, ch, [&](int rr, int cw, i32x4 v) {
+        const int rt = rb + rr, n = p.n0 + wn * WCOLS + cw;
+        if (p.m0 + rt >= M || n >= N) return;
+        bf16_t* dst = WHICH == 0 ? a.dwd + row0 + n : (n < a.I ? a.dwg + row0 + n : a.dwu + row0 + (n - a.I));
+        // weight gradients are not read again by this pass: streaming stores
+        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(dst + (uint32_t)rt * ld));
+      });
+    }
   }
 };
 

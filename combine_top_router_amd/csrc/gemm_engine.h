@@ -160,7 +160,9 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const bf16_t* s, int base, int kk, 
   return out;
 }
 
-// The bf16 MFMAs of one stage for a job J (J::A_KMAJ, J::B_KMAJ, J::ncol).
+// The bf16 MFMAs of one stage for a job J (J::A_KMAJ, J::B_KMAJ, J::ncol).  With J::TRANS
+// the two fragments enter the MFMA in swapped roles, so that each 32x32 accumulator block
+// holds the transpose of its block of C (see trans_chunks).
 template <class J>
 __device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, int wm, int wn) {
   const bf16_t* As = st;
@@ -179,8 +181,67 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, 
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = J::TRANS ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
   }
+}
+
+// A transposed accumulator block as bf16 row chunks.  The 32x32 MFMA leaves row
+// 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32 of its result in register r of lane l;
+// for a block accumulated with swapped operands (J::TRANS) that result is C^T, so lane l
+// holds row l % 32 of C and, in registers 4q .. 4q + 3, its columns 8q + 4 (l / 32) .. + 3.
+// Packed to bf16 pairs, lanes l and l + 32 trade halves with v_permlane32_swap (which
+// swaps lanes 32..63 of its first operand with lanes 0..31 of its second), after which
+// lane l holds two 16-byte chunks of its row: chunk s = columns 16 s + 8 (l / 32) .. + 7.
+__device__ __forceinline__ void trans_chunks(const f32x16& a, i32x4 (&out)[2]) {
+  uint32_t d[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    d[q][0] = pk_bf16(a[4 * q], a[4 * q + 1]);
+    d[q][1] = pk_bf16(a[4 * q + 2], a[4 * q + 3]);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const auto r = __builtin_amdgcn_permlane32_swap(d[2 * s][c], d[2 * s + 1][c], false, false);
+      d[2 * s][c] = r[0];
+      d[2 * s + 1][c] = r[1];
+    }
+    out[s] = i32x4{(int)d[2 * s][0], (int)d[2 * s][1], (int)d[2 * s + 1][0], (int)d[2 * s + 1][1]};
+  }
+}
+
+// One 32-row band (accumulator block row mi) of a wave's sub-tile, given as trans_chunks
+// output ch[ni][s] (lane l: row l % 32, 16-byte chunk 4 ni + 2 s + l / 32 of the row's
+// WCOLS columns), passes through the wave's own LDS region [32][WCOLS] bf16, chunk c of
+// row r stored at c ^ (r & 7) (the 8 lanes of each 128-byte LDS access phase then touch
+// 8 distinct chunks), so that afterwards 8 consecutive lanes hold the 8 chunks of one
+// row: store(row_in_band, column_in_wave, chunk) is called for rows lane / 8 + 8 j,
+// j = 0..3, and a store instruction writes 8 whole 128-byte row segments.
+static_assert(WCOLS == 64, "a band row is 8 chunks of 16 bytes");
+constexpr int BAND_ELEMS = 32 * WCOLS;  // per wave
+static_assert(NW * BAND_ELEMS <= STAGE_ELEMS, "the bands of all waves fit in one ring stage");
+template <class F>
+__device__ __forceinline__ void band_store(bf16_t* wreg, const i32x4 (&ch)[NI][2], F&& store) {
+  const int lane = threadIdx.x & 63, r = lane & 31;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = ni * 4 + 2 * s + (lane >> 5);
+      *reinterpret_cast<i32x4*>(wreg + r * WCOLS + ((c ^ (r & 7)) << 3)) = ch[ni][s];
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  i32x4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rr = (lane >> 3) + 8 * j, cc = lane & 7;
+    v[j] = *reinterpret_cast<const i32x4*>(wreg + rr * WCOLS + ((cc ^ (rr & 7)) << 3));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) store((lane >> 3) + 8 * j, (lane & 7) * 8, v[j]);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is free for the next band
 }
 
 __device__ __forceinline__ void zero_acc(Acc& acc) {
@@ -285,8 +346,9 @@ __device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, S sc, 
       done = cs;
       cs = cs == NSTAGE - 1 ? 0 : cs + 1;
     }
-    // every wave is done with the stage just read: stage the results there
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // every wave is done with the stage just read: stage the results there (a job whose
+    // epilogue writes from registers alone, !J::EPI_LDS, needs neither)
+    if constexpr (J::EPI_LDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     job.epilogue(cur, acc, reinterpret_cast<float*>(lds + done * STAGE_ELEMS));
     zero_acc(acc);
     if (!more) break;
@@ -351,7 +413,7 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
     issue(cs == 0 ? NSTAGE - 1 : cs - 1);  // (position + DEPTH) % NSTAGE
     cs = cs == NSTAGE - 1 ? 0 : cs + 1;
     if (++kc < lc) continue;
-    asm volatile("s_barrier" ::: "memory");  // the compute waves' epilogue barrier
+    if constexpr (J::EPI_LDS) asm volatile("s_barrier" ::: "memory");  // the compute waves' epilogue barrier
     if (!has_nxt) break;
     cur = nxt;
     vc = vn;
@@ -403,7 +465,7 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
 #pragma unroll
   for (int r = 0; r < REG_AHEAD; ++r) load_next(sl[r]);  // positions DEPTH .. DEPTH + REG_AHEAD - 1
   auto position = [&](int c, Slot& t) {
-    if (c > 0 && c % len == 0) asm volatile("s_barrier" ::: "memory");  // the previous tile's epilogue barrier
+    if (J::EPI_LDS && c > 0 && c % len == 0) asm volatile("s_barrier" ::: "memory");  // the previous tile's epilogue barrier
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // t's loads are the oldest in flight: the other slots' may still fly
     t.template ready<(REG_AHEAD - 1) * P::NLOAD>();
@@ -428,7 +490,7 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
   // values before the load has landed
 #pragma unroll
   for (int r = 0; r < REG_AHEAD; ++r) sl[r].template ready<0>();
-  asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
+  if constexpr (J::EPI_LDS) asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
 }
 
 template <class J>
