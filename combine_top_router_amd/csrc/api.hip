@@ -315,6 +315,32 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
   return hip_status(e, __func__);
 }
 
+int moe_dispatch_noscratch(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* row_src, int32_t* row_of, void* xp, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE(counts);
+  REQUIRE(offsets);
+  if (shape->T > 0) {
+    REQUIRE(topk_idx);
+    REQUIRE(row_src);
+    REQUIRE(row_of);
+    if (xp) REQUIRE(x);
+  }
+  const int64_t TK = (int64_t)shape->T * shape->k;
+  const int64_t nchunks = ceil_div(TK, index_chunk(TK, shape->e_local));
+  if (nchunks * shape->e_local > kStaticHistInts)
+    return fail(MOE_EUNSUPPORTED, "%s: the index needs %lld histogram entries, past the static buffer's %d",
+                __func__, (long long)(nchunks * shape->e_local), kStaticHistInts);
+  int32_t* hist = nullptr;
+  hipError_t e = static_hist_scratch(&hist);
+  if (e != hipSuccess) return hip_status(e, __func__);
+  hipStream_t st = (hipStream_t)stream;
+  e = launch_index(*shape, topk_idx, counts, offsets, row_src, row_of, hist, st);
+  if (e == hipSuccess && xp && shape->T > 0) e = launch_gather(*shape, x, offsets, row_src, xp, st);
+  return hip_status(e, __func__);
+}
+
 int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t* offsets,
             const int32_t* row_src, const float* topk_w, const void* w_gate, const void* w_up,
             const void* w_down, void* yp, void* saved, void* scratch, void* stream) {

@@ -90,6 +90,11 @@ inline int index_chunk(int64_t TK, int El) {
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// moe_dispatch_noscratch: the size of its static chunk-histogram buffer (int32 entries),
+// and the device address of the current GPU's copy
+constexpr int kStaticHistInts = 32768;
+hipError_t static_hist_scratch(int32_t** out);
+
 // Opt-in per-kernel timing of the calling host thread (moe_timing_enable): a pair of
 // HIP events recorded on the launch stream around each kernel.
 void ktimer_begin(const char* name, hipStream_t st);

@@ -11,9 +11,39 @@
 // every expert group, and the counts and offsets), then ranks its slots with wavefront
 // ballots (no atomic ordering), so the row order is deterministic: expert-major, then
 // token-ascending.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
+
+// Scratch of moe_dispatch_noscratch (for callers that cannot allocate): the chunk
+// histograms of the index build, kStaticHistInts int32 at most (index_chunk keeps
+// nchunks * El <= 32768 for every valid shape).  One copy per GPU, shared by every call
+// on that GPU; k_hist writes every entry that k_place then reads, so nothing needs
+// clearing between calls.
+static __device__ __align__(256) int32_t scratch[kStaticHistInts];
+
+// The device address of this GPU's copy of `scratch`, looked up once per device with that
+// device current (the host-side name is not a device address).
+hipError_t static_hist_scratch(int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 namespace {
 

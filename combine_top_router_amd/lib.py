@@ -11,7 +11,7 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_BWD_SAME", "MOE_BWD_MXFP8", "MOE_FWD_SAME", "MOE_FWD_MXFP8",
     "MoeShape", "MoeError", "load", "lib_path", "EXPORTS",
     "moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route_topk",
-    "moe_dispatch", "moe_fwd", "moe_combine", "moe_bwd", "moe_route_topk_bwd",
+    "moe_dispatch", "moe_dispatch_noscratch", "moe_fwd", "moe_combine", "moe_bwd", "moe_route_topk_bwd",
     "moe_mx_quantize", "moe_mx_quantize_cols", "moe_timing_enable", "moe_timing_read",
     "moe_router_fwd", "moe_router_bwd",
 ]
@@ -50,6 +50,7 @@ _SIG = {
     "moe_workspace_bytes": (ctypes.c_int, [_S, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route_topk": (ctypes.c_int, [_S, _P, _P, _P, _P]),
     "moe_dispatch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_noscratch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_fwd": (ctypes.c_int, [_S] + [_P] * 12),
     "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P]),
     "moe_bwd": (ctypes.c_int, [_S] + [_P] * 18),
@@ -112,6 +113,11 @@ def moe_route_topk(shape, logits, topk_idx, topk_w, stream=0):
 def moe_dispatch(shape, topk_idx, x, counts, offsets, row_src, row_of, xp, scratch, stream=0):
     _check(load().moe_dispatch(ctypes.byref(shape), topk_idx, x, counts, offsets, row_src, row_of, xp,
                                scratch, stream), "moe_dispatch")
+
+
+def moe_dispatch_noscratch(shape, topk_idx, x, counts, offsets, row_src, row_of, xp, stream=0):
+    _check(load().moe_dispatch_noscratch(ctypes.byref(shape), topk_idx, x, counts, offsets, row_src, row_of, xp,
+                                         stream), "moe_dispatch_noscratch")
 
 
 def moe_fwd(shape, x, xp, offsets, row_src, topk_w, w_gate, w_up, w_down, yp, saved, scratch, stream=0):

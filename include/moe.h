@@ -122,6 +122,20 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                  int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* row_of,
                  void* xp, void* scratch, void* stream);
 
+/* moe_dispatch without a scratch argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results as moe_dispatch (same arguments apart from scratch), with
+ * the index build's chunk histograms in a static device buffer of 32768 int32 (128 KiB)
+ * that the library holds on every GPU it runs on until the process ends.  That buffer
+ * holds the histograms of every valid shape (their count is at most 32768 by
+ * construction); a shape needing more would return MOE_EUNSUPPORTED.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine); its first call on a device looks
+ * up that device's copy of the buffer.  All calls on one GPU share the buffer: calls that
+ * overlap in time on one GPU (e.g. on two streams) race and must not be issued. */
+int moe_dispatch_noscratch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
+                           int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t* row_of,
+                           void* xp, void* stream);
+
 /* Expert MLP forward (Prime Mega MoE pages: two expert linear layers with SwiGLU
  * between them; NVIDIA article Figure 3: two grouped GEMMs over the variable-length
  * expert groups).  For each local row r of expert e and token t = row_src[r] / k:
