@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -35,12 +36,34 @@ FLAGS = [
 ]
 
 
+# Kernels whose load waves stage operands in registers through inline-asm loads (jobs with
+# REG = true).  The compiler sees such a load's destination as written at issue, so a
+# spill in the kernel could copy, or a reuse overwrite, a register whose load is still in
+# flight: these kernels must not spill at all.
+REG_KERNELS = ("k_fwd_gateupILb0E", "k_fwd_downILb0E", "k_bwd_daILb0E", "k_bwd_dxILb0E")
+
+
+def _check_no_spill(src: str, remarks: str) -> None:
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and any(k in name for k in REG_KERNELS) and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: register-staged kernel {name} spills {m.group(1)} bytes per lane")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if src == "gemm.hip" else []
+    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
+    if extra:
+        _check_no_spill(src, r.stderr)
     return obj
 
 

@@ -255,7 +255,7 @@ struct JGateUp {
   using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
-  static constexpr bool TRANS = false, EPI_LDS = true;
+  static constexpr bool TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
@@ -307,66 +307,59 @@ struct JGateUp {
     }
     p.bstep = (size_t)BK * a.I;
   }
-  // lane takes 8 intermediate columns of one row, G from the gate blocks and U from the
-  // up blocks (same columns), and writes 16-byte chunks of G, U and A
+  // The accumulators hold C^T (trans_chunks): gate block 0 and up block 1 of a band hold
+  // G and U of the same elements, so A = silu(G) U is formed in registers (MX: and its
+  // row-wise codes, from the fp32 values); G|U and A leave through the wave's LDS band.
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
-    constexpr int LPR = WCOLS / 16;          // lanes per row
-    constexpr int PASSES = EP_ROWS * LPR / 64;  // passes over a staged 16-row piece
-    static_assert(!MX || LPR * 8 == 32, "the lanes of a row span one MX block of A");
-    float* wsm = stage + wv * EP_ROWS * EP_LD;
+    static_assert(NI == 2, "one gate and one up block per band");
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+    bf16_t* const wreg = reinterpret_cast<bf16_t*>(stage) + wv * BAND_ELEMS;
     const uint32_t I2 = 2u * (uint32_t)a.I;
     // the tile's first row (uniform); lanes add 32-bit offsets.  G|U is not kept when the
     // backward recomputes it.
     const bool keep_gu = a.gu != nullptr;
     bf16_t* const gub = keep_gu ? a.gu + (size_t)p.t.rs * I2 : nullptr;
     bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
+    const int colw = p.n0 + wn * (WCOLS / 2);  // the wave's first intermediate column
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rb = wm * WROWS + mi * 32;   // the band's first row in the tile
+      f32x16 av;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        stage_quarter(wsm, acc, mi, h, lane);
-#pragma unroll
-        for (int j = 0; j < PASSES; ++j) {
-          const int rr = lane / LPR + (64 / LPR) * j, cc = (lane % LPR) * 8;
-          const int rt = wm * WROWS + mi * 32 + h * 16 + rr;
-          float g[8], u[8], av[8];
-          read8(wsm + rr * EP_LD + cc, g);
-          read8(wsm + rr * EP_LD + WCOLS / 2 + cc, u);
-          if (j == PASSES - 1) staging_done();
-          const int col = p.n0 + wn * (WCOLS / 2) + cc;
-          if constexpr (MX) {
-            // the down GEMM's row-wise codes of A, quantised here from the fp32 values: the
-            // LPR lanes of a row hold one 32-column block (all of it inside or outside I)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
-            float am = 0.f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(av[q]));
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
-            const int X = mx_scale_exp(am);
-            if (rt < p.t.cnt && col < a.I) {
-              const size_t r = (size_t)(p.t.rs + rt);
-              *reinterpret_cast<uint2*>(m.q_a + r * a.I + col) =
-                  make_uint2(e4m3_pack4(av[0], av[1], av[2], av[3], X), e4m3_pack4(av[4], av[5], av[6], av[7], X));
-              if (lane % LPR == 0) m.s_a[r * (a.I / 32) + col / 32] = (uint8_t)(X + 127);
-            }
-          }
-          if (rt < p.t.cnt && col < a.I) {
-            const uint32_t o = (uint32_t)rt * I2 + (uint32_t)col;
-            if constexpr (!MX) {
-#pragma unroll
-              for (int q = 0; q < 8; ++q) av[q] = silu_f(g[q]) * u[q];
-            }
-            if (keep_gu) {
-              *reinterpret_cast<i32x4*>(gub + o) = pack8(g);
-              *reinterpret_cast<i32x4*>(gub + o + a.I) = pack8(u);
-            }
-            *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = pack8(av);
-          }
+      for (int i = 0; i < 16; ++i) av[i] = silu_f(acc[mi][0][i]) * acc[mi][1][i];
+      if constexpr (MX) {
+        // the down GEMM's row-wise codes of A: the wave's 32 columns are one MX block
+        int X;
+        const i32x4 codes = mx_row_codes(av, X);
+        const int rt = rb + (lane & 31);
+        if (rt < p.t.cnt && colw < a.I) {
+          const size_t r = (size_t)(p.t.rs + rt);
+          *reinterpret_cast<i32x4*>(m.q_a + r * a.I + colw + 16 * (lane >> 5)) = codes;
+          if (lane < 32) m.s_a[r * (a.I / 32) + colw / 32] = (uint8_t)(X + 127);
         }
       }
+      if (keep_gu) {
+        // G and U (I columns apart in each G|U row) as two one-block bands
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          i32x4 ch[1][2];
+          trans_chunks(acc[mi][g], ch[0]);
+          band_store(wreg, ch, [&](int rr, int cb, i32x4 v) {
+            const int rt = rb + rr, col = colw + cb;
+            if (rt < p.t.cnt && col < a.I)
+              *reinterpret_cast<i32x4*>(gub + ((uint32_t)rt * I2 + (uint32_t)col + (g ? (uint32_t)a.I : 0u))) = v;
+          });
+        }
+      }
+      i32x4 ca[1][2];
+      trans_chunks(av, ca[0]);
+      band_store(wreg, ca, [&](int rr, int cb, i32x4 v) {
+        const int rt = rb + rr, col = colw + cb;
+        if (rt < p.t.cnt && col < a.I)
+          *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = v;
+      });
+    }
   }
 };
 
@@ -405,7 +398,7 @@ struct JDown {
   using Ld = typename std::conditional<MX, LMx, LMnB>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
-  static constexpr bool TRANS = false, EPI_LDS = true;
+  static constexpr bool TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
@@ -448,26 +441,31 @@ struct JDown {
     }
     p.bstep = (size_t)BK * a.H;
   }
+  // C^T accumulators: lane l holds row l % 32 of each band, so it scales by that row's
+  // routing weight alone, then the band leaves through LDS (band_store).
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
-    // the routing weights of the lane's rows, fetched before the staging starts
-    const int lane = threadIdx.x & 63, wm = (int)((unsigned)(threadIdx.x >> 6) % WM);
-    float wr[EP_LANE_ROWS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+    bf16_t* const wreg = reinterpret_cast<bf16_t*>(stage) + wv * BAND_ELEMS;
+    float wr[MI];
 #pragma unroll
-    for (int i = 0; i < EP_LANE_ROWS; ++i) {
-      const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
-      wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rt = min(wm * WROWS + mi * 32 + (lane & 31), p.t.cnt - 1);
+      wr[mi] = a.topk_w[a.row_src[p.t.rs + rt]];
     }
     bf16_t* const yb = a.yp + (size_t)p.t.rs * a.H;  // the tile's first row
-    epilogue_rows<true>(stage, acc, [&](int rt, int ct, const float (&v)[8], int slot) {
-      const int col = p.n0 + ct;
-      if (rt < p.t.cnt && col < a.H) {
-        const float w = wr[slot];
-        float o[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = w * v[q];
-        *reinterpret_cast<i32x4*>(yb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = pack8(o);
-      }
-    });
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rb = wm * WROWS + mi * 32;
+      i32x4 ch[NI][2];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) trans_chunks(acc[mi][ni] * wr[mi], ch[ni]);
+      band_store(wreg, ch, [&](int rr, int cb, i32x4 v) {
+        const int rt = rb + rr, col = p.n0 + wn * WCOLS + cb;
+        if (rt < p.t.cnt && col < a.H)
+          *reinterpret_cast<i32x4*>(yb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = v;
+      });
+    }
   }
 };
 
@@ -520,6 +518,7 @@ struct JDa {
   MxArgs m;
   int NT, nparts;
   uint8_t* scring;
+  float* wrow;  // LDS [NW][WROWS]: the routing weights of each compute wave's rows
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
@@ -560,20 +559,20 @@ struct JDa {
     const bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
     bf16_t* const dgub = a.dgu + (size_t)p.t.rs * I2;
     bf16_t* const awb = a.aw + (size_t)p.t.rs * a.I;
-    // the routing weights of the lane's rows, fetched before the staging starts
-    float wr[EP_LANE_ROWS];
-#pragma unroll
-    for (int i = 0; i < EP_LANE_ROWS; ++i) {
-      const int rt = min(ep_row(i, lane, wm), p.t.cnt - 1);
-      wr[i] = a.topk_w[a.row_src[p.t.rs + rt]];
-    }
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int slot) {
+    // the routing weights of the wave's WROWS rows, one per lane, into the wave's LDS slots
+    // before the staging starts (read back by row: no per-lane array indexed in the
+    // rolled row loop, which would live in scratch memory)
+    static_assert(WROWS <= 64, "one routing weight per lane");
+    const int wv = threadIdx.x >> 6;
+    if (lane < WROWS)
+      wrow[wv * WROWS + lane] = a.topk_w[a.row_src[p.t.rs + min(wm * WROWS + lane, p.t.cnt - 1)]];
+    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int) {
       const int col = p.n0 + ct;
       const bool ok = rt < p.t.cnt && col < a.I;
       float part = 0.f;
       if (ok) {
         const uint32_t og = (uint32_t)rt * I2 + (uint32_t)col, oa = (uint32_t)rt * (uint32_t)a.I + (uint32_t)col;
-        const float w = wr[slot];
+        const float w = wrow[wv * WROWS + (rt - wm * WROWS)];
         // two columns at a time, straight from and back to packed bf16 pairs
         __builtin_amdgcn_sched_barrier(0);
         const i32x4 gw = *reinterpret_cast<const i32x4*>(gub + og);
@@ -616,7 +615,8 @@ template <bool MX>
 __global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, MxArgs m, int nparts) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
-  JDa<MX> job{a, m, (int)ceil_div(a.I, BN), nparts, scring};
+  __shared__ float wrow[NW * WROWS];
+  JDa<MX> job{a, m, (int)ceil_div(a.I, BN), nparts, scring, wrow};
   run_stream(job, lds);
 }
 
@@ -627,8 +627,8 @@ struct JDx {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
-  static constexpr bool DYN = false, REG = true;
-  static constexpr bool TRANS = false, EPI_LDS = true;
+  static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (its compute side spills)
+  static constexpr bool TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
@@ -667,13 +667,24 @@ struct JDx {
       }
     }
   }
+  // C^T accumulators leave as bf16 row bands (trans_chunks, band_store)
   __device__ __forceinline__ void epilogue(const Tile& p, const Acc& acc, float* stage) const {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+    bf16_t* const wreg = reinterpret_cast<bf16_t*>(stage) + wv * BAND_ELEMS;
     bf16_t* const xb = a.dxp + (size_t)p.t.rs * a.H;  // the tile's first row
-    epilogue_rows<!MX>(stage, acc, [&](int rt, int ct, const float (&v)[8], int) {
-      const int col = p.n0 + ct;
-      if (rt < p.t.cnt && col < a.H)
-        *reinterpret_cast<i32x4*>(xb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = pack8(v);
-    });
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rb = wm * WROWS + mi * 32;
+      i32x4 ch[NI][2];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) trans_chunks(acc[mi][ni], ch[ni]);
+      band_store(wreg, ch, [&](int rr, int cb, i32x4 v) {
+        const int rt = rb + rr, col = p.n0 + wn * WCOLS + cb;
+        if (rt < p.t.cnt && col < a.H)
+          *reinterpret_cast<i32x4*>(xb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = v;
+      });
+    }
   }
 };
 

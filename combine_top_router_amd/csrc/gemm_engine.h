@@ -213,35 +213,66 @@ __device__ __forceinline__ void trans_chunks(const f32x16& a, i32x4 (&out)[2]) {
 }
 
 // One 32-row band (accumulator block row mi) of a wave's sub-tile, given as trans_chunks
-// output ch[ni][s] (lane l: row l % 32, 16-byte chunk 4 ni + 2 s + l / 32 of the row's
-// WCOLS columns), passes through the wave's own LDS region [32][WCOLS] bf16, chunk c of
-// row r stored at c ^ (r & 7) (the 8 lanes of each 128-byte LDS access phase then touch
-// 8 distinct chunks), so that afterwards 8 consecutive lanes hold the 8 chunks of one
-// row: store(row_in_band, column_in_wave, chunk) is called for rows lane / 8 + 8 j,
-// j = 0..3, and a store instruction writes 8 whole 128-byte row segments.
-static_assert(WCOLS == 64, "a band row is 8 chunks of 16 bytes");
+// output ch[b][s] of NB 32-column blocks (lane l: row l % 32, 16-byte chunk
+// 4 b + 2 s + l / 32 of the row's NCH = 4 NB chunks), passes through the wave's own LDS
+// region [32][8 NCH] bf16 so that afterwards NCH consecutive lanes hold the NCH chunks of
+// one row: store(row_in_band, column_in_band, chunk) is called for rows lane / NCH +
+// (64 / NCH) j, and one store instruction writes whole row segments of 16 NCH bytes.
+// Chunk c of row r sits at c ^ ((r / RPW) % NCH), RPW = rows per 256-byte bank window,
+// so that the 16 lanes of each 256-byte access phase hit 16 distinct 16-byte slots, for
+// the writes (16 rows, one chunk each) and the reads (16 / NCH rows, all their chunks) alike.
+static_assert(WCOLS == 64, "a band row holds at most 8 chunks of 16 bytes");
 constexpr int BAND_ELEMS = 32 * WCOLS;  // per wave
 static_assert(NW * BAND_ELEMS <= STAGE_ELEMS, "the bands of all waves fit in one ring stage");
-template <class F>
-__device__ __forceinline__ void band_store(bf16_t* wreg, const i32x4 (&ch)[NI][2], F&& store) {
+template <int NB, class F>
+__device__ __forceinline__ void band_store(bf16_t* wreg, const i32x4 (&ch)[NB][2], F&& store) {
+  constexpr int NCH = 4 * NB, W = 8 * NCH, RPW = 16 / NCH;
+  static_assert(NB == 1 || NB == 2, "one or two 32-column blocks per band row");
   const int lane = threadIdx.x & 63, r = lane & 31;
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int c = ni * 4 + 2 * s + (lane >> 5);
-      *reinterpret_cast<i32x4*>(wreg + r * WCOLS + ((c ^ (r & 7)) << 3)) = ch[ni][s];
+      const int c = b * 4 + 2 * s + (lane >> 5);
+      *reinterpret_cast<i32x4*>(wreg + r * W + ((c ^ ((r / RPW) & (NCH - 1))) << 3)) = ch[b][s];
     }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  i32x4 v[4];
+  // read j covers rows lane / NCH + (64 / NCH) j; its swizzle term ((rr / RPW) % NCH)
+  // is the lane's own term XOR (64 / NCH / RPW) j mod NCH, so every read addresses from
+  // one per-lane base
+  i32x4 v[NCH / 2];
+  const int rr0 = lane / NCH, cc = lane % NCH;
+  const int sw0 = (rr0 / RPW) & (NCH - 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rr = (lane >> 3) + 8 * j, cc = lane & 7;
-    v[j] = *reinterpret_cast<const i32x4*>(wreg + rr * WCOLS + ((cc ^ (rr & 7)) << 3));
+  for (int j = 0; j < NCH / 2; ++j) {
+    constexpr int STEP = 64 / NCH / RPW;  // swizzle increment per read (4 for NCH = 8 and 4)
+    static_assert((64 / NCH) % RPW == 0, "whole bank windows per read");
+    const int sw = (sw0 + STEP * j) & (NCH - 1);
+    v[j] = *reinterpret_cast<const i32x4*>(wreg + (rr0 + (64 / NCH) * j) * W + ((cc ^ sw) << 3));
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) store((lane >> 3) + 8 * j, (lane & 7) * 8, v[j]);
+  for (int j = 0; j < NCH / 2; ++j) store(lane / NCH + (64 / NCH) * j, (lane % NCH) * 8, v[j]);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the region is free for the next band
+}
+
+// The row-wise MXFP8 codes of a transposed accumulator block's 32 columns of row l % 32
+// (the rows' values x in fp32, in the trans_chunks layout): lanes l and l + 32 together
+// hold the row's 32 values, so the block's maximum takes one v_permlane32_swap; the
+// codes (E4M3 of x / 2^X, X the block's scale exponent) are rearranged as trans_chunks
+// does, after which lane l holds codes of columns 16 (l / 32) .. + 15 of its row.
+__device__ __forceinline__ i32x4 mx_row_codes(const f32x16& x, int& X) {
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+  am = fmaxf(am, __uint_as_float((threadIdx.x & 32) ? pr[0] : pr[1]));
+  X = mx_scale_exp(am);
+  uint32_t e[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) e[q] = e4m3_pack4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3], X);
+  const auto s02 = __builtin_amdgcn_permlane32_swap(e[0], e[2], false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(e[1], e[3], false, false);
+  return i32x4{(int)s02[0], (int)s02[1], (int)s13[0], (int)s13[1]};
 }
 
 __device__ __forceinline__ void zero_acc(Acc& acc) {
