@@ -19,47 +19,53 @@ namespace {
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// Row-wise: 4 lanes per 32-element block, 8 elements per lane.
-// rows_fixed < 0 (or a gather) means the row count is offsets[El]; with src2, columns
-// >= K / 2 of row r come from src2 (two [rows, K / 2] matrices side by side).
+// Row-wise: one wave per row, in passes of 512 columns per 64 lanes: lane l takes the
+// 8-element groups l + 64 i (8 consecutive columns each), so the 4 lanes 4j .. 4j + 3 of
+// a pass hold one 32-element block.  A lane issues the loads of up to RG passes (RG x 16
+// bytes) before it quantises any of them.  rows_fixed < 0 (or a gather) means the row
+// count is offsets[El]; with src2, columns >= K / 2 of row r come from src2 (two
+// [rows, K / 2] matrices side by side).
+constexpr int RG = 8;
 __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src, const bf16_t* __restrict__ src2,
                                                  int ld, const int32_t* __restrict__ row_src, int k,
                                                  const int32_t* __restrict__ offsets, int El, int64_t rows_fixed,
                                                  int K, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int64_t rows = (row_src || rows_fixed < 0) ? (int64_t)offsets[El] : rows_fixed;
-  const int gpr = K / 8;                                    // 8-element groups per row
-  const int64_t total = rows * gpr;
   const int lane = threadIdx.x & 63;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t g0 = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63); g0 < total; g0 += stride) {
-    const int64_t g = g0 + lane;
-    const bool ok = g < total;
-    float v[8];
-    int64_t r = 0;
-    int c = 0;
-    if (ok) {
-      r = g / gpr;
-      c = (int)(g - r * gpr) * 8;
-      const int64_t sr = row_src ? (int64_t)(row_src[r] / k) : r;
-      const bf16_t* p = src2 && c >= K / 2 ? src2 + sr * ld + (c - K / 2) : src + sr * ld + c;
-      const i32x4 u = *reinterpret_cast<const i32x4*>(p);
+  const int half = K / 2;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += (int64_t)gridDim.x * 4) {
+    const int64_t sr = row_src ? (int64_t)(row_src[r] / k) : r;
+    const bf16_t* const p1 = src + sr * ld;
+    const bf16_t* const p2 = src2 ? src2 + sr * ld - half : nullptr;
+    uint8_t* const qr = q + r * K;
+    uint8_t* const sq = s + r * (K / 32);
+    for (int c0 = 0; c0 < K; c0 += 512 * RG) {
+      i32x4 u[RG];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { v[2 * j] = bf_lo((uint32_t)u[j]); v[2 * j + 1] = bf_hi((uint32_t)u[j]); }
-    } else {
+      for (int i = 0; i < RG; ++i) {
+        const int c = c0 + 512 * i + 8 * lane;
+        u[i] = i32x4{0, 0, 0, 0};
+        if (c < K) u[i] = *reinterpret_cast<const i32x4*>((p2 && c >= half ? p2 : p1) + c);
+      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.f;
-    }
-    float am = 0.f;
+      for (int i = 0; i < RG; ++i) {
+        const int c = c0 + 512 * i + 8 * lane;
+        float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
-    am = fmaxf(am, __shfl_xor(am, 1, 64));
-    am = fmaxf(am, __shfl_xor(am, 2, 64));
-    if (ok) {
-      const int X = mx_scale_exp(am);
-      const uint32_t w0 = e4m3_pack4(v[0], v[1], v[2], v[3], X);
-      const uint32_t w1 = e4m3_pack4(v[4], v[5], v[6], v[7], X);
-      *reinterpret_cast<uint2*>(q + r * K + c) = make_uint2(w0, w1);
-      if ((c & 31) == 0) s[r * (K / 32) + (c >> 5)] = (uint8_t)(X + 127);
+        for (int j = 0; j < 4; ++j) { v[2 * j] = bf_lo((uint32_t)u[i][j]); v[2 * j + 1] = bf_hi((uint32_t)u[i][j]); }
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+        am = fmaxf(am, __shfl_xor(am, 2, 64));
+        if (c < K) {   // K is a multiple of 32: a block lies wholly inside or outside the row
+          const int X = mx_scale_exp(am);
+          const uint32_t w0 = e4m3_pack4(v[0], v[1], v[2], v[3], X);
+          const uint32_t w1 = e4m3_pack4(v[4], v[5], v[6], v[7], X);
+          *reinterpret_cast<uint2*>(qr + c) = make_uint2(w0, w1);
+          if ((lane & 3) == 0) sq[c >> 5] = (uint8_t)(X + 127);
+        }
+      }
     }
   }
 }
@@ -226,7 +232,7 @@ hipError_t launch_mx_rows(const bf16_t* src, const bf16_t* src2, int ld, const i
                           const int32_t* offsets, int El, int64_t rows, int64_t rows_bound, int K, uint8_t* q,
                           uint8_t* s, const char* name, hipStream_t st) {
   if (rows_bound <= 0) return hipSuccess;
-  const int64_t blocks = ceil_div(rows_bound * (K / 8), 256);
+  const int64_t blocks = ceil_div(rows_bound, 4);   // four rows (waves) per workgroup
   const int grid = (int)(blocks < 16384 ? blocks : 16384);
   MOE_LAUNCH(name, k_mx_rows, dim3(grid), dim3(256), 0, st, src, src2, ld, row_src, k, offsets, El, rows, K, q, s);
   return hipGetLastError();
