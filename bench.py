@@ -106,6 +106,87 @@ def counted_traffic(workload, kernel):
     return int(m.group(1)) if m else None
 
 
+def graph_kernel_ms(step_on, stream, names, reps=40, passes=3, warmup=3):
+    """Each kernel's marginal time inside a graph replay of the step.
+
+    The step launches its kernels on one stream, so its captured graph is one chain of
+    kernel nodes in launch order (`names`, from the library's timing records).  For
+    j = 1..n the chain is captured again and cut after its j-th node; each cut graph is
+    replayed `reps` times between two events on `stream`, in `passes` interleaved passes
+    over j (median per j), and kernel j's time is the difference of the j- and
+    (j-1)-node medians.  The prefixes run the same kernels on the buffers of earlier
+    full steps, so each reads valid data."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)   # torch's HIP runtime, already loaded
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sh = vp(stream.cuda_stream)
+
+    def ck(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: hipError_t {rc}")
+
+    def chain(graph):
+        n = sz(1)
+        node = (vp * 1)()
+        ck(hip.hipGraphGetRootNodes(graph, node, ctypes.byref(n)), "hipGraphGetRootNodes")
+        nodes = [node[0]] if n.value == 1 else []
+        while nodes:
+            n = sz(0)
+            ck(hip.hipGraphNodeGetDependentNodes(vp(nodes[-1]), None, ctypes.byref(n)), "dependents")
+            if n.value == 0:
+                break
+            if n.value != 1:
+                raise RuntimeError("the captured step is not one chain")
+            nxt = (vp * 1)()
+            ck(hip.hipGraphNodeGetDependentNodes(vp(nodes[-1]), nxt, ctypes.byref(n)), "dependents")
+            nodes.append(nxt[0])
+        return nodes
+
+    def prefix(j):
+        graph, gexec = vp(), vp()
+        torch.cuda.synchronize()
+        ck(hip.hipStreamBeginCapture(sh, 1), "hipStreamBeginCapture")   # thread-local mode
+        try:
+            with torch.cuda.stream(stream):
+                step_on()
+        finally:
+            ck(hip.hipStreamEndCapture(sh, ctypes.byref(graph)), "hipStreamEndCapture")
+        try:
+            nodes = chain(graph)
+            if len(nodes) != len(names):
+                raise RuntimeError(f"captured {len(nodes)} kernels, the step launches {len(names)}")
+            for node in reversed(nodes[j:]):
+                ck(hip.hipGraphDestroyNode(vp(node)), "hipGraphDestroyNode")
+            ck(hip.hipGraphInstantiateWithFlags(ctypes.byref(gexec), graph, ctypes.c_ulonglong(0)),
+               "hipGraphInstantiateWithFlags")
+        finally:
+            hip.hipGraphDestroy(graph)
+        return gexec
+
+    def replay_ms(gexec):
+        for _ in range(warmup):
+            ck(hip.hipGraphLaunch(gexec, sh), "hipGraphLaunch")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            ck(hip.hipGraphLaunch(gexec, sh), "hipGraphLaunch")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    execs = []
+    try:
+        for j in range(1, len(names) + 1):
+            execs.append(prefix(j))
+        runs = [[replay_ms(g) for g in execs] for _ in range(passes)]
+    finally:
+        for g in execs:
+            hip.hipGraphExecDestroy(g)
+    t = [0.0] + [float(np.median([r[j] for r in runs])) for j in range(len(names))]
+    return [(names[j], t[j + 1] - t[j]) for j in range(len(names))], t[-1]
+
+
 def cpu_baseline(cfg, inp, budget_s=20.0):
     """The oracle as it stands, on the host cores, over a bounded sample: routing and
     index of all tokens, then the forward of the first n local experts (all their rows),
@@ -282,7 +363,8 @@ def main():
     cold_ms = float(np.median(cold))
     del flush
 
-    # per-kernel durations from HIP events recorded inside the library on the launch stream
+    # per-kernel durations from HIP events that each kernel's dispatch stamps (the library's
+    # opt-in timing), on the stream the kernels are launched on
     L.moe_timing_enable(True)
     per = {}
     nrep = max(3, min(args.steps, 10))
@@ -293,13 +375,22 @@ def main():
     n_fwd = len(L.moe_timing_read())
     bwd(stream)
     L.moe_timing_read()
+    order = []
     for _ in range(nrep):
         fwd(stream)
         bwd(stream)
-        for i, (name, kms) in enumerate(L.moe_timing_read()):
+        recs = L.moe_timing_read()
+        order = [name for name, _ in recs]
+        for i, (name, kms) in enumerate(recs):
             per.setdefault(name, []).append(kms)
             part_ms["fwd" if i < n_fwd else "bwd"] += kms / nrep
     L.moe_timing_enable(False)
+    # the same kernels' marginal times inside graph replays (prefixes of the captured step)
+    in_graph, graph_sum = {}, None
+    if graph is not None:
+        marg, graph_sum = graph_kernel_ms(step_on, side, order)
+        for name, gms in marg:
+            in_graph.setdefault(name, []).append(gms)
     kernels = {}
     for name, v in per.items():
         avg = float(np.mean(v))
@@ -307,6 +398,8 @@ def main():
         kernels[name] = {"ms": round(avg, 4), "launches_per_step": len(v) // nrep,
                          "GB/s": round(byts / avg / 1e6, 1) if byts else None,
                          "TFLOP/s": round(flops / avg / 1e9, 1) if flops else None}
+        if name in in_graph:
+            kernels[name]["graph_ms"] = round(float(np.mean(in_graph[name])), 4)
     gemm = {n: kernels[n] for n in GEMMS if n in kernels}
     # each GEMM against the dense MFMA peak of its own operand type (bf16 or MXFP8)
     gemm_flops = sum(kernel_work(n, cfg.T, cfg.H, cfg.I, cfg.k, R, cfg.e_local)[1] * v["launches_per_step"]
@@ -356,8 +449,12 @@ def main():
         # the expert GEMMs only: their flops over the sum of their kernel times, each kernel
         # against its own operand type's dense peak (bf16 2.5, MXFP8 5.0 PFLOP/s)
         "mfma_frac_gemms": round(gemm_flops / gemm_peak_ms / 1e9, 4),
-        "kernel_timing": "HIP events recorded by the library on the launch stream around each kernel of "
-                         f"{nrep} eagerly launched steps (mean per launch); ms_per_step is the graph replay",
+        "kernel_timing": "HIP events stamped by each kernel's own dispatch (hipExtLaunchKernel, no "
+                         f"system-scope fence) over {nrep} eagerly launched steps (mean per launch); "
+                         "ms_per_step is the graph replay",
+        "graph_kernel_timing": "each kernel's marginal time in graph replays: the step's captured chain cut "
+                               "after kernel j, minus the chain cut before it (median of 3 passes of 40 replays)",
+        "graph_prefix_ms": round(graph_sum, 4) if graph_sum is not None else None,
         "fwd_ms_kernels": round(fwd_ms, 4),
         "bwd_ms_kernels": round(bwd_ms, 4),
         "hbm_frac_combine": round(kernels["combine"]["GB/s"] / HBM_PEAK_GBS, 4) if "combine" in kernels else None,

@@ -208,20 +208,15 @@ thread_local Timing g_timing;
 }  // namespace
 
 namespace moe {
-void ktimer_begin(const char* name, hipStream_t st) {
+bool ktimer_pair(const char* name, hipStream_t st, hipEvent_t* start, hipEvent_t* stop) {
   Timing& T = g_timing;
-  if (!T.on || T.used + 2 > (int)T.pool.size()) return;
-  hipEvent_t ev = T.next();
-  hipEventRecord(ev, st);
-  T.recs.push_back({name, T.used - 1, -1});
-}
-void ktimer_end(hipStream_t st) {
-  Timing& T = g_timing;
-  if (!T.on || T.recs.empty() || T.recs.back().e1 >= 0) return;
-  hipEvent_t ev = T.next();
-  if (!ev) return;
-  hipEventRecord(ev, st);
-  T.recs.back().e1 = T.used - 1;
+  if (!T.on || T.used + 2 > (int)T.pool.size()) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+  *start = T.next();
+  *stop = T.next();
+  T.recs.push_back({name, T.used - 2, T.used - 1});
+  return true;
 }
 }  // namespace moe
 
@@ -235,7 +230,8 @@ int moe_timing_enable(int on) {
   if (on) {
     while ((int)T.pool.size() < kTimingEvents) {
       hipEvent_t ev = nullptr;
-      const hipError_t e = hipEventCreate(&ev);
+      // timestamps only: no system-scope fence (and so no cache writeback) per event
+      const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
       if (e != hipSuccess) return hip_status(e, __func__);
       T.pool.push_back(ev);
     }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "../../include/moe.h"
@@ -96,18 +97,16 @@ constexpr int kStaticHistInts = 32768;
 hipError_t static_hist_scratch(int32_t** out);
 
 // Opt-in per-kernel timing of the calling host thread (moe_timing_enable): a pair of
-// HIP events recorded on the launch stream around each kernel.
-void ktimer_begin(const char* name, hipStream_t st);
-void ktimer_end(hipStream_t st);
-struct KTimer {
-  hipStream_t st;
-  KTimer(const char* name, hipStream_t s) : st(s) { ktimer_begin(name, s); }
-  ~KTimer() { ktimer_end(st); }
-};
-#define MOE_LAUNCH(name, kernel, grid, block, shmem, st, ...)              \
-  do {                                                                     \
-    ::moe::KTimer moe_kt_(name, st);                                       \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);       \
+// HIP events handed to hipExtLaunchKernel, which stamps them with the dispatch's own
+// start and end; with timing off (and always under graph capture) the plain launch.
+bool ktimer_pair(const char* name, hipStream_t st, hipEvent_t* start, hipEvent_t* stop);
+#define MOE_LAUNCH(name, kernel, grid, block, shmem, st, ...)                               \
+  do {                                                                                      \
+    hipEvent_t moe_e0_, moe_e1_;                                                            \
+    if (::moe::ktimer_pair(name, st, &moe_e0_, &moe_e1_))                                   \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, moe_e0_, moe_e1_, 0, __VA_ARGS__); \
+    else                                                                                    \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);                      \
   } while (0)
 
 // ---- launch wrappers (defined in the .hip files) ----

@@ -248,14 +248,16 @@ int moe_mx_quantize_cols(const void* x, int32_t N, const int32_t* offsets, int32
 
 /* Opt-in kernel timing for profilers and benchmarks (no effect on results).
  * moe_timing_enable(1) makes every kernel that this host thread launches through the
- * calls above be bracketed by two HIP events recorded on the call's stream; (0) stops
- * it.  Either call discards pending records.  moe_timing_read() waits for the last
- * recorded event, writes up to `capacity` kernel names (static strings owned by the
- * library) and elapsed milliseconds in launch order, sets *count to the number of
- * kernels recorded since the last read or enable, and discards the records.  The
- * events (a pool of 4096 per host thread) are created by moe_timing_enable(1), so the
- * calls above never create one; they are reused and live until the process ends.  Kernels
- * launched after the pool is used up (without a read in between) are not recorded. */
+ * calls above carry two HIP events that the dispatch itself stamps at its start and end
+ * (hipExtLaunchKernel; events without a system-scope fence); launches on a stream under
+ * graph capture are not recorded.  (0) stops it.  Either call discards pending
+ * records.  moe_timing_read() waits for the last recorded event, writes up to
+ * `capacity` kernel names (static strings owned by the library) and elapsed
+ * milliseconds in launch order, sets *count to the number of kernels recorded since the
+ * last read or enable, and discards the records.  The events (a pool of 4096 per host
+ * thread) are created by moe_timing_enable(1), so the calls above never create one; they
+ * are reused and live until the process ends.  Kernels launched after the pool is used
+ * up (without a read in between) are not recorded. */
 int moe_timing_enable(int on);
 int moe_timing_read(int capacity, const char** names, float* ms, int* count);
 
