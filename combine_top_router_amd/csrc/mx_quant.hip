@@ -75,23 +75,26 @@ __global__ __launch_bounds__(256) void k_mx_rows(const bf16_t* __restrict__ src,
 // chunk's row sources and weights are read once into LDS and its rows staged as bf16
 // (32 KB, so several workgroups share a CU); thread t takes the 32-row block t / 128 of
 // column t % 128 into registers (applying the optional row weight in fp32), quantizes
-// it into LDS, and the workgroup then writes each column's 128 codes as one 128-byte
-// line and its four scales as one word.  With qr given, the same staged tile also yields
+// it, the codes then overwrite the staged tile, and the workgroup writes each column's
+// 128 codes as one 128-byte line and its four scales as one word.  With qr given, the same staged tile also yields
 // the row-wise quantisation of the unweighted values (codes at qr[r * ldr + n] for the
 // dispatched row r, scales at sr[r * (ldr / 32) + n / 32]): thread t takes the 32
 // columns (t % 4) of staged row t / 4, so a matrix that both layouts need is read once.
 constexpr int COL_ROWS = 128, COL_COLS = 128;
 constexpr int COL_THREADS = 4 * COL_COLS;   // one per (column, 32-row block)
 static_assert(COL_ROWS == kMxRowPad, "a column chunk spans one padding unit");
-__global__ __launch_bounds__(COL_THREADS) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
+__global__ __launch_bounds__(COL_THREADS, 8) void k_mx_cols(const bf16_t* __restrict__ src, int ld,
                                                  const int32_t* __restrict__ row_src, int k,
                                                  const float* __restrict__ topk_w,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ poff, int El, int N, int Rp,
                                                  uint8_t* __restrict__ qt, uint8_t* __restrict__ stt,
                                                  uint8_t* __restrict__ qr, uint8_t* __restrict__ sr, int ldr) {
+  // the codes [COL_COLS][COL_ROWS / 4 + 4] (u32) take the staged tile's place once it is
+  // read, so the workgroup holds 33 KB of LDS and four fit on a CU
   __shared__ __attribute__((aligned(16))) uint16_t tile[COL_ROWS][COL_COLS];
-  __shared__ __attribute__((aligned(16))) uint32_t codes[COL_COLS][COL_ROWS / 4 + 4];
+  uint32_t (*const codes)[COL_ROWS / 4 + 4] = reinterpret_cast<uint32_t (*)[COL_ROWS / 4 + 4]>(&tile[0][0]);
+  static_assert(COL_COLS * (COL_ROWS / 4 + 4) * 4 <= COL_ROWS * COL_COLS * 2, "the codes fit over the tile");
   __shared__ uint32_t scales[COL_COLS];
   __shared__ int srow[COL_ROWS];
   __shared__ float wrow[COL_ROWS];
@@ -139,22 +142,6 @@ __global__ __launch_bounds__(COL_THREADS) void k_mx_cols(const bf16_t* __restric
     }
   }
   __syncthreads();
-  {
-    const int c = tid % COL_COLS, b = tid / COL_COLS;   // column, 32-row block
-    float v[32];
-    float am = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 32; ++rr) {
-      const int r = b * 32 + rr;
-      v[rr] = __uint_as_float((uint32_t)tile[r][c] << 16);
-      if (topk_w) v[rr] *= wrow[r];
-      am = fmaxf(am, fabsf(v[rr]));
-    }
-    const int X = mx_scale_exp(am);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) codes[c][b * 8 + j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
-    reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
-  }
   if (qr) {
     const int rr = tid / (COL_COLS / 32), h = tid % (COL_COLS / 32);   // staged row, 32-column block
     const int n = n0 + 32 * h;
@@ -184,6 +171,26 @@ __global__ __launch_bounds__(COL_THREADS) void k_mx_cols(const bf16_t* __restric
       sr[r * (ldr / 32) + n / 32] = (uint8_t)(X + 127);
     }
   }
+  const int c = tid % COL_COLS, b = tid / COL_COLS;   // column, 32-row block
+  uint32_t q[8];
+  {
+    float v[32];
+    float am = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 32; ++rr) {
+      const int r = b * 32 + rr;
+      v[rr] = __uint_as_float((uint32_t)tile[r][c] << 16);
+      if (topk_w) v[rr] *= wrow[r];
+      am = fmaxf(am, fabsf(v[rr]));
+    }
+    const int X = mx_scale_exp(am);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], X);
+    reinterpret_cast<uint8_t*>(scales)[c * 4 + b] = (uint8_t)(X + 127);
+  }
+  __syncthreads();   // every read of the staged tile is done: the codes take its place
+#pragma unroll
+  for (int j = 0; j < 8; ++j) codes[c][b * 8 + j] = q[j];
   __syncthreads();
   // write-out: COL_COLS columns x 128 codes, eight lanes per 128-byte line
 #pragma unroll
