@@ -127,7 +127,7 @@ void layout(const moe_shape& s, Layout& L) {
   L.off_tiles = 0;
   L.off_zeros = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
   L.off_order = L.off_zeros + align_up(kZeroBytes);
-  L.off_dgu = L.off_order + align_up((size_t)(El + 1) * 4);
+  L.off_dgu = L.off_order + align_up((size_t)(El + 3) * 4);
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
   L.off_part = L.off_dxp + align_up(R * s.H * L.es);
   L.off_aw = L.off_part + align_up(R * L.nparts * 4);

@@ -174,7 +174,8 @@ struct BwdArgs {
   float* dw_part;         // scratch [R_cap, nparts]
   bf16_t* aw;             // scratch [R_cap, I]: w * A
   const bf16_t* zeros;    // scratch: kZeroBytes of zeros
-  const int32_t* order;   // scratch [El + 1]: work order of the weight-gradient GEMMs (k_tile_table)
+  int32_t* order;         // scratch [El + 3]: the weight-gradient GEMMs' expert order, its dynamic
+                          // flag and their two item counters (written by k_tile_table)
   bf16_t* dwg;            // [El, H, I]
   bf16_t* dwu;
   bf16_t* dwd;            // [El, I, H]

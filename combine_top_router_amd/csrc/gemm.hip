@@ -256,7 +256,6 @@ struct JGateUp {
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
   static constexpr bool TRANS = true, EPI_LDS = true;
-  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
   }
@@ -399,7 +398,6 @@ struct JDown {
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
   static constexpr bool TRANS = true, EPI_LDS = true;
-  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
   MxFwdArgs m;
@@ -512,7 +510,6 @@ struct JDa {
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, REG = !MX;  // the fp8 B1 is faster with direct-to-LDS loads
   static constexpr bool TRANS = false, EPI_LDS = true;
-  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -629,7 +626,6 @@ struct JDx {
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (its compute side spills)
   static constexpr bool TRANS = true, EPI_LDS = true;
-  __device__ __forceinline__ bool serpentine() const { return false; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -771,17 +767,20 @@ struct JWgrad {
   static constexpr bool A_KMAJ = false, B_KMAJ = false;
   // items: position p in a.order, then the expert's tm x tn output tiles, m-major.
   // a.order lists the experts by cost, most rows first, and a.order[El] = 1, when
-  // their loads are skewed enough for serpentine rounds to pay; else it is the
-  // identity, a.order[El] = 0, and the items go out in contiguous XCD ranges.
+  // their loads are skewed enough for dynamic (greedy longest-first) scheduling to pay;
+  // else it is the identity, a.order[El] = 0, and the items go out in contiguous XCD
+  // ranges.  a.order[El + 1 + WHICH] is the launch's item counter (zeroed with the order).
   // the accumulators hold C^T; the epilogue writes them as bf16 row bands (band_store)
   static constexpr bool DYN = true, REG = false, TRANS = true, EPI_LDS = true;
-  __device__ __forceinline__ bool serpentine() const { return sload(a.order + a.El) != 0; }
+  __device__ __forceinline__ bool dynamic() const { return sload(a.order + a.El) != 0; }
+  __device__ __forceinline__ int32_t* counter() const { return a.order + a.El + 1 + WHICH; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
   int tm, tn;
   int32_t* ids;
   uint8_t* scring;
+  int32_t* dslot;   // LDS: the next item under dynamic scheduling, two slots by tile parity
   __device__ __forceinline__ int items() const { return a.El * tm * tn; }
   __device__ __forceinline__ void tile(int v, Tile& p) const {
     const int pos = uni(v / (tm * tn));
@@ -887,18 +886,19 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int 
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) int32_t ids[MX ? 4 : IDS_INTS];
   __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
+  __shared__ int32_t dslot[2];
   if constexpr (MX) {
-    JWgrad<WHICH, false, false, true> job{a, m, tm, tn, ids, scring};
+    JWgrad<WHICH, false, false, true> job{a, m, tm, tn, ids, scring, dslot};
     run_stream(job, lds);
   } else if constexpr (WHICH == 0) {
-    JWgrad<0, false, true, false> job{a, m, tm, tn, ids, scring};
+    JWgrad<0, false, true, false> job{a, m, tm, tn, ids, scring, dslot};
     run_stream(job, lds);
   } else {
     if (a.xp) {
-      JWgrad<1, false, false, false> job{a, m, tm, tn, ids, scring};
+      JWgrad<1, false, false, false> job{a, m, tm, tn, ids, scring, dslot};
       run_stream(job, lds);
     } else {
-      JWgrad<1, true, false, false> job{a, m, tm, tn, ids, scring};
+      JWgrad<1, true, false, false> job{a, m, tm, tn, ids, scring, dslot};
       run_stream(job, lds);
     }
   }

@@ -51,7 +51,7 @@ static_assert(MI * NI * 16 <= 128, "accumulators of one wave");
 static_assert(A_LP * NP == A_INSTR && B_LP * NP == B_INSTR, "wave loads divide among the load waves");
 constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
 constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per load wave, two positions of gathered row indices
-constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least
+constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least (see Sched::len)
 constexpr int REG_AHEAD = 2;                      // register-staged loads: K steps held in registers
 
 // ---- scalar loads ----
@@ -285,31 +285,37 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 }
 
 // ---- persistent scheduling ----
-// Workgroup b runs on XCD b % 8.  Two orders of the V work items:
+// Workgroup b runs on XCD b % 8.  Two ways to hand out the V work items:
 // * contiguous: the items are split into 8 contiguous ranges, one per XCD, and the
 //   XCD's workgroups walk their range in order, so work items sharing operands run
 //   together on one XCD and share its L2 (what a job of equal-cost items wants);
-// * serpentine, for items sorted by cost, largest first: round r deals the G items
-//   [r G, r G + G) to the G workgroups, in ascending rank in even rounds and
-//   descending rank in odd ones, the rank being XCD-major (b % 8) * (G / 8) + b / 8.
-//   Every workgroup's sum of costs then stays within about one item of the mean, and
-//   each XCD still takes a contiguous block of G / 8 items per round, but one
-//   operand's items spread over more XCDs.
-// Jobs with DYN = true choose per launch (J::serpentine(), a uniform device flag).
+// * dynamic, for items sorted by cost, largest first: workgroup b starts with item w,
+//   its XCD-major rank (b % 8) (G / 8) + b / 8, and each further item is G plus the old
+//   value of a counter that the launch's G workgroups share, taken when the workgroup
+//   starts its current tile: greedy longest-first, so a workgroup that finishes early
+//   takes the costliest item left and every workgroup ends within about one item of
+//   the others.  One compute wave takes the item and publishes it in LDS; the load
+//   waves read it there only when their cursor reaches the tile's last K step, so a
+//   dynamic tile spans at least DEPTH + 2 stream positions.
+// Jobs with DYN = true choose per launch (J::dynamic(), a uniform device flag, and
+// J::counter(), zero before the launch).
 template <bool DYN>
 struct Sched {
-  int v;        // the workgroup's current item; < 0: none
-  int hi;       // end of the items (contiguous: of the XCD's range)
-  int step;     // contiguous: stride
-  int w, g;     // serpentine: rank, grid size
-  bool serp;
-  __device__ Sched(int V, bool serpentine) {
+  int v;          // the workgroup's first item; < 0: none
+  int hi;         // contiguous: end of the XCD's range; dynamic: V
+  int step;       // contiguous: stride
+  int g;          // grid size
+  bool dyn;
+  int32_t* ctr;   // dynamic: the launch's item counter
+  __device__ Sched(int V, bool dynamic, int32_t* counter) {
     const int x = blockIdx.x & 7;
-    serp = DYN && serpentine;
-    if (serp) {
-      g = (int)gridDim.x;
-      w = x * (g >> 3) + (int)(blockIdx.x >> 3);
+    dyn = DYN && dynamic;
+    ctr = counter;
+    g = (int)gridDim.x;
+    if (dyn) {
+      const int w = x * (g >> 3) + (int)(blockIdx.x >> 3);
       hi = V;
+      step = 0;
       v = w < V ? w : -1;
     } else {
       const int lo = (int)(((int64_t)V * x) >> 3);
@@ -319,23 +325,25 @@ struct Sched {
       if (v >= hi) v = -1;
     }
   }
-  // the item after u (an item of this workgroup), or -1
+  // stream positions a tile of nk K steps takes
+  __device__ __forceinline__ int len(int nk) const { return max(nk, dyn ? DEPTH + 2 : DEPTH + 1); }
+  // contiguous: the item after u (an item of this workgroup), or -1
   __device__ __forceinline__ int next(int u) const {
-    int n;
-    if (DYN && serp) {
-      const int r = u / g + 1;
-      n = r * g + ((r & 1) ? g - 1 - w : w);
-    } else {
-      n = u + step;
-    }
+    const int n = u + step;
     return n < hi ? n : -1;
+  }
+  // dynamic: the next item from the shared counter, or -1 (one lane calls it)
+  __device__ __forceinline__ int grab() const {
+    const int n = g + atomicAdd(ctr, 1);
+    return n >= g && n < hi ? n : -1;
   }
 };
 
 // ---- the tile stream ----
 // A workgroup has NW compute waves and NP load waves.  Its tiles form one stream of K
-// steps ("positions"); every tile takes max(nk, MIN_STEPS) positions, positions past
-// nk repeating a valid step's loads and skipping the MFMAs.  At each position the
+// steps ("positions"); every tile takes Sched::len(nk) positions (max(nk, DEPTH + 1), or
+// DEPTH + 2 under dynamic scheduling), positions past nk repeating a valid step's loads
+// and skipping the MFMAs.  At each position the
 // load waves wait for their own loads of that position, all waves meet at a barrier,
 // the load waves issue the loads of the position DEPTH ahead (possibly the next
 // tile's) into the stage read one position ago, and the compute waves run the MFMAs
@@ -363,20 +371,36 @@ __device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, S sc, 
   int v = sc.v;
   Acc acc;
   zero_acc(acc);
+  int32_t* slot = nullptr;   // dynamic: two LDS slots for the next item, by tile parity
+  if constexpr (J::DYN) slot = job.dslot;
   int cs = 0;
-  for (;;) {
-    const int nk = cur.nk, len = max(nk, MIN_STEPS);
-    const int vn = sc.next(v);
-    const bool more = vn >= 0;
+  for (int t = 0;; ++t) {
+    const int nk = cur.nk, len = sc.len(nk);
+    int vn = sc.dyn ? -1 : sc.next(v);
     const bool act = __builtin_amdgcn_readfirstlane((int)job.active(cur, wm)) != 0;
-    int done = 0;
+    int done = 0, grabbed = 0;
     for (int kc = 0; kc < len; ++kc) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // dynamic: wave 0 takes the next item before its MFMAs and publishes it after
+      // them; every compute wave reads it after the next barrier
+      if (sc.dyn && kc == 0 && wv == 0 && lane == 0) grabbed = sc.grab();
       if (kc < nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wm, wn);
-      if (kc == 0 && more) job.tile(vn, nxt);
+      if (sc.dyn) {
+        if (kc == 0 && wv == 0) {
+          const int n = uni(grabbed);
+          if (lane == 0) slot[t & 1] = n;
+        }
+        if (kc == 1) {
+          vn = uni(slot[t & 1]);
+          if (vn >= 0) job.tile(vn, nxt);
+        }
+      } else if (kc == 0 && vn >= 0) {
+        job.tile(vn, nxt);
+      }
       done = cs;
       cs = cs == NSTAGE - 1 ? 0 : cs + 1;
     }
+    const bool more = vn >= 0;
     // every wave is done with the stage just read: stage the results there (a job whose
     // epilogue writes from registers alone, !J::EPI_LDS, needs neither)
     if constexpr (J::EPI_LDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -393,8 +417,11 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
   using P = typename J::Ld;
   P cur, nxt;
   job.setup(sc.v, cur, pw, lane);
+  int32_t* slot = nullptr;                  // dynamic: the compute side's next-item slots
+  if constexpr (J::DYN) slot = job.dslot;
+  int tl = 0;                               // tiles of this workgroup before cur
   int vc = sc.v, vn = -1;                   // items of cur and nxt
-  int lc = max(cur.nk, MIN_STEPS), ln = 0;  // stream positions of cur and nxt
+  int lc = sc.len(cur.nk), ln = 0;          // stream positions of cur and nxt
   bool has_nxt = false, looked = false;     // nxt set up; the item after cur looked up
   bool in_nxt = false;                      // the issue cursor is in nxt
   int ik = 0;                               // issue cursor: step within its tile
@@ -412,10 +439,12 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
       const bool last = k0 >= lc - 1;
       if (last && !looked) {
         looked = true;
-        vn = sc.next(vc);
+        // dynamic: published by the compute side during cur's first position, at least
+        // one barrier before this last position of cur is issued
+        vn = sc.dyn ? uni(slot[tl & 1]) : sc.next(vc);
         if (vn >= 0) {
           job.setup(vn, nxt, pw, lane);
-          ln = max(nxt.nk, MIN_STEPS);
+          ln = sc.len(nxt.nk);
           has_nxt = true;
         }
       }
@@ -449,6 +478,7 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
     cur = nxt;
     vc = vn;
     lc = ln;
+    ++tl;
     has_nxt = looked = in_nxt = false;
     kc = 0;
   }
@@ -463,6 +493,7 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
 // (the LDS ring alone holds DEPTH).  The compiler orders each LDS write after its loads.
 template <class J, class S>
 __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc, int pw, int lane) {
+  static_assert(!J::DYN, "register-staged streams walk a fixed schedule");
   using P = typename J::Ld;
   using Slot = typename P::Slot;
   int ntiles = 0;
@@ -527,7 +558,13 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
 template <class J>
 __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6);
-  Sched<J::DYN> sc(job.items(), job.serpentine());
+  bool dyn = false;
+  int32_t* ctr = nullptr;
+  if constexpr (J::DYN) {
+    dyn = job.dynamic();
+    ctr = job.counter();
+  }
+  Sched<J::DYN> sc(job.items(), dyn, ctr);
   if (sc.v < 0) return;
   if (wv >= NW) {
     if constexpr (J::REG) load_stream_reg(job, lds, sc, wv - NW, lane);

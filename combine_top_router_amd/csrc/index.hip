@@ -181,14 +181,16 @@ __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, 
 // output tiles cost about c = max(ceil(rows / 64), 3) + 2 K steps: if one expert costs
 // over twice the mean, or the costliest of the 8 contiguous expert ranges of the XCDs
 // exceeds their mean by over 2 %, order[p] = the expert with the p-th most rows (ties:
-// lower index first) and order[El] = 1 (serpentine rounds); else order[e] = e and
-// order[El] = 0 (contiguous ranges, which keep each expert's tiles on one XCD's L2).
+// lower index first) and order[El] = 1 (dynamic, greedy longest-first scheduling); else
+// order[e] = e and order[El] = 0 (contiguous ranges, which keep each expert's tiles on
+// one XCD's L2).  order[El + 1] and order[El + 2], the item counters of the dW_down and
+// dW_gate|dW_up launches, are zeroed.
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
                                                      int32_t* __restrict__ tiles, int32_t* __restrict__ zeros,
                                                      int32_t* __restrict__ order) {
   __shared__ int32_t buf[16];  // wave totals of the scan
   __shared__ int32_t rows[1024];
-  __shared__ int32_t xsum[8], cmax, serp;
+  __shared__ int32_t xsum[8], cmax, dyn;
   const int e = threadIdx.x;
   if (zeros && e < kZeroBytes / 4) zeros[e] = 0;
   if (e < 8) xsum[e] = 0;
@@ -213,13 +215,15 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
         tot += xsum[x];
         xm = max(xm, (int64_t)xsum[x]);
       }
-      serp = (int64_t)cmax * El > 2 * tot || xm * 8 * 50 > tot * 51;
-      order[El] = serp;
+      dyn = (int64_t)cmax * El > 2 * tot || xm * 8 * 50 > tot * 51;
+      order[El] = dyn;
+      order[El + 1] = 0;   // the item counters of the two weight-gradient launches
+      order[El + 2] = 0;
     }
     __syncthreads();
     if (e < El) {
       int rank = e;
-      if (serp) {
+      if (dyn) {
         rank = 0;
         for (int j = 0; j < El; ++j) {
           const int cj = rows[j];
