@@ -33,9 +33,11 @@
  *    expert-major, token-ascending.  Row buffers are sized for R_cap; rows >= R are
  *    left unspecified.
  *  - The caller owns every buffer, including `saved` and `scratch` whose sizes come
- *    from moe_workspace_bytes().  The library keeps no state between calls (apart
- *    from the opt-in timing records of moe_timing_enable); calls with distinct
- *    buffers may run concurrently on different streams.
+ *    from moe_workspace_bytes().  The library keeps no state between calls apart
+ *    from the opt-in timing records of moe_timing_enable, the error string of
+ *    moe_last_error, each device's CU count, and the device buffer of
+ *    moe_dispatch_noscratch; calls with distinct buffers may run concurrently on
+ *    different streams.
  *  - Outputs are overwritten, never accumulated.  dW slices of experts with no rows
  *    are written as zeros; tokens with no local slot get y = 0 and dx = 0.
  */
@@ -148,9 +150,9 @@ int moe_dispatch_noscratch(const moe_shape* shape, const int32_t* topk_idx, cons
  * scale and rounding rule of moe_mx_quantize: the rows of x along H and each column of
  * W_gate[e], W_up[e] in blocks of 32 consecutive h; then the rows of a along I
  * (quantised from its fp32 value, before the rounding of the saved bf16 a) and each
- * column of W_down[e] in blocks of 32 consecutive i.  g, u and a are still the bf16-rounded GEMM results, and the routing
- * weight still applies after the down GEMM.  Needs H and I multiples of 128
- * (MOE_EUNSUPPORTED otherwise). */
+ * column of W_down[e] in blocks of 32 consecutive i.  g, u and a are still the
+ * bf16-rounded GEMM results, and the routing weight still applies after the down GEMM.
+ * Needs H and I multiples of 128 (MOE_EUNSUPPORTED otherwise). */
 int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t* offsets,
             const int32_t* row_src, const float* topk_w, const void* w_gate, const void* w_up,
             const void* w_down, void* yp, void* saved, void* scratch, void* stream);
