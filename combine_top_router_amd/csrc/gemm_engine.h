@@ -343,15 +343,15 @@ struct Sched {
 // A workgroup has NW compute waves and NP load waves.  Its tiles form one stream of K
 // steps ("positions"); every tile takes Sched::len(nk) positions (max(nk, DEPTH + 1), or
 // DEPTH + 2 under dynamic scheduling), positions past nk repeating a valid step's loads
-// and skipping the MFMAs.  At each position the
-// load waves wait for their own loads of that position, all waves meet at a barrier,
-// the load waves issue the loads of the position DEPTH ahead (possibly the next
-// tile's) into the stage read one position ago, and the compute waves run the MFMAs
-// of the position.  After a tile's last position all waves meet once more and the
-// compute waves run the tile's epilogue in the stage just read, while the load waves
-// wait at the next position's barrier with DEPTH positions in flight.  Load-issue
-// stalls (the vector memory queue of a CU drains at a fixed rate) hold only the load
-// waves, and the compute waves issue no loads of their own besides the epilogue's.
+// and skipping the MFMAs.  At each position the load waves wait for their own loads of
+// that position, all waves meet at a barrier, the load waves issue the loads of the
+// position DEPTH ahead (possibly the next tile's) into the stage read one position ago,
+// and the compute waves run the MFMAs of the position.  After a tile's last position
+// all waves meet once more and the compute waves run the tile's epilogue in the stage
+// just read, while the load waves wait at the next position's barrier with DEPTH
+// positions in flight.  Load-issue stalls (the vector memory queue of a CU drains at a
+// fixed rate) hold only the load waves, and the compute waves issue no loads of their
+// own besides the epilogue's.
 //
 // A job J supplies: items(); steps(v) (K steps of item v; scalar loads only); the
 // compute side -- Tile, tile(v, Tile&) (what the epilogue needs, scalar loads only),
