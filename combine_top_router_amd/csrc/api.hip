@@ -10,7 +10,6 @@
 #include "common.h"
 
 namespace moe {
-int bwd_bf16_nparts(int I);
 }
 
 using namespace moe;

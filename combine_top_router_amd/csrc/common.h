@@ -181,6 +181,8 @@ struct BwdArgs {
   bf16_t* dwd;            // [El, I, H]
 };
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
+// column parts of the B1 row-dot partials per row (dw_part is [R_cap, nparts])
+int bwd_bf16_nparts(int I);
 
 // MXFP8 backward: E4M3 values with one e8m0 scale per 32 along each GEMM's contraction
 // axis.  Row-wise buffers are [rows, K] codes + [rows, K/32] scales; column-wise ones

@@ -904,8 +904,18 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int 
   }
 }
 
+template <bool MX>
+hipError_t launch_bwd_gemms(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
+  const int nparts = bwd_bf16_nparts(a.I);
+  if (a.max_tiles > 0)
+    MOE_LAUNCH(MX ? "bwd_dA_mx" : "bwd_dA", k_bwd_da<MX>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN))),
+               dim3(NTHR), 0, st, a, m, nparts);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+#if !MOE_GEMM_MX_TU
 hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
@@ -924,6 +934,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+#endif  // !MOE_GEMM_MX_TU
+
+#if MOE_GEMM_MX_TU
 // MXFP8 forward.  Order: quantise W_gate, W_up and W_down column-wise (one group per
 // expert) and the Xp rows row-wise; K1 on fp8 operands writes G|U and A (bf16) and the
 // row-wise codes of A (from its fp32 values); K2 on fp8 operands.
@@ -959,16 +972,10 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, b
   return hipGetLastError();
 }
 
-int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
+#endif  // MOE_GEMM_MX_TU
 
-template <bool MX>
-hipError_t launch_bwd_gemms(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
-  const int nparts = bwd_bf16_nparts(a.I);
-  if (a.max_tiles > 0)
-    MOE_LAUNCH(MX ? "bwd_dA_mx" : "bwd_dA", k_bwd_da<MX>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN))),
-               dim3(NTHR), 0, st, a, m, nparts);
-  return hipGetLastError();
-}
+#if !MOE_GEMM_MX_TU
+int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   MxArgs m{};
@@ -990,6 +997,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+#endif  // !MOE_GEMM_MX_TU
+
+#if MOE_GEMM_MX_TU
 // MXFP8 backward.  Order: quantise the weights row-wise (unless the MXFP8 forward left
 // their codes in the saved buffer), and dY' row-wise together with
 // w * dY' column-wise per expert; B1 (fp8) writes dG|dU (bf16); quantise dG|dU row-wise
@@ -1036,5 +1046,7 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
   }
   return hipGetLastError();
 }
+
+#endif  // MOE_GEMM_MX_TU
 
 }  // namespace moe

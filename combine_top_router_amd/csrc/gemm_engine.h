@@ -29,7 +29,13 @@ constexpr int BM = 128, BN = 256, BK = 64;
 constexpr int NSTAGE = 3;            // LDS ring stages (48 KB each)
 constexpr int DEPTH = NSTAGE - 1;    // K steps in flight ahead of the MFMAs
 constexpr int NW = 8;                // compute waves: 2 along M x 4 along N
-constexpr int NP = 8;                // load (producer) waves, two per SIMD
+// load (producer) waves: two per SIMD for the bf16 kernels (128 registers per wave);
+// one per SIMD for the MXFP8 kernels (gemm_mx.hip: 12 waves, 168 registers), whose fp8
+// fragments and scale operands spill at 128 registers
+#ifndef MOE_GEMM_MX_TU
+#define MOE_GEMM_MX_TU 0
+#endif
+constexpr int NP = MOE_GEMM_MX_TU ? 4 : 8;
 constexpr int NTHR = 64 * (NW + NP);
 constexpr int WM = 2;                // compute waves along M
 constexpr int WN = NW / WM;          // compute waves along N
