@@ -23,7 +23,24 @@ CASES = {
     # activation checkpointing: the backward's recompute of G|U and A is captured too
     "ragged_bf16_share_recompute": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
     "ragged_mxfp8_recompute": wl.MoeConfig("ragged_mxfp8", 700, 256, 256, 6, 2, 0, 6, 8, bwd="mxfp8", fwd="mxfp8"),
+    # Zipf-skewed loads: the weight gradients take their tiles from a device counter that the
+    # tile table zeroes, so every replay must start the greedy schedule afresh
+    "skew_bf16_dynamic": wl.MoeConfig("skew_bf16", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf"),
+    "skew_mx_dynamic": wl.MoeConfig("skew_mx", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf", bwd="mxfp8"),
 }
+
+
+def _schedules_dynamically(counts):
+    """Whether the tile table picks the greedy weight-gradient schedule for these expert
+    loads: an expert costing over twice the mean, or one of the 8 contiguous expert ranges
+    over 2 % above their mean (cost = max(ceil(rows / 64), 3) + 2 K steps per tile)."""
+    El = len(counts)
+    cost = [max((int(c) + 63) // 64, 3) + 2 for c in counts]
+    tot = sum(cost)
+    xsum = [0] * 8
+    for e, c in enumerate(cost):
+        xsum[e * 8 // El] += c
+    return max(cost) * El > 2 * tot or max(xsum) * 8 * 50 > tot * 51
 
 
 def _outputs(layer, y, g):
@@ -57,6 +74,8 @@ def test_graph_replays_match_eager(name):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     ref = _outputs(layer, y, g)
+    if name.endswith("_dynamic"):
+        assert _schedules_dynamically(layer.counts.cpu().numpy()), "the case must exercise the greedy schedule"
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
