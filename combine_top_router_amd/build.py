@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "index.hip", "gemm.hip", "gemm_mx.hip", "gemm_f32.hip", "mx_quant.hip",
+SOURCES = ["api.hip", "route.hip", "index.hip", "gemm.hip", "gemm_mx.hip", "gemm_fw.hip", "gemm_f32.hip", "mx_quant.hip",
            "router_gemm.hip"]
 ARCH = "gfx950"
 

@@ -40,7 +40,8 @@ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   int64_t R_cap;
   size_t es;         // element size of the data dtype
-  int max_tiles;     // row-group tile bound
+  int max_tiles;     // row-group tile bound, kGemmBM-row tiles (MXFP8 GEMMs)
+  int max_tiles_w;   // the same for kGemmBMWide-row tiles (bf16 GEMMs)
   int nparts;        // rowdot partials per row
   int nchunks;
   // saved
@@ -53,7 +54,7 @@ struct Layout {
   size_t off_rgu, off_ra;
   size_t off_router_part;
   // scratch
-  size_t off_tiles, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
+  size_t off_tiles, off_tiles_w, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
   // MXFP8 backward buffers (scratch), 0 when unused
   int64_t Rp;
   size_t off_mx[17];
@@ -106,6 +107,7 @@ void layout(const moe_shape& s, Layout& L) {
   L.R_cap = (int64_t)s.T * (s.k < El ? s.k : El);
   L.es = s.dtype == MOE_BF16 ? 2 : 4;
   L.max_tiles = (int)ceil_div(L.R_cap, kGemmBM) + El;
+  L.max_tiles_w = (int)ceil_div(L.R_cap, kGemmBMWide) + El;
   L.nparts = s.dtype == MOE_BF16 ? bwd_bf16_nparts(s.I) : s.I;
   L.nchunks = (int)ceil_div((int64_t)s.T * s.k, index_chunk((int64_t)s.T * s.k, El));
   const size_t R = (size_t)L.R_cap;
@@ -124,7 +126,8 @@ void layout(const moe_shape& s, Layout& L) {
   }
   const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
   L.off_tiles = 0;
-  L.off_zeros = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
+  L.off_tiles_w = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
+  L.off_zeros = L.off_tiles_w + align_up((size_t)(4 + 4 * L.max_tiles_w) * 4);
   L.off_order = L.off_zeros + align_up(kZeroBytes);
   L.off_dgu = L.off_order + align_up((size_t)(El + 3) * 4);
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
@@ -358,14 +361,16 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    e = launch_tile_table(s, offsets, kGemmBM, tiles, nullptr, nullptr, st);
+    // the MXFP8 GEMMs take kGemmBM-row tiles, the bf16 ones kGemmBMWide-row tiles
+    const bool mxf = s.fwd == MOE_FWD_MXFP8;
+    int32_t* tiles = at<int32_t>(scratch, mxf ? L.off_tiles : L.off_tiles_w);
+    e = launch_tile_table(s, offsets, mxf ? kGemmBM : kGemmBMWide, tiles, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     FwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
     a.x = (const bf16_t*)x; a.xp = (const bf16_t*)xp; a.offsets = offsets; a.row_src = row_src;
     a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up; a.wd = (const bf16_t*)w_down;
-    a.tiles = tiles; a.max_tiles = L.max_tiles;
+    a.tiles = tiles; a.max_tiles = mxf ? L.max_tiles : L.max_tiles_w;
     a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a); a.yp = (bf16_t*)yp;
     if (s.recompute) {  // nothing kept: the down GEMM's A in scratch, no G|U
       a.gu = nullptr;
@@ -440,8 +445,10 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    e = launch_tile_table(s, offsets, kGemmBM, tiles, at<int32_t>(scratch, L.off_zeros),
+    // the MXFP8 GEMMs take kGemmBM-row tiles, the bf16 ones kGemmBMWide-row tiles
+    const bool mxb = s.bwd == MOE_BWD_MXFP8;
+    int32_t* tiles = at<int32_t>(scratch, mxb ? L.off_tiles : L.off_tiles_w);
+    e = launch_tile_table(s, offsets, mxb ? kGemmBM : kGemmBMWide, tiles, at<int32_t>(scratch, L.off_zeros),
                           at<int32_t>(scratch, L.off_order), st);
     if (e != hipSuccess) return hip_status(e, __func__);
     BwdArgs a{};
@@ -449,7 +456,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.dy = (const bf16_t*)dy; a.x = (const bf16_t*)x; a.xp = (const bf16_t*)xp; a.offsets = offsets;
     a.row_src = row_src; a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up;
     a.wd = (const bf16_t*)w_down; a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a);
-    a.tiles = tiles; a.max_tiles = L.max_tiles;
+    a.tiles = tiles; a.max_tiles = mxb ? L.max_tiles : L.max_tiles_w;
     a.dgu = at<bf16_t>(scratch, L.off_dgu); a.dxp = at<bf16_t>(scratch, L.off_dxp);
     a.dw_part = at<float>(scratch, L.off_part);
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
@@ -463,8 +470,16 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
       FwdArgs f{};
       f.T = s.T; f.H = s.H; f.I = s.I; f.k = s.k; f.El = s.e_local;
       f.x = a.x; f.xp = a.xp; f.offsets = offsets; f.row_src = row_src; f.topk_w = topk_w;
-      f.wg = a.wg; f.wu = a.wu; f.wd = a.wd; f.tiles = tiles; f.max_tiles = L.max_tiles;
+      f.wg = a.wg; f.wu = a.wu; f.wd = a.wd; f.tiles = a.tiles; f.max_tiles = a.max_tiles;
       f.gu = rgu; f.a = ra; f.yp = nullptr;
+      const bool mxf = s.fwd == MOE_FWD_MXFP8;
+      if (mxf != mxb) {  // the recomputed gate/up GEMM takes the other tile height
+        int32_t* ftiles = at<int32_t>(scratch, mxf ? L.off_tiles : L.off_tiles_w);
+        e = launch_tile_table(s, offsets, mxf ? kGemmBM : kGemmBMWide, ftiles, nullptr, nullptr, st);
+        if (e != hipSuccess) return hip_status(e, __func__);
+        f.tiles = ftiles;
+        f.max_tiles = mxf ? L.max_tiles : L.max_tiles_w;
+      }
       if (s.fwd == MOE_FWD_MXFP8) {
         MxFwdArgs m{};
         uint8_t** bufs[8] = {&m.q_x, &m.s_x, &m.q_a, &m.s_a, &m.qt_wgu, &m.st_wgu, &m.qt_wd, &m.st_wd};

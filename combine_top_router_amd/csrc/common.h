@@ -75,7 +75,8 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, flo
 }
 
 // Host-side: the launch configuration constants shared by the host code and kernels.
-constexpr int kGemmBM = 128;     // rows of one row-group GEMM tile (bf16 path)
+constexpr int kGemmBM = 128;      // rows of one row-group GEMM tile (MXFP8 GEMMs)
+constexpr int kGemmBMWide = 256;  // rows of one row-group GEMM tile (bf16 GEMMs, fused stream)
 constexpr int kZeroBytes = 512;  // zeroed scratch area read in place of rows past a group's end
 // (token, slot) pairs per histogram chunk of the dispatch index: at least 1024, a
 // multiple of 256, and few enough chunks (<= 256 and <= 32768 / El) that every
@@ -181,6 +182,8 @@ struct BwdArgs {
   bf16_t* dwd;            // [El, I, H]
 };
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);  // B1 alone
+hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st);  // B3 alone
 // column parts of the B1 row-dot partials per row (dw_part is [R_cap, nparts])
 int bwd_bf16_nparts(int I);
 

@@ -245,6 +245,11 @@ struct LGateUp : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
+  __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
+    a.dma(kt, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
+  }
 };
 
 // MX: Xp rows (row-wise codes along H) against the transposed column-wise codes of
@@ -387,6 +392,11 @@ struct LMnB : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
+  __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
+    a.dma(kt, st, pw);
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
+  }
 };
 
 // MX: A rows (row-wise codes along I) against the transposed column-wise codes of
@@ -494,6 +504,13 @@ struct LKK : RowLd {
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
   }
+  __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
+    a.dma(kt, st, pw);
+    const bool second = kt >= ksplit;
+    const int k0 = (second ? kt - ksplit : kt) * BK;
+#pragma unroll
+    for (int q = 0; q < B_LP; ++q) dma16((second ? b2[q] : b[q]) + k0, b_dst(st, q, pw));
+  }
 };
 
 template <bool MX>
@@ -556,13 +573,13 @@ struct JDa {
     const bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
     bf16_t* const dgub = a.dgu + (size_t)p.t.rs * I2;
     bf16_t* const awb = a.aw + (size_t)p.t.rs * a.I;
-    // the routing weights of the wave's WROWS rows, one per lane, into the wave's LDS slots
-    // before the staging starts (read back by row: no per-lane array indexed in the
-    // rolled row loop, which would live in scratch memory)
-    static_assert(WROWS <= 64, "one routing weight per lane");
+    // the routing weights of the wave's WROWS rows into the wave's LDS slots before the
+    // staging starts (read back by row: no per-lane array indexed in the rolled row loop,
+    // which would live in scratch memory)
     const int wv = threadIdx.x >> 6;
-    if (lane < WROWS)
-      wrow[wv * WROWS + lane] = a.topk_w[a.row_src[p.t.rs + min(wm * WROWS + lane, p.t.cnt - 1)]];
+#pragma unroll
+    for (int i = lane; i < WROWS; i += 64)
+      wrow[wv * WROWS + i] = a.topk_w[a.row_src[p.t.rs + min(wm * WROWS + i, p.t.cnt - 1)]];
     epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int) {
       const int col = p.n0 + ct;
       const bool ok = rt < p.t.cnt && col < a.I;
@@ -915,7 +932,8 @@ hipError_t launch_bwd_gemms(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
 
 }  // namespace
 
-#if !MOE_GEMM_MX_TU
+#if MOE_GEMM_FW
+// The bf16 row-tiled GEMMs on the fused stream: a.tiles holds kGemmBMWide-row tiles.
 hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
@@ -934,7 +952,21 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-#endif  // !MOE_GEMM_MX_TU
+hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st) {
+  MxArgs m{};
+  return launch_bwd_gemms<false>(a, m, st);
+}
+
+hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st) {
+  if (a.max_tiles == 0) return hipSuccess;
+  MxArgs m{};
+  MOE_LAUNCH("bwd_dX", k_bwd_dx<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0, st,
+             a, m);
+  return hipGetLastError();
+}
+
+static_assert(BM == kGemmBMWide, "the fused-stream GEMMs read kGemmBMWide-row tiles");
+#endif  // MOE_GEMM_FW
 
 #if MOE_GEMM_MX_TU
 // MXFP8 forward.  Order: quantise W_gate, W_up and W_down column-wise (one group per
@@ -974,21 +1006,21 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, b
 
 #endif  // MOE_GEMM_MX_TU
 
-#if !MOE_GEMM_MX_TU
+#if !MOE_GEMM_MX_TU && !MOE_GEMM_FW
 int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
 
+// B1 and B3 run on the fused stream (gemm_fw.hip), the weight gradients here.
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   MxArgs m{};
-  hipError_t e = launch_bwd_gemms<false>(a, m, st);
+  hipError_t e = launch_bwd_da_bf16(a, st);
   if (e != hipSuccess) return e;
   {
     const int tm = (int)ceil_div(a.I, BM), tn = (int)ceil_div(a.H, BN);
     MOE_LAUNCH("bwd_dWd", (k_bwd_wgrad<0, false>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a, m,
                tm, tn);
   }
-  if (a.max_tiles > 0)
-    MOE_LAUNCH("bwd_dX", k_bwd_dx<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0, st,
-               a, m);
+  e = launch_bwd_dx_bf16(a, st);
+  if (e != hipSuccess) return e;
   {
     const int tm = (int)ceil_div(a.H, BM), tn = (int)ceil_div(2 * a.I, BN);
     MOE_LAUNCH("bwd_dWgu", (k_bwd_wgrad<1, false>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a, m,
@@ -997,7 +1029,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-#endif  // !MOE_GEMM_MX_TU
+#endif  // !MOE_GEMM_MX_TU && !MOE_GEMM_FW
 
 #if MOE_GEMM_MX_TU
 // MXFP8 backward.  Order: quantise the weights row-wise (unless the MXFP8 forward left

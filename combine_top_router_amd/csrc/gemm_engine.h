@@ -25,18 +25,31 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int NSTAGE = 3;            // LDS ring stages (48 KB each)
+// Two workgroup shapes, one per translation unit:
+// * load-wave streams (gemm.hip, gemm_mx.hip): 128 x 256 tiles, a three-stage ring (48 KB
+//   stages), NW compute waves and NP dedicated load waves;
+// * the fused stream (MOE_GEMM_FW, gemm_fw.hip: the bf16 row-tiled GEMMs): 256 x 256
+//   tiles, a two-stage ring (64 KB stages), eight waves that each issue one eighth of the
+//   operand loads and compute a 128 x 64 sub-tile.  Eight waves per CU leave each 256
+//   registers, room for 128 accumulators; the larger tile asks a third fewer operand
+//   bytes per flop of the CU's L2 request path, which bounds the load-wave kernels.
+#ifndef MOE_GEMM_MX_TU
+#define MOE_GEMM_MX_TU 0
+#endif
+#ifndef MOE_GEMM_FW
+#define MOE_GEMM_FW 0
+#endif
+constexpr bool FW = MOE_GEMM_FW;
+constexpr int BM = FW ? 256 : 128, BN = 256, BK = 64;
+constexpr int NSTAGE = FW ? 2 : 3;   // LDS ring stages
 constexpr int DEPTH = NSTAGE - 1;    // K steps in flight ahead of the MFMAs
 constexpr int NW = 8;                // compute waves: 2 along M x 4 along N
 // load (producer) waves: two per SIMD for the bf16 kernels (128 registers per wave);
 // one per SIMD for the MXFP8 kernels (gemm_mx.hip: 12 waves, 168 registers), whose fp8
-// fragments and scale operands spill at 128 registers
-#ifndef MOE_GEMM_MX_TU
-#define MOE_GEMM_MX_TU 0
-#endif
-constexpr int NP = MOE_GEMM_MX_TU ? 4 : 8;
-constexpr int NTHR = 64 * (NW + NP);
+// fragments and scale operands spill at 128 registers.  The fused stream's waves are
+// load waves 0 .. NW - 1 as well.
+constexpr int NP = FW ? NW : (MOE_GEMM_MX_TU ? 4 : 8);
+constexpr int NTHR = 64 * (FW ? NW : NW + NP);
 constexpr int WM = 2;                // compute waves along M
 constexpr int WN = NW / WM;          // compute waves along N
 constexpr int MI = BM / (32 * WM);   // 32-row accumulator blocks per wave
@@ -561,6 +574,69 @@ __device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc,
   if constexpr (J::EPI_LDS) asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
 }
 
+// The fused stream (FW): every wave is compute wave wv and load wave wv.  At each
+// position it waits for its own loads of the position, meets the other waves at the
+// barrier (after which the position's stage is complete and the stage read one position
+// ago is free), issues its loads of the position DEPTH ahead into that free stage and
+// runs the position's MFMAs.  After a tile's last position the waves meet once more and
+// run the epilogue in the stage just read, which the next issue refills only after the
+// next barrier.  Vector memory instructions that the compiler emits (the epilogues') only
+// lengthen the explicit vmcnt waits, which count the direct-to-LDS loads alone: every
+// such instruction is younger than the loads it waits for.  For jobs whose tiles all take
+// the same number of K steps (Ld::dma(kt, stage) issues Ld::NLOAD loads).
+template <class J, class S>
+__device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, int wv, int lane) {
+  static_assert(!J::DYN, "the fused stream walks a fixed schedule");
+  using P = typename J::Ld;
+  using T = typename J::Tile;
+  const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+  int ntiles = 0;
+  for (int u = sc.v; u >= 0; u = sc.next(u)) ++ntiles;
+  P L;
+  int lv = sc.v, lk = 0;                    // load cursor: step lk of item lv
+  job.setup(lv, L, wv, lane);
+  const int len = max(L.nk, MIN_STEPS);     // the same for every tile of the job
+  const int total = ntiles * len;           // stream positions of this workgroup
+  auto issue = [&](int stage) {
+    L.dma(min(lk, L.nk - 1), lds + stage * STAGE_ELEMS);
+    if (++lk == len) {
+      lk = 0;
+      lv = sc.next(lv);
+      if (lv >= 0) job.setup(lv, L, wv, lane);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d);  // total >= MIN_STEPS > DEPTH
+  T cur;
+  int cv = sc.v;
+  job.tile(cv, cur);
+  bool act = uni((int)job.active(cur, wm)) != 0;
+  Acc acc;
+  zero_acc(acc);
+  int ck = 0, cs = 0;
+  for (int p = 0; p < total; ++p) {
+    // the loads of positions p + 1 .. p + DEPTH - 1 may still fly (fewer near the end)
+    if (total - p >= DEPTH)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((DEPTH - 1) * P::NLOAD) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (p + DEPTH < total) issue(cs + DEPTH < NSTAGE ? cs + DEPTH : cs + DEPTH - NSTAGE);
+    if (ck < cur.nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wm, wn);
+    const int done = cs;
+    cs = cs == NSTAGE - 1 ? 0 : cs + 1;
+    if (++ck < len) continue;
+    if constexpr (J::EPI_LDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    job.epilogue(cur, acc, reinterpret_cast<float*>(lds + done * STAGE_ELEMS));
+    zero_acc(acc);
+    ck = 0;
+    cv = sc.next(cv);
+    if (cv < 0) break;
+    job.tile(cv, cur);
+    act = uni((int)job.active(cur, wm)) != 0;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <class J>
 __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wv = uni(tid >> 6);
@@ -572,7 +648,9 @@ __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   }
   Sched<J::DYN> sc(job.items(), dyn, ctr);
   if (sc.v < 0) return;
-  if (wv >= NW) {
+  if constexpr (FW) {
+    fused_stream(job, lds, sc, wv, lane);
+  } else if (wv >= NW) {
     if constexpr (J::REG) load_stream_reg(job, lds, sc, wv - NW, lane);
     else load_stream(job, lds, sc, wv - NW, lane);
   } else {
@@ -719,6 +797,10 @@ struct KRows {
   __device__ __forceinline__ void put(const i32x4 (&v)[A_LP], bf16_t* st, int pw) const {
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) lds_put16(a_dst(st, q, pw), v[q]);
+  }
+  __device__ __forceinline__ void dma(int kt, bf16_t* st, int pw) const {
+#pragma unroll
+    for (int q = 0; q < A_LP; ++q) dma16(p[q] + kt * BK, a_dst(st, q, pw));
   }
 };
 
