@@ -251,6 +251,9 @@ def main():
                          "gate/up GEMM (value still counts the 18RHI of the layer, not the 4RHI recomputed)")
     ap.add_argument("--router", action="store_true",
                     help="logits from the router GEMM x W_r inside the step (and its backward into dx and dW_r)")
+    ap.add_argument("--gather-copy", action="store_true",
+                    help="the dispatch writes the gathered token rows Xp, which the GEMMs then read densely "
+                         "(default: the GEMM loaders read x through row_src)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -276,7 +279,8 @@ def main():
     x, wg, wu, wd, dy = t(inp["x"]), t(inp["w_gate"]), t(inp["w_up"]), t(inp["w_down"]), t(inp["dy"])
     layer = MoeLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.e_begin, cfg.e_local, L.MOE_BF16,
                      L.MOE_BWD_MXFP8 if mx else L.MOE_BWD_SAME, cfg.renorm, device=dev,
-                     fwd=L.MOE_FWD_MXFP8 if mxf else L.MOE_FWD_SAME, recompute=int(args.recompute))
+                     fwd=L.MOE_FWD_MXFP8 if mxf else L.MOE_FWD_SAME, recompute=int(args.recompute),
+                     fuse_gather=not args.gather_copy)
     stream = torch.cuda.current_stream()
     if args.router:
         w_r = t(wl.make_router_weight(cfg))
@@ -445,7 +449,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (", activation checkpointing (backward recomputes "
                                                             "the gate/up GEMM)" if args.recompute else "")
-                   + (", router GEMM x W_r in the step" if args.router else ""),
+                   + (", router GEMM x W_r in the step" if args.router else "")
+                   + (", gathered rows Xp written by the dispatch" if args.gather_copy else ""),
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "e_local": cfg.e_local, "rows": R},
         # the layer's algorithmic flops (router GEMM included with --router) over the step
         # time, against the dense bf16 peak

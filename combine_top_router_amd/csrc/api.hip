@@ -1,5 +1,6 @@
 // Host entry points of libmoe: argument checks, workspace layout and launch order.
 // The declarations and their contracts are in include/moe.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -41,7 +42,7 @@ struct Layout {
   int64_t R_cap;
   size_t es;         // element size of the data dtype
   int max_tiles;     // row-group tile bound, kGemmBM-row tiles (MXFP8 GEMMs)
-  int max_tiles_w;   // the same for kGemmBMWide-row tiles (bf16 GEMMs)
+  int max_tiles_w;   // the same for 256-row tiles (bound for the bf16 fused-stream GEMMs' tiles)
   int nparts;        // rowdot partials per row
   int nchunks;
   // saved
@@ -102,12 +103,28 @@ int check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
+// Tile height of the bf16 fused-stream GEMMs (256 or 320 rows): the one that pads an
+// expert's rows least, summed over the row counts m - sd, m, m + sd around the mean
+// m = T k / E of uniform routing (sd = sqrt(m), a Poisson-like spread).  320 keeps a
+// Qwen3-30B-A3B expert (m = 256) in one tile; 256 fits the 235B share's m = 1024.
+int fused_bm(const moe_shape& s) {
+  const double m = (double)s.T * s.k / s.E, sd = sqrt(m);
+  const int bm[2] = {256, 320};
+  int64_t pad[2] = {0, 0};
+  for (int i = 0; i < 2; ++i)
+    for (const double n : {m - sd, m, m + sd}) {
+      const int64_t r = n < 1.0 ? 1 : (int64_t)ceil(n);
+      pad[i] += (r + bm[i] - 1) / bm[i] * bm[i];
+    }
+  return pad[1] < pad[0] ? 320 : 256;
+}
+
 void layout(const moe_shape& s, Layout& L) {
   const int El = s.e_local;
   L.R_cap = (int64_t)s.T * (s.k < El ? s.k : El);
   L.es = s.dtype == MOE_BF16 ? 2 : 4;
   L.max_tiles = (int)ceil_div(L.R_cap, kGemmBM) + El;
-  L.max_tiles_w = (int)ceil_div(L.R_cap, kGemmBMWide) + El;
+  L.max_tiles_w = (int)ceil_div(L.R_cap, 256) + El;
   L.nparts = s.dtype == MOE_BF16 ? bwd_bf16_nparts(s.I) : s.I;
   L.nchunks = (int)ceil_div((int64_t)s.T * s.k, index_chunk((int64_t)s.T * s.k, El));
   const size_t R = (size_t)L.R_cap;
@@ -361,10 +378,11 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    // the MXFP8 GEMMs take kGemmBM-row tiles, the bf16 ones kGemmBMWide-row tiles
+    // the MXFP8 GEMMs take kGemmBM-row tiles, the bf16 ones fused_bm-row tiles
     const bool mxf = s.fwd == MOE_FWD_MXFP8;
+    const int bmw = fused_bm(s);
     int32_t* tiles = at<int32_t>(scratch, mxf ? L.off_tiles : L.off_tiles_w);
-    e = launch_tile_table(s, offsets, mxf ? kGemmBM : kGemmBMWide, tiles, nullptr, nullptr, st);
+    e = launch_tile_table(s, offsets, mxf ? kGemmBM : bmw, tiles, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     FwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
@@ -391,7 +409,7 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
       }
       e = launch_fwd_mx(a, m, st);
     } else {
-      e = launch_fwd_bf16(a, st);
+      e = bmw == 320 ? fw320::launch_fwd_bf16(a, st) : fw256::launch_fwd_bf16(a, st);
     }
   } else {
     FwdArgsF32 a{};
@@ -445,18 +463,29 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    // the MXFP8 GEMMs take kGemmBM-row tiles, the bf16 ones kGemmBMWide-row tiles
+    // kGemmBM-row tiles for the MXFP8 GEMMs, fused_bm-row tiles for the bf16 ones (B1, B3
+    // and a recomputed bf16 gate/up GEMM): one tile-table launch writes what the call needs
     const bool mxb = s.bwd == MOE_BWD_MXFP8;
-    int32_t* tiles = at<int32_t>(scratch, mxb ? L.off_tiles : L.off_tiles_w);
-    e = launch_tile_table(s, offsets, mxb ? kGemmBM : kGemmBMWide, tiles, at<int32_t>(scratch, L.off_zeros),
-                          at<int32_t>(scratch, L.off_order), st);
+    const bool mxf = s.fwd == MOE_FWD_MXFP8;
+    const bool narrow = mxb || (s.recompute && mxf);
+    const bool wide = !mxb || (s.recompute && !mxf);
+    const int bmw = fused_bm(s);
+    int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
+    int32_t* tiles_w = at<int32_t>(scratch, L.off_tiles_w);
+    int32_t* zeros = at<int32_t>(scratch, L.off_zeros);
+    int32_t* order = at<int32_t>(scratch, L.off_order);
+    if (narrow)
+      e = launch_tile_table(s, offsets, kGemmBM, tiles, zeros, order, st, bmw, wide ? tiles_w : nullptr);
+    else
+      e = launch_tile_table(s, offsets, bmw, tiles_w, zeros, order, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     BwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
     a.dy = (const bf16_t*)dy; a.x = (const bf16_t*)x; a.xp = (const bf16_t*)xp; a.offsets = offsets;
     a.row_src = row_src; a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up;
     a.wd = (const bf16_t*)w_down; a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a);
-    a.tiles = tiles; a.max_tiles = mxb ? L.max_tiles : L.max_tiles_w;
+    a.tiles = tiles; a.max_tiles = L.max_tiles;
+    a.tiles_w = tiles_w; a.max_tiles_w = L.max_tiles_w; a.bm_w = bmw;
     a.dgu = at<bf16_t>(scratch, L.off_dgu); a.dxp = at<bf16_t>(scratch, L.off_dxp);
     a.dw_part = at<float>(scratch, L.off_part);
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
@@ -470,16 +499,10 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
       FwdArgs f{};
       f.T = s.T; f.H = s.H; f.I = s.I; f.k = s.k; f.El = s.e_local;
       f.x = a.x; f.xp = a.xp; f.offsets = offsets; f.row_src = row_src; f.topk_w = topk_w;
-      f.wg = a.wg; f.wu = a.wu; f.wd = a.wd; f.tiles = a.tiles; f.max_tiles = a.max_tiles;
+      f.wg = a.wg; f.wu = a.wu; f.wd = a.wd;
+      f.tiles = mxf ? tiles : tiles_w;
+      f.max_tiles = mxf ? L.max_tiles : L.max_tiles_w;
       f.gu = rgu; f.a = ra; f.yp = nullptr;
-      const bool mxf = s.fwd == MOE_FWD_MXFP8;
-      if (mxf != mxb) {  // the recomputed gate/up GEMM takes the other tile height
-        int32_t* ftiles = at<int32_t>(scratch, mxf ? L.off_tiles : L.off_tiles_w);
-        e = launch_tile_table(s, offsets, mxf ? kGemmBM : kGemmBMWide, ftiles, nullptr, nullptr, st);
-        if (e != hipSuccess) return hip_status(e, __func__);
-        f.tiles = ftiles;
-        f.max_tiles = mxf ? L.max_tiles : L.max_tiles_w;
-      }
       if (s.fwd == MOE_FWD_MXFP8) {
         MxFwdArgs m{};
         uint8_t** bufs[8] = {&m.q_x, &m.s_x, &m.q_a, &m.s_a, &m.qt_wgu, &m.st_wgu, &m.qt_wd, &m.st_wd};
@@ -489,7 +512,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
         m.R_cap = L.R_cap;
         e = launch_fwd_mx(f, m, st, true);
       } else {
-        e = launch_fwd_gateup_bf16(f, st);
+        e = bmw == 320 ? fw320::launch_fwd_gateup_bf16(f, st) : fw256::launch_fwd_gateup_bf16(f, st);
       }
       if (e != hipSuccess) return hip_status(e, __func__);
     }

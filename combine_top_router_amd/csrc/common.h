@@ -75,8 +75,7 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, flo
 }
 
 // Host-side: the launch configuration constants shared by the host code and kernels.
-constexpr int kGemmBM = 128;      // rows of one row-group GEMM tile (MXFP8 GEMMs)
-constexpr int kGemmBMWide = 256;  // rows of one row-group GEMM tile (bf16 GEMMs, fused stream)
+constexpr int kGemmBM = 128;  // rows of one row-group GEMM tile (bf16 B1, the MXFP8 GEMMs)
 constexpr int kZeroBytes = 512;  // zeroed scratch area read in place of rows past a group's end
 // (token, slot) pairs per histogram chunk of the dispatch index: at least 1024, a
 // multiple of 256, and few enough chunks (<= 256 and <= 32768 / El) that every
@@ -118,7 +117,8 @@ hipError_t launch_route_bwd(const moe_shape& s, const float* logits, const int32
 hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
                         int32_t* row_src, int32_t* row_of, int32_t* chunk_hist, hipStream_t st);
 hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
-                             int32_t* zeros, int32_t* order, hipStream_t st);
+                             int32_t* zeros, int32_t* order, hipStream_t st, int bm2 = 0,
+                             int32_t* tiles2 = nullptr);
 hipError_t launch_gather(const moe_shape& s, const void* x, const int32_t* offsets,
                          const int32_t* row_src, void* xp, hipStream_t st);
 // bf16 with part != null: also d_topk_w from the partial row-dots (the dX combine)
@@ -152,8 +152,16 @@ struct FwdArgs {
   bf16_t* a;              // [R_cap, I]
   bf16_t* yp;             // [R_cap, H]
 };
+// The bf16 forward GEMMs on the fused stream, one build per tile height (a.tiles holds
+// tiles of that height): 256 rows (gemm_fw256.hip) or 320 rows (gemm_fw320.hip).
+namespace fw256 {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st);  // K1 only
+}  // namespace fw256
+namespace fw320 {
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st);
+}  // namespace fw320
 
 struct BwdArgs {
   int T, H, I, k, El;
@@ -168,8 +176,11 @@ struct BwdArgs {
   const bf16_t* wd;
   const bf16_t* gu;       // saved
   const bf16_t* a;        // saved
-  const int32_t* tiles;
+  const int32_t* tiles;   // kGemmBM-row tiles (B1, the MXFP8 GEMMs)
   int max_tiles;
+  const int32_t* tiles_w; // bm_w-row tiles (the bf16 B3 on the fused stream)
+  int max_tiles_w;
+  int bm_w;               // 256 or 320
   bf16_t* dgu;            // scratch [R_cap, 2I]
   bf16_t* dxp;            // scratch [R_cap, H]
   float* dw_part;         // scratch [R_cap, nparts]
@@ -182,8 +193,15 @@ struct BwdArgs {
   bf16_t* dwd;            // [El, I, H]
 };
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);  // B1 alone
-hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st);  // B3 alone
+// B1 alone and B3 alone on the fused stream, on a.tiles_w (a.bm_w-row tiles)
+namespace fw256 {
+hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st);
+}  // namespace fw256
+namespace fw320 {
+hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st);
+}  // namespace fw320
 // column parts of the B1 row-dot partials per row (dw_part is [R_cap, nparts])
 int bwd_bf16_nparts(int I);
 

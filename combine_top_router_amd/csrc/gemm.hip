@@ -6,13 +6,15 @@
 // GEMMs (Prime Mega MoE pages: one call fusing the linears, SwiGLU and combine, with
 // scratch buffers instead of intermediate tensors).
 //
-// Engine (gemm_engine.h): persistent workgroups (one per CU) of 8 compute waves and
-// dedicated load waves, BM x 256 output tile, K step 64, each compute wave a (BM / 2) x
-// 64 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  The load waves move operand
-// tiles global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4)
-// into a ring of LDS stages, DEPTH K steps ahead, one barrier per K step, and a
-// workgroup's tiles form one stream of K steps, so the next tile's loads fly while the
-// current tile's epilogue runs.  An operand whose contraction axis is contiguous in
+// Engine (gemm_engine.h): persistent workgroups (one per CU), BM x 256 output tile, K
+// step 64, each of 8 compute waves a (BM / 2) x 64 sub-tile of v_mfma_f32_32x32x16_bf16
+// accumulators.  Operand tiles move global -> LDS with the gfx950 direct-to-LDS loads
+// (global_load_lds_dwordx4) into a ring of LDS stages, DEPTH K steps ahead, one barrier
+// per K step, and a workgroup's tiles form one stream of K steps, so the next tile's
+// loads fly while the current tile's epilogue runs.  The bf16 gate/up, down, dA and dX
+// GEMMs run on the fused stream (256- or 320-row tiles; every wave loads and computes,
+// gemm_fw256.hip / gemm_fw320.hip); the weight gradients and the MXFP8 GEMMs on
+// dedicated load waves (128-row tiles; gemm.hip / gemm_mx.hip).  An operand whose contraction axis is contiguous in
 // memory ("K-major") is stored [rows][64] and read with 16-byte LDS reads; an operand
 // contiguous along M or N ("MN-major": row-major weights as the B of x*W, and both
 // operands of the weight gradients, which contract over token rows) is stored
@@ -45,26 +47,12 @@ struct RowTileInfo {
   int nk;
 };
 
-// Row-tiled loader state common to every kernel.  These loaders stage through registers
-// (load / store of a Slot).
+// Row-tiled bf16 loader state common to the fused-stream kernels: dma(kt, stage) issues
+// the wave's NLOAD direct-to-LDS loads of K step kt.
 struct RowLd {
-  static constexpr int NLOAD = A_LP + B_LP;  // register loads per position
+  static constexpr int NLOAD = A_LP + B_LP;
   int nk;
   int pw;
-};
-struct RowSlot {
-  i32x4 a[A_LP];
-  i32x4 b[B_LP];
-  // wait until at most N of this wave's loads are in flight; each register is then
-  // passed through an empty asm, so nothing reads it before the wait
-  template <int N>
-  __device__ __forceinline__ void ready() {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-#pragma unroll
-    for (int q = 0; q < A_LP; ++q) asm volatile("" : "+v"(a[q]));
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) asm volatile("" : "+v"(b[q]));
-  }
 };
 
 // K-major A rows of a row tile for load wave pw: the lane's chunk of each of its A_LP
@@ -102,7 +90,7 @@ constexpr int MX_STEP = 128;               // codes per K step
 constexpr int MX_SC_SLOT = 512 * 4;        // scale bytes per stage
 constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per load wave
 static_assert(MX_STEP == 2 * BK, "an fp8 step must span the bytes of a bf16 step");
-static_assert(MX_SC_LP * NP * 64 == 512 && BM + BN <= 512, "scale slots");
+static_assert(FW || (MX_SC_LP * NP * 64 == 512 && BM + BN <= 512), "scale slots");
 
 __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int lane) {
   const int c0 = kk * 4 + (lane >> 5);
@@ -117,14 +105,14 @@ __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int
 // The scaled MFMAs of one stage for a job J: B rows J::ncol(wn, ni) as in mma_stage.
 template <class J>
 __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, Acc& acc, int lane,
-                                           int wm, int wn) {
+                                           const WaveRows& w, int wn) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     i32x8 af[MI], bf[NI];
     int sa[MI], sb[NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int r = wm * WROWS + mi * 32 + (lane & 31);
+      const int r = w.base + mi * 32 + (lane & 31);
       af[mi] = frag_fp8(st, r, kk, lane);
       sa[mi] = sc[r * 4 + kk * 2 + (lane >> 5)];
     }
@@ -148,22 +136,6 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
 struct LMx {
   static constexpr bool GATHER = false;
   static constexpr int NVMEM = LOADS + MX_SC_LP;
-  static constexpr int NLOAD = NVMEM;  // register loads per position (row-tiled jobs)
-  struct Slot {
-    i32x4 a[A_LP];
-    i32x4 b[B_LP];
-    int s[MX_SC_LP];
-    template <int N>
-    __device__ __forceinline__ void ready() {
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-#pragma unroll
-      for (int q = 0; q < A_LP; ++q) asm volatile("" : "+v"(a[q]));
-#pragma unroll
-      for (int q = 0; q < B_LP; ++q) asm volatile("" : "+v"(b[q]));
-#pragma unroll
-      for (int q = 0; q < MX_SC_LP; ++q) asm volatile("" : "+v"(s[q]));
-    }
-  };
   int nk, pw;
   const uint8_t* a[A_LP];       // codes of the lane's slot at K step 0
   const uint8_t* b[B_LP];
@@ -179,23 +151,6 @@ struct LMx {
 #pragma unroll
     for (int q = 0; q < MX_SC_LP; ++q)
       dma4(sp[q] + kt * (MX_STEP / 32), scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256);
-  }
-  __device__ __forceinline__ void load(int kt, Slot& t) const {
-#pragma unroll
-    for (int q = 0; q < A_LP; ++q) t.a[q] = gload16(reinterpret_cast<const bf16_t*>(a[q] + kt * MX_STEP));
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) t.b[q] = gload16(reinterpret_cast<const bf16_t*>(b[q] + kt * MX_STEP));
-#pragma unroll
-    for (int q = 0; q < MX_SC_LP; ++q) t.s[q] = gload4(sp[q] + kt * (MX_STEP / 32));
-  }
-  __device__ __forceinline__ void store(const Slot& t, bf16_t* st, int slot) const {
-#pragma unroll
-    for (int q = 0; q < A_LP; ++q) lds_put16(a_dst(st, q, pw), t.a[q]);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), t.b[q]);
-#pragma unroll
-    for (int q = 0; q < MX_SC_LP; ++q)
-      *reinterpret_cast<int*>(scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256 + (threadIdx.x & 63) * 4) = t.s[q];
   }
   // operand rows: A row r (of tile) at a_base + ra(r) * lda, B row n at b_base + rb(n) * ldb;
   // both matrices' scales have row stride ld / 32 and start at s_a / s_b
@@ -234,17 +189,6 @@ struct LGateUp : RowLd {
   KRows a;
   const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
   size_t bstep;           // elements per K step of the weights (64 rows)
-  using Slot = RowSlot;
-  __device__ __forceinline__ void load(int kt, Slot& s) const {
-    a.load(kt, s.a);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
-  }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
-    a.put(s.a, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
-  }
   __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
     a.dma(kt, st, pw);
 #pragma unroll
@@ -259,8 +203,7 @@ struct JGateUp {
   using Tile = RowTileInfo;
   using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
-  static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
-  static constexpr bool TRANS = true, EPI_LDS = true;
+  static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
   }
@@ -273,10 +216,11 @@ struct JGateUp {
   __device__ __forceinline__ void tile(int v, Tile& p) const {
     row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN / 2, p);
   }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm, int wn) const {
-    if constexpr (MX) mx_compute<JGateUp>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
-    else mma_stage<JGateUp>(st, acc, lane, wm, wn);
+  __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
+                                          int wn) const {
+    if constexpr (MX) mx_compute<JGateUp>(st, scring + slot * MX_SC_SLOT, acc, lane, w, wn);
+    else mma_stage<JGateUp>(st, acc, lane, w, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
@@ -326,9 +270,10 @@ struct JGateUp {
     bf16_t* const gub = keep_gu ? a.gu + (size_t)p.t.rs * I2 : nullptr;
     bf16_t* const ab = a.a + (size_t)p.t.rs * a.I;
     const int colw = p.n0 + wn * (WCOLS / 2);  // the wave's first intermediate column
+    const WaveRows w = wave_rows(p.t.cnt, wm);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int rb = wm * WROWS + mi * 32;   // the band's first row in the tile
+      const int rb = w.base + mi * 32;   // the band's first row in the tile
       f32x16 av;
 #pragma unroll
       for (int i = 0; i < 16; ++i) av[i] = silu_f(acc[mi][0][i]) * acc[mi][1][i];
@@ -337,7 +282,7 @@ struct JGateUp {
         int X;
         const i32x4 codes = mx_row_codes(av, X);
         const int rt = rb + (lane & 31);
-        if (rt < p.t.cnt && colw < a.I) {
+        if (rt < w.end && colw < a.I) {
           const size_t r = (size_t)(p.t.rs + rt);
           *reinterpret_cast<i32x4*>(m.q_a + r * a.I + colw + 16 * (lane >> 5)) = codes;
           if (lane < 32) m.s_a[r * (a.I / 32) + colw / 32] = (uint8_t)(X + 127);
@@ -351,7 +296,7 @@ struct JGateUp {
           trans_chunks(acc[mi][g], ch[0]);
           band_store(wreg, ch, [&](int rr, int cb, i32x4 v) {
             const int rt = rb + rr, col = colw + cb;
-            if (rt < p.t.cnt && col < a.I)
+            if (rt < w.end && col < a.I)
               *reinterpret_cast<i32x4*>(gub + ((uint32_t)rt * I2 + (uint32_t)col + (g ? (uint32_t)a.I : 0u))) = v;
           });
         }
@@ -360,7 +305,7 @@ struct JGateUp {
       trans_chunks(av, ca[0]);
       band_store(wreg, ca, [&](int rr, int cb, i32x4 v) {
         const int rt = rb + rr, col = colw + cb;
-        if (rt < p.t.cnt && col < a.I)
+        if (rt < w.end && col < a.I)
           *reinterpret_cast<i32x4*>(ab + ((uint32_t)rt * (uint32_t)a.I + (uint32_t)col)) = v;
       });
     }
@@ -381,17 +326,6 @@ struct LMnB : RowLd {
   KRows a;
   const bf16_t* b[B_LP];
   size_t bstep;
-  using Slot = RowSlot;
-  __device__ __forceinline__ void load(int kt, Slot& s) const {
-    a.load(kt, s.a);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16(b[q] + kt * bstep);
-  }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
-    a.put(s.a, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
-  }
   __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
     a.dma(kt, st, pw);
 #pragma unroll
@@ -406,8 +340,7 @@ struct JDown {
   using Tile = RowTileInfo;
   using Ld = typename std::conditional<MX, LMx, LMnB>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
-  static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (register staging spills)
-  static constexpr bool TRANS = true, EPI_LDS = true;
+  static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
   MxFwdArgs m;
@@ -416,10 +349,11 @@ struct JDown {
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.I / MX_STEP : a.I / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm, int wn) const {
-    if constexpr (MX) mx_compute<JDown>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
-    else mma_stage<JDown>(st, acc, lane, wm, wn);
+  __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
+                                          int wn) const {
+    if constexpr (MX) mx_compute<JDown>(st, scring + slot * MX_SC_SLOT, acc, lane, w, wn);
+    else mma_stage<JDown>(st, acc, lane, w, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
@@ -455,22 +389,23 @@ struct JDown {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
     bf16_t* const wreg = reinterpret_cast<bf16_t*>(stage) + wv * BAND_ELEMS;
+    const WaveRows w = wave_rows(p.t.cnt, wm);
     float wr[MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int rt = min(wm * WROWS + mi * 32 + (lane & 31), p.t.cnt - 1);
+      const int rt = min(w.base + mi * 32 + (lane & 31), p.t.cnt - 1);
       wr[mi] = a.topk_w[a.row_src[p.t.rs + rt]];
     }
     bf16_t* const yb = a.yp + (size_t)p.t.rs * a.H;  // the tile's first row
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int rb = wm * WROWS + mi * 32;
+      const int rb = w.base + mi * 32;
       i32x4 ch[NI][2];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) trans_chunks(acc[mi][ni] * wr[mi], ch[ni]);
       band_store(wreg, ch, [&](int rr, int cb, i32x4 v) {
         const int rt = rb + rr, col = p.n0 + wn * WCOLS + cb;
-        if (rt < p.t.cnt && col < a.H)
+        if (rt < w.end && col < a.H)
           *reinterpret_cast<i32x4*>(yb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = v;
       });
     }
@@ -491,19 +426,6 @@ struct LKK : RowLd {
   const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
   const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
   int ksplit;              // B3: I / 64; B1: larger than any step count
-  using Slot = RowSlot;
-  __device__ __forceinline__ void load(int kt, Slot& s) const {
-    a.load(kt, s.a);
-    const bool second = kt >= ksplit;
-    const int k0 = (second ? kt - ksplit : kt) * BK;
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) s.b[q] = gload16((second ? b2[q] : b[q]) + k0);
-  }
-  __device__ __forceinline__ void store(const Slot& s, bf16_t* st, int) const {
-    a.put(s.a, st, pw);
-#pragma unroll
-    for (int q = 0; q < B_LP; ++q) lds_put16(b_dst(st, q, pw), s.b[q]);
-  }
   __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
     a.dma(kt, st, pw);
     const bool second = kt >= ksplit;
@@ -525,8 +447,7 @@ struct JDa {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
-  static constexpr bool DYN = false, REG = !MX;  // the fp8 B1 is faster with direct-to-LDS loads
-  static constexpr bool TRANS = false, EPI_LDS = true;
+  static constexpr bool DYN = false, TRANS = false, EPI_LDS = true;
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -536,11 +457,11 @@ struct JDa {
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
+  __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
-    if constexpr (MX) mx_compute<JDa>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
-    else mma_stage<JDa>(st, acc, lane, wm, wn);
+    if constexpr (MX) mx_compute<JDa>(st, scring + slot * MX_SC_SLOT, acc, lane, w, wn);
+    else mma_stage<JDa>(st, acc, lane, w, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
@@ -577,16 +498,17 @@ struct JDa {
     // staging starts (read back by row: no per-lane array indexed in the rolled row loop,
     // which would live in scratch memory)
     const int wv = threadIdx.x >> 6;
+    const WaveRows w = wave_rows(p.t.cnt, wm);
 #pragma unroll
     for (int i = lane; i < WROWS; i += 64)
-      wrow[wv * WROWS + i] = a.topk_w[a.row_src[p.t.rs + min(wm * WROWS + i, p.t.cnt - 1)]];
-    epilogue_rows(stage, acc, [&](int rt, int ct, const float (&dap)[8], int) {
+      wrow[wv * WROWS + i] = a.topk_w[a.row_src[p.t.rs + min(w.base + i, p.t.cnt - 1)]];
+    epilogue_rows(stage, acc, w, [&](int rt, int ct, const float (&dap)[8], int) {
       const int col = p.n0 + ct;
-      const bool ok = rt < p.t.cnt && col < a.I;
+      const bool ok = rt < w.end && col < a.I;
       float part = 0.f;
       if (ok) {
         const uint32_t og = (uint32_t)rt * I2 + (uint32_t)col, oa = (uint32_t)rt * (uint32_t)a.I + (uint32_t)col;
-        const float w = wrow[wv * WROWS + (rt - wm * WROWS)];
+        const float wt = wrow[wv * WROWS + (rt - w.base)];
         // two columns at a time, straight from and back to packed bf16 pairs
         __builtin_amdgcn_sched_barrier(0);
         const i32x4 gw = *reinterpret_cast<const i32x4*>(gub + og);
@@ -604,8 +526,8 @@ struct JDa {
             const float av = __uint_as_float(h ? ab & 0xffff0000u : ab << 16);
             const float d = dap[2 * q + h];
             part += d * av;
-            aw2[h] = w * av;
-            const float da = w * d;
+            aw2[h] = wt * av;
+            const float da = wt * d;
             const float sg = sigmoid_f(g);
             du2[h] = da * g * sg;
             dg2[h] = da * u * sg * (1.f + g * (1.f - sg));
@@ -620,7 +542,7 @@ struct JDa {
       }
 #pragma unroll
       for (int off = 1; off < EP_LPR; off <<= 1) part += __shfl_xor(part, off, 64);
-      if (rt < p.t.cnt && lane % EP_LPR == 0) a.dw_part[(size_t)(p.t.rs + rt) * nparts + p.t.nt * WN + wn] = part;
+      if (rt < w.end && lane % EP_LPR == 0) a.dw_part[(size_t)(p.t.rs + rt) * nparts + p.t.nt * WN + wn] = part;
     });
   }
 };
@@ -641,8 +563,7 @@ struct JDx {
   using Tile = RowTileInfo;
   using Ld = KKLd<MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
-  static constexpr bool DYN = false, REG = !MX;  // fp8: direct-to-LDS loads (its compute side spills)
-  static constexpr bool TRANS = true, EPI_LDS = true;
+  static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -651,11 +572,11 @@ struct JDx {
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? 2 * a.I / MX_STEP : 2 * a.I / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
-  __device__ __forceinline__ bool active(const Tile& p, int wm) const { return wm * WROWS < p.t.cnt; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
+  __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
-    if constexpr (MX) mx_compute<JDx>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
-    else mma_stage<JDx>(st, acc, lane, wm, wn);
+    if constexpr (MX) mx_compute<JDx>(st, scring + slot * MX_SC_SLOT, acc, lane, w, wn);
+    else mma_stage<JDx>(st, acc, lane, w, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
@@ -686,15 +607,16 @@ struct JDx {
     const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
     bf16_t* const wreg = reinterpret_cast<bf16_t*>(stage) + wv * BAND_ELEMS;
     bf16_t* const xb = a.dxp + (size_t)p.t.rs * a.H;  // the tile's first row
+    const WaveRows w = wave_rows(p.t.cnt, wm);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int rb = wm * WROWS + mi * 32;
+      const int rb = w.base + mi * 32;
       i32x4 ch[NI][2];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) trans_chunks(acc[mi][ni], ch[ni]);
       band_store(wreg, ch, [&](int rr, int cb, i32x4 v) {
         const int rt = rb + rr, col = p.n0 + wn * WCOLS + cb;
-        if (rt < p.t.cnt && col < a.H)
+        if (rt < w.end && col < a.H)
           *reinterpret_cast<i32x4*>(xb + ((uint32_t)rt * (uint32_t)a.H + (uint32_t)col)) = v;
       });
     }
@@ -788,7 +710,7 @@ struct JWgrad {
   // else it is the identity, a.order[El] = 0, and the items go out in contiguous XCD
   // ranges.  a.order[El + 1 + WHICH] is the launch's item counter (zeroed with the order).
   // the accumulators hold C^T; the epilogue writes them as bf16 row bands (band_store)
-  static constexpr bool DYN = true, REG = false, TRANS = true, EPI_LDS = true;
+  static constexpr bool DYN = true, TRANS = true, EPI_LDS = true;
   __device__ __forceinline__ bool dynamic() const { return sload(a.order + a.El) != 0; }
   __device__ __forceinline__ int32_t* counter() const { return a.order + a.El + 1 + WHICH; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
@@ -812,11 +734,11 @@ struct JWgrad {
       p.nk = uni((cnt + BK - 1) / BK);
     }
   }
-  __device__ __forceinline__ bool active(const Tile&, int) const { return true; }
-  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, int wm,
+  __device__ __forceinline__ WaveRows rows(const Tile&, int wm) const { return {wm * WROWS, BM, MI}; }
+  __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
-    if constexpr (MX) mx_compute<JWgrad>(st, scring + slot * MX_SC_SLOT, acc, lane, wm, wn);
-    else mma_stage<JWgrad>(st, acc, lane, wm, wn);
+    if constexpr (MX) mx_compute<JWgrad>(st, scring + slot * MX_SC_SLOT, acc, lane, w, wn);
+    else mma_stage<JWgrad>(st, acc, lane, w, wn);
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     const int M = WHICH == 0 ? a.I : a.H, N = WHICH == 0 ? a.H : 2 * a.I;
@@ -933,7 +855,11 @@ hipError_t launch_bwd_gemms(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
 }  // namespace
 
 #if MOE_GEMM_FW
-// The bf16 row-tiled GEMMs on the fused stream: a.tiles holds kGemmBMWide-row tiles.
+// The bf16 gate/up, down and dX GEMMs on the fused stream, in namespace fw256 or fw320 by
+// tile height; a.tiles (B3: a.tiles_w) holds tiles of that height.
+#define MOE_FW_CAT2(a, b) a##b
+#define MOE_FW_CAT(a, b) MOE_FW_CAT2(a, b)
+namespace MOE_FW_CAT(fw, MOE_GEMM_FW) {
 hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
@@ -954,18 +880,24 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st) {
   MxArgs m{};
-  return launch_bwd_gemms<false>(a, m, st);
+  BwdArgs b = a;
+  b.tiles = a.tiles_w;
+  b.max_tiles = a.max_tiles_w;
+  return launch_bwd_gemms<false>(b, m, st);
 }
 
 hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st) {
-  if (a.max_tiles == 0) return hipSuccess;
+  if (a.max_tiles_w == 0) return hipSuccess;
   MxArgs m{};
-  MOE_LAUNCH("bwd_dX", k_bwd_dx<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0, st,
-             a, m);
+  BwdArgs b = a;
+  b.tiles = a.tiles_w;
+  b.max_tiles = a.max_tiles_w;
+  MOE_LAUNCH("bwd_dX", k_bwd_dx<false>, dim3(grid_for((int64_t)b.max_tiles * ceil_div(b.H, BN))), dim3(NTHR), 0, st,
+             b, m);
   return hipGetLastError();
 }
 
-static_assert(BM == kGemmBMWide, "the fused-stream GEMMs read kGemmBMWide-row tiles");
+}  // namespace fw256 / fw320
 #endif  // MOE_GEMM_FW
 
 #if MOE_GEMM_MX_TU
@@ -1009,17 +941,20 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, b
 #if !MOE_GEMM_MX_TU && !MOE_GEMM_FW
 int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
 
-// B1 and B3 run on the fused stream (gemm_fw.hip), the weight gradients here.
+
+// B1 and B3 run on the fused stream (gemm_fw256.hip or gemm_fw320.hip, by a.bm_w), the
+// weight gradients here.
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   MxArgs m{};
-  hipError_t e = launch_bwd_da_bf16(a, st);
+  const bool f320 = a.bm_w == 320;
+  hipError_t e = f320 ? fw320::launch_bwd_da_bf16(a, st) : fw256::launch_bwd_da_bf16(a, st);
   if (e != hipSuccess) return e;
   {
     const int tm = (int)ceil_div(a.I, BM), tn = (int)ceil_div(a.H, BN);
     MOE_LAUNCH("bwd_dWd", (k_bwd_wgrad<0, false>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a, m,
                tm, tn);
   }
-  e = launch_bwd_dx_bf16(a, st);
+  e = f320 ? fw320::launch_bwd_dx_bf16(a, st) : fw256::launch_bwd_dx_bf16(a, st);
   if (e != hipSuccess) return e;
   {
     const int tm = (int)ceil_div(a.H, BM), tn = (int)ceil_div(2 * a.I, BN);

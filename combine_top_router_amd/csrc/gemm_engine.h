@@ -1,11 +1,11 @@
 // Shared GEMM engine of the bf16 and MXFP8 grouped GEMMs (internal header).
 //
-// Persistent workgroups (one per CU) of NW compute waves and NP load waves.  BM x 256
-// output tile, each compute wave a (BM / 2) x 64 sub-tile as 32x32 MFMA accumulator
-// blocks.  Operand tiles move global -> LDS into a three-stage LDS ring, one barrier per
-// K step, either with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4) issued
-// two K steps ahead, or (row-tiled jobs) through the load waves' registers, read four
-// K steps ahead and written to the ring two steps ahead.  An operand whose contraction
+// Persistent workgroups (one per CU).  BM x 256 output tile, each of the NW compute waves
+// a (BM / 2) x 64 sub-tile as 32x32 MFMA accumulator blocks.  Operand tiles move
+// global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4) into a ring
+// of LDS stages, one barrier per K step: issued by NP dedicated load waves two K steps
+// ahead into three stages (load-wave streams), or by the compute waves themselves one
+// step ahead into two larger stages (the fused stream).  An operand whose contraction
 // axis is contiguous in memory ("K-major") is stored [rows][BK] and read with 16-byte LDS
 // reads; an operand contiguous along M or N ("MN-major") is stored [BK][width] and read
 // with the transposing LDS read ds_read_b64_tr_b16.  Both layouts are XOR-swizzled by
@@ -25,22 +25,25 @@
 namespace moe {
 namespace {
 
-// Two workgroup shapes, one per translation unit:
+// Two workgroup shapes, chosen per translation unit:
 // * load-wave streams (gemm.hip, gemm_mx.hip): 128 x 256 tiles, a three-stage ring (48 KB
 //   stages), NW compute waves and NP dedicated load waves;
-// * the fused stream (MOE_GEMM_FW, gemm_fw.hip: the bf16 row-tiled GEMMs): 256 x 256
-//   tiles, a two-stage ring (64 KB stages), eight waves that each issue one eighth of the
-//   operand loads and compute a 128 x 64 sub-tile.  Eight waves per CU leave each 256
-//   registers, room for 128 accumulators; the larger tile asks a third fewer operand
-//   bytes per flop of the CU's L2 request path, which bounds the load-wave kernels.
+// * the fused stream (MOE_GEMM_FW = the tile height, 256 in gemm_fw256.hip or 320 in
+//   gemm_fw320.hip: the bf16 gate/up, down and dX GEMMs): 256- or 320-row tiles of 256
+//   columns, a two-stage ring (64 or 72 KB stages), eight waves that each issue one eighth
+//   of the operand loads and compute a (BM / 2) x 64 sub-tile.  Eight waves per CU leave
+//   each 256 registers, room for up to 160 accumulators; the larger tile asks a third
+//   fewer operand bytes per flop of the CU's L2 request path, which bounds the load-wave
+//   kernels.
 #ifndef MOE_GEMM_MX_TU
 #define MOE_GEMM_MX_TU 0
 #endif
 #ifndef MOE_GEMM_FW
 #define MOE_GEMM_FW 0
 #endif
-constexpr bool FW = MOE_GEMM_FW;
-constexpr int BM = FW ? 256 : 128, BN = 256, BK = 64;
+constexpr bool FW = MOE_GEMM_FW != 0;
+static_assert(MOE_GEMM_FW == 0 || MOE_GEMM_FW == 256 || MOE_GEMM_FW == 320, "fused-stream tile heights");
+constexpr int BM = FW ? MOE_GEMM_FW : 128, BN = 256, BK = 64;
 constexpr int NSTAGE = FW ? 2 : 3;   // LDS ring stages
 constexpr int DEPTH = NSTAGE - 1;    // K steps in flight ahead of the MFMAs
 constexpr int NW = 8;                // compute waves: 2 along M x 4 along N
@@ -66,12 +69,11 @@ constexpr int B_LP = B_INSTR / NP;
 constexpr int LOADS = A_LP + B_LP;                // operand loads per load wave per stage
 constexpr int LDS_ELEMS = NSTAGE * STAGE_ELEMS;
 using Acc = f32x16[MI][NI];                       // a compute wave's accumulators
-static_assert(MI * NI * 16 <= 128, "accumulators of one wave");
+static_assert(MI * NI * 16 <= (FW ? 160 : 128), "accumulators of one wave");
 static_assert(A_LP * NP == A_INSTR && B_LP * NP == B_INSTR, "wave loads divide among the load waves");
 constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
 constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per load wave, two positions of gathered row indices
 constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least (see Sched::len)
-constexpr int REG_AHEAD = 2;                      // register-staged loads: K steps held in registers
 
 // ---- scalar loads ----
 // A wave-uniform load through the scalar data cache (address space 4): it is counted
@@ -132,24 +134,6 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
 __device__ __forceinline__ bf16_t* a_dst(bf16_t* st, int q, int pw) { return st + load_instr(q, pw) * 512; }
 __device__ __forceinline__ bf16_t* b_dst(bf16_t* st, int q, int pw) { return st + A_ELEMS + load_instr(q, pw) * 512; }
 
-// Register-staged loads: a load wave reads its 16-byte chunks of a stage into
-// registers and later writes them to the same LDS slots a direct-to-LDS load would fill
-// (lane l at slot base + 16 l bytes).  The load is inline assembly, so the compiler
-// adds no wait of its own: the stream waits with an explicit vmcnt that also names the
-// registers (slot_ready), so no use of them can be placed before it.
-__device__ __forceinline__ i32x4 gload16(const bf16_t* p) {
-  i32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ void lds_put16(bf16_t* wave_base, i32x4 v) {
-  *reinterpret_cast<i32x4*>(wave_base + (threadIdx.x & 63) * 8) = v;
-}
-__device__ __forceinline__ int gload4(const void* p) {
-  int v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
 
 // MFMA 32x32x16 operand fragment: lane l gets 8 consecutive k of row/col (l & 31),
 // k = 8 * (l >> 5) .. +7 inside the 16-wide k sub-step kk.
@@ -179,11 +163,25 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const bf16_t* s, int base, int kk, 
   return out;
 }
 
-// The bf16 MFMAs of one stage for a job J (J::A_KMAJ, J::B_KMAJ, J::ncol).  With J::TRANS
+// The rows [base, end) of a row tile of cnt rows that compute wave row wm holds, in nblk
+// 32-row accumulator blocks with rows (wave-uniform): wave row wm takes rows
+// wm * WROWS .. + WROWS - 1.  A wave without rows (nblk = 0) skips its MFMAs.
+struct WaveRows {
+  int base, end, nblk;
+};
+__device__ __forceinline__ WaveRows wave_rows(int cnt, int wm) {
+  const int b = wm * WROWS, e = min(cnt, b + WROWS);
+  return {b, e, e > b ? (e - b + 31) >> 5 : 0};
+}
+
+// The bf16 MFMAs of one stage for a job J (J::A_KMAJ, J::B_KMAJ, J::ncol) over the
+// wave's MI 32-row blocks from row w.base (blocks past w.nblk compute on rows that the
+// tile does not hold and their results are discarded: skipping them by branch measured
+// slower).  With J::TRANS
 // the two fragments enter the MFMA in swapped roles, so that each 32x32 accumulator block
 // holds the transpose of its block of C (see trans_chunks).
 template <class J>
-__device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, int wm, int wn) {
+__device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, const WaveRows& w, int wn) {
   const bf16_t* As = st;
   const bf16_t* Bs = st + A_ELEMS;
 #pragma unroll
@@ -191,8 +189,7 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, 
     bf16x8 af[MI], bf[NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
-      af[mi] = J::A_KMAJ ? frag_kmaj(As, wm * WROWS + mi * 32, kk, lane)
-                         : frag_mnmaj<BM>(As, wm * WROWS + mi * 32, kk, lane);
+      af[mi] = J::A_KMAJ ? frag_kmaj(As, w.base + mi * 32, kk, lane) : frag_mnmaj<BM>(As, w.base + mi * 32, kk, lane);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
       bf[ni] = J::B_KMAJ ? frag_kmaj(Bs, J::ncol(wn, ni), kk, lane) : frag_mnmaj<BN>(Bs, J::ncol(wn, ni), kk, lane);
@@ -202,6 +199,10 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, 
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = J::TRANS ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[ni], af[mi], acc[mi][ni], 0, 0, 0)
                                : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    // 320-row fused stream: the next sub-step's fragments are not read ahead of these
+    // MFMAs (160 accumulators leave no room for them; the SIMD's other wave fills the
+    // LDS wait)
+    if constexpr (FW && MI > 4) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -374,7 +375,8 @@ struct Sched {
 //
 // A job J supplies: items(); steps(v) (K steps of item v; scalar loads only); the
 // compute side -- Tile, tile(v, Tile&) (what the epilogue needs, scalar loads only),
-// active(const Tile&, wm), compute(stage pointer, stage index, acc, lane, wm, wn) and
+// rows(const Tile&, wm) (the WaveRows of wave row wm), compute(stage pointer, stage index,
+// acc, lane, WaveRows, wn) and
 // epilogue(const Tile&, acc, staging); and the load side -- Ld, setup(v, Ld&, pw,
 // lane) and Ld::NVMEM, Ld::GATHER, Ld::issue(kt, stage pointer, stage index, parity,
 // fetch_next) and Ld::fetch(kt, parity).  Each issue makes exactly NVMEM vector memory
@@ -396,14 +398,15 @@ __device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, S sc, 
   for (int t = 0;; ++t) {
     const int nk = cur.nk, len = sc.len(nk);
     int vn = sc.dyn ? -1 : sc.next(v);
-    const bool act = __builtin_amdgcn_readfirstlane((int)job.active(cur, wm)) != 0;
+    const WaveRows wr = job.rows(cur, wm);
+    const bool act = wr.nblk > 0;
     int done = 0, grabbed = 0;
     for (int kc = 0; kc < len; ++kc) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       // dynamic: wave 0 takes the next item before its MFMAs and publishes it after
       // them; every compute wave reads it after the next barrier
       if (sc.dyn && kc == 0 && wv == 0 && lane == 0) grabbed = sc.grab();
-      if (kc < nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wm, wn);
+      if (kc < nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wr, wn);
       if (sc.dyn) {
         if (kc == 0 && wv == 0) {
           const int n = uni(grabbed);
@@ -504,76 +507,6 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing repeated loads
 }
 
-// The load side for jobs whose loaders stage through registers (J::REG) and whose
-// tiles all take the same number of K steps.  The load cursor runs DEPTH + REG_AHEAD
-// positions ahead of the MFMAs: at position c the load waves write the registers of
-// position c + DEPTH into the stage freed by the barrier and refill them with the loads
-// of position c + DEPTH + REG_AHEAD, so 2 + DEPTH K steps of operands are in flight
-// (the LDS ring alone holds DEPTH).  The compiler orders each LDS write after its loads.
-template <class J, class S>
-__device__ __forceinline__ void load_stream_reg(const J& job, bf16_t* lds, S sc, int pw, int lane) {
-  static_assert(!J::DYN, "register-staged streams walk a fixed schedule");
-  using P = typename J::Ld;
-  using Slot = typename P::Slot;
-  int ntiles = 0;
-  for (int u = sc.v; u >= 0; u = sc.next(u)) ++ntiles;
-  P L;
-  int lv = sc.v;
-  job.setup(lv, L, pw, lane);
-  const int len = max(L.nk, MIN_STEPS);     // the same for every tile of the job
-  const int total = ntiles * len;           // stream positions of this workgroup
-  int lk = 0;                               // load cursor: step lk of item lv
-  // Every call issues its loads, also past the stream's end (then of the last tile,
-  // unused), so the two slots' loads alternate in a fixed order and the compiler's waits
-  // before each slot's LDS writes stay exact.
-  auto load_next = [&](Slot& t) {
-    L.load(min(lk, L.nk - 1), t);
-    if (lv >= 0 && ++lk == len) {
-      lk = 0;
-      const int nv = sc.next(lv);
-      lv = nv;
-      if (nv >= 0) job.setup(nv, L, pw, lane);
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    Slot t;
-    load_next(t);
-    t.template ready<0>();
-    L.store(t, lds + d * STAGE_ELEMS, d);  // total >= MIN_STEPS > DEPTH
-  }
-  Slot sl[REG_AHEAD];
-#pragma unroll
-  for (int r = 0; r < REG_AHEAD; ++r) load_next(sl[r]);  // positions DEPTH .. DEPTH + REG_AHEAD - 1
-  auto position = [&](int c, Slot& t) {
-    if (J::EPI_LDS && c > 0 && c % len == 0) asm volatile("s_barrier" ::: "memory");  // the previous tile's epilogue barrier
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // t's loads are the oldest in flight: the other slots' may still fly
-    t.template ready<(REG_AHEAD - 1) * P::NLOAD>();
-    // past the stream's end (p >= total) this fills a stage no position reads any more
-    const int p = c + DEPTH;
-    L.store(t, lds + (p % NSTAGE) * STAGE_ELEMS, p % NSTAGE);
-    load_next(t);  // position p + REG_AHEAD
-  };
-  for (int c = 0;; c += REG_AHEAD) {
-    bool end = false;
-#pragma unroll
-    for (int r = 0; r < REG_AHEAD; ++r) {
-      if (!end) {
-        position(c + r, sl[r]);
-        end = c + r + 1 >= total;
-      }
-    }
-    if (end) break;
-  }
-  // the loads past the end: waited for with their registers still live (read and
-  // written after the wait), so no register of an in-flight load is given to other
-  // values before the load has landed
-#pragma unroll
-  for (int r = 0; r < REG_AHEAD; ++r) sl[r].template ready<0>();
-  if constexpr (J::EPI_LDS) asm volatile("s_barrier" ::: "memory");  // the last tile's epilogue barrier
-}
-
 // The fused stream (FW): every wave is compute wave wv and load wave wv.  At each
 // position it waits for its own loads of the position, meets the other waves at the
 // barrier (after which the position's stage is complete and the stage read one position
@@ -602,7 +535,11 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
     if (++lk == len) {
       lk = 0;
       lv = sc.next(lv);
-      if (lv >= 0) job.setup(lv, L, wv, lane);
+      // an opaque copy of the lane index: the per-lane load offsets are recomputed here
+      // rather than held in registers across the whole stream
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      if (lv >= 0) job.setup(lv, L, wv, ln);
     }
   };
 #pragma unroll
@@ -610,7 +547,7 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
   T cur;
   int cv = sc.v;
   job.tile(cv, cur);
-  bool act = uni((int)job.active(cur, wm)) != 0;
+  WaveRows wr = job.rows(cur, wm);
   Acc acc;
   zero_acc(acc);
   int ck = 0, cs = 0;
@@ -621,7 +558,7 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (p + DEPTH < total) issue(cs + DEPTH < NSTAGE ? cs + DEPTH : cs + DEPTH - NSTAGE);
-    if (ck < cur.nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wm, wn);
+    if (ck < cur.nk && wr.nblk > 0) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wr, wn);
     const int done = cs;
     cs = cs == NSTAGE - 1 ? 0 : cs + 1;
     if (++ck < len) continue;
@@ -632,7 +569,7 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
     cv = sc.next(cv);
     if (cv < 0) break;
     job.tile(cv, cur);
-    act = uni((int)job.active(cur, wm)) != 0;
+    wr = job.rows(cur, wm);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -651,8 +588,7 @@ __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   if constexpr (FW) {
     fused_stream(job, lds, sc, wv, lane);
   } else if (wv >= NW) {
-    if constexpr (J::REG) load_stream_reg(job, lds, sc, wv - NW, lane);
-    else load_stream(job, lds, sc, wv - NW, lane);
+    load_stream(job, lds, sc, wv - NW, lane);
   } else {
     compute_stream(job, lds, sc, wv, lane);
   }
@@ -712,8 +648,8 @@ constexpr int EP_RPP = 64 / EP_LPR;    // rows per pass
 // global stores can overlap (jobs with small epilogues; the heavy ones keep them rolled
 // to stay within the register budget).
 template <bool UNROLL = false, class F>
-__device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, F&& f) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
+__device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, const WaveRows& w, F&& f) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wn = (int)((unsigned)wv / WM);
   float* wsm = stage + wv * EP_ROWS * EP_LD;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -727,7 +663,7 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, F&& 
           read8(wsm + (lane / EP_LPR + EP_RPP * j) * EP_LD + (lane % EP_LPR) * 8, v[j]);
 #pragma unroll
         for (int j = 0; j < EP_ROWS / EP_RPP; ++j)
-          f(wm * WROWS + mi * 32 + h * 16 + lane / EP_LPR + EP_RPP * j, wn * WCOLS + (lane % EP_LPR) * 8, v[j],
+          f(w.base + mi * 32 + h * 16 + lane / EP_LPR + EP_RPP * j, wn * WCOLS + (lane % EP_LPR) * 8, v[j],
             (mi * 2 + h) * (EP_ROWS / EP_RPP) + j);
       } else {
 #pragma unroll 1
@@ -735,18 +671,11 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, F&& 
           const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
           float v[8];
           read8(wsm + rr * EP_LD + cc, v);
-          f(wm * WROWS + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v, (mi * 2 + h) * (EP_ROWS / EP_RPP) + j);
+          f(w.base + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v, (mi * 2 + h) * (EP_ROWS / EP_RPP) + j);
         }
       }
       staging_done();
     }
-}
-// The rows of the tile that epilogue_rows hands this lane, in call order (the f's last
-// argument): slot (mi * 2 + h) * (EP_ROWS / EP_RPP) + j.
-constexpr int EP_LANE_ROWS = MI * 2 * (EP_ROWS / EP_RPP);
-__device__ __forceinline__ int ep_row(int slot, int lane, int wm) {
-  const int j = slot % (EP_ROWS / EP_RPP), q = slot / (EP_ROWS / EP_RPP);
-  return wm * WROWS + q * 16 + lane / EP_LPR + EP_RPP * j;
 }
 
 // Row-group tile: virtual item v -> expert, first row, valid rows and column tile, in
@@ -762,8 +691,15 @@ __device__ __forceinline__ void row_tile(const int32_t* tiles, const int32_t* of
   const int mt = uni(local % ent[2]);
   t.nt = uni(local / ent[2]);
   const int o0 = sload(offsets + t.e), o1 = sload(offsets + t.e + 1);
-  t.rs = uni(o0 + mt * BM);
-  t.cnt = uni(min(BM, o1 - t.rs));
+  if constexpr (FW) {
+    // the expert's rows split into its ent[2] = ceil(rows / BM) tiles as evenly as possible
+    const int n = o1 - o0, parts = uni(ent[2]);
+    t.rs = uni(o0 + (int)(((int64_t)mt * n) / parts));
+    t.cnt = uni(o0 + (int)(((int64_t)(mt + 1) * n) / parts) - t.rs);
+  } else {
+    t.rs = uni(o0 + mt * BM);
+    t.cnt = uni(min(BM, o1 - t.rs));
+  }
 }
 
 // Row-source indices of the A rows a load wave's K-major loads cover (load q fills rows
@@ -790,14 +726,6 @@ __device__ __forceinline__ void gather_rows_a(const int32_t* row_src, const RowT
 // the lane's chunk) of the slot it fills; step kt adds kt * 64 elements.
 struct KRows {
   const bf16_t* p[A_LP];
-  __device__ __forceinline__ void load(int kt, i32x4 (&v)[A_LP]) const {
-#pragma unroll
-    for (int q = 0; q < A_LP; ++q) v[q] = gload16(p[q] + kt * BK);
-  }
-  __device__ __forceinline__ void put(const i32x4 (&v)[A_LP], bf16_t* st, int pw) const {
-#pragma unroll
-    for (int q = 0; q < A_LP; ++q) lds_put16(a_dst(st, q, pw), v[q]);
-  }
   __device__ __forceinline__ void dma(int kt, bf16_t* st, int pw) const {
 #pragma unroll
     for (int q = 0; q < A_LP; ++q) dma16(p[q] + kt * BK, a_dst(st, q, pw));

@@ -185,8 +185,10 @@ __global__ __launch_bounds__(256) void k_place(const int32_t* __restrict__ idx, 
 // order[e] = e and order[El] = 0 (contiguous ranges, which keep each expert's tiles on
 // one XCD's L2).  order[El + 1] and order[El + 2], the item counters of the dW_down and
 // dW_gate|dW_up launches, are zeroed.
+// With tiles2 given, the same table for m-tiles of bm2 rows goes to tiles2.
 __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__ offsets, int El, int bm,
-                                                     int32_t* __restrict__ tiles, int32_t* __restrict__ zeros,
+                                                     int32_t* __restrict__ tiles, int bm2,
+                                                     int32_t* __restrict__ tiles2, int32_t* __restrict__ zeros,
                                                      int32_t* __restrict__ order) {
   __shared__ int32_t buf[16];  // wave totals of the scan
   __shared__ int32_t rows[1024];
@@ -236,23 +238,29 @@ __global__ __launch_bounds__(1024) void k_tile_table(const int32_t* __restrict__
   // inclusive scan of the tile counts: within each wave by shuffles, then over the
   // sixteen wave totals
   const int lane = e & 63, wv = e >> 6;
-  int incl = n;
+  for (int t = 0; t < (tiles2 ? 2 : 1); ++t) {
+    int32_t* const out = t ? tiles2 : tiles;
+    const int b = t ? bm2 : bm;
+    n = e < El ? (c + b - 1) / b : 0;
+    int incl = n;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    __syncthreads();   // the previous table's reads of buf are done
+    if (lane == 63) buf[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += buf[w];
+    incl += before;
+    const int start = incl - n;
+    for (int j = 0; j < n; ++j) {
+      i32x4 ent = {e, start, n, 0};
+      *reinterpret_cast<i32x4*>(out + 4 + 4 * (start + j)) = ent;
+    }
+    if (e == 1023) out[0] = incl;
   }
-  if (lane == 63) buf[wv] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wv; ++w) before += buf[w];
-  incl += before;
-  const int start = incl - n;
-  for (int j = 0; j < n; ++j) {
-    i32x4 ent = {e, start, n, 0};
-    *reinterpret_cast<i32x4*>(tiles + 4 + 4 * (start + j)) = ent;
-  }
-  if (e == 1023) tiles[0] = incl;
 }
 
 // xp[r] = x[row_src[r] / k]: one wave per row, 16-byte vectors.
@@ -393,8 +401,9 @@ hipError_t launch_index(const moe_shape& s, const int32_t* idx, int32_t* counts,
 }
 
 hipError_t launch_tile_table(const moe_shape& s, const int32_t* offsets, int bm, int32_t* tiles,
-                             int32_t* zeros, int32_t* order, hipStream_t st) {
-  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles, zeros, order);
+                             int32_t* zeros, int32_t* order, hipStream_t st, int bm2, int32_t* tiles2) {
+  MOE_LAUNCH("tile_table", k_tile_table, dim3(1), dim3(1024), 0, st, offsets, s.e_local, bm, tiles, bm2, tiles2,
+             zeros, order);
   return hipGetLastError();
 }
 

@@ -27,6 +27,11 @@ SMALL = {
     # Zipf-skewed loads with 8 empty experts; the weight gradients' 768 and 384 output
     # tiles take several rounds of the persistent grid in cost order
     "skew_bf16": wl.MoeConfig("skew_bf16", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf"),
+    # about 320 rows per expert (T k / E = 320), so the bf16 gate/up, down and dX GEMMs take
+    # 320-row tiles (the smaller configs take 256-row ones): tiles that reach the second
+    # wave row, experts past 320 rows with a short second tile, 64-column N tails
+    "tall_bf16": wl.MoeConfig("tall_bf16", 1280, 320, 192, 8, 2, 0, 8, 11),
+    "tall_bf16_share": wl.MoeConfig("tall_bf16_share", 1280, 320, 192, 8, 2, 2, 5, 12),
 }
 
 
