@@ -41,8 +41,7 @@ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   int64_t R_cap;
   size_t es;         // element size of the data dtype
-  int max_tiles;     // row-group tile bound, kGemmBM-row tiles (MXFP8 GEMMs)
-  int max_tiles_w;   // the same for 256-row tiles (bound for the bf16 fused-stream GEMMs' tiles)
+  int max_tiles;     // row-group tile bound (256-row tiles; 320-row ones are fewer)
   int nparts;        // rowdot partials per row
   int nchunks;
   // saved
@@ -123,8 +122,7 @@ void layout(const moe_shape& s, Layout& L) {
   const int El = s.e_local;
   L.R_cap = (int64_t)s.T * (s.k < El ? s.k : El);
   L.es = s.dtype == MOE_BF16 ? 2 : 4;
-  L.max_tiles = (int)ceil_div(L.R_cap, kGemmBM) + El;
-  L.max_tiles_w = (int)ceil_div(L.R_cap, 256) + El;
+  L.max_tiles = (int)ceil_div(L.R_cap, 256) + El;
   L.nparts = s.dtype == MOE_BF16 ? bwd_bf16_nparts(s.I) : s.I;
   L.nchunks = (int)ceil_div((int64_t)s.T * s.k, index_chunk((int64_t)s.T * s.k, El));
   const size_t R = (size_t)L.R_cap;
@@ -144,7 +142,7 @@ void layout(const moe_shape& s, Layout& L) {
   const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
   L.off_tiles = 0;
   L.off_tiles_w = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
-  L.off_zeros = L.off_tiles_w + align_up((size_t)(4 + 4 * L.max_tiles_w) * 4);
+  L.off_zeros = L.off_tiles_w + align_up((size_t)(4 + 4 * L.max_tiles) * 4);
   L.off_order = L.off_zeros + align_up(kZeroBytes);
   L.off_dgu = L.off_order + align_up((size_t)(El + 3) * 4);
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
@@ -378,17 +376,17 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    // the MXFP8 GEMMs take kGemmBM-row tiles, the bf16 ones fused_bm-row tiles
+    // the MXFP8 GEMMs take kGemmBMMx-row tiles, the bf16 ones fused_bm-row tiles
     const bool mxf = s.fwd == MOE_FWD_MXFP8;
     const int bmw = fused_bm(s);
-    int32_t* tiles = at<int32_t>(scratch, mxf ? L.off_tiles : L.off_tiles_w);
-    e = launch_tile_table(s, offsets, mxf ? kGemmBM : bmw, tiles, nullptr, nullptr, st);
+    int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
+    e = launch_tile_table(s, offsets, mxf ? kGemmBMMx : bmw, tiles, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     FwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
     a.x = (const bf16_t*)x; a.xp = (const bf16_t*)xp; a.offsets = offsets; a.row_src = row_src;
     a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up; a.wd = (const bf16_t*)w_down;
-    a.tiles = tiles; a.max_tiles = mxf ? L.max_tiles : L.max_tiles_w;
+    a.tiles = tiles; a.max_tiles = L.max_tiles;
     a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a); a.yp = (bf16_t*)yp;
     if (s.recompute) {  // nothing kept: the down GEMM's A in scratch, no G|U
       a.gu = nullptr;
@@ -463,19 +461,21 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    // kGemmBM-row tiles for the MXFP8 GEMMs, fused_bm-row tiles for the bf16 ones (B1, B3
-    // and a recomputed bf16 gate/up GEMM): one tile-table launch writes what the call needs
+    // kGemmBMMx-row tiles for the MXFP8 row-tiled GEMMs (B1, B3 and a recomputed MXFP8
+    // gate/up GEMM), fused_bm-row tiles for the bf16 ones: one tile-table launch writes
+    // the one or two tables the call needs (one, when the heights agree)
     const bool mxb = s.bwd == MOE_BWD_MXFP8;
     const bool mxf = s.fwd == MOE_FWD_MXFP8;
-    const bool narrow = mxb || (s.recompute && mxf);
-    const bool wide = !mxb || (s.recompute && !mxf);
+    const bool need_mx = mxb || (s.recompute && mxf);
+    const bool need_bf = !mxb || (s.recompute && !mxf);
     const int bmw = fused_bm(s);
     int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    int32_t* tiles_w = at<int32_t>(scratch, L.off_tiles_w);
+    int32_t* tiles_w = need_mx && bmw == kGemmBMMx ? tiles : at<int32_t>(scratch, L.off_tiles_w);
     int32_t* zeros = at<int32_t>(scratch, L.off_zeros);
     int32_t* order = at<int32_t>(scratch, L.off_order);
-    if (narrow)
-      e = launch_tile_table(s, offsets, kGemmBM, tiles, zeros, order, st, bmw, wide ? tiles_w : nullptr);
+    if (need_mx)
+      e = launch_tile_table(s, offsets, kGemmBMMx, tiles, zeros, order, st, bmw,
+                            need_bf && tiles_w != tiles ? tiles_w : nullptr);
     else
       e = launch_tile_table(s, offsets, bmw, tiles_w, zeros, order, st);
     if (e != hipSuccess) return hip_status(e, __func__);
@@ -485,7 +485,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.row_src = row_src; a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up;
     a.wd = (const bf16_t*)w_down; a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a);
     a.tiles = tiles; a.max_tiles = L.max_tiles;
-    a.tiles_w = tiles_w; a.max_tiles_w = L.max_tiles_w; a.bm_w = bmw;
+    a.tiles_w = tiles_w; a.max_tiles_w = L.max_tiles; a.bm_w = bmw;
     a.dgu = at<bf16_t>(scratch, L.off_dgu); a.dxp = at<bf16_t>(scratch, L.off_dxp);
     a.dw_part = at<float>(scratch, L.off_part);
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
@@ -501,7 +501,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
       f.x = a.x; f.xp = a.xp; f.offsets = offsets; f.row_src = row_src; f.topk_w = topk_w;
       f.wg = a.wg; f.wu = a.wu; f.wd = a.wd;
       f.tiles = mxf ? tiles : tiles_w;
-      f.max_tiles = mxf ? L.max_tiles : L.max_tiles_w;
+      f.max_tiles = L.max_tiles;
       f.gu = rgu; f.a = ra; f.yp = nullptr;
       if (s.fwd == MOE_FWD_MXFP8) {
         MxFwdArgs m{};

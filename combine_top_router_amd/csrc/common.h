@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, flo
 }
 
 // Host-side: the launch configuration constants shared by the host code and kernels.
-constexpr int kGemmBM = 128;  // rows of one row-group GEMM tile (bf16 B1, the MXFP8 GEMMs)
+constexpr int kGemmBMMx = 256;  // rows of one row-group tile of the MXFP8 row-tiled GEMMs
 constexpr int kZeroBytes = 512;  // zeroed scratch area read in place of rows past a group's end
 // (token, slot) pairs per histogram chunk of the dispatch index: at least 1024, a
 // multiple of 256, and few enough chunks (<= 256 and <= 32768 / El) that every
@@ -176,7 +176,7 @@ struct BwdArgs {
   const bf16_t* wd;
   const bf16_t* gu;       // saved
   const bf16_t* a;        // saved
-  const int32_t* tiles;   // kGemmBM-row tiles (B1, the MXFP8 GEMMs)
+  const int32_t* tiles;   // kGemmBMMx-row tiles (the MXFP8 B1 and B3)
   int max_tiles;
   const int32_t* tiles_w; // bm_w-row tiles (the bf16 B3 on the fused stream)
   int max_tiles_w;
@@ -265,6 +265,13 @@ struct MxFwdArgs {
 };
 // k1_only: the gate/up GEMM and what it needs (the backward's recompute)
 hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, bool k1_only = false);
+// the MXFP8 row-tiled GEMMs on the 256-row fused stream (a.tiles: kGemmBMMx-row tiles)
+namespace fw256 {
+hipError_t launch_fwd_gateup_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st);
+hipError_t launch_fwd_down_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st);
+hipError_t launch_bwd_da_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
+hipError_t launch_bwd_dx_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
+}  // namespace fw256
 
 // fp32 (SIMT) grouped GEMMs: the same chain in fp32 arithmetic
 struct FwdArgsF32 {

@@ -90,7 +90,8 @@ constexpr int MX_STEP = 128;               // codes per K step
 constexpr int MX_SC_SLOT = 512 * 4;        // scale bytes per stage
 constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per load wave
 static_assert(MX_STEP == 2 * BK, "an fp8 step must span the bytes of a bf16 step");
-static_assert(FW || (MX_SC_LP * NP * 64 == 512 && BM + BN <= 512), "scale slots");
+// (the 320-row fused-stream build compiles no MXFP8 kernel)
+static_assert(BM == 320 || (MX_SC_LP * NP * 64 == 512 && BM + BN <= 512), "scale slots");
 
 __device__ __forceinline__ i32x8 frag_fp8(const bf16_t* tile, int r, int kk, int lane) {
   const int c0 = kk * 4 + (lane >> 5);
@@ -136,6 +137,7 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
 struct LMx {
   static constexpr bool GATHER = false;
   static constexpr int NVMEM = LOADS + MX_SC_LP;
+  static constexpr int NLOAD = NVMEM;  // fused stream: loads per K step
   int nk, pw;
   const uint8_t* a[A_LP];       // codes of the lane's slot at K step 0
   const uint8_t* b[B_LP];
@@ -152,6 +154,7 @@ struct LMx {
     for (int q = 0; q < MX_SC_LP; ++q)
       dma4(sp[q] + kt * (MX_STEP / 32), scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256);
   }
+  __device__ __forceinline__ void dma(int kt, bf16_t* st, int slot) const { issue(kt, st, slot, 0, [] {}); }
   // operand rows: A row r (of tile) at a_base + ra(r) * lda, B row n at b_base + rb(n) * ldb;
   // both matrices' scales have row stride ld / 32 and start at s_a / s_b
   template <class RA, class RB>
@@ -189,7 +192,7 @@ struct LGateUp : RowLd {
   KRows a;
   const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
   size_t bstep;           // elements per K step of the weights (64 rows)
-  __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
+  __device__ __forceinline__ void dma(int kt, bf16_t* st, int) const {
     a.dma(kt, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
@@ -326,7 +329,7 @@ struct LMnB : RowLd {
   KRows a;
   const bf16_t* b[B_LP];
   size_t bstep;
-  __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
+  __device__ __forceinline__ void dma(int kt, bf16_t* st, int) const {
     a.dma(kt, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
@@ -426,7 +429,7 @@ struct LKK : RowLd {
   const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
   const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
   int ksplit;              // B3: I / 64; B1: larger than any step count
-  __device__ __forceinline__ void dma(int kt, bf16_t* st) const {
+  __device__ __forceinline__ void dma(int kt, bf16_t* st, int) const {
     a.dma(kt, st, pw);
     const bool second = kt >= ksplit;
     const int k0 = (second ? kt - ksplit : kt) * BK;
@@ -897,13 +900,43 @@ hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+#if MOE_GEMM_FW == 256
+// The MXFP8 row-tiled GEMMs (256-row tiles only: a step's scale slots, one per A and B
+// row, fill the 512 the loads carry).  a.tiles holds 256-row tiles.
+hipError_t launch_fwd_gateup_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
+  if (a.max_tiles == 0) return hipSuccess;
+  MOE_LAUNCH("fwd_gateup_mx", k_fwd_gateup<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))),
+             dim3(NTHR), 0, st, a, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_down_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st) {
+  if (a.max_tiles == 0) return hipSuccess;
+  MOE_LAUNCH("fwd_down_mx", k_fwd_down<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0,
+             st, a, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_da_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
+  return launch_bwd_gemms<true>(a, m, st);
+}
+
+hipError_t launch_bwd_dx_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
+  if (a.max_tiles == 0) return hipSuccess;
+  MOE_LAUNCH("bwd_dX_mx", k_bwd_dx<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0,
+             st, a, m);
+  return hipGetLastError();
+}
+#endif  // MOE_GEMM_FW == 256
+
 }  // namespace fw256 / fw320
 #endif  // MOE_GEMM_FW
 
 #if MOE_GEMM_MX_TU
 // MXFP8 forward.  Order: quantise W_gate, W_up and W_down column-wise (one group per
 // expert) and the Xp rows row-wise; K1 on fp8 operands writes G|U and A (bf16) and the
-// row-wise codes of A (from its fp32 values); K2 on fp8 operands.
+// row-wise codes of A (from its fp32 values); K2 on fp8 operands.  K1 and K2 run on the
+// 256-row fused stream (gemm_fw256.hip; a.tiles holds 256-row tiles).
 hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, bool k1_only) {
   if (a.max_tiles == 0) return hipSuccess;
   hipError_t e;
@@ -927,13 +960,10 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, b
   else
     MOE_TRY(launch_mx_rows(a.x, nullptr, H, a.row_src, a.k, a.offsets, El, -1, m.R_cap, H, m.q_x, m.s_x, "mx_q_x",
                            st));
-  MOE_LAUNCH("fwd_gateup_mx", k_fwd_gateup<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(I, BN / 2))),
-             dim3(NTHR), 0, st, a, m);
+  MOE_TRY(fw256::launch_fwd_gateup_mx(a, m, st));
+  if (!k1_only) MOE_TRY(fw256::launch_fwd_down_mx(a, m, st));
 #undef MOE_TRY
-  if (k1_only) return hipGetLastError();
-  MOE_LAUNCH("fwd_down_mx", k_fwd_down<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(H, BN))), dim3(NTHR), 0,
-             st, a, m);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 #endif  // MOE_GEMM_MX_TU
@@ -967,7 +997,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
 #endif  // !MOE_GEMM_MX_TU && !MOE_GEMM_FW
 
 #if MOE_GEMM_MX_TU
-// MXFP8 backward.  Order: quantise the weights row-wise (unless the MXFP8 forward left
+// MXFP8 backward (B1 and B3 on the 256-row fused stream, a.tiles holding 256-row tiles;
+// the weight gradients here).  Order: quantise the weights row-wise (unless the MXFP8 forward left
 // their codes in the saved buffer), and dY' row-wise together with
 // w * dY' column-wise per expert; B1 (fp8) writes dG|dU (bf16); quantise dG|dU row-wise
 // and column-wise in one pass, A and Xp column-wise; then B2, B3, B4 on fp8 operands.
@@ -986,7 +1017,7 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
   // dY' rows: row-wise for B1 and, from the same read, column-wise w * dY' for B2
   MOE_TRY(launch_mx_cols(a.dy, H, a.row_src, a.k, a.topk_w, a.offsets, m.poff, El, H, m.Rp, m.qt_dy, m.st_dy,
                          "mx_q_dy", st, m.q_dy, m.s_dy));
-  MOE_TRY(launch_bwd_gemms<true>(a, m, st));
+  MOE_TRY(fw256::launch_bwd_da_mx(a, m, st));
   // dG|dU: row-wise for B3 and column-wise for B4 in one pass
   MOE_TRY(launch_mx_cols(a.dgu, 2 * I, nullptr, 1, nullptr, a.offsets, m.poff, El, 2 * I, m.Rp, m.qt_dgu, m.st_dgu,
                          "mx_q_dgu", st, m.q_dgu, m.s_dgu));
@@ -997,20 +1028,18 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
   else
     MOE_TRY(launch_mx_cols(a.x, H, a.row_src, a.k, nullptr, a.offsets, m.poff, El, H, m.Rp, m.qt_x, m.st_x,
                            "mx_qt_x", st));
-#undef MOE_TRY
   {
     const int tm = (int)ceil_div(I, BM), tn = (int)ceil_div(H, BN);
     MOE_LAUNCH("bwd_dWd_mx", (k_bwd_wgrad<0, true>), dim3(grid_for((int64_t)El * tm * tn)), dim3(NTHR), 0, st, a, m,
                tm, tn);
   }
-  if (a.max_tiles > 0)
-    MOE_LAUNCH("bwd_dX_mx", k_bwd_dx<true>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(H, BN))), dim3(NTHR), 0, st,
-               a, m);
+  MOE_TRY(fw256::launch_bwd_dx_mx(a, m, st));
   {
     const int tm = (int)ceil_div(H, BM), tn = (int)ceil_div(2 * I, BN);
     MOE_LAUNCH("bwd_dWgu_mx", (k_bwd_wgrad<1, true>), dim3(grid_for((int64_t)El * tm * tn)), dim3(NTHR), 0, st, a, m,
                tm, tn);
   }
+#undef MOE_TRY
   return hipGetLastError();
 }
 

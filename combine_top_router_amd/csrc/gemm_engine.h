@@ -516,7 +516,7 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
 // next barrier.  Vector memory instructions that the compiler emits (the epilogues') only
 // lengthen the explicit vmcnt waits, which count the direct-to-LDS loads alone: every
 // such instruction is younger than the loads it waits for.  For jobs whose tiles all take
-// the same number of K steps (Ld::dma(kt, stage) issues Ld::NLOAD loads).
+// the same number of K steps (Ld::dma(kt, stage pointer, stage index) issues Ld::NLOAD loads).
 template <class J, class S>
 __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, int wv, int lane) {
   static_assert(!J::DYN, "the fused stream walks a fixed schedule");
@@ -531,7 +531,7 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
   const int len = max(L.nk, MIN_STEPS);     // the same for every tile of the job
   const int total = ntiles * len;           // stream positions of this workgroup
   auto issue = [&](int stage) {
-    L.dma(min(lk, L.nk - 1), lds + stage * STAGE_ELEMS);
+    L.dma(min(lk, L.nk - 1), lds + stage * STAGE_ELEMS, stage);
     if (++lk == len) {
       lk = 0;
       lv = sc.next(lv);
@@ -691,15 +691,8 @@ __device__ __forceinline__ void row_tile(const int32_t* tiles, const int32_t* of
   const int mt = uni(local % ent[2]);
   t.nt = uni(local / ent[2]);
   const int o0 = sload(offsets + t.e), o1 = sload(offsets + t.e + 1);
-  if constexpr (FW) {
-    // the expert's rows split into its ent[2] = ceil(rows / BM) tiles as evenly as possible
-    const int n = o1 - o0, parts = uni(ent[2]);
-    t.rs = uni(o0 + (int)(((int64_t)mt * n) / parts));
-    t.cnt = uni(o0 + (int)(((int64_t)(mt + 1) * n) / parts) - t.rs);
-  } else {
-    t.rs = uni(o0 + mt * BM);
-    t.cnt = uni(min(BM, o1 - t.rs));
-  }
+  t.rs = uni(o0 + mt * BM);
+  t.cnt = uni(min(BM, o1 - t.rs));
 }
 
 // Row-source indices of the A rows a load wave's K-major loads cover (load q fills rows
