@@ -193,10 +193,13 @@ struct BwdArgs {
   bf16_t* dwd;            // [El, I, H]
 };
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
-// B1 alone and B3 alone on the fused stream, on a.tiles_w (a.bm_w-row tiles)
+// B1 alone and B3 alone on the fused stream, on a.tiles_w (a.bm_w-row tiles); the
+// weight gradients on the 256-row build
 namespace fw256 {
 hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dwd_bf16(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dwgu_bf16(const BwdArgs& a, hipStream_t st);
 }  // namespace fw256
 namespace fw320 {
 hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);

@@ -47,12 +47,14 @@ struct RowTileInfo {
   int nk;
 };
 
-// Row-tiled bf16 loader state common to the fused-stream kernels: dma(kt, stage) issues
-// the wave's NLOAD direct-to-LDS loads of K step kt.
+// Row-tiled bf16 loader state common to the fused-stream kernels: issue(kt, stage, ...)
+// issues the wave's direct-to-LDS loads of K step kt; the rows are fixed per tile, so
+// there are no row indices to fetch.
 struct RowLd {
-  static constexpr int NLOAD = A_LP + B_LP;
+  static constexpr bool GATHER = false;
   int nk;
   int pw;
+  __device__ __forceinline__ void fetch(int, int) const {}
 };
 
 // K-major A rows of a row tile for load wave pw: the lane's chunk of each of its A_LP
@@ -137,7 +139,6 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
 struct LMx {
   static constexpr bool GATHER = false;
   static constexpr int NVMEM = LOADS + MX_SC_LP;
-  static constexpr int NLOAD = NVMEM;  // fused stream: loads per K step
   int nk, pw;
   const uint8_t* a[A_LP];       // codes of the lane's slot at K step 0
   const uint8_t* b[B_LP];
@@ -154,7 +155,6 @@ struct LMx {
     for (int q = 0; q < MX_SC_LP; ++q)
       dma4(sp[q] + kt * (MX_STEP / 32), scring + slot * MX_SC_SLOT + load_instr(q, pw) * 256);
   }
-  __device__ __forceinline__ void dma(int kt, bf16_t* st, int slot) const { issue(kt, st, slot, 0, [] {}); }
   // operand rows: A row r (of tile) at a_base + ra(r) * lda, B row n at b_base + rb(n) * ldb;
   // both matrices' scales have row stride ld / 32 and start at s_a / s_b
   template <class RA, class RB>
@@ -192,7 +192,8 @@ struct LGateUp : RowLd {
   KRows a;
   const bf16_t* b[B_LP];  // weight row k = 0 of the slot's column
   size_t bstep;           // elements per K step of the weights (64 rows)
-  __device__ __forceinline__ void dma(int kt, bf16_t* st, int) const {
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
     a.dma(kt, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
@@ -329,7 +330,8 @@ struct LMnB : RowLd {
   KRows a;
   const bf16_t* b[B_LP];
   size_t bstep;
-  __device__ __forceinline__ void dma(int kt, bf16_t* st, int) const {
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
     a.dma(kt, st, pw);
 #pragma unroll
     for (int q = 0; q < B_LP; ++q) dma16(b[q] + kt * bstep, b_dst(st, q, pw));
@@ -429,7 +431,8 @@ struct LKK : RowLd {
   const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
   const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
   int ksplit;              // B3: I / 64; B1: larger than any step count
-  __device__ __forceinline__ void dma(int kt, bf16_t* st, int) const {
+  template <class F>
+  __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
     a.dma(kt, st, pw);
     const bool second = kt >= ksplit;
     const int k0 = (second ? kt - ksplit : kt) * BK;
@@ -654,10 +657,14 @@ struct LWgrad {
   int nk;
   int32_t* ids;                  // this wave's two LDS slots of BK row indices
   int acol[A_LP], bcol[B_LP];    // element column of the lane's chunk
-  __device__ __forceinline__ void fetch(int kt, int par) const {  // row_src of step kt -> slot par
-    if (!GATHER) return;
+  // row_src of step kt of rows [rs, rs + cnt) -> index slot par of a wave's slots ids
+  __device__ __forceinline__ static void fetch_rows(const int32_t* row_src, const bf16_t* zeros, int rs, int cnt,
+                                                    int32_t* ids, int lane, int kt, int par) {
     const int32_t* src = cnt > 0 ? row_src + rs + min(kt * BK + lane, cnt - 1) : reinterpret_cast<const int32_t*>(zeros);
     dma4(src, ids + par * IDS_SLOT);
+  }
+  __device__ __forceinline__ void fetch(int kt, int par) const {  // row_src of step kt -> slot par
+    if (GATHER) fetch_rows(row_src, zeros, rs, cnt, ids, lane, kt, par);
   }
   template <class F>
   __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int par, F&& fetch_next) const {
@@ -738,6 +745,13 @@ struct JWgrad {
     }
   }
   __device__ __forceinline__ WaveRows rows(const Tile&, int wm) const { return {wm * WROWS, BM, MI}; }
+  // fused stream, gathering loaders: the row indices of item v's first K step into index
+  // slot par of load wave pw (as its loader's fetch(0, par) would)
+  __device__ __forceinline__ void fetch_first(int v, int pw, int lane, int par) const {
+    const int e = sload(a.order + uni(v / (tm * tn)));
+    const int o0 = sload(a.offsets + e), o1 = sload(a.offsets + e + 1);
+    Ld::fetch_rows(a.row_src, a.zeros, o0, uni(o1 - o0), ids + pw * 2 * IDS_SLOT, lane, 0, par);
+  }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
     if constexpr (MX) mx_compute<JWgrad>(st, scring + slot * MX_SC_SLOT, acc, lane, w, wn);
@@ -823,7 +837,8 @@ struct JWgrad {
   }
 };
 
-template <int WHICH, bool MX>
+// GX (bf16 dW_gate|dW_up only): the Xp rows gathered from x through row_src (no Xp buffer)
+template <int WHICH, bool MX, bool GX = false>
 __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int tm, int tn) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) int32_t ids[MX ? 4 : IDS_INTS];
@@ -836,13 +851,8 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_wgrad(BwdArgs a, MxArgs m, int 
     JWgrad<0, false, true, false> job{a, m, tm, tn, ids, scring, dslot};
     run_stream(job, lds);
   } else {
-    if (a.xp) {
-      JWgrad<1, false, false, false> job{a, m, tm, tn, ids, scring, dslot};
-      run_stream(job, lds);
-    } else {
-      JWgrad<1, true, false, false> job{a, m, tm, tn, ids, scring, dslot};
-      run_stream(job, lds);
-    }
+    JWgrad<1, GX, false, false> job{a, m, tm, tn, ids, scring, dslot};
+    run_stream(job, lds);
   }
 }
 
@@ -927,6 +937,26 @@ hipError_t launch_bwd_dx_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
              st, a, m);
   return hipGetLastError();
 }
+
+// The bf16 weight gradients: 256 x 256 output tiles of each expert's dW, K over its rows.
+hipError_t launch_bwd_dwd_bf16(const BwdArgs& a, hipStream_t st) {
+  MxArgs m{};
+  const int tm = (int)ceil_div(a.I, BM), tn = (int)ceil_div(a.H, BN);
+  MOE_LAUNCH("bwd_dWd", (k_bwd_wgrad<0, false>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a, m,
+             tm, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dwgu_bf16(const BwdArgs& a, hipStream_t st) {
+  MxArgs m{};
+  const int tm = (int)ceil_div(a.H, BM), tn = (int)ceil_div(2 * a.I, BN);
+  const dim3 grid(grid_for((int64_t)a.El * tm * tn));
+  if (a.xp)
+    MOE_LAUNCH("bwd_dWgu", (k_bwd_wgrad<1, false, false>), grid, dim3(NTHR), 0, st, a, m, tm, tn);
+  else
+    MOE_LAUNCH("bwd_dWgu", (k_bwd_wgrad<1, false, true>), grid, dim3(NTHR), 0, st, a, m, tm, tn);
+  return hipGetLastError();
+}
 #endif  // MOE_GEMM_FW == 256
 
 }  // namespace fw256 / fw320
@@ -973,25 +1003,14 @@ int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
 
 
 // B1 and B3 run on the fused stream (gemm_fw256.hip or gemm_fw320.hip, by a.bm_w), the
-// weight gradients here.
+// weight gradients on its 256-row build.
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
-  MxArgs m{};
   const bool f320 = a.bm_w == 320;
   hipError_t e = f320 ? fw320::launch_bwd_da_bf16(a, st) : fw256::launch_bwd_da_bf16(a, st);
-  if (e != hipSuccess) return e;
-  {
-    const int tm = (int)ceil_div(a.I, BM), tn = (int)ceil_div(a.H, BN);
-    MOE_LAUNCH("bwd_dWd", (k_bwd_wgrad<0, false>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a, m,
-               tm, tn);
-  }
-  e = f320 ? fw320::launch_bwd_dx_bf16(a, st) : fw256::launch_bwd_dx_bf16(a, st);
-  if (e != hipSuccess) return e;
-  {
-    const int tm = (int)ceil_div(a.H, BM), tn = (int)ceil_div(2 * a.I, BN);
-    MOE_LAUNCH("bwd_dWgu", (k_bwd_wgrad<1, false>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a, m,
-               tm, tn);
-  }
-  return hipGetLastError();
+  if (e == hipSuccess) e = fw256::launch_bwd_dwd_bf16(a, st);
+  if (e == hipSuccess) e = f320 ? fw320::launch_bwd_dx_bf16(a, st) : fw256::launch_bwd_dx_bf16(a, st);
+  if (e == hipSuccess) e = fw256::launch_bwd_dwgu_bf16(a, st);
+  return e;
 }
 
 #endif  // !MOE_GEMM_MX_TU && !MOE_GEMM_FW

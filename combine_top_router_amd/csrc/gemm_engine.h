@@ -507,69 +507,96 @@ __device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing repeated loads
 }
 
-// The fused stream (FW): every wave is compute wave wv and load wave wv.  At each
-// position it waits for its own loads of the position, meets the other waves at the
-// barrier (after which the position's stage is complete and the stage read one position
-// ago is free), issues its loads of the position DEPTH ahead into that free stage and
-// runs the position's MFMAs.  After a tile's last position the waves meet once more and
-// run the epilogue in the stage just read, which the next issue refills only after the
-// next barrier.  Vector memory instructions that the compiler emits (the epilogues') only
-// lengthen the explicit vmcnt waits, which count the direct-to-LDS loads alone: every
-// such instruction is younger than the loads it waits for.  For jobs whose tiles all take
-// the same number of K steps (Ld::dma(kt, stage pointer, stage index) issues Ld::NLOAD loads).
+// The fused stream (FW): every wave is compute wave wv and load wave wv, with one K step
+// in flight.  At each position a wave waits for everything it has issued (its loads of
+// the position and its index fetch for the next, and any epilogue stores), meets the
+// other waves at the barrier (after which the position's stage is complete and the
+// stage read one position ago is free), issues its loads of the next position into that
+// free stage and runs the position's MFMAs.  After a tile's last position the waves meet
+// once more and run the epilogue in the stage just read, which the next issue refills
+// only after the next barrier.  Tiles may differ in K steps (Sched::len).  The next tile
+// is fixed at the current tile's next-to-last position: at once for contiguous ranges;
+// under dynamic scheduling wave 0 takes it at the tile's first position and publishes it
+// in LDS, and the waves read it after a later barrier (a dynamic tile spans at least
+// DEPTH + 2 positions).  The loads of that next-to-last position also fetch the next
+// tile's first row indices for a gathering loader (J::fetch_first); the loader is set up
+// for the next tile in place when its first loads are issued.
 template <class J, class S>
 __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, int wv, int lane) {
-  static_assert(!J::DYN, "the fused stream walks a fixed schedule");
+  static_assert(DEPTH == 1, "the fused stream keeps one K step in flight");
   using P = typename J::Ld;
   using T = typename J::Tile;
   const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
-  int ntiles = 0;
-  for (int u = sc.v; u >= 0; u = sc.next(u)) ++ntiles;
-  P L;
-  int lv = sc.v, lk = 0;                    // load cursor: step lk of item lv
-  job.setup(lv, L, wv, lane);
-  const int len = max(L.nk, MIN_STEPS);     // the same for every tile of the job
-  const int total = ntiles * len;           // stream positions of this workgroup
-  auto issue = [&](int stage) {
-    L.dma(min(lk, L.nk - 1), lds + stage * STAGE_ELEMS, stage);
-    if (++lk == len) {
-      lk = 0;
-      lv = sc.next(lv);
-      // an opaque copy of the lane index: the per-lane load offsets are recomputed here
-      // rather than held in registers across the whole stream
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      if (lv >= 0) job.setup(lv, L, wv, ln);
-    }
+  int32_t* slot = nullptr;   // dynamic: two LDS slots for the next item, by tile parity
+  if constexpr (J::DYN) slot = job.dslot;
+  auto clampk = [](int kt, int nk) { return max(0, min(kt, nk - 1)); };
+  // an opaque copy of the lane index for the per-tile load setup: the per-lane load
+  // offsets are recomputed per tile rather than held in registers across the stream
+  auto setup = [&](int item, P& L) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    job.setup(item, L, wv, ln);
   };
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue(d);  // total >= MIN_STEPS > DEPTH
+  P lcur;
   T cur;
-  int cv = sc.v;
-  job.tile(cv, cur);
+  int v = sc.v, vn = -1;
+  setup(v, lcur);
+  job.tile(v, cur);
   WaveRows wr = job.rows(cur, wm);
+  int len = sc.len(cur.nk);
+  bool has_nxt = false;
+  int gpar = 0;   // index slot of the next issue
+  if (P::GATHER) {
+    lcur.fetch(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  lcur.issue(0, lds, 0, gpar, [&] { lcur.fetch(1, gpar ^ 1); });   // len >= 2
+  gpar ^= 1;
   Acc acc;
   zero_acc(acc);
-  int ck = 0, cs = 0;
-  for (int p = 0; p < total; ++p) {
-    // the loads of positions p + 1 .. p + DEPTH - 1 may still fly (fewer near the end)
-    if (total - p >= DEPTH)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((DEPTH - 1) * P::NLOAD) : "memory");
-    else
+  int cs = 0, grabbed = 0;
+  for (int t = 0;; ++t) {
+    for (int kc = 0; kc < len; ++kc) {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (p + DEPTH < total) issue(cs + DEPTH < NSTAGE ? cs + DEPTH : cs + DEPTH - NSTAGE);
-    if (ck < cur.nk && wr.nblk > 0) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wr, wn);
-    const int done = cs;
-    cs = cs == NSTAGE - 1 ? 0 : cs + 1;
-    if (++ck < len) continue;
+      if (sc.dyn && kc == 0 && wv == 0 && lane == 0) grabbed = sc.grab();
+      if (kc + 2 == len) {   // the next tile, before the issue that fetches its first indices
+        vn = sc.dyn ? uni(slot[t & 1]) : sc.next(v);
+        has_nxt = vn >= 0;
+      }
+      bf16_t* const st = lds + (cs ^ 1) * STAGE_ELEMS;   // NSTAGE = 2: the stage freed
+      if (kc + 1 < len) {
+        const int k1 = kc + 1;
+        lcur.issue(clampk(k1, lcur.nk), st, cs ^ 1, gpar, [&] {
+          if (k1 + 1 < len) {
+            lcur.fetch(clampk(k1 + 1, lcur.nk), gpar ^ 1);
+          } else if (has_nxt) {
+            if constexpr (P::GATHER) job.fetch_first(vn, wv, lane, gpar ^ 1);
+          } else {
+            lcur.fetch(clampk(k1, lcur.nk), gpar ^ 1);
+          }
+        });
+        gpar ^= 1;
+      } else if (has_nxt) {
+        setup(vn, lcur);
+        lcur.issue(0, st, cs ^ 1, gpar, [&] { lcur.fetch(1, gpar ^ 1); });
+        gpar ^= 1;
+      }
+      if (kc < cur.nk && wr.nblk > 0) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wr, wn);
+      if (sc.dyn && kc == 0 && wv == 0) {   // published after the MFMAs, read after a barrier
+        const int n = uni(grabbed);
+        if (lane == 0) slot[t & 1] = n;
+      }
+      cs ^= 1;
+    }
     if constexpr (J::EPI_LDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    job.epilogue(cur, acc, reinterpret_cast<float*>(lds + done * STAGE_ELEMS));
+    job.epilogue(cur, acc, reinterpret_cast<float*>(lds + (cs ^ 1) * STAGE_ELEMS));
     zero_acc(acc);
-    ck = 0;
-    cv = sc.next(cv);
-    if (cv < 0) break;
-    job.tile(cv, cur);
+    if (!has_nxt) break;
+    v = vn;
+    has_nxt = false;
+    job.tile(v, cur);
     wr = job.rows(cur, wm);
+    len = sc.len(cur.nk);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
