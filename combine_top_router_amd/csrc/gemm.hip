@@ -11,10 +11,11 @@
 // accumulators.  Operand tiles move global -> LDS with the gfx950 direct-to-LDS loads
 // (global_load_lds_dwordx4) into a ring of LDS stages, DEPTH K steps ahead, one barrier
 // per K step, and a workgroup's tiles form one stream of K steps, so the next tile's
-// loads fly while the current tile's epilogue runs.  The bf16 gate/up, down, dA and dX
-// GEMMs run on the fused stream (256- or 320-row tiles; every wave loads and computes,
-// gemm_fw256.hip / gemm_fw320.hip); the weight gradients and the MXFP8 GEMMs on
-// dedicated load waves (128-row tiles; gemm.hip / gemm_mx.hip).  An operand whose contraction axis is contiguous in
+// loads fly while the current tile's epilogue runs.  The bf16 GEMMs and the MXFP8
+// gate/up, down, dA and dX GEMMs run on the fused stream (every wave loads and computes;
+// gemm_fw256.hip, and gemm_fw320.hip for 320-row bf16 tiles); the MXFP8 weight gradients
+// on dedicated load waves (128-row tiles, gemm_mx.hip).  This file, compiled alone, holds
+// the bf16 backward's launch order.  An operand whose contraction axis is contiguous in
 // memory ("K-major") is stored [rows][64] and read with 16-byte LDS reads; an operand
 // contiguous along M or N ("MN-major": row-major weights as the B of x*W, and both
 // operands of the weight gradients, which contract over token rows) is stored

@@ -26,12 +26,12 @@ namespace moe {
 namespace {
 
 // Two workgroup shapes, chosen per translation unit:
-// * load-wave streams (gemm.hip, gemm_mx.hip): 128 x 256 tiles, a three-stage ring (48 KB
-//   stages), NW compute waves and NP dedicated load waves;
+// * load-wave streams (gemm_mx.hip: the MXFP8 weight gradients): 128 x 256 tiles, a
+//   three-stage ring (48 KB stages), NW compute waves and NP dedicated load waves;
 // * the fused stream (MOE_GEMM_FW = the tile height, 256 in gemm_fw256.hip or 320 in
-//   gemm_fw320.hip: the bf16 gate/up, down and dX GEMMs): 256- or 320-row tiles of 256
-//   columns, a two-stage ring (64 or 72 KB stages), eight waves that each issue one eighth
-//   of the operand loads and compute a (BM / 2) x 64 sub-tile.  Eight waves per CU leave
+//   gemm_fw320.hip: every bf16 GEMM and the MXFP8 row-tiled ones): 256- or 320-row tiles of
+//   256 columns, a two-stage ring (64 or 72 KB stages), eight waves that each issue one
+//   eighth of the operand loads and compute a (BM / 2) x 64 sub-tile.  Eight waves per CU leave
 //   each 256 registers, room for up to 160 accumulators; the larger tile asks a third
 //   fewer operand bytes per flop of the CU's L2 request path, which bounds the load-wave
 //   kernels.
