@@ -54,7 +54,7 @@ struct Layout {
   size_t off_rgu, off_ra;
   size_t off_router_part;
   // scratch
-  size_t off_tiles, off_tiles_w, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
+  size_t off_tiles, off_tiles320, off_zeros, off_order, off_dgu, off_dxp, off_part, off_aw, scratch_bytes;
   // MXFP8 backward buffers (scratch), 0 when unused
   int64_t Rp;
   size_t off_mx[17];
@@ -94,6 +94,8 @@ int check_shape(const moe_shape* s) {
   if (s->fwd != MOE_FWD_SAME && s->fwd != MOE_FWD_MXFP8) return fail(MOE_EINVAL, "fwd = %d", s->fwd);
   if (s->recompute != 0 && s->recompute != 1) return fail(MOE_EINVAL, "recompute = %d", s->recompute);
   if (s->recompute && s->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "recompute needs bf16 data");
+  if (s->row_tile != 0 && s->row_tile != 256 && s->row_tile != 320)
+    return fail(MOE_EINVAL, "row_tile = %d (0, 256 or 320)", s->row_tile);
   if (s->fwd == MOE_FWD_MXFP8) {  // e_local * H <= 2^30 by the limits above: int column strides
     if (s->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the MXFP8 forward needs bf16 data");
     if (s->H % 128 != 0 || s->I % 128 != 0)
@@ -102,20 +104,48 @@ int check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
-// Tile height of the bf16 fused-stream GEMMs (256 or 320 rows): the one that pads an
-// expert's rows least, summed over the row counts m - sd, m, m + sd around the mean
-// m = T k / E of uniform routing (sd = sqrt(m), a Poisson-like spread).  320 keeps a
-// Qwen3-30B-A3B expert (m = 256) in one tile; 256 fits the 235B share's m = 1024.
-int fused_bm(const moe_shape& s) {
-  const double m = (double)s.T * s.k / s.E, sd = sqrt(m);
-  const int bm[2] = {256, 320};
-  int64_t pad[2] = {0, 0};
-  for (int i = 0; i < 2; ++i)
-    for (const double n : {m - sd, m, m + sd}) {
-      const int64_t r = n < 1.0 ? 1 : (int64_t)ceil(n);
-      pad[i] += (r + bm[i] - 1) / bm[i] * bm[i];
-    }
-  return pad[1] < pad[0] ? 320 : 256;
+// Tile heights of the bf16 row-tiled GEMMs on the fused stream, 256 or 320 rows, per GEMM.
+// A token picks a given expert with probability k / E, so an expert's row count c is
+// Binomial(T, k / E); read as a normal law (continuity-corrected), it needs
+// E[ceil(c / bm)] = sum over j >= 0 of P(c > j bm) tiles of height bm.  A GEMM with nt
+// column tiles gives the persistent grid about ceil(El E[..] nt / CUs) rounds of tiles,
+// each taking time in proportion to its height (MFMA work and operand bytes per K step),
+// and the height with the fewer rounds x rows wins; 256 on a tie (less padding and fewer
+// bytes per step).  Qwen3-30B-A3B (about 256 rows an expert): 320 for all four; the
+// 235B-A22B share (about 1024): 320 for the gate/up GEMM only.
+struct RowTiles {
+  int k1, k2, da, dx;
+};
+
+static double tiles_per_expert(const moe_shape& s, int bm) {
+  const double p = (double)s.k / s.E, m = s.T * p, sd = sqrt(s.T * p * (1.0 - p));
+  double t = 0.0;
+  for (int j = 0;; ++j) {
+    const double x = (double)j * bm;  // P(c > x) = P(c >= x + 1)
+    if (x > m + 12.0 * sd) break;
+    t += sd > 0.0 ? 0.5 * erfc((x + 0.5 - m) / (sd * sqrt(2.0))) : (m > x ? 1.0 : 0.0);
+  }
+  return t;
+}
+
+RowTiles row_tile_heights(const moe_shape& s) {
+  if (s.row_tile != 0) return {s.row_tile, s.row_tile, s.row_tile, s.row_tile};
+  const double t256 = s.e_local * tiles_per_expert(s, 256), t320 = s.e_local * tiles_per_expert(s, 320);
+  const int64_t cus = gemm_cus();
+  auto pick = [&](int64_t nt) {
+    const int64_t c256 = ceil_div(llround(t256 * nt), cus) * 256, c320 = ceil_div(llround(t320 * nt), cus) * 320;
+    return c320 < c256 ? 320 : 256;
+  };
+  return {pick(ceil_div(s.I, 128)), pick(ceil_div(s.H, 256)), pick(ceil_div(s.I, 256)), pick(ceil_div(s.H, 256))};
+}
+
+// The 256-row and / or the 320-row tile table (one launch; zeros and order, when given,
+// are written with them)
+static hipError_t tile_tables(const moe_shape& s, const int32_t* offsets, bool n256, bool n320, int32_t* t256,
+                              int32_t* t320, int32_t* zeros, int32_t* order, hipStream_t st) {
+  if (n256 || !n320)
+    return launch_tile_table(s, offsets, 256, t256, zeros, order, st, n320 ? 320 : 0, n320 ? t320 : nullptr);
+  return launch_tile_table(s, offsets, 320, t320, zeros, order, st);
 }
 
 void layout(const moe_shape& s, Layout& L) {
@@ -141,8 +171,8 @@ void layout(const moe_shape& s, Layout& L) {
   }
   const size_t dispatch_bytes = align_up((size_t)L.nchunks * El * 4);
   L.off_tiles = 0;
-  L.off_tiles_w = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
-  L.off_zeros = L.off_tiles_w + align_up((size_t)(4 + 4 * L.max_tiles) * 4);
+  L.off_tiles320 = align_up((size_t)(4 + 4 * L.max_tiles) * 4);
+  L.off_zeros = L.off_tiles320 + align_up((size_t)(4 + 4 * L.max_tiles) * 4);
   L.off_order = L.off_zeros + align_up(kZeroBytes);
   L.off_dgu = L.off_order + align_up((size_t)(El + 3) * 4);
   L.off_dxp = L.off_dgu + align_up(R * 2 * s.I * L.es);
@@ -376,11 +406,13 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (s.dtype == MOE_BF16) {
-    // the MXFP8 GEMMs take kGemmBMMx-row tiles, the bf16 ones fused_bm-row tiles
+    // the MXFP8 GEMMs take kGemmBMMx-row tiles, the bf16 ones 256- or 320-row tiles by GEMM
     const bool mxf = s.fwd == MOE_FWD_MXFP8;
-    const int bmw = fused_bm(s);
+    const RowTiles h = row_tile_heights(s);
     int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    e = launch_tile_table(s, offsets, mxf ? kGemmBMMx : bmw, tiles, nullptr, nullptr, st);
+    int32_t* tiles320 = at<int32_t>(scratch, L.off_tiles320);
+    e = tile_tables(s, offsets, mxf || h.k1 == 256 || h.k2 == 256, !mxf && (h.k1 == 320 || h.k2 == 320), tiles,
+                    tiles320, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     FwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
@@ -407,7 +439,12 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
       }
       e = launch_fwd_mx(a, m, st);
     } else {
-      e = bmw == 320 ? fw320::launch_fwd_bf16(a, st) : fw256::launch_fwd_bf16(a, st);
+      FwdArgs k1 = a, k2 = a;
+      k1.tiles = h.k1 == 320 ? tiles320 : tiles;
+      k2.tiles = h.k2 == 320 ? tiles320 : tiles;
+      e = h.k1 == 320 ? fw320::launch_fwd_gateup_bf16(k1, st) : fw256::launch_fwd_gateup_bf16(k1, st);
+      if (e == hipSuccess)
+        e = h.k2 == 320 ? fw320::launch_fwd_down_bf16(k2, st) : fw256::launch_fwd_down_bf16(k2, st);
     }
   } else {
     FwdArgsF32 a{};
@@ -462,22 +499,21 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
   hipError_t e;
   if (s.dtype == MOE_BF16) {
     // kGemmBMMx-row tiles for the MXFP8 row-tiled GEMMs (B1, B3 and a recomputed MXFP8
-    // gate/up GEMM), fused_bm-row tiles for the bf16 ones: one tile-table launch writes
-    // the one or two tables the call needs (one, when the heights agree)
+    // gate/up GEMM), 256- or 320-row tiles by GEMM for the bf16 ones: one tile-table
+    // launch writes the one or two tables the call needs
     const bool mxb = s.bwd == MOE_BWD_MXFP8;
     const bool mxf = s.fwd == MOE_FWD_MXFP8;
-    const bool need_mx = mxb || (s.recompute && mxf);
-    const bool need_bf = !mxb || (s.recompute && !mxf);
-    const int bmw = fused_bm(s);
+    const RowTiles h = row_tile_heights(s);
+    int hb[3] = {0, 0, 0};   // heights of the bf16 row-tiled GEMMs this call runs
+    if (!mxb) { hb[0] = h.da; hb[1] = h.dx; }
+    if (s.recompute && !mxf) hb[2] = h.k1;
+    const bool n256 = mxb || (s.recompute && mxf) || hb[0] == 256 || hb[1] == 256 || hb[2] == 256;
+    const bool n320 = hb[0] == 320 || hb[1] == 320 || hb[2] == 320;
     int32_t* tiles = at<int32_t>(scratch, L.off_tiles);
-    int32_t* tiles_w = need_mx && bmw == kGemmBMMx ? tiles : at<int32_t>(scratch, L.off_tiles_w);
+    int32_t* tiles320 = at<int32_t>(scratch, L.off_tiles320);
     int32_t* zeros = at<int32_t>(scratch, L.off_zeros);
     int32_t* order = at<int32_t>(scratch, L.off_order);
-    if (need_mx)
-      e = launch_tile_table(s, offsets, kGemmBMMx, tiles, zeros, order, st, bmw,
-                            need_bf && tiles_w != tiles ? tiles_w : nullptr);
-    else
-      e = launch_tile_table(s, offsets, bmw, tiles_w, zeros, order, st);
+    e = tile_tables(s, offsets, n256, n320, tiles, tiles320, zeros, order, st);
     if (e != hipSuccess) return hip_status(e, __func__);
     BwdArgs a{};
     a.T = s.T; a.H = s.H; a.I = s.I; a.k = s.k; a.El = s.e_local;
@@ -485,7 +521,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
     a.row_src = row_src; a.topk_w = topk_w; a.wg = (const bf16_t*)w_gate; a.wu = (const bf16_t*)w_up;
     a.wd = (const bf16_t*)w_down; a.gu = at<bf16_t>(saved, L.off_gu); a.a = at<bf16_t>(saved, L.off_a);
     a.tiles = tiles; a.max_tiles = L.max_tiles;
-    a.tiles_w = tiles_w; a.max_tiles_w = L.max_tiles; a.bm_w = bmw;
+    a.tiles320 = tiles320; a.bm_da = h.da; a.bm_dx = h.dx;
     a.dgu = at<bf16_t>(scratch, L.off_dgu); a.dxp = at<bf16_t>(scratch, L.off_dxp);
     a.dw_part = at<float>(scratch, L.off_part);
     a.aw = at<bf16_t>(scratch, L.off_aw); a.zeros = at<bf16_t>(scratch, L.off_zeros);
@@ -500,7 +536,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
       f.T = s.T; f.H = s.H; f.I = s.I; f.k = s.k; f.El = s.e_local;
       f.x = a.x; f.xp = a.xp; f.offsets = offsets; f.row_src = row_src; f.topk_w = topk_w;
       f.wg = a.wg; f.wu = a.wu; f.wd = a.wd;
-      f.tiles = mxf ? tiles : tiles_w;
+      f.tiles = !mxf && h.k1 == 320 ? tiles320 : tiles;
       f.max_tiles = L.max_tiles;
       f.gu = rgu; f.a = ra; f.yp = nullptr;
       if (s.fwd == MOE_FWD_MXFP8) {
@@ -512,7 +548,7 @@ int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* x
         m.R_cap = L.R_cap;
         e = launch_fwd_mx(f, m, st, true);
       } else {
-        e = bmw == 320 ? fw320::launch_fwd_gateup_bf16(f, st) : fw256::launch_fwd_gateup_bf16(f, st);
+        e = h.k1 == 320 ? fw320::launch_fwd_gateup_bf16(f, st) : fw256::launch_fwd_gateup_bf16(f, st);
       }
       if (e != hipSuccess) return hip_status(e, __func__);
     }

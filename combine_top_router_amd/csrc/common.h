@@ -155,13 +155,15 @@ struct FwdArgs {
 // The bf16 forward GEMMs on the fused stream, one build per tile height (a.tiles holds
 // tiles of that height): 256 rows (gemm_fw256.hip) or 320 rows (gemm_fw320.hip).
 namespace fw256 {
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
-hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st);  // K1 only
+hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st);  // K1
+hipError_t launch_fwd_down_bf16(const FwdArgs& a, hipStream_t st);    // K2
 }  // namespace fw256
 namespace fw320 {
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_down_bf16(const FwdArgs& a, hipStream_t st);
 }  // namespace fw320
+// compute units the GEMMs' persistent grids are sized for
+int gemm_cus();
 
 struct BwdArgs {
   int T, H, I, k, El;
@@ -176,11 +178,10 @@ struct BwdArgs {
   const bf16_t* wd;
   const bf16_t* gu;       // saved
   const bf16_t* a;        // saved
-  const int32_t* tiles;   // kGemmBMMx-row tiles (the MXFP8 B1 and B3)
+  const int32_t* tiles;   // 256-row tiles (kGemmBMMx: the MXFP8 B1 and B3; bf16 ones of 256 rows)
+  const int32_t* tiles320;// 320-row tiles (bf16 B1 or B3 of 320 rows), same entry bound
   int max_tiles;
-  const int32_t* tiles_w; // bm_w-row tiles (the bf16 B3 on the fused stream)
-  int max_tiles_w;
-  int bm_w;               // 256 or 320
+  int bm_da, bm_dx;       // tile heights of the bf16 B1 and B3: 256 or 320
   bf16_t* dgu;            // scratch [R_cap, 2I]
   bf16_t* dxp;            // scratch [R_cap, H]
   float* dw_part;         // scratch [R_cap, nparts]
@@ -193,7 +194,7 @@ struct BwdArgs {
   bf16_t* dwd;            // [El, I, H]
 };
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
-// B1 alone and B3 alone on the fused stream, on a.tiles_w (a.bm_w-row tiles); the
+// B1 alone and B3 alone on the fused stream, each build on the table of its height; the
 // weight gradients on the 256-row build
 namespace fw256 {
 hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st);

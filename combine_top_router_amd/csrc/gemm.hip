@@ -869,8 +869,8 @@ hipError_t launch_bwd_gemms(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
 }  // namespace
 
 #if MOE_GEMM_FW
-// The bf16 gate/up, down and dX GEMMs on the fused stream, in namespace fw256 or fw320 by
-// tile height; a.tiles (B3: a.tiles_w) holds tiles of that height.
+// The bf16 row-tiled GEMMs on the fused stream, in namespace fw256 or fw320 by tile height:
+// FwdArgs::tiles holds tiles of that height, BwdArgs holds both tables (tiles, tiles320).
 #define MOE_FW_CAT2(a, b) a##b
 #define MOE_FW_CAT(a, b) MOE_FW_CAT2(a, b)
 namespace MOE_FW_CAT(fw, MOE_GEMM_FW) {
@@ -882,30 +882,30 @@ hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_fwd_down_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
-  MOE_LAUNCH("fwd_gateup", k_fwd_gateup<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))),
-             dim3(NTHR), 0, st, a, m);
   MOE_LAUNCH("fwd_down", k_fwd_down<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0,
              st, a, m);
   return hipGetLastError();
 }
 
+// the backward's table of this build's tile height
+static BwdArgs own_tiles(const BwdArgs& a) {
+  BwdArgs b = a;
+  if (MOE_GEMM_FW == 320) b.tiles = a.tiles320;
+  return b;
+}
+
 hipError_t launch_bwd_da_bf16(const BwdArgs& a, hipStream_t st) {
   MxArgs m{};
-  BwdArgs b = a;
-  b.tiles = a.tiles_w;
-  b.max_tiles = a.max_tiles_w;
-  return launch_bwd_gemms<false>(b, m, st);
+  return launch_bwd_gemms<false>(own_tiles(a), m, st);
 }
 
 hipError_t launch_bwd_dx_bf16(const BwdArgs& a, hipStream_t st) {
-  if (a.max_tiles_w == 0) return hipSuccess;
+  if (a.max_tiles == 0) return hipSuccess;
   MxArgs m{};
-  BwdArgs b = a;
-  b.tiles = a.tiles_w;
-  b.max_tiles = a.max_tiles_w;
+  const BwdArgs b = own_tiles(a);
   MOE_LAUNCH("bwd_dX", k_bwd_dx<false>, dim3(grid_for((int64_t)b.max_tiles * ceil_div(b.H, BN))), dim3(NTHR), 0, st,
              b, m);
   return hipGetLastError();
@@ -1001,15 +1001,15 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, b
 
 #if !MOE_GEMM_MX_TU && !MOE_GEMM_FW
 int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
+int gemm_cus() { return num_cus(); }
 
 
-// B1 and B3 run on the fused stream (gemm_fw256.hip or gemm_fw320.hip, by a.bm_w), the
-// weight gradients on its 256-row build.
+// B1 and B3 run on the fused stream (gemm_fw256.hip or gemm_fw320.hip, by a.bm_da and
+// a.bm_dx), the weight gradients on its 256-row build.
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
-  const bool f320 = a.bm_w == 320;
-  hipError_t e = f320 ? fw320::launch_bwd_da_bf16(a, st) : fw256::launch_bwd_da_bf16(a, st);
+  hipError_t e = a.bm_da == 320 ? fw320::launch_bwd_da_bf16(a, st) : fw256::launch_bwd_da_bf16(a, st);
   if (e == hipSuccess) e = fw256::launch_bwd_dwd_bf16(a, st);
-  if (e == hipSuccess) e = f320 ? fw320::launch_bwd_dx_bf16(a, st) : fw256::launch_bwd_dx_bf16(a, st);
+  if (e == hipSuccess) e = a.bm_dx == 320 ? fw320::launch_bwd_dx_bf16(a, st) : fw256::launch_bwd_dx_bf16(a, st);
   if (e == hipSuccess) e = fw256::launch_bwd_dwgu_bf16(a, st);
   return e;
 }

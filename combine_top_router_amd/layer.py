@@ -28,9 +28,9 @@ class MoeLayer:
     """
 
     def __init__(self, T, H, I, E, k, e_begin=0, e_local=None, dtype=L.MOE_BF16, bwd=L.MOE_BWD_SAME,
-                 renorm=1, device="cuda", fuse_gather=True, fwd=L.MOE_FWD_SAME, recompute=0):
+                 renorm=1, device="cuda", fuse_gather=True, fwd=L.MOE_FWD_SAME, recompute=0, row_tile=0):
         e_local = E if e_local is None else e_local
-        self.shape = L.MoeShape(T, H, I, E, k, e_begin, e_local, dtype, bwd, renorm, fwd, recompute)
+        self.shape = L.MoeShape(T, H, I, E, k, e_begin, e_local, dtype, bwd, renorm, fwd, recompute, row_tile)
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())

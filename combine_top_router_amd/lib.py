@@ -30,7 +30,8 @@ def lib_path() -> str:
 
 class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "H", "I", "E", "k", "e_begin", "e_local", "dtype", "bwd", "renorm", "fwd", "recompute")]
+                ("T", "H", "I", "E", "k", "e_begin", "e_local", "dtype", "bwd", "renorm", "fwd", "recompute",
+                 "row_tile")]
 
     def __repr__(self):
         return "MoeShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -80,6 +80,10 @@ typedef struct {
   int32_t renorm;   /* 1: weights = softmax over the k selected logits; 0: softmax over all E */
   int32_t fwd;      /* moe_fwd_prec: MOE_FWD_MXFP8 needs MOE_BF16 (added in ABI version 2) */
   int32_t recompute;/* 1: activation checkpointing, see moe_bwd; needs MOE_BF16 (ABI version 2) */
+  int32_t row_tile; /* rows per tile of the bf16 row-tiled GEMMs (gate/up, down, dA', dX'):
+                       0 lets the library choose per GEMM from the shape; 256 or 320 puts all
+                       four on that height.  Results do not depend on it: a row's sums run in
+                       the same order at either height (ABI version 3) */
 } moe_shape;
 /* The pages' precision modes map onto (fwd, bwd): bf16 = (SAME, SAME) with MOE_BF16,
  * fp8_bwd = (SAME, MXFP8), mxfp8 = (MXFP8, MXFP8). */

@@ -45,7 +45,7 @@ def run_layer(cfg, inp, fuse_gather=True, scale_up=1.0, recompute=0):
                      L.MOE_F32 if cfg.dtype == "f32" else L.MOE_BF16,
                      L.MOE_BWD_MXFP8 if cfg.bwd == "mxfp8" else L.MOE_BWD_SAME, cfg.renorm,
                      fuse_gather=fuse_gather, fwd=L.MOE_FWD_MXFP8 if cfg.fwd == "mxfp8" else L.MOE_FWD_SAME,
-                     recompute=recompute)
+                     recompute=recompute, row_tile=cfg.row_tile)
     assert (layer.saved is None) == bool(recompute)
     logits = torch.from_numpy(np.ascontiguousarray(inp["logits"])).cuda()
     x = to_dev(inp["x"], dt)

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(L.lib_path())
     for n in _declared():
         assert hasattr(raw, n), n
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def _shape(L, **kw):
@@ -57,6 +57,8 @@ BAD = [
     (dict(fwd=2), -1), (dict(dtype=0, fwd=1), -2), (dict(fwd=1), -2), (dict(fwd=1, I=128, H=192), -2),
     # recompute: an unknown value, fp32 data
     (dict(recompute=2), -1), (dict(dtype=0, recompute=1), -2),
+    # row tile height: neither automatic (0) nor one of the two builds
+    (dict(row_tile=128), -1), (dict(row_tile=-1), -1),
 ]
 
 

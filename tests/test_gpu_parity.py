@@ -27,11 +27,12 @@ SMALL = {
     # Zipf-skewed loads with 8 empty experts; the weight gradients' 768 and 384 output
     # tiles take several rounds of the persistent grid in cost order
     "skew_bf16": wl.MoeConfig("skew_bf16", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf"),
-    # about 320 rows per expert (T k / E = 320), so the bf16 gate/up, down and dX GEMMs take
-    # 320-row tiles (the smaller configs take 256-row ones): tiles that reach the second
-    # wave row, experts past 320 rows with a short second tile, 64-column N tails
-    "tall_bf16": wl.MoeConfig("tall_bf16", 1280, 320, 192, 8, 2, 0, 8, 11),
-    "tall_bf16_share": wl.MoeConfig("tall_bf16_share", 1280, 320, 192, 8, 2, 2, 5, 12),
+    # about 320 rows per expert (T k / E = 320), every bf16 row-tiled GEMM on 320-row tiles
+    # (row_tile = 320; one round of the grid makes the library's own choice 256): tiles that
+    # reach the second wave row, experts past 320 rows with a short second tile, 64-column
+    # N tails
+    "tall_bf16": wl.MoeConfig("tall_bf16", 1280, 320, 192, 8, 2, 0, 8, 11, row_tile=320),
+    "tall_bf16_share": wl.MoeConfig("tall_bf16_share", 1280, 320, 192, 8, 2, 2, 5, 12, row_tile=320),
 }
 
 
@@ -165,6 +166,27 @@ def test_deterministic_across_runs():
     inp = inputs(cfg)
     a = run_layer(cfg, inp)
     b = run_layer(cfg, inp)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+ROW_TILE = {
+    "tall_bf16_share": SMALL["tall_bf16_share"],
+    "ragged_bf16": SMALL["ragged_bf16"],
+    # fp8_bwd: only the gate/up and down GEMMs are bf16 row-tiled ones
+    "tall_fp8bwd": wl.MoeConfig("tall_fp8bwd", 1280, 256, 256, 8, 2, 0, 8, 21, bwd="mxfp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(ROW_TILE))
+def test_row_tile_height_does_not_change_results(name):
+    # the 256- and 320-row builds run each output's K loop in the same order, so every
+    # output agrees bit for bit whichever height the bf16 row-tiled GEMMs take
+    cfg = ROW_TILE[name]
+    inp = inputs(cfg)
+    print(f"[row_tile] {name}", flush=True)
+    a = run_layer(cfg.replace(row_tile=256), inp)
+    b = run_layer(cfg.replace(row_tile=320), inp)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
 

@@ -4,7 +4,8 @@ forward's own gate/up GEMM.  The kernels are deterministic, so every output must
 the outputs of the saved-activation path bit for bit; that path's parity with the
 oracle is tested elsewhere, so this also holds the recompute path to the oracle.  Each
 precision mode (bf16, fp8_bwd, mxfp8, MXFP8 forward with a bf16 backward), both weight
-modes, a local share, a skewed layer and the full Qwen3-30B-A3B layer."""
+modes, a local share, a skewed layer, forced 320-row tiles, and the full Qwen3-30B-A3B layer
+and 235B-A22B share."""
 import numpy as np
 import pytest
 
@@ -19,6 +20,8 @@ CASES = {
     "tiny_bf16": wl.CONFIGS["tiny_bf16"],
     "ragged_bf16_share": wl.MoeConfig("ragged_bf16_share", 700, 192, 320, 10, 3, 4, 5, 6),
     "skew_bf16": wl.MoeConfig("skew_bf16", 1024, 256, 192, 64, 4, 0, 64, 16, routing="zipf"),
+    # every bf16 row-tiled GEMM, the recomputed gate/up one included, on 320-row tiles
+    "tall_bf16_share": wl.MoeConfig("tall_bf16_share", 1280, 320, 192, 8, 2, 2, 5, 12, row_tile=320),
     "ragged_fp8bwd": wl.MoeConfig("ragged_fp8bwd", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
     "ragged_mxfp8_share": wl.MoeConfig("ragged_mxfp8_share", 500, 256, 256, 10, 3, 4, 5, 13, bwd="mxfp8",
                                        fwd="mxfp8"),
@@ -43,7 +46,10 @@ def test_recompute_equals_saved_path(name, fuse):
     _check_equal(CASES[name], fuse)
 
 
-def test_recompute_full_size_30b():
-    cfg = wl.CONFIGS["qwen3_30b"]
+@pytest.mark.parametrize("name", ["qwen3_30b", "qwen3_235b_ep8"])
+def test_recompute_full_size(name):
+    # 30B: every bf16 row-tiled GEMM on 320-row tiles; the 235B share: the (recomputed)
+    # gate/up GEMM on 320-row tiles, dA' and dX' on 256-row ones (both tables, one launch)
+    cfg = wl.CONFIGS[name]
     print(f"[recompute-full] {cfg.name}", flush=True)
     _check_equal(cfg, True)

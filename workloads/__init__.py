@@ -42,6 +42,7 @@ class MoeConfig:
     fwd: str = "bf16"        # "bf16" or "mxfp8" forward GEMMs
     routing: str = "gauss"   # "gauss": N(0,1) logits; "zipf": biased Gumbel logits
     renorm: int = 1          # 1: softmax over the k selected logits; 0: over all E
+    row_tile: int = 0        # rows per tile of the bf16 row-tiled GEMMs: 0 chosen by the library, 256, 320
 
     def replace(self, **kw) -> "MoeConfig":
         return dataclasses.replace(self, **kw)
