@@ -275,6 +275,8 @@ hipError_t launch_fwd_gateup_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_
 hipError_t launch_fwd_down_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st);
 hipError_t launch_bwd_da_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
 hipError_t launch_bwd_dx_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
+hipError_t launch_bwd_dwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
+hipError_t launch_bwd_dwgu_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st);
 }  // namespace fw256
 
 // fp32 (SIMT) grouped GEMMs: the same chain in fp32 arithmetic

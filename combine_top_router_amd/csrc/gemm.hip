@@ -958,6 +958,21 @@ hipError_t launch_bwd_dwgu_bf16(const BwdArgs& a, hipStream_t st) {
     MOE_LAUNCH("bwd_dWgu", (k_bwd_wgrad<1, false, true>), grid, dim3(NTHR), 0, st, a, m, tm, tn);
   return hipGetLastError();
 }
+
+// the fp8 weight gradients (transposed column-wise codes over the padded row space)
+hipError_t launch_bwd_dwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
+  const int tm = (int)ceil_div(a.I, BM), tn = (int)ceil_div(a.H, BN);
+  MOE_LAUNCH("bwd_dWd_mx", (k_bwd_wgrad<0, true>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st, a,
+             m, tm, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dwgu_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
+  const int tm = (int)ceil_div(a.H, BM), tn = (int)ceil_div(2 * a.I, BN);
+  MOE_LAUNCH("bwd_dWgu_mx", (k_bwd_wgrad<1, true>), dim3(grid_for((int64_t)a.El * tm * tn)), dim3(NTHR), 0, st,
+             a, m, tm, tn);
+  return hipGetLastError();
+}
 #endif  // MOE_GEMM_FW == 256
 
 }  // namespace fw256 / fw320
@@ -1048,17 +1063,9 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
   else
     MOE_TRY(launch_mx_cols(a.x, H, a.row_src, a.k, nullptr, a.offsets, m.poff, El, H, m.Rp, m.qt_x, m.st_x,
                            "mx_qt_x", st));
-  {
-    const int tm = (int)ceil_div(I, BM), tn = (int)ceil_div(H, BN);
-    MOE_LAUNCH("bwd_dWd_mx", (k_bwd_wgrad<0, true>), dim3(grid_for((int64_t)El * tm * tn)), dim3(NTHR), 0, st, a, m,
-               tm, tn);
-  }
+  MOE_TRY(fw256::launch_bwd_dwd_mx(a, m, st));
   MOE_TRY(fw256::launch_bwd_dx_mx(a, m, st));
-  {
-    const int tm = (int)ceil_div(H, BM), tn = (int)ceil_div(2 * I, BN);
-    MOE_LAUNCH("bwd_dWgu_mx", (k_bwd_wgrad<1, true>), dim3(grid_for((int64_t)El * tm * tn)), dim3(NTHR), 0, st, a, m,
-               tm, tn);
-  }
+  MOE_TRY(fw256::launch_bwd_dwgu_mx(a, m, st));
 #undef MOE_TRY
   return hipGetLastError();
 }
