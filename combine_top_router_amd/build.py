@@ -17,8 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "index.hip", "gemm.hip", "gemm_mx.hip", "gemm_fw256.hip", "gemm_fw320.hip",
-           "gemm_f32.hip", "mx_quant.hip", "router_gemm.hip"]
+# gemm.hip is compiled twice, through gemm_fw256.hip and gemm_fw320.hip (one tile height each)
+SOURCES = ["api.hip", "route.hip", "index.hip", "gemm_fw256.hip", "gemm_fw320.hip", "gemm_f32.hip", "mx_quant.hip",
+           "router_gemm.hip"]
 ARCH = "gfx950"
 
 
@@ -38,9 +39,9 @@ FLAGS = [
 
 
 # The GEMM translation units: every kernel in them is sized to its register budget (256
-# registers per wave on the fused stream, 128 or 168 with load waves), and a spill
-# (scratch memory traffic inside the MFMA loop or the epilogue) fails the build.
-GEMM_SOURCES = ("gemm.hip", "gemm_mx.hip", "gemm_fw256.hip", "gemm_fw320.hip")
+# registers per wave), and a spill (scratch memory traffic inside the MFMA loop or the
+# epilogue) fails the build.
+GEMM_SOURCES = ("gemm_fw256.hip", "gemm_fw320.hip")
 
 
 def _check_no_spill(src: str, remarks: str) -> None:

@@ -7,15 +7,14 @@
 // scratch buffers instead of intermediate tensors).
 //
 // Engine (gemm_engine.h): persistent workgroups (one per CU), BM x 256 output tile, K
-// step 64, each of 8 compute waves a (BM / 2) x 64 sub-tile of v_mfma_f32_32x32x16_bf16
+// step 64, each of 8 waves a (BM / 2) x 64 sub-tile of v_mfma_f32_32x32x16_bf16
 // accumulators.  Operand tiles move global -> LDS with the gfx950 direct-to-LDS loads
-// (global_load_lds_dwordx4) into a ring of LDS stages, DEPTH K steps ahead, one barrier
-// per K step, and a workgroup's tiles form one stream of K steps, so the next tile's
-// loads fly while the current tile's epilogue runs.  The bf16 GEMMs and the MXFP8
-// gate/up, down, dA and dX GEMMs run on the fused stream (every wave loads and computes;
-// gemm_fw256.hip, and gemm_fw320.hip for 320-row bf16 tiles); the MXFP8 weight gradients
-// on dedicated load waves (128-row tiles, gemm_mx.hip).  This file, compiled alone, holds
-// the bf16 backward's launch order.  An operand whose contraction axis is contiguous in
+// (global_load_lds_dwordx4) into a two-stage LDS ring, one K step ahead, one barrier per
+// K step, and a workgroup's tiles form one stream of K steps, so the next tile's loads
+// fly while the current tile's epilogue runs (the fused stream: every wave loads and
+// computes).  This file is compiled twice, by gemm_fw256.hip (256-row tiles: every GEMM,
+// and the host-side launch order of the bf16 and MXFP8 passes) and gemm_fw320.hip
+// (320-row tiles: the bf16 row-tiled GEMMs).  An operand whose contraction axis is contiguous in
 // memory ("K-major") is stored [rows][64] and read with 16-byte LDS reads; an operand
 // contiguous along M or N ("MN-major": row-major weights as the B of x*W, and both
 // operands of the weight gradients, which contract over token rows) is stored
@@ -41,7 +40,7 @@ namespace moe {
 namespace {
 
 // ---------------- shared pieces ----------------
-// What the compute waves of a row-tiled kernel know about a tile.
+// What the waves of a row-tiled kernel know about a tile.
 struct RowTileInfo {
   RowTile t;
   int n0;
@@ -86,12 +85,12 @@ __device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_
 // slots and swizzle are shared.  For v_mfma_scale_f32_32x32x64_f8f6f4 lane l of row
 // l & 31 holds codes 16 (l >> 5) .. +15 of each of the two 32-blocks of a 64-code
 // sub-step and supplies the scale of block l >> 5 of its row.  The scales of a step (4
-// bytes per row) come with 512 / (64 NP) more direct-to-LDS loads per load wave into a
-// small ring: scale slot t < BM carries A row t, BM <= t < BM + BN B row t - BM (the
-// slots past BM + BN repeat A row 0).
+// bytes per row) come with 512 / (64 NP) more direct-to-LDS loads per wave into a small
+// ring: scale slot t < BM carries A row t, BM <= t < BM + BN B row t - BM (the slots past
+// BM + BN repeat A row 0).
 constexpr int MX_STEP = 128;               // codes per K step
 constexpr int MX_SC_SLOT = 512 * 4;        // scale bytes per stage
-constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per load wave
+constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per wave
 static_assert(MX_STEP == 2 * BK, "an fp8 step must span the bytes of a bf16 step");
 // (the 320-row fused-stream build compiles no MXFP8 kernel)
 static_assert(BM == 320 || (MX_SC_LP * NP * 64 == 512 && BM + BN <= 512), "scale slots");
@@ -139,7 +138,6 @@ __device__ __forceinline__ void mx_compute(const bf16_t* st, const uint8_t* sc, 
 
 struct LMx {
   static constexpr bool GATHER = false;
-  static constexpr int NVMEM = LOADS + MX_SC_LP;
   int nk, pw;
   const uint8_t* a[A_LP];       // codes of the lane's slot at K step 0
   const uint8_t* b[B_LP];
@@ -641,15 +639,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_dx(BwdArgs a, MxArgs m) {
 // ---------------- weight gradients: contraction over an expert's rows ----------------
 // Both operands are MN-major tiles of 64 token rows; rows past the expert's end are
 // loaded from a zeroed scratch area.  For a gathered operand (rows of x or dy picked
-// by row_src) each load wave also copies the 64 row_src entries of a stream position
-// into its own LDS index slot one position ahead, with one more direct-to-LDS load, so
-// its vector memory queue holds only direct-to-LDS loads and the counts stay exact.
-// Within issue() the index load of the next position goes first, and the next issue()
-// waits for it with vmcnt(LOADS): only the operand loads may still be in flight.
+// by row_src) each wave also copies the 64 row_src entries of a stream position into its
+// own LDS index slot one position ahead, with one more direct-to-LDS load; the stream's
+// full wait at the next position completes it before the next issue() reads the slot.
 template <bool AG, bool BG>
 struct LWgrad {
   static constexpr bool GATHER = AG || BG;
-  static constexpr int NVMEM = LOADS + (GATHER ? 1 : 0);
   static constexpr int AR = 512 / BM, BR = 512 / BN;  // token rows per wave load of A and B
   const bf16_t* abase; int lda;
   const bf16_t* bbase; int ldb;
@@ -670,7 +665,6 @@ struct LWgrad {
   template <class F>
   __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int par, F&& fetch_next) const {
     const int32_t* my = ids + par * IDS_SLOT;
-    if (GATHER) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
     const bf16_t* ap[A_LP];
     const bf16_t* bp[B_LP];
     // all gathered indices are read (the slot holds valid entries for every row) before
@@ -868,7 +862,6 @@ hipError_t launch_bwd_gemms(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
 
 }  // namespace
 
-#if MOE_GEMM_FW
 // The bf16 row-tiled GEMMs on the fused stream, in namespace fw256 or fw320 by tile height:
 // FwdArgs::tiles holds tiles of that height, BwdArgs holds both tables (tiles, tiles320).
 #define MOE_FW_CAT2(a, b) a##b
@@ -976,9 +969,9 @@ hipError_t launch_bwd_dwgu_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st)
 #endif  // MOE_GEMM_FW == 256
 
 }  // namespace fw256 / fw320
-#endif  // MOE_GEMM_FW
 
-#if MOE_GEMM_MX_TU
+// The host-side launch order of the passes, compiled once (in the 256-row build).
+#if MOE_GEMM_FW == 256
 // MXFP8 forward.  Order: quantise W_gate, W_up and W_down column-wise (one group per
 // expert) and the Xp rows row-wise; K1 on fp8 operands writes G|U and A (bf16) and the
 // row-wise codes of A (from its fp32 values); K2 on fp8 operands.  K1 and K2 run on the
@@ -1012,12 +1005,8 @@ hipError_t launch_fwd_mx(const FwdArgs& a, const MxFwdArgs& m, hipStream_t st, b
   return hipSuccess;
 }
 
-#endif  // MOE_GEMM_MX_TU
-
-#if !MOE_GEMM_MX_TU && !MOE_GEMM_FW
 int bwd_bf16_nparts(int I) { return WN * (int)ceil_div(I, BN); }
 int gemm_cus() { return num_cus(); }
-
 
 // B1 and B3 run on the fused stream (gemm_fw256.hip or gemm_fw320.hip, by a.bm_da and
 // a.bm_dx), the weight gradients on its 256-row build.
@@ -1029,11 +1018,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   return e;
 }
 
-#endif  // !MOE_GEMM_MX_TU && !MOE_GEMM_FW
-
-#if MOE_GEMM_MX_TU
-// MXFP8 backward (B1 and B3 on the 256-row fused stream, a.tiles holding 256-row tiles;
-// the weight gradients here).  Order: quantise the weights row-wise (unless the MXFP8 forward left
+// MXFP8 backward (every GEMM on the 256-row fused stream; a.tiles holds 256-row tiles).
+// Order: quantise the weights row-wise (unless the MXFP8 forward left
 // their codes in the saved buffer), and dY' row-wise together with
 // w * dY' column-wise per expert; B1 (fp8) writes dG|dU (bf16); quantise dG|dU row-wise
 // and column-wise in one pass, A and Xp column-wise; then B2, B3, B4 on fp8 operands.
@@ -1070,6 +1056,6 @@ hipError_t launch_bwd_mx(const BwdArgs& a, const MxArgs& m, hipStream_t st) {
   return hipGetLastError();
 }
 
-#endif  // MOE_GEMM_MX_TU
+#endif  // MOE_GEMM_FW == 256
 
 }  // namespace moe

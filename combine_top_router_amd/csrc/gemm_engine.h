@@ -1,23 +1,21 @@
 // Shared GEMM engine of the bf16 and MXFP8 grouped GEMMs (internal header).
 //
-// Persistent workgroups (one per CU).  BM x 256 output tile, each of the NW compute waves
-// a (BM / 2) x 64 sub-tile as 32x32 MFMA accumulator blocks.  Operand tiles move
-// global -> LDS with the gfx950 direct-to-LDS loads (global_load_lds_dwordx4) into a ring
-// of LDS stages, one barrier per K step: issued by NP dedicated load waves two K steps
-// ahead into three stages (load-wave streams), or by the compute waves themselves one
-// step ahead into two larger stages (the fused stream).  An operand whose contraction
-// axis is contiguous in memory ("K-major") is stored [rows][BK] and read with 16-byte LDS
-// reads; an operand contiguous along M or N ("MN-major") is stored [BK][width] and read
-// with the transposing LDS read ds_read_b64_tr_b16.  Both layouts are XOR-swizzled by
-// 16-byte chunk against LDS bank conflicts; the swizzle is applied by choosing which
-// global chunk each lane of a load fetches.
+// Persistent workgroups (one per CU) of eight waves.  BM x 256 output tile (BM = 256 or
+// 320 rows, one build each), each wave a (BM / 2) x 64 sub-tile as 32x32 MFMA
+// accumulator blocks.  Operand tiles move global -> LDS with the gfx950 direct-to-LDS
+// loads (global_load_lds_dwordx4) into a two-stage ring, one barrier per K step: every
+// wave issues one eighth of the next step's loads, then computes the current one (the
+// fused stream).  An operand whose contraction axis is contiguous in memory ("K-major")
+// is stored [rows][BK] and read with 16-byte LDS reads; an operand contiguous along M or
+// N ("MN-major") is stored [BK][width] and read with the transposing LDS read
+// ds_read_b64_tr_b16.  Both layouts are XOR-swizzled by 16-byte chunk against LDS bank
+// conflicts; the swizzle is applied by choosing which global chunk each lane of a load
+// fetches.
 //
 // A workgroup's tiles form one stream of K steps: the loads of the next tile's first
-// steps are issued while the current tile's last steps compute, and the current
-// tile's epilogue runs in the ring stage that its last step freed while those loads
-// are in flight.  Tile descriptors and gathered row indices are read with scalar
-// loads, so each load wave's vector memory counter holds only its own operand loads
-// and its waits stay exact.
+// step are issued while the current tile's last step computes, and the current tile's
+// epilogue runs in the ring stage that its last step freed while those loads are in
+// flight.  Tile descriptors and gathered row indices are read with scalar loads.
 #pragma once
 
 #include "common.h"
@@ -25,36 +23,20 @@
 namespace moe {
 namespace {
 
-// Two workgroup shapes, chosen per translation unit:
-// * load-wave streams (gemm_mx.hip: the MXFP8 weight gradients): 128 x 256 tiles, a
-//   three-stage ring (48 KB stages), NW compute waves and NP dedicated load waves;
-// * the fused stream (MOE_GEMM_FW = the tile height, 256 in gemm_fw256.hip or 320 in
-//   gemm_fw320.hip: every bf16 GEMM and the MXFP8 row-tiled ones): 256- or 320-row tiles of
-//   256 columns, a two-stage ring (64 or 72 KB stages), eight waves that each issue one
-//   eighth of the operand loads and compute a (BM / 2) x 64 sub-tile.  Eight waves per CU leave
-//   each 256 registers, room for up to 160 accumulators; the larger tile asks a third
-//   fewer operand bytes per flop of the CU's L2 request path, which bounds the load-wave
-//   kernels.
-#ifndef MOE_GEMM_MX_TU
-#define MOE_GEMM_MX_TU 0
+// The tile height is the translation unit's MOE_GEMM_FW (256 in gemm_fw256.hip, 320 in
+// gemm_fw320.hip): 256 or 320 rows of 256 columns, 64 or 72 KB stages.  Eight waves per CU
+// leave each 256 registers, room for up to 160 accumulators.
+#if MOE_GEMM_FW != 256 && MOE_GEMM_FW != 320
+#error "gemm.hip is compiled through gemm_fw256.hip or gemm_fw320.hip"
 #endif
-#ifndef MOE_GEMM_FW
-#define MOE_GEMM_FW 0
-#endif
-constexpr bool FW = MOE_GEMM_FW != 0;
-static_assert(MOE_GEMM_FW == 0 || MOE_GEMM_FW == 256 || MOE_GEMM_FW == 320, "fused-stream tile heights");
-constexpr int BM = FW ? MOE_GEMM_FW : 128, BN = 256, BK = 64;
-constexpr int NSTAGE = FW ? 2 : 3;   // LDS ring stages
+constexpr int BM = MOE_GEMM_FW, BN = 256, BK = 64;
+constexpr int NSTAGE = 2;            // LDS ring stages
 constexpr int DEPTH = NSTAGE - 1;    // K steps in flight ahead of the MFMAs
-constexpr int NW = 8;                // compute waves: 2 along M x 4 along N
-// load (producer) waves: two per SIMD for the bf16 kernels (128 registers per wave);
-// one per SIMD for the MXFP8 kernels (gemm_mx.hip: 12 waves, 168 registers), whose fp8
-// fragments and scale operands spill at 128 registers.  The fused stream's waves are
-// load waves 0 .. NW - 1 as well.
-constexpr int NP = FW ? NW : (MOE_GEMM_MX_TU ? 4 : 8);
-constexpr int NTHR = 64 * (FW ? NW : NW + NP);
-constexpr int WM = 2;                // compute waves along M
-constexpr int WN = NW / WM;          // compute waves along N
+constexpr int NW = 8;                // waves: 2 along M x 4 along N
+constexpr int NP = NW;               // every wave issues its share of each step's loads
+constexpr int NTHR = 64 * NW;
+constexpr int WM = 2;                // waves along M
+constexpr int WN = NW / WM;          // waves along N
 constexpr int MI = BM / (32 * WM);   // 32-row accumulator blocks per wave
 constexpr int NI = BN / (32 * WN);   // 32-column accumulator blocks per wave
 constexpr int WROWS = 32 * MI;       // rows per wave
@@ -64,16 +46,14 @@ constexpr int B_ELEMS = BN * BK;
 constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
 constexpr int A_INSTR = A_ELEMS * 2 / 1024;       // 1 KB wave loads per stage, of A
 constexpr int B_INSTR = B_ELEMS * 2 / 1024;       // and of B
-constexpr int A_LP = A_INSTR / NP;                // per load wave
+constexpr int A_LP = A_INSTR / NP;                // per wave
 constexpr int B_LP = B_INSTR / NP;
-constexpr int LOADS = A_LP + B_LP;                // operand loads per load wave per stage
 constexpr int LDS_ELEMS = NSTAGE * STAGE_ELEMS;
-using Acc = f32x16[MI][NI];                       // a compute wave's accumulators
-static_assert(MI * NI * 16 <= (FW ? 160 : 128), "accumulators of one wave");
-static_assert(A_LP * NP == A_INSTR && B_LP * NP == B_INSTR, "wave loads divide among the load waves");
+using Acc = f32x16[MI][NI];                       // a wave's accumulators
+static_assert(MI * NI * 16 <= 160, "accumulators of one wave");
+static_assert(A_LP * NP == A_INSTR && B_LP * NP == B_INSTR, "wave loads divide among the waves");
 constexpr int IDS_SLOT = 64;                      // ints per index slot (one per lane)
-constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per load wave, two positions of gathered row indices
-constexpr int MIN_STEPS = DEPTH + 1;              // stream positions per tile, at least (see Sched::len)
+constexpr int IDS_INTS = NP * 2 * IDS_SLOT;       // per wave, two positions of gathered row indices
 
 // ---- scalar loads ----
 // A wave-uniform load through the scalar data cache (address space 4): it is counted
@@ -202,7 +182,7 @@ __device__ __forceinline__ void mma_stage(const bf16_t* st, Acc& acc, int lane, 
     // 320-row fused stream: the next sub-step's fragments are not read ahead of these
     // MFMAs (160 accumulators leave no room for them; the SIMD's other wave fills the
     // LDS wait)
-    if constexpr (FW && MI > 4) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MI > 4) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -314,9 +294,9 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 //   value of a counter that the launch's G workgroups share, taken when the workgroup
 //   starts its current tile: greedy longest-first, so a workgroup that finishes early
 //   takes the costliest item left and every workgroup ends within about one item of
-//   the others.  One compute wave takes the item and publishes it in LDS; the load
-//   waves read it there only when their cursor reaches the tile's last K step, so a
-//   dynamic tile spans at least DEPTH + 2 stream positions.
+//   the others.  Wave 0 takes the item at the tile's first position and publishes it in
+//   LDS; the waves read it there at the tile's next-to-last position, so a dynamic tile
+//   spans at least DEPTH + 2 stream positions.
 // Jobs with DYN = true choose per launch (J::dynamic(), a uniform device flag, and
 // J::counter(), zero before the launch).
 template <bool DYN>
@@ -360,154 +340,19 @@ struct Sched {
 };
 
 // ---- the tile stream ----
-// A workgroup has NW compute waves and NP load waves.  Its tiles form one stream of K
-// steps ("positions"); every tile takes Sched::len(nk) positions (max(nk, DEPTH + 1), or
-// DEPTH + 2 under dynamic scheduling), positions past nk repeating a valid step's loads
-// and skipping the MFMAs.  At each position the load waves wait for their own loads of
-// that position, all waves meet at a barrier, the load waves issue the loads of the
-// position DEPTH ahead (possibly the next tile's) into the stage read one position ago,
-// and the compute waves run the MFMAs of the position.  After a tile's last position
-// all waves meet once more and the compute waves run the tile's epilogue in the stage
-// just read, while the load waves wait at the next position's barrier with DEPTH
-// positions in flight.  Load-issue stalls (the vector memory queue of a CU drains at a
-// fixed rate) hold only the load waves, and the compute waves issue no loads of their
-// own besides the epilogue's.
+// A workgroup's tiles form one stream of K steps ("positions"); every tile takes
+// Sched::len(nk) positions (max(nk, DEPTH + 1), or DEPTH + 2 under dynamic scheduling),
+// positions past nk repeating a valid step's loads and skipping the MFMAs.
 //
-// A job J supplies: items(); steps(v) (K steps of item v; scalar loads only); the
-// compute side -- Tile, tile(v, Tile&) (what the epilogue needs, scalar loads only),
-// rows(const Tile&, wm) (the WaveRows of wave row wm), compute(stage pointer, stage index,
-// acc, lane, WaveRows, wn) and
-// epilogue(const Tile&, acc, staging); and the load side -- Ld, setup(v, Ld&, pw,
-// lane) and Ld::NVMEM, Ld::GATHER, Ld::issue(kt, stage pointer, stage index, parity,
-// fetch_next) and Ld::fetch(kt, parity).  Each issue makes exactly NVMEM vector memory
-// instructions (fetch_next, when the loader calls it, is one of them: it fetches the
-// row indices of the next position into the other index slot), which keeps the vmcnt
-// waits exact.
-template <class J, class S>
-__device__ __forceinline__ void compute_stream(const J& job, bf16_t* lds, S sc, int wv, int lane) {
-  using T = typename J::Tile;
-  const int wm = (int)((unsigned)wv % WM), wn = (int)((unsigned)wv / WM);
-  T cur, nxt;
-  job.tile(sc.v, cur);
-  int v = sc.v;
-  Acc acc;
-  zero_acc(acc);
-  int32_t* slot = nullptr;   // dynamic: two LDS slots for the next item, by tile parity
-  if constexpr (J::DYN) slot = job.dslot;
-  int cs = 0;
-  for (int t = 0;; ++t) {
-    const int nk = cur.nk, len = sc.len(nk);
-    int vn = sc.dyn ? -1 : sc.next(v);
-    const WaveRows wr = job.rows(cur, wm);
-    const bool act = wr.nblk > 0;
-    int done = 0, grabbed = 0;
-    for (int kc = 0; kc < len; ++kc) {
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // dynamic: wave 0 takes the next item before its MFMAs and publishes it after
-      // them; every compute wave reads it after the next barrier
-      if (sc.dyn && kc == 0 && wv == 0 && lane == 0) grabbed = sc.grab();
-      if (kc < nk && act) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wr, wn);
-      if (sc.dyn) {
-        if (kc == 0 && wv == 0) {
-          const int n = uni(grabbed);
-          if (lane == 0) slot[t & 1] = n;
-        }
-        if (kc == 1) {
-          vn = uni(slot[t & 1]);
-          if (vn >= 0) job.tile(vn, nxt);
-        }
-      } else if (kc == 0 && vn >= 0) {
-        job.tile(vn, nxt);
-      }
-      done = cs;
-      cs = cs == NSTAGE - 1 ? 0 : cs + 1;
-    }
-    const bool more = vn >= 0;
-    // every wave is done with the stage just read: stage the results there (a job whose
-    // epilogue writes from registers alone, !J::EPI_LDS, needs neither)
-    if constexpr (J::EPI_LDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    job.epilogue(cur, acc, reinterpret_cast<float*>(lds + done * STAGE_ELEMS));
-    zero_acc(acc);
-    if (!more) break;
-    cur = nxt;
-    v = vn;
-  }
-}
-
-template <class J, class S>
-__device__ __forceinline__ void load_stream(const J& job, bf16_t* lds, S sc, int pw, int lane) {
-  using P = typename J::Ld;
-  P cur, nxt;
-  job.setup(sc.v, cur, pw, lane);
-  int32_t* slot = nullptr;                  // dynamic: the compute side's next-item slots
-  if constexpr (J::DYN) slot = job.dslot;
-  int tl = 0;                               // tiles of this workgroup before cur
-  int vc = sc.v, vn = -1;                   // items of cur and nxt
-  int lc = sc.len(cur.nk), ln = 0;          // stream positions of cur and nxt
-  bool has_nxt = false, looked = false;     // nxt set up; the item after cur looked up
-  bool in_nxt = false;                      // the issue cursor is in nxt
-  int ik = 0;                               // issue cursor: step within its tile
-  int gpar = 0;                             // parity of the issue position
-  auto clampk = [](int kt, int nk) { return max(0, min(kt, nk - 1)); };
-  auto issue = [&](int stage) {
-    bf16_t* st = lds + stage * STAGE_ELEMS;
-    if (in_nxt) {
-      // never the last position of nxt: the compute cursor enters nxt first
-      const int k0 = ik;
-      nxt.issue(clampk(k0, nxt.nk), st, stage, gpar, [&] { nxt.fetch(k0 + 1, gpar ^ 1); });
-      ++ik;
-    } else {
-      const int k0 = ik;
-      const bool last = k0 >= lc - 1;
-      if (last && !looked) {
-        looked = true;
-        // dynamic: published by the compute side during cur's first position, at least
-        // one barrier before this last position of cur is issued
-        vn = sc.dyn ? uni(slot[tl & 1]) : sc.next(vc);
-        if (vn >= 0) {
-          job.setup(vn, nxt, pw, lane);
-          ln = sc.len(nxt.nk);
-          has_nxt = true;
-        }
-      }
-      cur.issue(clampk(k0, cur.nk), st, stage, gpar, [&] {
-        if (!last) cur.fetch(k0 + 1, gpar ^ 1);
-        else if (has_nxt) nxt.fetch(0, gpar ^ 1);
-        else cur.fetch(k0, gpar ^ 1);
-      });
-      if (!last) ++ik;
-      else if (has_nxt) { in_nxt = true; ik = 0; }
-    }
-    gpar ^= 1;
-  };
-  if (P::GATHER) {
-    cur.fetch(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue(d);
-  int cs = 0, kc = 0;
-  for (;;) {
-    // this wave's loads of the position have landed (the DEPTH - 1 later positions may
-    // still fly); the barrier then hands the stage to the compute waves and frees the
-    // stage they read one position ago
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"((DEPTH - 1) * P::NVMEM) : "memory");
-    issue(cs == 0 ? NSTAGE - 1 : cs - 1);  // (position + DEPTH) % NSTAGE
-    cs = cs == NSTAGE - 1 ? 0 : cs + 1;
-    if (++kc < lc) continue;
-    if constexpr (J::EPI_LDS) asm volatile("s_barrier" ::: "memory");  // the compute waves' epilogue barrier
-    if (!has_nxt) break;
-    cur = nxt;
-    vc = vn;
-    lc = ln;
-    ++tl;
-    has_nxt = looked = in_nxt = false;
-    kc = 0;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing repeated loads
-}
-
-// The fused stream (FW): every wave is compute wave wv and load wave wv, with one K step
+// A job J supplies: items(); the compute side -- Tile, tile(v, Tile&) (what the epilogue
+// needs, scalar loads only), rows(const Tile&, wm) (the WaveRows of wave row wm),
+// compute(stage pointer, stage index, acc, lane, WaveRows, wn) and epilogue(const Tile&,
+// acc, staging); and the load side -- Ld, setup(v, Ld&, pw, lane) and Ld::GATHER,
+// Ld::issue(kt, stage pointer, stage index, parity, fetch_next) and Ld::fetch(kt,
+// parity) (fetch_next, when the loader calls it, fetches the row indices of the next
+// position into the other index slot); a gathering loader's job also supplies
+// fetch_first(v, pw, lane, parity), the row indices of item v's first step.
+// The fused stream: every wave is compute wave wv and load wave wv, with one K step
 // in flight.  At each position a wave waits for everything it has issued (its loads of
 // the position and its index fetch for the next, and any epilogue stores), meets the
 // other waves at the barrier (after which the position's stage is complete and the
@@ -612,13 +457,7 @@ __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
   }
   Sched<J::DYN> sc(job.items(), dyn, ctr);
   if (sc.v < 0) return;
-  if constexpr (FW) {
-    fused_stream(job, lds, sc, wv, lane);
-  } else if (wv >= NW) {
-    load_stream(job, lds, sc, wv - NW, lane);
-  } else {
-    compute_stream(job, lds, sc, wv, lane);
-  }
+  fused_stream(job, lds, sc, wv, lane);
 }
 
 // ---- epilogue staging ----

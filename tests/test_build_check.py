@@ -17,9 +17,9 @@ def test_spill_in_a_gemm_kernel_fails_the_build():
     with pytest.raises(RuntimeError, match="spills 8 bytes"):
         b._check_no_spill("gemm_fw320.hip", bad)
     with pytest.raises(RuntimeError, match="spills 8 bytes"):
-        b._check_no_spill("gemm_mx.hip", bad.replace("k_bwd_daILb0E", "k_bwd_daILb1E"))
+        b._check_no_spill("gemm_fw256.hip", bad.replace("k_bwd_daILb0E", "k_bwd_daILb1E"))
     # no spill: accepted
-    b._check_no_spill("gemm.hip", bad.replace("ScratchSize [bytes/lane]: 8", "ScratchSize [bytes/lane]: 0"))
+    b._check_no_spill("gemm_fw256.hip", bad.replace("ScratchSize [bytes/lane]: 8", "ScratchSize [bytes/lane]: 0"))
 
 
 def test_every_gemm_source_is_checked():
