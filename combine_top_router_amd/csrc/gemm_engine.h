@@ -218,37 +218,42 @@ __device__ __forceinline__ void trans_chunks(const f32x16& a, i32x4 (&out)[2]) {
 // region [32][8 NCH] bf16 so that afterwards NCH consecutive lanes hold the NCH chunks of
 // one row: store(row_in_band, column_in_band, chunk) is called for rows lane / NCH +
 // (64 / NCH) j, and one store instruction writes whole row segments of 16 NCH bytes.
-// Chunk c of row r sits at c ^ ((r / RPW) % NCH), RPW = rows per 256-byte bank window,
-// so that the 16 lanes of each 256-byte access phase hit 16 distinct 16-byte slots, for
-// the writes (16 rows, one chunk each) and the reads (16 / NCH rows, all their chunks) alike.
+// Chunk c of row r sits at slot c ^ band_swz(r).  A write puts one chunk of 32
+// consecutive rows; band_swz gives any 8 consecutive rows distinct 16-byte slots of a
+// 128-byte window and any 16 distinct slots of a 256-byte window (rows of 128 bytes: the
+// row parity picks the window half; of 64 bytes: r % 4 picks the quarter), which is what
+// keeps 16-byte LDS writes free of bank conflicts on gfx950 (the form c ^ (r / 2), free
+// for 16-byte reads, measured 16 % conflicted cycles in the weight gradients).  A read
+// takes whole rows, so any swizzle keeps it conflict-free.
 static_assert(WCOLS == 64, "a band row holds at most 8 chunks of 16 bytes");
 constexpr int BAND_ELEMS = 32 * WCOLS;  // per wave
 static_assert(NW * BAND_ELEMS <= STAGE_ELEMS, "the bands of all waves fit in one ring stage");
+template <int NCH>
+__device__ __forceinline__ int band_swz(int r) {
+  static_assert(NCH == 4 || NCH == 8, "rows of 64 or 128 bytes");
+  if constexpr (NCH == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
 template <int NB, class F>
 __device__ __forceinline__ void band_store(bf16_t* wreg, const i32x4 (&ch)[NB][2], F&& store) {
-  constexpr int NCH = 4 * NB, W = 8 * NCH, RPW = 16 / NCH;
+  constexpr int NCH = 4 * NB, W = 8 * NCH;
   static_assert(NB == 1 || NB == 2, "one or two 32-column blocks per band row");
   const int lane = threadIdx.x & 63, r = lane & 31;
+  const int swr = band_swz<NCH>(r);
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = b * 4 + 2 * s + (lane >> 5);
-      *reinterpret_cast<i32x4*>(wreg + r * W + ((c ^ ((r / RPW) & (NCH - 1))) << 3)) = ch[b][s];
+      *reinterpret_cast<i32x4*>(wreg + r * W + ((c ^ swr) << 3)) = ch[b][s];
     }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  // read j covers rows lane / NCH + (64 / NCH) j; its swizzle term ((rr / RPW) % NCH)
-  // is the lane's own term XOR (64 / NCH / RPW) j mod NCH, so every read addresses from
-  // one per-lane base
   i32x4 v[NCH / 2];
   const int rr0 = lane / NCH, cc = lane % NCH;
-  const int sw0 = (rr0 / RPW) & (NCH - 1);
 #pragma unroll
   for (int j = 0; j < NCH / 2; ++j) {
-    constexpr int STEP = 64 / NCH / RPW;  // swizzle increment per read (4 for NCH = 8 and 4)
-    static_assert((64 / NCH) % RPW == 0, "whole bank windows per read");
-    const int sw = (sw0 + STEP * j) & (NCH - 1);
-    v[j] = *reinterpret_cast<const i32x4*>(wreg + (rr0 + (64 / NCH) * j) * W + ((cc ^ sw) << 3));
+    const int rr = rr0 + (64 / NCH) * j;
+    v[j] = *reinterpret_cast<const i32x4*>(wreg + rr * W + ((cc ^ band_swz<NCH>(rr)) << 3));
   }
 #pragma unroll
   for (int j = 0; j < NCH / 2; ++j) store(lane / NCH + (64 / NCH) * j, (lane % NCH) * 8, v[j]);
@@ -482,11 +487,15 @@ __device__ __forceinline__ void stage_quarter(float* wsm, const Acc& acc, int mi
 }
 __device__ __forceinline__ void staging_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+// 8 consecutive floats of staged row r: the rows lie EP_LD * 4 = 288 bytes apart (32 mod
+// 256), so in one 16-byte read the lanes of rows r and r + 1 would meet on the same banks;
+// odd rows read their two halves in the other order, which puts them on the other banks
+__device__ __forceinline__ void read8(const float* p, int r, float (&v)[8]) {
+  const int h = (r & 1) * 4;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + h);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + (4 - h));
+  v[0] = h ? b[0] : a[0]; v[1] = h ? b[1] : a[1]; v[2] = h ? b[2] : a[2]; v[3] = h ? b[3] : a[3];
+  v[4] = h ? a[0] : b[0]; v[5] = h ? a[1] : b[1]; v[6] = h ? a[2] : b[2]; v[7] = h ? a[3] : b[3];
 }
 
 __device__ __forceinline__ i32x4 pack8(const float (&v)[8]) {
@@ -526,7 +535,7 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, cons
         float v[EP_ROWS / EP_RPP][8];
 #pragma unroll
         for (int j = 0; j < EP_ROWS / EP_RPP; ++j)
-          read8(wsm + (lane / EP_LPR + EP_RPP * j) * EP_LD + (lane % EP_LPR) * 8, v[j]);
+          read8(wsm + (lane / EP_LPR + EP_RPP * j) * EP_LD + (lane % EP_LPR) * 8, lane / EP_LPR + EP_RPP * j, v[j]);
 #pragma unroll
         for (int j = 0; j < EP_ROWS / EP_RPP; ++j)
           f(w.base + mi * 32 + h * 16 + lane / EP_LPR + EP_RPP * j, wn * WCOLS + (lane % EP_LPR) * 8, v[j],
@@ -536,7 +545,7 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, cons
         for (int j = 0; j < EP_ROWS / EP_RPP; ++j) {
           const int rr = lane / EP_LPR + EP_RPP * j, cc = (lane % EP_LPR) * 8;
           float v[8];
-          read8(wsm + rr * EP_LD + cc, v);
+          read8(wsm + rr * EP_LD + cc, rr, v);
           f(w.base + mi * 32 + h * 16 + rr, wn * WCOLS + cc, v, (mi * 2 + h) * (EP_ROWS / EP_RPP) + j);
         }
       }
