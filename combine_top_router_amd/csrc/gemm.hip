@@ -184,7 +184,7 @@ struct LMx {
 };
 
 // ---------------- K1: gate/up + SwiGLU ----------------
-// B tile: gate columns 0..BN/2-1 and up columns BN/2..BN-1; wave column wn takes the same
+// B tile: gate columns 0..BN/2-1 and up columns BN/2..BN-1; compute wave wn takes the same
 // WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
 // and U of one element share a lane.
 struct LGateUp : RowLd {
@@ -458,7 +458,7 @@ struct JDa {
   MxArgs m;
   int NT, nparts;
   uint8_t* scring;
-  float* wrow;  // LDS [NW][WROWS]: the routing weights of each wave's rows
+  float* wrow;  // LDS [NW][WROWS]: the routing weights of each compute wave's rows
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
   __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }

@@ -143,7 +143,7 @@ __device__ __forceinline__ bf16x8 frag_mnmaj(const bf16_t* s, int base, int kk, 
   return out;
 }
 
-// The rows [base, end) of a row tile of cnt rows that wave row wm holds, in nblk
+// The rows [base, end) of a row tile of cnt rows that compute wave row wm holds, in nblk
 // 32-row accumulator blocks with rows (wave-uniform): wave row wm takes rows
 // wm * WROWS .. + WROWS - 1.  A wave without rows (nblk = 0) skips its MFMAs.
 struct WaveRows {
