@@ -45,7 +45,12 @@ struct RowTileInfo {
   RowTile t;
   int n0;
   int nk;
+  int ncols;   // output columns from n0 (BN, or BN / 2 for a column half)
 };
+// Column halves (jobs with NSPLIT, see Sched): the job's value is item * 4 + hs
+__device__ __forceinline__ int split_item(int v) { return v >> 2; }
+__device__ __forceinline__ int split_off(int v) { return (v & 3) == 2 ? BN / 2 : 0; }
+__device__ __forceinline__ int split_cols(int v) { return (v & 3) ? BN / 2 : BN; }
 
 // Row-tiled bf16 loader state common to the fused-stream kernels: issue(kt, stage, ...)
 // issues the wave's direct-to-LDS loads of K step kt; the rows are fixed per tile, so
@@ -77,6 +82,17 @@ __device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_
   row_tile(tiles, offsets, v, NT, p.t);
   p.n0 = p.t.nt * ntw;
   p.nk = nk;
+  p.ncols = BN;
+}
+// a job's tile for its value v (a column half when NS and v says so)
+template <bool NS>
+__device__ __forceinline__ void row_tile_info_split(const int32_t* tiles, const int32_t* offsets, int v, int NT,
+                                                    int nk, RowTileInfo& p) {
+  row_tile_info(tiles, offsets, NS ? split_item(v) : v, NT, nk, BN, p);
+  if constexpr (NS) {
+    p.n0 += split_off(v);
+    p.ncols = split_cols(v);
+  }
 }
 
 // ---------------- MXFP8 operands (mxfp8 forward, fp8_bwd / mxfp8 backward) ----------------
@@ -91,6 +107,7 @@ __device__ __forceinline__ void row_tile_info(const int32_t* tiles, const int32_
 constexpr int MX_STEP = 128;               // codes per K step
 constexpr int MX_SC_SLOT = 512 * 4;        // scale bytes per stage
 constexpr int MX_SC_LP = 512 / (64 * NP);  // scale loads per wave
+static_assert(B_LP % 2 == 0, "a column half is B_LP / 2 whole loads");
 static_assert(MX_STEP == 2 * BK, "an fp8 step must span the bytes of a bf16 step");
 // (the 320-row fused-stream build compiles no MXFP8 kernel)
 static_assert(BM == 320 || (MX_SC_LP * NP * 64 == 512 && BM + BN <= 512), "scale slots");
@@ -207,6 +224,7 @@ struct JGateUp {
   using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
+  static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
   }
@@ -345,6 +363,7 @@ struct JDown {
   using Ld = typename std::conditional<MX, LMx, LMnB>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
+  static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
   MxFwdArgs m;
@@ -352,7 +371,9 @@ struct JDown {
   uint8_t* scring;
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.I / MX_STEP : a.I / BK; }
-  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
+  __device__ __forceinline__ void tile(int v, Tile& p) const {
+    row_tile_info_split<NSPLIT>(a.tiles, a.offsets, v, NT, nk(), p);
+  }
   __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
@@ -361,8 +382,8 @@ struct JDown {
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
-    row_tile(a.tiles, a.offsets, v, NT, t);
-    const int n0 = t.nt * BN;
+    row_tile(a.tiles, a.offsets, NSPLIT ? split_item(v) : v, NT, t);
+    const int n0 = t.nt * BN + (NSPLIT ? split_off(v) : 0);
     p.pw = pw;
     p.nk = nk();
     if constexpr (MX) {
@@ -425,23 +446,28 @@ __global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a, MxFwdArgs m) {
 }
 
 // ---------------- B1 / B3: both operands K-major ----------------
+template <bool NS>
 struct LKK : RowLd {
   KRows a;
   const bf16_t* b[B_LP];   // B rows for K steps [0, ksplit)
   const bf16_t* b2[B_LP];  // B3: W_up rows for K steps [ksplit, nk)
   int ksplit;              // B3: I / 64; B1: larger than any step count
+  // a column half (uniform): B load q fills tile rows 64 q .. 64 q + 63 (one eighth
+  // of each to every wave), so the half's BN / 2 rows are loads q < B_LP / 2 exactly
+  int half;
   template <class F>
   __device__ __forceinline__ void issue(int kt, bf16_t* st, int, int, F&&) const {
     a.dma(kt, st, pw);
     const bool second = kt >= ksplit;
     const int k0 = (second ? kt - ksplit : kt) * BK;
 #pragma unroll
-    for (int q = 0; q < B_LP; ++q) dma16((second ? b2[q] : b[q]) + k0, b_dst(st, q, pw));
+    for (int q = 0; q < B_LP; ++q)
+      if (!NS || q < B_LP / 2 || !half) dma16((second ? b2[q] : b[q]) + k0, b_dst(st, q, pw));
   }
 };
 
-template <bool MX>
-using KKLd = typename std::conditional<MX, LMx, LKK>::type;
+template <bool MX, bool NS>
+using KKLd = typename std::conditional<MX, LMx, LKK<NS>>::type;
 
 // B1: dA' = dY' Wd^T.  Epilogue: SwiGLU backward on 8 columns per lane, w * A for B2, and
 // the rowdot of dA' and A over this wave's 64 columns, reduced across the 8 lanes of a row.
@@ -450,9 +476,10 @@ using KKLd = typename std::conditional<MX, LMx, LKK>::type;
 template <bool MX>
 struct JDa {
   using Tile = RowTileInfo;
-  using Ld = KKLd<MX>;
+  using Ld = KKLd<MX, !MX>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, TRANS = false, EPI_LDS = true;
+  static constexpr bool NSPLIT = !MX;   // column halves of a last round (Sched)
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -461,7 +488,9 @@ struct JDa {
   float* wrow;  // LDS [NW][WROWS]: the routing weights of each compute wave's rows
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? a.H / MX_STEP : a.H / BK; }
-  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
+  __device__ __forceinline__ void tile(int v, Tile& p) const {
+    row_tile_info_split<NSPLIT>(a.tiles, a.offsets, v, NT, nk(), p);
+  }
   __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
@@ -470,8 +499,8 @@ struct JDa {
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
-    row_tile(a.tiles, a.offsets, v, NT, t);
-    const int n0 = t.nt * BN;
+    row_tile(a.tiles, a.offsets, NSPLIT ? split_item(v) : v, NT, t);
+    const int n0 = t.nt * BN + (NSPLIT ? split_off(v) : 0);
     p.pw = pw;
     p.nk = nk();
     if constexpr (MX) {
@@ -481,6 +510,8 @@ struct JDa {
       p.ksplit = 1 << 30;
       a_rows_kmaj(p.a, nullptr, a.dy, a.row_src, a.k, a.H, t, pw, lane);
       const bf16_t* wd = a.wd + (size_t)t.e * a.I * a.H;
+      const int ncols = NSPLIT ? split_cols(v) : BN;
+      p.half = uni(ncols < BN ? 1 : 0);
 #pragma unroll
       for (int q = 0; q < B_LP; ++q) {
         int r, c;
@@ -547,7 +578,9 @@ struct JDa {
       }
 #pragma unroll
       for (int off = 1; off < EP_LPR; off <<= 1) part += __shfl_xor(part, off, 64);
-      if (rt < w.end && lane % EP_LPR == 0) a.dw_part[(size_t)(p.t.rs + rt) * nparts + p.t.nt * WN + wn] = part;
+      // the wave's absolute 64-column block of the tile (a right column half starts at BN / 2)
+      if (rt < w.end && lane % EP_LPR == 0)
+        a.dw_part[(size_t)(p.t.rs + rt) * nparts + p.t.nt * WN + (p.n0 - p.t.nt * BN) / WCOLS + wn] = part;
     });
   }
 };
@@ -566,9 +599,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_bwd_da(BwdArgs a, MxArgs m, int npa
 template <bool MX>
 struct JDx {
   using Tile = RowTileInfo;
-  using Ld = KKLd<MX>;
+  using Ld = KKLd<MX, false>;
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
+  static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -576,7 +610,9 @@ struct JDx {
   uint8_t* scring;
   __device__ __forceinline__ int items() const { return sload(a.tiles) * NT; }
   __device__ __forceinline__ int nk() const { return MX ? 2 * a.I / MX_STEP : 2 * a.I / BK; }
-  __device__ __forceinline__ void tile(int v, Tile& p) const { row_tile_info(a.tiles, a.offsets, v, NT, nk(), BN, p); }
+  __device__ __forceinline__ void tile(int v, Tile& p) const {
+    row_tile_info_split<NSPLIT>(a.tiles, a.offsets, v, NT, nk(), p);
+  }
   __device__ __forceinline__ WaveRows rows(const Tile& p, int wm) const { return wave_rows(p.t.cnt, wm); }
   __device__ __forceinline__ void compute(const bf16_t* st, int slot, Acc& acc, int lane, const WaveRows& w,
                                           int wn) const {
@@ -585,8 +621,8 @@ struct JDx {
   }
   __device__ __forceinline__ void setup(int v, Ld& p, int pw, int lane) const {
     RowTile t;
-    row_tile(a.tiles, a.offsets, v, NT, t);
-    const int n0 = t.nt * BN;
+    row_tile(a.tiles, a.offsets, NSPLIT ? split_item(v) : v, NT, t);
+    const int n0 = t.nt * BN + (NSPLIT ? split_off(v) : 0);
     p.pw = pw;
     p.nk = nk();
     if constexpr (MX) {
@@ -716,6 +752,7 @@ struct JWgrad {
   // ranges.  a.order[El + 1 + WHICH] is the launch's item counter (zeroed with the order).
   // the accumulators hold C^T; the epilogue writes them as bf16 row bands (band_store)
   static constexpr bool DYN = true, TRANS = true, EPI_LDS = true;
+  static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
   __device__ __forceinline__ bool dynamic() const { return sload(a.order + a.El) != 0; }
   __device__ __forceinline__ int32_t* counter() const { return a.order + a.El + 1 + WHICH; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }

@@ -304,35 +304,66 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 //   spans at least DEPTH + 2 stream positions.
 // Jobs with DYN = true choose per launch (J::dynamic(), a uniform device flag, and
 // J::counter(), zero before the launch).
-template <bool DYN>
+// Column halves (contiguous ranges of a job with NSPLIT): when the last round of an XCD's
+// range is at most half full (rem items for its G / 8 workgroups, 2 rem <= G / 8), each of
+// those rem tiles is handed out as two halves of BN / 2 columns, so that the round keeps
+// every workgroup busy on about half a tile instead of half the workgroups on whole ones.
+// A half computes its own output columns (no partial sums to combine), so results do not
+// change.  The stream walks work indices u; enc(u) is the job's value: the item, or for
+// NSPLIT jobs item * 4 + hs with hs = 0 (whole tile), 1 (left half) or 2 (right half).
+template <bool DYN, bool NSPLIT = false>
 struct Sched {
-  int v;          // the workgroup's first item; < 0: none
-  int hi;         // contiguous: end of the XCD's range; dynamic: V
+  int v;          // the workgroup's first work index; < 0: none
+  int hi;         // contiguous: end of the XCD's work indices; dynamic: V
   int step;       // contiguous: stride
   int g;          // grid size
   bool dyn;
   int32_t* ctr;   // dynamic: the launch's item counter
+  int lo;         // contiguous: the XCD's first item
+  int whole;      // contiguous: work indices below it are whole tiles
   __device__ Sched(int V, bool dynamic, int32_t* counter) {
     const int x = blockIdx.x & 7;
     dyn = DYN && dynamic;
     ctr = counter;
     g = (int)gridDim.x;
+    lo = 0;
+    whole = 0;
     if (dyn) {
       const int w = x * (g >> 3) + (int)(blockIdx.x >> 3);
       hi = V;
       step = 0;
       v = w < V ? w : -1;
     } else {
-      const int lo = (int)(((int64_t)V * x) >> 3);
-      hi = (int)(((int64_t)V * (x + 1)) >> 3);
+      lo = (int)(((int64_t)V * x) >> 3);
+      const int n = (int)(((int64_t)V * (x + 1)) >> 3) - lo;
       step = (int)(gridDim.x >> 3);
-      v = lo + (int)(blockIdx.x >> 3);
+      whole = n;
+      hi = n;
+      if constexpr (NSPLIT) {
+        const int R = n / step, rem = n - R * step;
+        if (rem > 0 && 2 * rem <= step) {
+          whole = R * step;
+          hi = whole + 2 * rem;
+        }
+      }
+      v = (int)(blockIdx.x >> 3);
       if (v >= hi) v = -1;
+    }
+  }
+  // the job's value of work index u
+  __device__ __forceinline__ int enc(int u) const {
+    if (dyn) return u;
+    if constexpr (NSPLIT) {
+      if (u < whole) return (lo + u) << 2;
+      const int h = u - whole;
+      return ((lo + whole + (h >> 1)) << 2) | (1 + (h & 1));
+    } else {
+      return lo + u;
     }
   }
   // stream positions a tile of nk K steps takes
   __device__ __forceinline__ int len(int nk) const { return max(nk, dyn ? DEPTH + 2 : DEPTH + 1); }
-  // contiguous: the item after u (an item of this workgroup), or -1
+  // contiguous: the work index after u (one of this workgroup's), or -1
   __device__ __forceinline__ int next(int u) const {
     const int n = u + step;
     return n < hi ? n : -1;
@@ -389,10 +420,12 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
   };
   P lcur;
   T cur;
-  int v = sc.v, vn = -1;
-  setup(v, lcur);
-  job.tile(v, cur);
+  int v = sc.v, vn = -1;   // work indices (sc.enc gives the job's value)
+  setup(sc.enc(v), lcur);
+  job.tile(sc.enc(v), cur);
   WaveRows wr = job.rows(cur, wm);
+  if constexpr (J::NSPLIT)
+    if (wn * WCOLS >= cur.ncols) wr.nblk = 0;   // a column half: this wave's columns lie outside it
   int len = sc.len(cur.nk);
   bool has_nxt = false;
   int gpar = 0;   // index slot of the next issue
@@ -420,14 +453,14 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
           if (k1 + 1 < len) {
             lcur.fetch(clampk(k1 + 1, lcur.nk), gpar ^ 1);
           } else if (has_nxt) {
-            if constexpr (P::GATHER) job.fetch_first(vn, wv, lane, gpar ^ 1);
+            if constexpr (P::GATHER) job.fetch_first(sc.enc(vn), wv, lane, gpar ^ 1);
           } else {
             lcur.fetch(clampk(k1, lcur.nk), gpar ^ 1);
           }
         });
         gpar ^= 1;
       } else if (has_nxt) {
-        setup(vn, lcur);
+        setup(sc.enc(vn), lcur);
         lcur.issue(0, st, cs ^ 1, gpar, [&] { lcur.fetch(1, gpar ^ 1); });
         gpar ^= 1;
       }
@@ -439,13 +472,17 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
       cs ^= 1;
     }
     if constexpr (J::EPI_LDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    job.epilogue(cur, acc, reinterpret_cast<float*>(lds + (cs ^ 1) * STAGE_ELEMS));
+    bool epi = true;
+    if constexpr (J::NSPLIT) epi = wn * WCOLS < cur.ncols;
+    if (epi) job.epilogue(cur, acc, reinterpret_cast<float*>(lds + (cs ^ 1) * STAGE_ELEMS));
     zero_acc(acc);
     if (!has_nxt) break;
     v = vn;
     has_nxt = false;
-    job.tile(v, cur);
+    job.tile(sc.enc(v), cur);
     wr = job.rows(cur, wm);
+    if constexpr (J::NSPLIT)
+      if (wn * WCOLS >= cur.ncols) wr.nblk = 0;
     len = sc.len(cur.nk);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -460,7 +497,7 @@ __device__ __forceinline__ void run_stream(const J& job, bf16_t* lds) {
     dyn = job.dynamic();
     ctr = job.counter();
   }
-  Sched<J::DYN> sc(job.items(), dyn, ctr);
+  Sched<J::DYN, J::NSPLIT> sc(job.items(), dyn, ctr);
   if (sc.v < 0) return;
   fused_stream(job, lds, sc, wv, lane);
 }
