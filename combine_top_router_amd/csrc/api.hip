@@ -148,6 +148,17 @@ static hipError_t tile_tables(const moe_shape& s, const int32_t* offsets, bool n
   return launch_tile_table(s, offsets, 320, t320, zeros, order, st);
 }
 
+// fp8_bwd: the forward's bf16 GEMMs write the weights' row-wise codes for the backward
+// when each expert's weight slices pass through at least three row tiles of both GEMMs
+// (the row tiles share the quantising steps; the 235B-A22B share has about four).  With
+// fewer, those tiles' extra stores cost more than the backward's own weight passes (an
+// expert of one row tile would quantise every step of its stream).
+static bool fwd_writes_wcodes(const moe_shape& s) {
+  if (s.dtype != MOE_BF16 || s.bwd != MOE_BWD_MXFP8 || s.fwd == MOE_FWD_MXFP8 || s.recompute) return false;
+  const RowTiles h = row_tile_heights(s);
+  return tiles_per_expert(s, h.k1) >= 3.0 && tiles_per_expert(s, h.k2) >= 3.0;
+}
+
 void layout(const moe_shape& s, Layout& L) {
   const int El = s.e_local;
   L.R_cap = (int64_t)s.T * (s.k < El ? s.k : El);
@@ -159,7 +170,10 @@ void layout(const moe_shape& s, Layout& L) {
   L.off_gu = 0;
   L.off_a = align_up(R * 2 * s.I * L.es);
   L.saved_bytes = s.recompute ? 0 : L.off_a + align_up(R * s.I * L.es);
-  L.wrows_saved = s.fwd == MOE_FWD_MXFP8 && s.bwd == MOE_BWD_MXFP8 && !s.recompute;
+  // the weights' row-wise codes for the MXFP8 backward, written by the forward (its weight
+  // passes in mxfp8, its bf16 GEMMs' B stages in fp8_bwd where that pays) and kept with
+  // the activations; else the backward quantises the weights itself
+  L.wrows_saved = s.bwd == MOE_BWD_MXFP8 && !s.recompute && (s.fwd == MOE_FWD_MXFP8 || fwd_writes_wcodes(s));
   for (int i = 0; i < 4; ++i) L.off_wrows[i] = 0;
   if (L.wrows_saved) {
     const size_t Eh = (size_t)El * s.H, Ei = (size_t)El * s.I;
@@ -187,7 +201,7 @@ void layout(const moe_shape& s, Layout& L) {
     const size_t Rp = (size_t)L.Rp;
     // codes then scales of: dY' rows, W_down rows, dG|dU rows, [W_gate|W_up] rows,
     // A^T, (w dY')^T, Xp^T, (dG|dU)^T; then the padded offsets
-    // (the weights' row-wise codes live in saved in mxfp8 mode)
+    // (the weights' row-wise codes live in saved when the forward writes them)
     const size_t wsz = L.wrows_saved ? 0 : 1;
     const size_t sizes[17] = {R * H, R * H / 32, wsz * Ei * H, wsz * Ei * H / 32, R * 2 * I, R * 2 * I / 32,
                               wsz * Eh * 2 * I, wsz * Eh * 2 * I / 32, I * Rp, I * Rp / 32, H * Rp, H * Rp / 32,
@@ -442,6 +456,12 @@ int moe_fwd(const moe_shape* shape, const void* x, const void* xp, const int32_t
       FwdArgs k1 = a, k2 = a;
       k1.tiles = h.k1 == 320 ? tiles320 : tiles;
       k2.tiles = h.k2 == 320 ? tiles320 : tiles;
+      if (L.wrows_saved) {  // fp8_bwd: the GEMMs also write the weights' codes for moe_bwd
+        k2.q_wrows = at<uint8_t>(saved, L.off_wrows[0]);
+        k2.s_wrows = at<uint8_t>(saved, L.off_wrows[1]);
+        k1.q_wrows = at<uint8_t>(saved, L.off_wrows[2]);
+        k1.s_wrows = at<uint8_t>(saved, L.off_wrows[3]);
+      }
       e = h.k1 == 320 ? fw320::launch_fwd_gateup_bf16(k1, st) : fw256::launch_fwd_gateup_bf16(k1, st);
       if (e == hipSuccess)
         e = h.k2 == 320 ? fw320::launch_fwd_down_bf16(k2, st) : fw256::launch_fwd_down_bf16(k2, st);

@@ -151,6 +151,12 @@ struct FwdArgs {
   bf16_t* gu;             // [R_cap, 2I]  (g | u), or null: not kept
   bf16_t* a;              // [R_cap, I]
   bf16_t* yp;             // [R_cap, H]
+  // fp8_bwd: the row-wise MXFP8 codes of the weights for the backward, written by the
+  // GEMM that streams them (null: not written).  Gate/up: [W_gate | W_up] along I,
+  // [El*H, 2I] codes and [El*H, 2I/32] scales; down: W_down along H, [El*I, H] and
+  // [El*I, H/32].  Only experts with rows get codes.
+  uint8_t* q_wrows;
+  uint8_t* s_wrows;
 };
 // The bf16 forward GEMMs on the fused stream, one build per tile height (a.tiles holds
 // tiles of that height): 256 rows (gemm_fw256.hip) or 320 rows (gemm_fw320.hip).
@@ -226,7 +232,7 @@ struct MxArgs {
   int32_t* poff;                     // [El + 1] padded row offsets
   int Rp;                            // padded row capacity (multiple of kMxRowPad)
   int64_t R_cap;                     // row capacity of the row-wise activation buffers
-  bool w_ready;                      // q_wd / q_wg already hold the weights' codes (mxfp8 forward)
+  bool w_ready;                      // q_wd / q_wg hold the weights' codes (written by the forward)
 };
 inline int64_t mx_rp_cap(int64_t R_cap, int El) { return ceil_div(R_cap + (int64_t)(kMxRowPad - 1) * El, kMxRowPad) * kMxRowPad; }
 

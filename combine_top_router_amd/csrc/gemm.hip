@@ -200,6 +200,49 @@ struct LMx {
   }
 };
 
+// ---------------- fp8_bwd: the weights' row-wise codes from the forward's B stages ----------------
+// The bf16 forward streams every weight slice of an expert through the B stages of each
+// of that expert's row tiles, MN-major [BK][BN]: k-row r of step kt is weight row
+// kt * BK + r, chunk c its output columns 8c .. 8c + 7.  Row tile mt of n also writes
+// the row-wise MXFP8 codes of the steps kt with kt mod n = mt for the backward (blocks
+// of 32 along the output columns, the scale and rounding rule of k_mx_rows, so the
+// codes are the same bytes).
+// Thread t takes the chunk pairs t + NTHR i (16 columns each): the two lanes of a block
+// are adjacent, so its maximum takes one lane exchange; 16 lanes read one k-row's 512
+// bytes and write its 256 code bytes, 16 per lane.  put(r, c, codes, X) stores the
+// codes of chunks c, c + 1 (c even; the block's scale from the lanes with c % 4 = 0).
+template <class Put>
+__device__ __forceinline__ void quant_bstage(const bf16_t* Bs, int tid, Put&& put) {
+#pragma unroll 1
+  for (int it = 0; it < BK * BN / 16 / NTHR; ++it) {
+    const int g = it * NTHR + tid, r = g / (BN / 16), c = 2 * (g % (BN / 16));
+    const bf16_t* const row = Bs + r * BN;
+    const i32x4 u0 = *reinterpret_cast<const i32x4*>(row + (mnmaj_chunk(r, c) << 3));
+    const i32x4 u1 = *reinterpret_cast<const i32x4*>(row + (mnmaj_chunk(r, c + 1) << 3));
+    // the block maximum of |x| from the bf16 magnitudes (integer order is magnitude
+    // order; a NaN counts as 0, as fmaxf drops it)
+    uint32_t mb = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t w = (uint32_t)(q < 4 ? u0[q] : u1[q - 4]);
+      const uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
+      mb = max(mb, max(lo > 0x7f80u ? 0u : lo, hi > 0x7f80u ? 0u : hi));
+    }
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 1, 64));
+    const int X = mx_scale_exp(__uint_as_float(mb << 16));
+    auto f = [&](int q, int h) {
+      const uint32_t w = (uint32_t)(q < 4 ? u0[q] : u1[q - 4]);
+      return __uint_as_float(h ? w & 0xffff0000u : w << 16);
+    };
+    uint4 cw;
+    cw.x = e4m3_pack4(f(0, 0), f(0, 1), f(1, 0), f(1, 1), X);
+    cw.y = e4m3_pack4(f(2, 0), f(2, 1), f(3, 0), f(3, 1), X);
+    cw.z = e4m3_pack4(f(4, 0), f(4, 1), f(5, 0), f(5, 1), X);
+    cw.w = e4m3_pack4(f(6, 0), f(6, 1), f(7, 0), f(7, 1), X);
+    put(r, c, cw, X);
+  }
+}
+
 // ---------------- K1: gate/up + SwiGLU ----------------
 // B tile: gate columns 0..BN/2-1 and up columns BN/2..BN-1; compute wave wn takes the same
 // WCOLS / 2 intermediate columns of both (blocks ni < NI / 2 gate, the rest up), so G
@@ -218,13 +261,17 @@ struct LGateUp : RowLd {
 
 // MX: Xp rows (row-wise codes along H) against the transposed column-wise codes of
 // [W_gate | W_up] (rows n < I gate, I + n up; expert e's K range starts at e * H).
-template <bool MX>
+// QW (fp8_bwd, bf16 operands): the expert's row tiles also write the row-wise codes of
+// [W_gate | W_up] (quant_bstage).
+template <bool MX, bool QW = false>
 struct JGateUp {
   using Tile = RowTileInfo;
   using Ld = typename std::conditional<MX, LMx, LGateUp>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
   static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
+  static constexpr bool SIDE = QW;
+  static_assert(!(MX && QW), "the weight codes come from bf16 B stages");
   __device__ __forceinline__ static int ncol(int wn, int ni) {
     return (ni < NI / 2 ? 0 : BN / 2) + wn * (WCOLS / 2) + (ni % (NI / 2)) * 32;
   }
@@ -260,6 +307,22 @@ struct JGateUp {
     } else {
       setup_bf16(t, n0, p, pw, lane);
     }
+  }
+  // B chunk c: gate (c < BN / 16) or up column p.n0 + 8 (c % (BN / 16)), row e * H + h of the codes
+  __device__ __forceinline__ void side(const bf16_t* st, const Tile& p, int kt, int tid) const {
+    if (kt % p.t.nmt != p.t.mt) return;   // the expert's row tiles share the steps
+    const uint32_t I2 = 2u * (uint32_t)a.I;
+    uint8_t* const qb = a.q_wrows + ((size_t)p.t.e * a.H + (size_t)kt * BK) * I2;
+    uint8_t* const sb = a.s_wrows + ((size_t)p.t.e * a.H + (size_t)kt * BK) * (I2 / 32);
+    quant_bstage(st + A_ELEMS, tid, [&](int r, int c, uint4 w, int X) {
+      constexpr int HC = BN / 16;
+      const int col = p.n0 + (c % HC) * 8;
+      if (col < a.I) {
+        const uint32_t cc = (c < HC ? 0u : (uint32_t)a.I) + (uint32_t)col;
+        *reinterpret_cast<uint4*>(qb + (uint32_t)r * I2 + cc) = w;
+        if ((c & 3) == 0) sb[(uint32_t)r * (I2 / 32) + cc / 32] = (uint8_t)(X + 127);
+      }
+    });
   }
   __device__ __forceinline__ void setup_bf16(const RowTile& t, int n0, LGateUp& p, int pw, int lane) const {
     a_rows_kmaj(p.a, a.xp, a.x, a.row_src, a.k, a.H, t, pw, lane);
@@ -333,11 +396,11 @@ struct JGateUp {
   }
 };
 
-template <bool MX>
+template <bool MX, bool QW = false>
 __global__ __launch_bounds__(NTHR, 1) void k_fwd_gateup(FwdArgs a, MxFwdArgs m) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
-  JGateUp<MX> job{a, m, (int)ceil_div(a.I, BN / 2), scring};
+  JGateUp<MX, QW> job{a, m, (int)ceil_div(a.I, BN / 2), scring};
   run_stream(job, lds);
 }
 
@@ -357,13 +420,17 @@ struct LMnB : RowLd {
 
 // MX: A rows (row-wise codes along I) against the transposed column-wise codes of
 // W_down (row n = hidden column n; expert e's K range starts at e * I).
-template <bool MX>
+// QW (fp8_bwd, bf16 operands): the expert's row tiles also write the row-wise codes of
+// W_down along H (quant_bstage).
+template <bool MX, bool QW = false>
 struct JDown {
   using Tile = RowTileInfo;
   using Ld = typename std::conditional<MX, LMx, LMnB>::type;
   static constexpr bool A_KMAJ = true, B_KMAJ = MX;
   static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
   static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
+  static constexpr bool SIDE = QW;
+  static_assert(!(MX && QW), "the weight codes come from bf16 B stages");
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   FwdArgs a;
   MxFwdArgs m;
@@ -394,6 +461,20 @@ struct JDown {
     } else {
       setup_bf16(t, n0, p, pw, lane);
     }
+  }
+  // B chunk c: hidden columns p.n0 + 8c .., row e * I + i of the codes
+  __device__ __forceinline__ void side(const bf16_t* st, const Tile& p, int kt, int tid) const {
+    if (kt % p.t.nmt != p.t.mt) return;   // the expert's row tiles share the steps
+    const uint32_t H = (uint32_t)a.H;
+    uint8_t* const qb = a.q_wrows + ((size_t)p.t.e * a.I + (size_t)kt * BK) * H;
+    uint8_t* const sb = a.s_wrows + ((size_t)p.t.e * a.I + (size_t)kt * BK) * (H / 32);
+    quant_bstage(st + A_ELEMS, tid, [&](int r, int c, uint4 w, int X) {
+      const uint32_t col = (uint32_t)(p.n0 + c * 8);
+      if (col < H) {
+        *reinterpret_cast<uint4*>(qb + (uint32_t)r * H + col) = w;
+        if ((c & 3) == 0) sb[(uint32_t)r * (H / 32) + col / 32] = (uint8_t)(X + 127);
+      }
+    });
   }
   __device__ __forceinline__ void setup_bf16(const RowTile& t, int n0, LMnB& p, int pw, int lane) const {
     a_rows_kmaj(p.a, a.a, nullptr, nullptr, 1, a.I, t, pw, lane);
@@ -437,11 +518,11 @@ struct JDown {
   }
 };
 
-template <bool MX>
+template <bool MX, bool QW = false>
 __global__ __launch_bounds__(NTHR, 1) void k_fwd_down(FwdArgs a, MxFwdArgs m) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) uint8_t scring[MX ? NSTAGE * MX_SC_SLOT : 4];
-  JDown<MX> job{a, m, (int)ceil_div(a.H, BN), scring};
+  JDown<MX, QW> job{a, m, (int)ceil_div(a.H, BN), scring};
   run_stream(job, lds);
 }
 
@@ -480,6 +561,7 @@ struct JDa {
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, TRANS = false, EPI_LDS = true;
   static constexpr bool NSPLIT = !MX;   // column halves of a last round (Sched)
+  static constexpr bool SIDE = false;   // no extra per-step work
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -603,6 +685,7 @@ struct JDx {
   static constexpr bool A_KMAJ = true, B_KMAJ = true;
   static constexpr bool DYN = false, TRANS = true, EPI_LDS = true;
   static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
+  static constexpr bool SIDE = false;   // no extra per-step work
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
   BwdArgs a;
   MxArgs m;
@@ -753,6 +836,7 @@ struct JWgrad {
   // the accumulators hold C^T; the epilogue writes them as bf16 row bands (band_store)
   static constexpr bool DYN = true, TRANS = true, EPI_LDS = true;
   static constexpr bool NSPLIT = false;   // column halves of a last round (Sched)
+  static constexpr bool SIDE = false;   // no extra per-step work
   __device__ __forceinline__ bool dynamic() const { return sload(a.order + a.El) != 0; }
   __device__ __forceinline__ int32_t* counter() const { return a.order + a.El + 1 + WHICH; }
   __device__ __forceinline__ static int ncol(int wn, int ni) { return wn * WCOLS + ni * 32; }
@@ -907,16 +991,18 @@ namespace MOE_FW_CAT(fw, MOE_GEMM_FW) {
 hipError_t launch_fwd_gateup_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
-  MOE_LAUNCH("fwd_gateup", k_fwd_gateup<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2))),
-             dim3(NTHR), 0, st, a, m);
+  const dim3 grid(grid_for((int64_t)a.max_tiles * ceil_div(a.I, BN / 2)));
+  if (a.q_wrows) MOE_LAUNCH("fwd_gateup", (k_fwd_gateup<false, true>), grid, dim3(NTHR), 0, st, a, m);
+  else MOE_LAUNCH("fwd_gateup", k_fwd_gateup<false>, grid, dim3(NTHR), 0, st, a, m);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_down_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.max_tiles == 0) return hipSuccess;
   MxFwdArgs m{};
-  MOE_LAUNCH("fwd_down", k_fwd_down<false>, dim3(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN))), dim3(NTHR), 0,
-             st, a, m);
+  const dim3 grid(grid_for((int64_t)a.max_tiles * ceil_div(a.H, BN)));
+  if (a.q_wrows) MOE_LAUNCH("fwd_down", (k_fwd_down<false, true>), grid, dim3(NTHR), 0, st, a, m);
+  else MOE_LAUNCH("fwd_down", k_fwd_down<false>, grid, dim3(NTHR), 0, st, a, m);
   return hipGetLastError();
 }
 
@@ -1056,7 +1142,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
 }
 
 // MXFP8 backward (every GEMM on the 256-row fused stream; a.tiles holds 256-row tiles).
-// Order: quantise the weights row-wise (unless the MXFP8 forward left
+// Order: quantise the weights row-wise (unless the forward left
 // their codes in the saved buffer), and dY' row-wise together with
 // w * dY' column-wise per expert; B1 (fp8) writes dG|dU (bf16); quantise dG|dU row-wise
 // and column-wise in one pass, A and Xp column-wise; then B2, B3, B4 on fp8 operands.

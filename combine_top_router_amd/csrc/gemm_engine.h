@@ -464,6 +464,10 @@ __device__ __forceinline__ void fused_stream(const J& job, bf16_t* lds, S sc, in
         lcur.issue(0, st, cs ^ 1, gpar, [&] { lcur.fetch(1, gpar ^ 1); });
         gpar ^= 1;
       }
+      // extra work of every wave on the position's stage, ahead of its MFMAs so that its
+      // stores are on their way long before the next position's wait
+      if constexpr (J::SIDE)
+        if (kc < cur.nk) job.side(lds + cs * STAGE_ELEMS, cur, kc, wv * 64 + lane);
       if (kc < cur.nk && wr.nblk > 0) job.compute(lds + cs * STAGE_ELEMS, cs, acc, lane, wr, wn);
       if (sc.dyn && kc == 0 && wv == 0) {   // published after the MFMAs, read after a barrier
         const int n = uni(grabbed);
@@ -594,6 +598,7 @@ __device__ __forceinline__ void epilogue_rows(float* stage, const Acc& acc, cons
 // the expert-major order of the tile table (k_tile_table).  Scalar loads only.
 struct RowTile {
   int e, rs, cnt, nt;
+  int mt, nmt;   // the tile's index among its expert's row tiles, and their number
 };
 __device__ __forceinline__ void row_tile(const int32_t* tiles, const int32_t* offsets, int v, int NT, RowTile& t) {
   const int q = uni(v / NT);
@@ -603,6 +608,8 @@ __device__ __forceinline__ void row_tile(const int32_t* tiles, const int32_t* of
   const int mt = uni(local % ent[2]);
   t.nt = uni(local / ent[2]);
   const int o0 = sload(offsets + t.e), o1 = sload(offsets + t.e + 1);
+  t.mt = mt;
+  t.nmt = uni(ent[2]);
   t.rs = uni(o0 + mt * BM);
   t.cnt = uni(min(BM, o1 - t.rs));
 }

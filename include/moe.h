@@ -96,8 +96,11 @@ const char* moe_last_error(void);
 
 /* Byte sizes of the two caller-owned workspaces for `shape`:
  *  saved   -- written by moe_fwd, read by moe_bwd (the saved G, U and A rows; in
- *             mxfp8 mode, fwd and bwd both MOE_*_MXFP8, also the backward's row-wise
- *             MXFP8 codes of the weights, which the forward's weight passes produce);
+ *             mxfp8 mode also the backward's row-wise MXFP8 codes of the weights,
+ *             which the forward's weight passes produce; in fp8_bwd mode the same
+ *             codes written by the forward's bf16 GEMMs from the weight tiles they
+ *             stream, when the expected rows per expert fill at least three row
+ *             tiles of each; else the backward quantises the weights itself);
  *  scratch -- temporary space of moe_dispatch, moe_fwd, moe_bwd, moe_router_fwd and
  *             moe_router_bwd; its contents do not need to survive between calls.
  * Both pointers must be non-NULL.  Returns MOE_EINVAL for an invalid shape.  With
@@ -180,7 +183,7 @@ int moe_combine(const moe_shape* shape, const void* yp, const int32_t* row_of, v
  * backward): moe_fwd keeps g, u, a only in scratch and moe_bwd recomputes them from the
  * same inputs with the same gate/up GEMM (in the forward's precision) before the backward
  * GEMMs, so `saved` may be NULL in both calls and every output is bit-identical to
- * recompute = 0.  In mxfp8 mode the backward then quantises its weights itself. */
+ * recompute = 0.  With the MXFP8 backward it then quantises its weights itself. */
 int moe_bwd(const moe_shape* shape, const void* dy, const void* x, const void* xp,
             const int32_t* offsets, const int32_t* row_src, const int32_t* row_of,
             const float* topk_w, const void* w_gate, const void* w_up, const void* w_down,

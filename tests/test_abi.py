@@ -109,6 +109,15 @@ def test_workspace_sizes_grow_with_the_layer():
     wcodes = 128 * 3 * 2048 * 768 * (1 + 1 / 32)
     assert L.moe_workspace_bytes(_shape(L, **mx))[0] >= big[0] + wcodes
     assert L.moe_workspace_bytes(_shape(L, **mx, recompute=1))[0] == 0
+    # fp8_bwd: the forward writes the weight codes only where an expert's rows fill three
+    # or more row tiles (the 235B-A22B share: about 1024 rows), not at 30B (about 256 rows)
+    fp8 = dict(mx, fwd=0)
+    assert L.moe_workspace_bytes(_shape(L, **fp8))[0] == big[0]
+    share = dict(T=16384, H=4096, I=1536, E=128, k=8, e_local=16)
+    plain = L.moe_workspace_bytes(_shape(L, **share))
+    fused = L.moe_workspace_bytes(_shape(L, **share, bwd=1))
+    assert fused[0] >= plain[0] + 16 * 3 * 4096 * 1536 * (1 + 1 / 32)
+    assert L.moe_workspace_bytes(_shape(L, **share, bwd=1, recompute=1))[0] == 0
 
 
 def test_quantizer_arguments_are_checked_before_launch():
