@@ -162,6 +162,9 @@ SMALL_MX = {
     "ragged_mx": wl.MoeConfig("ragged_mx", 700, 256, 192, 6, 2, 0, 6, 8, bwd="mxfp8"),
     "ragged_mx_share": wl.MoeConfig("ragged_mx_share", 500, 384, 320, 10, 3, 4, 5, 9, bwd="mxfp8"),
     "skew_mx": wl.MoeConfig("skew_mx", 1024, 512, 384, 64, 4, 0, 64, 10, routing="zipf", bwd="mxfp8"),
+    # about 1000 rows per expert (four or more row tiles): the forward GEMMs write the
+    # weights' codes for the backward; H = 384 leaves the down GEMM a half-empty column tile
+    "deep_mx_share": wl.MoeConfig("deep_mx_share", 2400, 384, 192, 7, 3, 1, 5, 11, bwd="mxfp8"),
 }
 
 
